@@ -1,0 +1,165 @@
+/*
+ * stca.h -- C ABI of libstca: the Stacked Target Cross Attention (STCA) forward pass
+ * on AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * Method (web pages on the STCA paper, "Make It Long, Keep It Fast: End-to-End
+ * 10k-Sequence Modeling at Billion Scale on Douyin", WWW'26, arXiv 2511.06077):
+ *   eq. (1)  SwiGLUFFN(x) = ((x W_u) * SiLU(x W_v)) W_o            (W_u, W_v: d x rd, W_o: rd x d;
+ *            the three-matrix reading of the review page, section 2.2; no biases)
+ *   eq. (2)  X~(i) = LN(SwiGLUFFN(i)(X))                  per history token, every layer from raw X
+ *   eq. (3)  q(1)  = LN(SwiGLUFFN(1)(x_t))
+ *   eq. (13) u_j = (q W_Q,j) W_K,j^T,  alpha_j = softmax(u_j X~^T / sqrt(d_h)),  o_j = (alpha_j X~) W_V,j
+ *            (the reordered form of the single-query cross attention of eqs. (4)-(5), (12))
+ *   eq. (6)  o(i) = [o_1 || ... || o_h] W_O
+ *   eq. (7)  q(i+1) = SwiGLUFFN(i+1)([o(1) || ... || o(i) || x_t] W_C(i+1)),  W_C(i+1): (i+1)d x d
+ *   eq. (8)  Z = [o(1); ...; o(M)]  per target
+ * Request level batching (section 2.2 of the same notes): the targets of one user share that
+ * user's history, which is encoded once; users are ragged segments described by offset arrays.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all memory; the library
+ *     allocates nothing, keeps no global mutable state and is reentrant.  Device pointers must be
+ *     16-byte aligned (STCA_E_ALIGN otherwise).
+ *   - Matrices are row-major.  Storage type of X, x_t, X~ and of every weight matrix is
+ *     dims->dtype (fp32 or bf16); LayerNorm gamma/beta, q, o and Z are always fp32.  All
+ *     arithmetic accumulates in fp32.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).  Outputs are
+ *     valid once the stream has reached the call's end.  No call synchronises the device.
+ *   - Every argument error the host can see is returned as a negative stca_status BEFORE any
+ *     work is enqueued.  A failed launch returns STCA_E_HIP (stca_last_error() has the detail).
+ *   - Offsets are caller contract, not checked on the device: hist_off/tgt_off start at 0, are
+ *     nondecreasing and end at total_L/total_T.  A user with no targets is allowed; a user with
+ *     an empty history (softmax over no tokens is undefined) gets NaN outputs for its targets.
+ */
+#ifndef STCA_H
+#define STCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STCA_MAX_M 8 /* most stacked layers a call accepts (the pages stack up to 4) */
+
+#if defined(__GNUC__)
+#define STCA_API __attribute__((visibility("default")))
+#else
+#define STCA_API
+#endif
+
+typedef enum {
+  STCA_OK = 0,
+  STCA_E_ARG = -1,       /* NULL pointer, negative size, bad layer index, ... */
+  STCA_E_DIMS = -2,      /* unsupported d / h / r / M / dtype combination */
+  STCA_E_WORKSPACE = -3, /* workspace NULL or smaller than the *_workspace_size result */
+  STCA_E_ALIGN = -4,     /* a device pointer is not 16-byte aligned */
+  STCA_E_HIP = -5        /* a HIP runtime call or kernel launch failed */
+} stca_status;
+
+typedef enum { STCA_F32 = 0, STCA_BF16 = 1 } stca_dtype;
+
+/* Model sizes.  Supported: d in {64, 128, 256, 512}; h divides d; 1 <= r <= 8; 1 <= M <= STCA_MAX_M.
+ * dtype STCA_BF16 runs the MFMA path (bf16 storage, fp32 accumulation); STCA_F32 runs the fp32
+ * debug path (fp32 everywhere, plain vector ALU). */
+typedef struct {
+  int32_t d, h, M, r;
+  int32_t dtype;      /* stca_dtype */
+  float ln_eps;       /* LayerNorm epsilon (biased variance); must be > 0 */
+  int32_t query_ln;   /* 1: apply the layer's LayerNorm after the FFN of eq. (7); 0: as printed */
+  int32_t attn_chunk; /* history tokens per attention work item, multiple of 32; 0 = automatic */
+} stca_dims;
+
+/* One SwiGLU FFN + LayerNorm block (eqs. (1)-(3), (7)).  Wu, Wv: d x rd; Wo: rd x d (dtype);
+ * gamma, beta: d floats.  gamma/beta may be NULL only where no LayerNorm is applied. */
+typedef struct {
+  const void *Wu, *Wv, *Wo;
+  const float *gamma, *beta;
+} stca_ffn;
+
+/* All parameters of an M-layer stack; index i = 0..M-1 is the pages' layer i+1.
+ *   hist[i]  : FFN + LN encoding the history for layer i (eq. (2)).
+ *   query[i] : FFN (+LN) of the query path: eq. (3) for i = 0, eq. (7) for i >= 1.  The pages use
+ *              the same symbol SwiGLUFFN(i) for both; pass the hist[i] pointers for that reading.
+ *   WQ, WK, WV, WO[i] : d x d; head j owns columns j*d_h .. (j+1)*d_h - 1 of WQ, WK, WV.
+ *   WC[i]    : (i+1)d x d for i >= 1, row blocks ordered [o(1); ...; o(i); x_t]; WC[0] unused. */
+typedef struct {
+  stca_ffn hist[STCA_MAX_M];
+  stca_ffn query[STCA_MAX_M];
+  const void *WQ[STCA_MAX_M], *WK[STCA_MAX_M], *WV[STCA_MAX_M], *WO[STCA_MAX_M];
+  const void *WC[STCA_MAX_M];
+} stca_weights;
+
+/* A ragged request-level batch: user u owns history rows hist_off[u] .. hist_off[u+1]-1 and
+ * target rows tgt_off[u] .. tgt_off[u+1]-1 (the segment index tensor of ragged target attention). */
+typedef struct {
+  int32_t n_users;
+  const int64_t *hist_off; /* n_users + 1 entries (device) */
+  const int64_t *tgt_off;  /* n_users + 1 entries (device) */
+  int64_t total_L;         /* [host] hist_off[n_users] */
+  int64_t total_T;         /* [host] tgt_off[n_users] */
+  int64_t max_L;           /* [host] largest per-user history length (an upper bound is fine) */
+  int64_t max_T;           /* [host] largest per-user target count (an upper bound is fine) */
+} stca_batch;
+
+/* Workspace sizes in bytes (host only, no device work).  Return STCA_OK or an argument error. */
+STCA_API int stca_encode_workspace_size(const stca_dims *dims, int64_t n_rows, size_t *bytes);
+STCA_API int stca_attend_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
+STCA_API int stca_forward_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
+
+/* eq. (2): Xt[n_rows x d] = LN(SwiGLUFFN(X[n_rows x d])) with the weights of `ffn`
+ * (gamma/beta required).  X and Xt are dims->dtype.  Rows are independent tokens. */
+STCA_API int stca_encode(const stca_dims *dims, const stca_ffn *ffn, int64_t n_rows, const void *X, void *Xt,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* eqs. (13), (6) for layer `layer` (0-based): given the layer's encoded history Xt
+ * (total_L x d, dims->dtype) and the queries q (total_T x d, fp32), writes
+ * o (total_T x d, fp32): each target attends only to its own user's history segment. */
+STCA_API int stca_attend(const stca_dims *dims, const stca_weights *w, int32_t layer, const stca_batch *batch,
+                const void *Xt, const float *q, float *o, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* eqs. (2)-(8): the whole stack.  X: total_L x d, xt: total_T x d (dims->dtype);
+ * Z: total_T x M x d fp32, Z[t][i] = o(i+1) of target t. */
+STCA_API int stca_forward(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
+                 const void *xt, float *Z, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- per-kernel timing (HIP events on the call's stream) ---------------------------------- */
+typedef struct stca_profiler stca_profiler; /* opaque, host-side; not thread-safe */
+
+enum {
+  STCA_PHASE_PACK = 0,   /* weight re-layout for the MFMA encode */
+  STCA_PHASE_ENCODE,     /* history encode, eq. (2) (one launch per layer) */
+  STCA_PHASE_QUERY,      /* query path, eqs. (3), (7) */
+  STCA_PHASE_UPROJ,      /* u = (q W_Q) W_K^T, eq. (13) */
+  STCA_PHASE_ATTEND,     /* split-L attention over the history (one launch per layer) */
+  STCA_PHASE_COMBINE,    /* merge of split-L partial softmax states */
+  STCA_PHASE_PROJECT,    /* (alpha X~) W_V and W_O, eqs. (13), (6) */
+  STCA_N_PHASES
+};
+
+typedef struct {
+  double ms[STCA_N_PHASES];      /* summed elapsed milliseconds per phase since the last reset */
+  int64_t launches[STCA_N_PHASES];
+} stca_profile_report;
+
+STCA_API int stca_profiler_create(stca_profiler **out);
+STCA_API int stca_profiler_destroy(stca_profiler *p);
+STCA_API int stca_profiler_reset(stca_profiler *p);
+/* Waits for the recorded events to complete, then sums them (host blocks; the device is not synced). */
+STCA_API int stca_profiler_read(stca_profiler *p, stca_profile_report *out);
+/* stca_forward with an event pair recorded around every phase launch (prof may be NULL). */
+STCA_API int stca_forward_profiled(const stca_dims *dims, const stca_weights *w, const stca_batch *batch,
+                          const void *X, const void *xt, float *Z, void *workspace,
+                          size_t workspace_bytes, void *stream, stca_profiler *prof);
+
+/* ---- diagnostics ---------------------------------------------------------------------------- */
+STCA_API const char *stca_status_string(int status);
+STCA_API const char *stca_last_error(void); /* thread-local detail of the last failure in this thread */
+STCA_API const char *stca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STCA_H */

@@ -1,0 +1,303 @@
+"""ctypes binding of libstca (include/stca.h), same call names, argument marshalling only.
+
+Every step of the STCA forward runs in the HIP library; this module only lays inputs out in
+device memory (through PyTorch tensors), fills the C structs and checks status codes.  If the
+library has not been built it raises at import time: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstca.so")
+MAX_M = 8
+
+F32, BF16 = 0, 1
+(PHASE_PACK, PHASE_ENCODE, PHASE_QUERY, PHASE_UPROJ, PHASE_ATTEND, PHASE_COMBINE, PHASE_PROJECT) = range(7)
+PHASE_NAMES = ["pack", "encode", "query", "uproj", "attend", "combine", "project"]
+N_PHASES = 7
+
+EXPORTS = [
+    "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
+    "stca_encode", "stca_attend", "stca_forward", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
+    "stca_last_error", "stca_version",
+]
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("d", c_int32), ("h", c_int32), ("M", c_int32), ("r", c_int32), ("dtype", c_int32),
+                ("ln_eps", c_float), ("query_ln", c_int32), ("attn_chunk", c_int32)]
+
+
+class Ffn(ctypes.Structure):
+    _fields_ = [("Wu", c_void_p), ("Wv", c_void_p), ("Wo", c_void_p), ("gamma", c_void_p), ("beta", c_void_p)]
+
+
+class WeightsC(ctypes.Structure):
+    _fields_ = [("hist", Ffn * MAX_M), ("query", Ffn * MAX_M), ("WQ", c_void_p * MAX_M),
+                ("WK", c_void_p * MAX_M), ("WV", c_void_p * MAX_M), ("WO", c_void_p * MAX_M),
+                ("WC", c_void_p * MAX_M)]
+
+
+class BatchC(ctypes.Structure):
+    _fields_ = [("n_users", c_int32), ("hist_off", c_void_p), ("tgt_off", c_void_p), ("total_L", c_int64),
+                ("total_T", c_int64), ("max_L", c_int64), ("max_T", c_int64)]
+
+
+class ProfileReport(ctypes.Structure):
+    _fields_ = [("ms", c_double * N_PHASES), ("launches", c_int64 * N_PHASES)]
+
+
+class StcaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status}): {last_error()}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libstca.so not built at {LIB_PATH}; run `python -m target_cross_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    sig = {
+        "stca_encode_workspace_size": [P, c_int64, POINTER(c_size_t)],
+        "stca_attend_workspace_size": [P, P, POINTER(c_size_t)],
+        "stca_forward_workspace_size": [P, P, POINTER(c_size_t)],
+        "stca_encode": [P, P, c_int64, P, P, P, c_size_t, P],
+        "stca_attend": [P, P, c_int32, P, P, P, P, P, c_size_t, P],
+        "stca_forward": [P, P, P, P, P, P, P, c_size_t, P],
+        "stca_forward_profiled": [P, P, P, P, P, P, P, c_size_t, P, P],
+        "stca_profiler_create": [POINTER(c_void_p)],
+        "stca_profiler_destroy": [P],
+        "stca_profiler_reset": [P],
+        "stca_profiler_read": [P, P],
+        "stca_status_string": [c_int],
+        "stca_last_error": [],
+        "stca_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = c_char_p if name in ("stca_status_string", "stca_last_error", "stca_version") else c_int
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.stca_status_string(status).decode()
+
+
+def last_error() -> str:
+    return LIB.stca_last_error().decode()
+
+
+def version() -> str:
+    return LIB.stca_version().decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise StcaError(status, where)
+
+
+def _ref(s):
+    return ctypes.byref(s)
+
+
+# ----------------------------------------------------------------------------------------------
+# plain structs
+# ----------------------------------------------------------------------------------------------
+def make_dims(d: int, h: int, M: int, r: int, dtype: str = "bf16", ln_eps: float = 1e-5,
+              query_ln: bool = False, attn_chunk: int = 0) -> Dims:
+    return Dims(d, h, M, r, BF16 if dtype == "bf16" else F32, ln_eps, int(bool(query_ln)), attn_chunk)
+
+
+def dims_for(cfg, **kw) -> Dims:
+    """Dims of a ``stca_inputs.Config``."""
+    return make_dims(cfg.d, cfg.h, cfg.M, cfg.r, cfg.dtype, **kw)
+
+
+def batch_struct(n_users: int, hist_off, tgt_off, total_L: int, total_T: int, max_L: int, max_T: int) -> BatchC:
+    return BatchC(n_users, _ptr(hist_off), _ptr(tgt_off), total_L, total_T, max_L, max_T)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ----------------------------------------------------------------------------------------------
+# device-resident inputs
+# ----------------------------------------------------------------------------------------------
+def to_device(a: np.ndarray, dtype: str, device):
+    """Host array -> device tensor in the storage type: uint16 bf16 patterns or float32."""
+    import torch
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            from stca_inputs import bf16_bits
+            a = bf16_bits(a)
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class DeviceWeights:
+    """``stca_inputs.Weights`` uploaded in the storage type, plus the filled ``stca_weights`` struct."""
+
+    def __init__(self, W, dtype: str, device="cuda"):
+        import torch
+        self.keep = []
+        self.c = WeightsC()
+        M = len(W.Wu)
+        cache = {}
+
+        def up(a, store=dtype):
+            if a is None:
+                return None
+            key = (id(a), store)
+            if key not in cache:
+                t = to_device(a, store, device) if store != "f32ln" else \
+                    torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+                cache[key] = t
+                self.keep.append(t)
+            return cache[key].data_ptr()
+
+        for i in range(M):
+            self.c.hist[i] = Ffn(up(W.Wu[i]), up(W.Wv[i]), up(W.Wo[i]), up(W.gamma[i], "f32ln"),
+                                 up(W.beta[i], "f32ln"))
+            self.c.query[i] = Ffn(up(W.qWu[i]), up(W.qWv[i]), up(W.qWo[i]), up(W.qgamma[i], "f32ln"),
+                                  up(W.qbeta[i], "f32ln"))
+            self.c.WQ[i] = up(W.WQ[i])
+            self.c.WK[i] = up(W.WK[i])
+            self.c.WV[i] = up(W.WV[i])
+            self.c.WO[i] = up(W.WO[i])
+            self.c.WC[i] = up(W.WC[i]) if W.WC[i] is not None else None
+
+
+class DeviceBatch:
+    """A ``stca_inputs.Inputs`` batch uploaded to the device, plus the ``stca_batch`` struct."""
+
+    def __init__(self, inp, device="cuda"):
+        import torch
+        self.inp = inp
+        dt = inp.cfg.dtype
+        self.X = to_device(inp.X, dt, device) if inp.X.size else torch.empty(0, device=device)
+        self.xt = to_device(inp.xt, dt, device) if inp.xt.size else torch.empty(0, device=device)
+        self.hist_off = torch.from_numpy(inp.hist_off.astype(np.int64)).to(device)
+        self.tgt_off = torch.from_numpy(inp.tgt_off.astype(np.int64)).to(device)
+        self.total_L = int(inp.hist_off[-1])
+        self.total_T = int(inp.tgt_off[-1])
+        self.max_L = int(inp.L.max()) if len(inp.L) else 0
+        self.max_T = int(inp.m.max()) if len(inp.m) else 0
+        self.c = batch_struct(inp.n_users, self.hist_off, self.tgt_off, self.total_L, self.total_T,
+                              self.max_L, self.max_T)
+
+
+# ----------------------------------------------------------------------------------------------
+# calls
+# ----------------------------------------------------------------------------------------------
+def encode_workspace_size(dims: Dims, n_rows: int) -> int:
+    n = c_size_t(0)
+    _check(LIB.stca_encode_workspace_size(_ref(dims), n_rows, ctypes.byref(n)), "stca_encode_workspace_size")
+    return n.value
+
+
+def attend_workspace_size(dims: Dims, batch: BatchC) -> int:
+    n = c_size_t(0)
+    _check(LIB.stca_attend_workspace_size(_ref(dims), _ref(batch), ctypes.byref(n)), "stca_attend_workspace_size")
+    return n.value
+
+
+def forward_workspace_size(dims: Dims, batch: BatchC) -> int:
+    n = c_size_t(0)
+    _check(LIB.stca_forward_workspace_size(_ref(dims), _ref(batch), ctypes.byref(n)),
+           "stca_forward_workspace_size")
+    return n.value
+
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def stca_encode(dims: Dims, ffn: Ffn, X, Xt=None, ws=None, stream=None):
+    """eq. (2) for every row of X (device tensor, storage dtype).  Returns Xt."""
+    import torch
+    n = X.shape[0]
+    if Xt is None:
+        Xt = torch.empty_like(X)
+    if ws is None:
+        ws = workspace(encode_workspace_size(dims, n), X.device)
+    _check(LIB.stca_encode(_ref(dims), _ref(ffn), n, _ptr(X), _ptr(Xt), _ptr(ws), ws.numel(), _stream(stream)),
+           "stca_encode")
+    return Xt
+
+
+def stca_attend(dims: Dims, w: DeviceWeights, layer: int, batch: DeviceBatch, Xt, q, o=None, ws=None, stream=None):
+    """eqs. (13), (6) for one layer.  q: total_T x d float32 (device).  Returns o (total_T x d)."""
+    import torch
+    if o is None:
+        o = torch.empty((batch.total_T, dims.d), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(attend_workspace_size(dims, batch.c), q.device)
+    _check(LIB.stca_attend(_ref(dims), _ref(w.c), layer, _ref(batch.c), _ptr(Xt), _ptr(q), _ptr(o), _ptr(ws),
+                           ws.numel(), _stream(stream)), "stca_attend")
+    return o
+
+
+def stca_forward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, Z=None, ws=None, stream=None, profiler=None):
+    """eqs. (2)-(8) for the whole batch.  Returns Z (total_T x M x d float32)."""
+    import torch
+    if Z is None:
+        Z = torch.empty((batch.total_T, dims.M, dims.d), dtype=torch.float32, device=batch.X.device)
+    if ws is None:
+        ws = workspace(forward_workspace_size(dims, batch.c), batch.X.device)
+    if profiler is None:
+        st = LIB.stca_forward(_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(Z),
+                              _ptr(ws), ws.numel(), _stream(stream))
+    else:
+        st = LIB.stca_forward_profiled(_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt),
+                                       _ptr(Z), _ptr(ws), ws.numel(), _stream(stream), profiler.handle)
+    _check(st, "stca_forward")
+    return Z
+
+
+class Profiler:
+    """Per-phase HIP-event timing of stca_forward_profiled calls."""
+
+    def __init__(self):
+        h = c_void_p()
+        _check(LIB.stca_profiler_create(ctypes.byref(h)), "stca_profiler_create")
+        self.handle = h
+
+    def reset(self):
+        _check(LIB.stca_profiler_reset(self.handle), "stca_profiler_reset")
+
+    def read(self) -> dict:
+        rep = ProfileReport()
+        _check(LIB.stca_profiler_read(self.handle, _ref(rep)), "stca_profiler_read")
+        return {PHASE_NAMES[i]: (rep.ms[i], rep.launches[i]) for i in range(N_PHASES)}
+
+    def close(self):
+        if self.handle:
+            LIB.stca_profiler_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,659 @@
+// libstca C ABI: argument checks, workspace layout, launch sequence.  See include/stca.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/stca.h"
+#include "internal.hpp"
+
+using namespace stca;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+#define HIP_TRY(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(STCA_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_dims(const stca_dims *dm) {
+  if (!dm) return fail(STCA_E_ARG, "dims is NULL");
+  const int d = dm->d, h = dm->h;
+  if (!(d == 64 || d == 128 || d == 256 || d == 512)) return fail(STCA_E_DIMS, "d=%d not in {64,128,256,512}", d);
+  if (h <= 0 || d % h != 0) return fail(STCA_E_DIMS, "h=%d must be positive and divide d=%d", h, d);
+  if (dm->r < 1 || dm->r > 8) return fail(STCA_E_DIMS, "r=%d not in [1,8]", dm->r);
+  if (dm->M < 1 || dm->M > STCA_MAX_M) return fail(STCA_E_DIMS, "M=%d not in [1,%d]", dm->M, STCA_MAX_M);
+  if (dm->dtype != STCA_F32 && dm->dtype != STCA_BF16) return fail(STCA_E_DIMS, "dtype=%d unknown", dm->dtype);
+  if (!(dm->ln_eps > 0.f)) return fail(STCA_E_DIMS, "ln_eps must be > 0");
+  if (dm->attn_chunk < 0 || dm->attn_chunk % 32 != 0)
+    return fail(STCA_E_DIMS, "attn_chunk=%d must be 0 or a positive multiple of 32", dm->attn_chunk);
+  return STCA_OK;
+}
+
+int check_batch(const stca_batch *b) {
+  if (!b) return fail(STCA_E_ARG, "batch is NULL");
+  if (b->n_users < 0) return fail(STCA_E_ARG, "n_users < 0");
+  if (b->total_L < 0 || b->total_T < 0 || b->max_L < 0 || b->max_T < 0)
+    return fail(STCA_E_ARG, "negative batch size");
+  if (b->total_L > 0 && b->n_users == 0) return fail(STCA_E_ARG, "total_L > 0 with no users");
+  if (b->total_T > 0 && b->n_users == 0) return fail(STCA_E_ARG, "total_T > 0 with no users");
+  if (b->n_users > 0 && (!b->hist_off || !b->tgt_off)) return fail(STCA_E_ARG, "offsets are NULL");
+  if (b->max_L > b->total_L || b->max_T > b->total_T) return fail(STCA_E_ARG, "max_L/max_T exceed totals");
+  if (b->n_users > 0 && b->total_L > 0 && b->max_L * (int64_t)b->n_users < b->total_L)
+    return fail(STCA_E_ARG, "max_L * n_users < total_L: max_L is not an upper bound");
+  if (b->n_users > 0 && b->total_T > 0 && b->max_T * (int64_t)b->n_users < b->total_T)
+    return fail(STCA_E_ARG, "max_T * n_users < total_T: max_T is not an upper bound");
+  if (!aligned16(b->hist_off) || !aligned16(b->tgt_off)) return fail(STCA_E_ALIGN, "offsets not 16-byte aligned");
+  return STCA_OK;
+}
+
+int check_ffn(const stca_ffn *f, bool need_ln, const char *what) {
+  if (!f) return fail(STCA_E_ARG, "%s: ffn is NULL", what);
+  if (!f->Wu || !f->Wv || !f->Wo) return fail(STCA_E_ARG, "%s: W_u/W_v/W_o NULL", what);
+  if (need_ln && (!f->gamma || !f->beta)) return fail(STCA_E_ARG, "%s: LayerNorm gamma/beta NULL", what);
+  if (!aligned16(f->Wu) || !aligned16(f->Wv) || !aligned16(f->Wo) || (f->gamma && !aligned16(f->gamma)) ||
+      (f->beta && !aligned16(f->beta)))
+    return fail(STCA_E_ALIGN, "%s: weights not 16-byte aligned", what);
+  return STCA_OK;
+}
+
+int check_layer_weights(const stca_dims *dm, const stca_weights *w, int i) {
+  if (!w->WQ[i] || !w->WK[i] || !w->WV[i] || !w->WO[i]) return fail(STCA_E_ARG, "layer %d: W_Q/W_K/W_V/W_O NULL", i);
+  if (!aligned16(w->WQ[i]) || !aligned16(w->WK[i]) || !aligned16(w->WV[i]) || !aligned16(w->WO[i]))
+    return fail(STCA_E_ALIGN, "layer %d: attention weights not 16-byte aligned", i);
+  (void)dm;
+  return STCA_OK;
+}
+
+int check_weights(const stca_dims *dm, const stca_weights *w) {
+  if (!w) return fail(STCA_E_ARG, "weights are NULL");
+  for (int i = 0; i < dm->M; ++i) {
+    int st;
+    if ((st = check_ffn(&w->hist[i], true, "hist")) != STCA_OK) return st;
+    const bool q_ln = (i == 0) || dm->query_ln;
+    if ((st = check_ffn(&w->query[i], q_ln, "query")) != STCA_OK) return st;
+    if ((st = check_layer_weights(dm, w, i)) != STCA_OK) return st;
+    if (i >= 1) {
+      if (!w->WC[i]) return fail(STCA_E_ARG, "layer %d: W_C NULL", i);
+      if (!aligned16(w->WC[i])) return fail(STCA_E_ALIGN, "layer %d: W_C not aligned", i);
+    }
+  }
+  return STCA_OK;
+}
+
+// ---- attention plan -------------------------------------------------------------------------
+int auto_chunk(const stca_dims *dm, const stca_batch *b) {
+  if (dm->attn_chunk > 0) return dm->attn_chunk;
+  // Aim for >= ~2 work items per workgroup slot of the chip, but keep chunks long enough
+  // that the partial-state traffic stays small next to the history bytes.
+  const int64_t groups = std::max<int64_t>(1, (b->max_T * dm->h + kRowsPerGroup - 1) / kRowsPerGroup);
+  const int64_t target_items = 2048;
+  int64_t c = (b->total_L * groups + target_items - 1) / target_items;
+  c = std::max<int64_t>(c, 512);
+  c = std::min<int64_t>(c, std::max<int64_t>(b->max_L, 32));
+  c = (c + 31) / 32 * 32;
+  return (int)std::min<int64_t>(c, 1 << 30);
+}
+
+AttnPlan make_plan(const stca_dims *dm, const stca_batch *b) {
+  AttnPlan p;
+  p.n_users = b->n_users;
+  p.h = dm->h;
+  p.d = dm->d;
+  p.chunk = auto_chunk(dm, b);
+  p.total_L = b->total_L;
+  p.total_T = b->total_T;
+  const int64_t groups = (b->max_T * dm->h + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int64_t chunks_ceil = (b->total_L + p.chunk - 1) / p.chunk;
+  // sum_u ceil(L_u / c) ceil(m_u h / 128) <= (total_L / c + n_users) * ceil(max_T h / 128)
+  p.max_items = b->total_T > 0 ? (chunks_ceil + b->n_users) * groups : 0;
+  // Partial-state rows of users with >= 2 chunks: sum_u ceil(L_u / c) m_u h
+  //   <= h (max_T total_L / c + total_T).
+  p.max_part_rows = b->max_L > p.chunk ? (int64_t)dm->h * (b->max_T * chunks_ceil + b->total_T) : 0;
+  return p;
+}
+
+// ---- workspace layout -------------------------------------------------------------------------
+struct Carver {
+  char *base;
+  size_t off = 0;
+  explicit Carver(void *b) : base((char *)b) {}
+  template <typename T> T *take(size_t count) {
+    off = round_up(off, 256);
+    T *p = base ? (T *)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+size_t esize(const stca_dims *dm) { return dm->dtype == STCA_BF16 ? 2 : 4; }
+constexpr int64_t kFfnRows = 32768;  // row chunk of the generic (fp32) FFN path
+
+struct AttendWs {
+  AttnBuffers ab;
+  void *U = nullptr;       // T*h x d (dtype)
+  float *abar = nullptr;   // T*h x d
+  float *obar = nullptr;   // T x d
+};
+
+void carve_attend(Carver &c, const stca_dims *dm, const stca_batch *b, const AttnPlan &p, AttendWs &w) {
+  const int64_t T = b->total_T, d = dm->d, h = dm->h;
+  w.U = c.take<char>((size_t)(T * h * d) * esize(dm));
+  w.abar = c.take<float>((size_t)(T * h * d));
+  w.obar = c.take<float>((size_t)(T * d));
+  w.ab.items = c.take<WorkItem>((size_t)std::max<int64_t>(p.max_items, 1));
+  w.ab.n_items = c.take<int32_t>(4);
+  w.ab.user_nchunks = c.take<int32_t>((size_t)std::max(b->n_users, 1));
+  w.ab.part_base = c.take<int64_t>((size_t)std::max(b->n_users, 1));
+  w.ab.tgt_user = c.take<int32_t>((size_t)std::max<int64_t>(T, 1));
+  w.ab.part_A = c.take<float>((size_t)(p.max_part_rows * d));
+  w.ab.part_ms = c.take<float>((size_t)(p.max_part_rows * 2));
+}
+
+struct FfnWs {
+  float *A = nullptr, *G = nullptr;  // kFfnRows x rd each (generic path)
+};
+
+void carve_ffn(Carver &c, const stca_dims *dm, int64_t rows, FfnWs &w) {
+  const int64_t rc = std::min<int64_t>(std::max<int64_t>(rows, 1), kFfnRows);
+  w.A = c.take<float>((size_t)(rc * dm->r * dm->d));
+  w.G = c.take<float>((size_t)(rc * dm->r * dm->d));
+}
+
+// ---- profiling ------------------------------------------------------------------------------
+}  // namespace
+
+struct stca_profiler {
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  struct Mark {
+    int phase;
+    hipEvent_t a, b;
+  };
+  std::vector<Mark> marks;
+};
+
+namespace {
+
+struct Phase {
+  stca_profiler *p;
+  hipStream_t s;
+  int phase;
+  hipEvent_t b = nullptr;
+  hipError_t err = hipSuccess;
+  Phase(stca_profiler *p_, hipStream_t s_, int ph) : p(p_), s(s_), phase(ph) {
+    if (!p) return;
+    hipEvent_t a = take(), e = take();
+    if (!a || !e) {
+      p = nullptr;
+      return;
+    }
+    p->marks.push_back({phase, a, e});
+    b = e;
+    err = hipEventRecord(a, s);
+  }
+  hipEvent_t take() {
+    if (p->used == p->pool.size()) {
+      if (p->pool.size() >= 65536) return nullptr;
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      p->pool.push_back(e);
+    }
+    return p->pool[p->used++];
+  }
+  hipError_t end() {
+    if (p && b) return hipEventRecord(b, s);
+    return err;
+  }
+};
+
+// ---- building blocks --------------------------------------------------------------------------
+// out[rows x d] = [LN](SwiGLUFFN(x)) with fp32 accumulation through the generic kernels.
+int ffn_generic(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t rows, const void *x, int64_t ldx,
+                bool x_bf16, void *out, int64_t ldo, bool out_bf16, bool apply_ln, const FfnWs &w) {
+  const int d = dm->d, rd = dm->r * dm->d;
+  const bool wb = dm->dtype == STCA_BF16;
+  const size_t xes = x_bf16 ? 2 : 4, oes = out_bf16 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < rows; r0 += kFfnRows) {
+    const int n = (int)std::min<int64_t>(kFfnRows, rows - r0);
+    const char *xp = (const char *)x + (size_t)r0 * ldx * xes;
+    GemmArgs g;
+    g.M = n;
+    g.N = rd;
+    g.K = d;
+    g.A = xp;
+    g.lda = ldx;
+    g.ta_bf16 = x_bf16;
+    g.B = f->Wu;
+    g.ldb = rd;
+    g.tb_bf16 = wb;
+    g.C = w.A;
+    g.ldc = rd;
+    HIP_TRY(gemm(s, g));
+    g.B = f->Wv;
+    g.C = w.G;
+    HIP_TRY(gemm(s, g));
+    HIP_TRY(swiglu_gate_inplace(s, (int64_t)n * rd, w.A, w.G));
+    GemmArgs g2;
+    g2.M = n;
+    g2.N = d;
+    g2.K = rd;
+    g2.A = w.A;
+    g2.lda = rd;
+    g2.B = f->Wo;
+    g2.ldb = d;
+    g2.tb_bf16 = wb;
+    if (apply_ln) {
+      g2.C = w.G;  // fp32 staging, then LayerNorm into out
+      g2.ldc = d;
+      HIP_TRY(gemm(s, g2));
+      HIP_TRY(layernorm_rows(s, n, d, w.G, d, (char *)out + (size_t)r0 * ldo * oes, ldo, out_bf16, f->gamma, f->beta,
+                             dm->ln_eps));
+    } else {
+      g2.C = (char *)out + (size_t)r0 * ldo * oes;
+      g2.ldc = ldo;
+      g2.tc_bf16 = out_bf16;
+      HIP_TRY(gemm(s, g2));
+    }
+  }
+  return STCA_OK;
+}
+
+// eq. (2) for all history rows.
+int encode_rows(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t rows, const void *X, void *Xt,
+                const void *packed, const FfnWs &w) {
+  if (dm->dtype == STCA_BF16) {
+    HIP_TRY(encode_mfma(s, dm->d, dm->r, rows, X, dm->d, packed, Xt, dm->d, true, true, f->gamma, f->beta,
+                        dm->ln_eps));
+    return STCA_OK;
+  }
+  return ffn_generic(s, dm, f, rows, X, dm->d, false, Xt, dm->d, false, true, w);
+}
+
+// eqs. (13), (6) for one layer: o[T x d] (row stride ldo) from the encoded history and q.
+int attend_layer(hipStream_t s, const stca_dims *dm, const stca_weights *w, int i, const stca_batch *b,
+                 const AttnPlan &p, const void *Xt, const float *q, float *o, int64_t ldo, const AttendWs &aw,
+                 stca_profiler *prof) {
+  const int64_t T = b->total_T;
+  if (T == 0) return STCA_OK;
+  const int d = dm->d, h = dm->h, dh = d / h;
+  const bool bf = dm->dtype == STCA_BF16;
+  {
+    Phase ph(prof, s, STCA_PHASE_UPROJ);
+    // P = q W_Q  (T x d, into obar as scratch)
+    GemmArgs g;
+    g.M = (int)T;
+    g.N = d;
+    g.K = d;
+    g.A = q;
+    g.lda = d;
+    g.B = w->WQ[i];
+    g.ldb = d;
+    g.tb_bf16 = bf;
+    g.C = aw.obar;
+    g.ldc = d;
+    HIP_TRY(gemm(s, g));
+    // U[:, j, :] = P[:, head j] W_K[:, head j]^T * log2(e) / sqrt(d_h)
+    GemmArgs u;
+    u.M = (int)T;
+    u.N = d;
+    u.K = dh;
+    u.batch = h;
+    u.A = aw.obar;
+    u.lda = d;
+    u.sA = dh;
+    u.B = w->WK[i];
+    u.ldb = d;
+    u.sB = dh;
+    u.tb_bf16 = bf;
+    u.trans_b = true;
+    u.C = aw.U;
+    u.ldc = (int64_t)h * d;
+    u.sC = d;
+    u.tc_bf16 = bf;
+    u.alpha = 1.4426950408889634f / sqrtf((float)dh);
+    HIP_TRY(gemm(s, u));
+    HIP_TRY(ph.end());
+  }
+  {
+    Phase ph(prof, s, STCA_PHASE_ATTEND);
+    HIP_TRY(attend_split(s, p, bf, b->hist_off, b->tgt_off, Xt, aw.U, aw.abar, aw.ab));
+    HIP_TRY(ph.end());
+  }
+  if (p.max_part_rows > 0 || b->n_users > 0) {
+    Phase ph(prof, s, STCA_PHASE_COMBINE);
+    HIP_TRY(attend_combine(s, p, b->tgt_off, aw.abar, aw.ab));
+    HIP_TRY(ph.end());
+  }
+  {
+    Phase ph(prof, s, STCA_PHASE_PROJECT);
+    // obar[:, head j] = abar[:, j, :] W_V[:, head j]
+    GemmArgs v;
+    v.M = (int)T;
+    v.N = dh;
+    v.K = d;
+    v.batch = h;
+    v.A = aw.abar;
+    v.lda = (int64_t)h * d;
+    v.sA = d;
+    v.B = w->WV[i];
+    v.ldb = d;
+    v.sB = dh;
+    v.tb_bf16 = bf;
+    v.C = aw.obar;
+    v.ldc = d;
+    v.sC = dh;
+    HIP_TRY(gemm(s, v));
+    // o = obar W_O
+    GemmArgs g;
+    g.M = (int)T;
+    g.N = d;
+    g.K = d;
+    g.A = aw.obar;
+    g.lda = d;
+    g.B = w->WO[i];
+    g.ldb = d;
+    g.tb_bf16 = bf;
+    g.C = o;
+    g.ldc = ldo;
+    HIP_TRY(gemm(s, g));
+    HIP_TRY(ph.end());
+  }
+  return STCA_OK;
+}
+
+struct ForwardWs {
+  void *packed_hist[STCA_MAX_M] = {};
+  void *packed_query[STCA_MAX_M] = {};
+  void *Xt = nullptr;
+  float *q = nullptr;
+  float *c = nullptr;
+  FfnWs ffn;
+  AttendWs aw;
+};
+
+bool same_ffn(const stca_ffn &a, const stca_ffn &b) { return a.Wu == b.Wu && a.Wv == b.Wv && a.Wo == b.Wo; }
+
+size_t carve_forward(void *base, const stca_dims *dm, const stca_batch *b, const AttnPlan &p, ForwardWs &w,
+                     const stca_weights *wt) {
+  Carver c(base);
+  if (dm->dtype == STCA_BF16) {
+    const size_t pb = encode_packed_bytes(dm->d, dm->r);
+    for (int i = 0; i < dm->M; ++i) w.packed_hist[i] = c.take<char>(pb);
+    (void)wt;
+  }
+  w.Xt = c.take<char>((size_t)(b->total_L * dm->d) * esize(dm));
+  w.q = c.take<float>((size_t)(b->total_T * dm->d));
+  w.c = c.take<float>((size_t)(b->total_T * dm->d));
+  const int64_t ffn_rows = dm->dtype == STCA_BF16 ? b->total_T : std::max(b->total_T, b->total_L);
+  carve_ffn(c, dm, ffn_rows, w.ffn);
+  carve_attend(c, dm, b, p, w.aw);
+  return round_up(c.off, 256);
+}
+
+int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b, const void *X, const void *xt,
+                 float *Z, void *ws, size_t ws_bytes, void *stream, stca_profiler *prof) {
+  int st;
+  if ((st = check_dims(dm)) != STCA_OK) return st;
+  if ((st = check_batch(b)) != STCA_OK) return st;
+  if ((st = check_weights(dm, w)) != STCA_OK) return st;
+  if (b->total_L > 0 && !X) return fail(STCA_E_ARG, "X is NULL");
+  if (b->total_T > 0 && (!xt || !Z)) return fail(STCA_E_ARG, "xt or Z is NULL");
+  if (!aligned16(X) || !aligned16(xt) || !aligned16(Z)) return fail(STCA_E_ALIGN, "X/xt/Z not 16-byte aligned");
+  const AttnPlan p = make_plan(dm, b);
+  ForwardWs fw;
+  const size_t need = carve_forward(nullptr, dm, b, p, fw, w);
+  if (!ws || ws_bytes < need)
+    return fail(STCA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(STCA_E_ALIGN, "workspace not 16-byte aligned");
+  carve_forward(ws, dm, b, p, fw, w);
+  if (b->total_T == 0) return STCA_OK;  // nothing to produce
+
+  hipStream_t s = (hipStream_t)stream;
+  const int d = dm->d, M = dm->M;
+  const bool bf = dm->dtype == STCA_BF16;
+
+  if (bf) {
+    Phase ph(prof, s, STCA_PHASE_PACK);
+    for (int i = 0; i < M; ++i) {
+      int j = 0;
+      for (; j < i; ++j)
+        if (same_ffn(w->hist[j], w->hist[i])) break;
+      if (j < i) {
+        fw.packed_hist[i] = fw.packed_hist[j];
+        continue;
+      }
+      HIP_TRY(encode_pack(s, d, dm->r, w->hist[i].Wu, w->hist[i].Wv, w->hist[i].Wo, fw.packed_hist[i]));
+    }
+    HIP_TRY(ph.end());
+  }
+  HIP_TRY(build_worklist(s, p, b->hist_off, b->tgt_off, fw.aw.ab));
+
+  {  // eq. (3): q(1) = LN(SwiGLUFFN(1)(x_t))
+    Phase ph(prof, s, STCA_PHASE_QUERY);
+    if ((st = ffn_generic(s, dm, &w->query[0], b->total_T, xt, d, bf, fw.q, d, false, true, fw.ffn)) != STCA_OK)
+      return st;
+    HIP_TRY(ph.end());
+  }
+  for (int i = 0; i < M; ++i) {
+    {
+      Phase ph(prof, s, STCA_PHASE_ENCODE);
+      if ((st = encode_rows(s, dm, &w->hist[i], b->total_L, X, fw.Xt, fw.packed_hist[i], fw.ffn)) != STCA_OK)
+        return st;
+      HIP_TRY(ph.end());
+    }
+    if ((st = attend_layer(s, dm, w, i, b, p, fw.Xt, fw.q, Z + (size_t)i * d, (int64_t)M * d, fw.aw, prof)) !=
+        STCA_OK)
+      return st;
+    if (i + 1 < M) {  // eq. (7): q(i+1) = SwiGLUFFN([o(1..i) || x_t] W_C) (+LN)
+      Phase ph(prof, s, STCA_PHASE_QUERY);
+      const int nblk = i + 1;  // o blocks already in Z
+      GemmArgs g;
+      g.M = (int)b->total_T;
+      g.N = d;
+      g.K = nblk * d;
+      g.A = Z;
+      g.lda = (int64_t)M * d;
+      g.B = w->WC[i + 1];
+      g.ldb = d;
+      g.tb_bf16 = bf;
+      g.C = fw.c;
+      g.ldc = d;
+      HIP_TRY(gemm(s, g));
+      GemmArgs gx = g;
+      gx.K = d;
+      gx.A = xt;
+      gx.lda = d;
+      gx.ta_bf16 = bf;
+      gx.B = (const char *)w->WC[i + 1] + (size_t)nblk * d * d * esize(dm);
+      gx.beta = 1.f;
+      HIP_TRY(gemm(s, gx));
+      if ((st = ffn_generic(s, dm, &w->query[i + 1], b->total_T, fw.c, d, false, fw.q, d, false, dm->query_ln != 0,
+                            fw.ffn)) != STCA_OK)
+        return st;
+      HIP_TRY(ph.end());
+    }
+  }
+  return STCA_OK;
+}
+
+}  // namespace
+
+// =============================================================================================
+extern "C" {
+
+int stca_encode_workspace_size(const stca_dims *dims, int64_t n_rows, size_t *bytes) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if (!bytes) return fail(STCA_E_ARG, "bytes is NULL");
+  if (n_rows < 0) return fail(STCA_E_ARG, "n_rows < 0");
+  Carver c(nullptr);
+  if (dims->dtype == STCA_BF16) {
+    c.take<char>(encode_packed_bytes(dims->d, dims->r));
+  } else {
+    FfnWs f;
+    carve_ffn(c, dims, n_rows, f);
+  }
+  *bytes = round_up(c.off, 256);
+  return STCA_OK;
+}
+
+int stca_attend_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_batch(batch)) != STCA_OK) return st;
+  if (!bytes) return fail(STCA_E_ARG, "bytes is NULL");
+  const AttnPlan p = make_plan(dims, batch);
+  Carver c(nullptr);
+  AttendWs aw;
+  carve_attend(c, dims, batch, p, aw);
+  *bytes = round_up(c.off, 256);
+  return STCA_OK;
+}
+
+int stca_forward_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_batch(batch)) != STCA_OK) return st;
+  if (!bytes) return fail(STCA_E_ARG, "bytes is NULL");
+  const AttnPlan p = make_plan(dims, batch);
+  ForwardWs fw;
+  *bytes = carve_forward(nullptr, dims, batch, p, fw, nullptr);
+  return STCA_OK;
+}
+
+int stca_encode(const stca_dims *dims, const stca_ffn *ffn, int64_t n_rows, const void *X, void *Xt,
+                void *workspace, size_t workspace_bytes, void *stream) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_ffn(ffn, true, "encode")) != STCA_OK) return st;
+  if (n_rows < 0) return fail(STCA_E_ARG, "n_rows < 0");
+  if (n_rows > 0 && (!X || !Xt)) return fail(STCA_E_ARG, "X or Xt is NULL");
+  if (!aligned16(X) || !aligned16(Xt)) return fail(STCA_E_ALIGN, "X/Xt not 16-byte aligned");
+  size_t need = 0;
+  stca_encode_workspace_size(dims, n_rows, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(STCA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(STCA_E_ALIGN, "workspace not 16-byte aligned");
+  if (n_rows == 0) return STCA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  if (dims->dtype == STCA_BF16) {
+    void *packed = c.take<char>(encode_packed_bytes(dims->d, dims->r));
+    HIP_TRY(encode_pack(s, dims->d, dims->r, ffn->Wu, ffn->Wv, ffn->Wo, packed));
+    return encode_rows(s, dims, ffn, n_rows, X, Xt, packed, FfnWs{});
+  }
+  FfnWs f;
+  carve_ffn(c, dims, n_rows, f);
+  return encode_rows(s, dims, ffn, n_rows, X, Xt, nullptr, f);
+}
+
+int stca_attend(const stca_dims *dims, const stca_weights *w, int32_t layer, const stca_batch *batch,
+                const void *Xt, const float *q, float *o, void *workspace, size_t workspace_bytes, void *stream) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_batch(batch)) != STCA_OK) return st;
+  if (!w) return fail(STCA_E_ARG, "weights are NULL");
+  if (layer < 0 || layer >= dims->M) return fail(STCA_E_ARG, "layer %d not in [0, M)", layer);
+  if ((st = check_layer_weights(dims, w, layer)) != STCA_OK) return st;
+  if (batch->total_L > 0 && !Xt) return fail(STCA_E_ARG, "Xt is NULL");
+  if (batch->total_T > 0 && (!q || !o)) return fail(STCA_E_ARG, "q or o is NULL");
+  if (!aligned16(Xt) || !aligned16(q) || !aligned16(o)) return fail(STCA_E_ALIGN, "Xt/q/o not 16-byte aligned");
+  const AttnPlan p = make_plan(dims, batch);
+  Carver c0(nullptr);
+  AttendWs aw;
+  carve_attend(c0, dims, batch, p, aw);
+  const size_t need = round_up(c0.off, 256);
+  if (!workspace || workspace_bytes < need)
+    return fail(STCA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(STCA_E_ALIGN, "workspace not 16-byte aligned");
+  if (batch->total_T == 0) return STCA_OK;
+  Carver c(workspace);
+  carve_attend(c, dims, batch, p, aw);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(build_worklist(s, p, batch->hist_off, batch->tgt_off, aw.ab));
+  return attend_layer(s, dims, w, layer, batch, p, Xt, q, o, dims->d, aw, nullptr);
+}
+
+int stca_forward(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
+                 const void *xt, float *Z, void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_impl(dims, w, batch, X, xt, Z, workspace, workspace_bytes, stream, nullptr);
+}
+
+int stca_forward_profiled(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
+                          const void *xt, float *Z, void *workspace, size_t workspace_bytes, void *stream,
+                          stca_profiler *prof) {
+  return forward_impl(dims, w, batch, X, xt, Z, workspace, workspace_bytes, stream, prof);
+}
+
+int stca_profiler_create(stca_profiler **out) {
+  if (!out) return fail(STCA_E_ARG, "out is NULL");
+  *out = new stca_profiler();
+  return STCA_OK;
+}
+
+int stca_profiler_destroy(stca_profiler *p) {
+  if (!p) return STCA_OK;
+  for (hipEvent_t e : p->pool) hipEventDestroy(e);
+  delete p;
+  return STCA_OK;
+}
+
+int stca_profiler_reset(stca_profiler *p) {
+  if (!p) return fail(STCA_E_ARG, "profiler is NULL");
+  p->marks.clear();
+  p->used = 0;
+  return STCA_OK;
+}
+
+int stca_profiler_read(stca_profiler *p, stca_profile_report *out) {
+  if (!p || !out) return fail(STCA_E_ARG, "profiler or report is NULL");
+  memset(out, 0, sizeof *out);
+  if (!p->marks.empty()) HIP_TRY(hipEventSynchronize(p->marks.back().b));
+  for (const auto &m : p->marks) {
+    float ms = 0.f;
+    HIP_TRY(hipEventSynchronize(m.b));
+    HIP_TRY(hipEventElapsedTime(&ms, m.a, m.b));
+    out->ms[m.phase] += ms;
+    out->launches[m.phase] += 1;
+  }
+  return STCA_OK;
+}
+
+const char *stca_status_string(int status) {
+  switch (status) {
+    case STCA_OK: return "ok";
+    case STCA_E_ARG: return "invalid argument";
+    case STCA_E_DIMS: return "unsupported dimensions";
+    case STCA_E_WORKSPACE: return "workspace too small";
+    case STCA_E_ALIGN: return "pointer not 16-byte aligned";
+    case STCA_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *stca_last_error(void) { return g_last_error.c_str(); }
+
+const char *stca_version(void) { return "libstca 0.1 (gfx950)"; }
+
+}  // extern "C"

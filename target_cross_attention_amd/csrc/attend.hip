@@ -1,0 +1,423 @@
+// Ragged split-L single-query cross attention in the reordered form of eq. (13)
+// ("Make It Long, Keep It Fast", section 2.1: u = (q W_Q) W_K^T, alpha = softmax(u X~^T / sqrt(d_h)),
+// then alpha X~; the W_V / W_O projections run afterwards on the per-target results).
+//
+// Every (target, head) pair of a user is one query row u (d wide).  All m_u * h rows of a user
+// attend to that user's encoded history only (ragged target attention over segment offsets,
+// section 2.2 of the same notes), so one pass over the user's history serves all of its rows:
+// the request-level-batching reuse.
+//
+// Work item = (user, chunk of the history, group of up to 128 query rows).  A workgroup streams
+// its chunk through LDS in 32-token tiles (direct global->LDS loads, double-buffered); each of
+// its 4 waves owns 32 query rows and keeps, per row, a running max, a running sum and the
+// fp32 accumulator of alpha X~ (online softmax).  A user with one chunk is finalised in place;
+// otherwise the partial (max, sum, accumulator) triples are merged by attend_combine.
+#include <math.h>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace stca {
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// ------------------------------------------------------------------------------------------
+// Work list: the segment index tensor turned into (user, chunk, row group) items.
+// One workgroup; users in blocks of 1024 with a block-wide prefix sum.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64_t *__restrict__ hoff,
+                                                        const int64_t *__restrict__ toff, int h, int chunk,
+                                                        int64_t max_items, WorkItem *__restrict__ items,
+                                                        int32_t *__restrict__ n_items,
+                                                        int32_t *__restrict__ user_nchunks,
+                                                        int64_t *__restrict__ part_base,
+                                                        int32_t *__restrict__ tgt_user) {
+  __shared__ int64_t sc_i[1024];
+  __shared__ int64_t sc_p[1024];
+  const int tid = threadIdx.x;
+  int64_t carry_i = 0, carry_p = 0;
+  for (int base = 0; base < n_users; base += 1024) {
+    const int u = base + tid;
+    int64_t ni = 0, np = 0;
+    int nc = 0, ng = 0;
+    if (u < n_users) {
+      const int64_t L = hoff[u + 1] - hoff[u];
+      const int64_t R = (toff[u + 1] - toff[u]) * h;
+      nc = L > 0 ? (int)((L + chunk - 1) / chunk) : 0;
+      ng = (int)((R + kRowsPerGroup - 1) / kRowsPerGroup);
+      ni = R > 0 ? (int64_t)nc * ng : 0;
+      np = nc > 1 ? (int64_t)nc * R : 0;
+      user_nchunks[u] = nc;
+      for (int64_t t = toff[u]; t < toff[u + 1]; ++t) tgt_user[t] = u;
+    }
+    sc_i[tid] = ni;
+    sc_p[tid] = np;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int64_t a = tid >= off ? sc_i[tid - off] : 0;
+      const int64_t b = tid >= off ? sc_p[tid - off] : 0;
+      __syncthreads();
+      sc_i[tid] += a;
+      sc_p[tid] += b;
+      __syncthreads();
+    }
+    if (u < n_users) {
+      part_base[u] = carry_p + sc_p[tid] - np;
+      int64_t k = carry_i + sc_i[tid] - ni;
+      if (ni > 0)
+        for (int c = 0; c < nc; ++c)
+          for (int g = 0; g < ng; ++g, ++k)
+            if (k < max_items) items[k] = WorkItem{u, c, g, nc};
+    }
+    carry_i += sc_i[1023];
+    carry_p += sc_p[1023];
+    __syncthreads();
+  }
+  if (tid == 0) *n_items = (int32_t)(carry_i < max_items ? carry_i : max_items);
+}
+
+hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_off, const int64_t *tgt_off,
+                          const AttnBuffers &b) {
+  hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, p.n_users, hist_off, tgt_off, p.h, p.chunk,
+                     p.max_items, b.items, b.n_items, b.user_nchunks, b.part_base, b.tgt_user);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16 for both contractions).
+//   scores  S^T[tok x row] = X~_tile[tok x d] U^T[d x row]      (A from LDS, B = U in registers)
+//   update  O^T[d x row]  += X~_tile^T[d x tok] P^T[tok x row]  (A from LDS, B = P in registers)
+// The accumulator layout of S^T is, per lane, one query row and 16 tokens; taking the
+// probabilities of registers 8 kk .. 8 kk + 7 as the B operand of k-step kk pairs them with the
+// tokens phi(kk, g, e) = 16 kk + 8 (e>>2) + 4 g + (e&3), which the A operand reads from LDS.
+// LDS tile layout: 32 rows x d/8 16-byte chunks, chunk c of row t stored at position
+// c ^ (t & SWZ) so both the row-wise and the column-wise reads spread over the banks.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
+    const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
+    const int64_t *__restrict__ toff, int h, int chunk, const bf16 *__restrict__ Xt,
+    const bf16 *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
+    float *__restrict__ part_ms, const int64_t *__restrict__ part_base) {
+  constexpr int CPR = D / 8;                      // 16-byte chunks per history row
+  constexpr int SWZ = (CPR < 32 ? CPR : 32) - 1;  // swizzle mask
+  constexpr int NKS = D / 16, NOB = D / 32;
+  constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
+  __shared__ bf16x8 tiles[2][32 * CPR];
+
+  if ((int)blockIdx.x >= *n_items) return;
+  const WorkItem it = items[blockIdx.x];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, gl = lane >> 5;
+  const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
+  const int64_t t0 = L0 + (int64_t)it.chunk * chunk;
+  const int64_t t1 = (t0 + chunk < L1) ? t0 + chunk : L1;
+  const int64_t T0 = toff[it.user];
+  const int R = (int)((toff[it.user + 1] - T0) * h);
+  const int64_t rowbase = T0 * h;
+  const int r0 = it.group * kRowsPerGroup + wave * 32;
+  const bool wave_active = r0 < R;
+  const int myrow = r0 + col;
+  const bool row_ok = myrow < R;
+  const int ntiles = (int)((t1 - t0 + 31) / 32);
+
+  auto stage = [&](int k, int b) {
+    const int64_t tb = t0 + 32 * (int64_t)k;
+#pragma unroll
+    for (int j = wave; j < INSTR; j += 4) {
+      const int slot = j * 64 + lane;
+      const int row = slot / CPR, cs = slot % CPR;
+      const int c = cs ^ (row & SWZ);
+      const int64_t tok = (tb + row < t1) ? tb + row : t1 - 1;
+      __builtin_amdgcn_global_load_lds(Xt + tok * D + c * 8, (STCA_LDS void *)&tiles[b][j * 64], 16, 0, 0);
+    }
+  };
+
+  stage(0, 0);
+
+  bf16x8 ub[NKS];
+  {
+    const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (row_ok)
+        ub[ks] = *reinterpret_cast<const bf16x8 *>(urow + 16 * ks);
+      else
+        ub[ks] = bf16x8{};
+    }
+  }
+  f32x16 oacc[NOB];
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob) oacc[ob] = f32x16{};
+  float m_run = -INFINITY, s_run = 0.f;
+  // Per-lane LDS byte offsets (see the column reads below).
+  const uint32_t row_off = (uint32_t)(col * CPR * 16);
+  const uint32_t rx16 = (uint32_t)((gl ^ (col & SWZ)) * 16);
+  uint32_t cbase[2][4];
+#pragma unroll
+  for (int sgn = 0; sgn < 2; ++sgn)
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+      cbase[sgn][kq] = (uint32_t)(64 * CPR * gl + (sgn ? -64 : 64) * gl + 16 * ((col >> 3) ^ kq) + 2 * (col & 7));
+
+  for (int k = 0; k < ntiles; ++k) {
+    const int b = k & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile k is in LDS; buffer b^1 is free
+    if (k + 1 < ntiles) stage(k + 1, b ^ 1);
+    if (!wave_active) continue;
+
+    const bf16x8 *tile = tiles[b];
+    const char *tbytes = reinterpret_cast<const char *>(tile);
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      // chunk (2 ks + gl) of row col, stored at (2 ks + gl) ^ (col & SWZ) = (2 ks) ^ rx
+      const uint32_t off = row_off + (((uint32_t)(32 * ks)) ^ rx16);
+      sc = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(tbytes + off), ub[ks], sc);
+    }
+    const int64_t rem = t1 - (t0 + 32 * (int64_t)k);
+    if (rem < 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tau = 8 * (i >> 2) + 4 * gl + (i & 3);
+        if (tau >= rem) sc[i] = -INFINITY;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx);
+    if (wave_any(m_new > m_run)) {
+      const float sf = fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[ob][i] *= sf;
+      s_run *= sf;
+      m_run = m_new;
+    }
+    bf16x8 pb[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bf16 p = f32_to_bf16(fast_exp2(sc[i] - m_run));
+      pb[i >> 3][i & 7] = p;
+      psum += (float)p;
+    }
+    s_run += psum;
+
+    // Column reads: A operand row = feature f = 32 ob + col, slot (gl, e) = token
+    // tau = 16 kk + 8 (e>>2) + 4 gl + (e&3), element f & 7 of chunk (f >> 3) ^ (tau & SWZ).
+    // (4 ob + (col>>3)) ^ tau splits into 4 (P ^ gl) + ((col>>3) ^ (e&3)) with the compile-time
+    // P = ob ^ ((4 kk + 2 (e>>2)) & (SWZ>>2)), and P ^ gl = P + gl (P even) or P - gl (P odd);
+    // so every address is one of 8 per-lane bases plus an immediate.
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 xa;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int P = ob ^ ((4 * kk + 2 * (e >> 2)) & (SWZ >> 2));
+          const uint32_t C = (uint32_t)((16 * kk + 8 * (e >> 2) + (e & 3)) * CPR * 16 + 64 * P);
+          xa[e] = *reinterpret_cast<const bf16 *>(tbytes + (cbase[P & 1][e & 3] + C));
+        }
+        oacc[ob] = mfma32x32x16(xa, pb[kk], oacc[ob]);
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  const float s_tot = s_run + swap_halves(s_run);
+  if (!row_ok) return;
+  if (it.n_chunks == 1) {
+    const float inv = 1.0f / s_tot;
+    float *dst = abar + (rowbase + myrow) * D;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f0 = 32 * ob + 8 * q + 4 * gl;
+        *reinterpret_cast<f32x4 *>(dst + f0) = f32x4{oacc[ob][4 * q] * inv, oacc[ob][4 * q + 1] * inv,
+                                                     oacc[ob][4 * q + 2] * inv, oacc[ob][4 * q + 3] * inv};
+      }
+  } else {
+    const int64_t p = part_base[it.user] + (int64_t)it.chunk * R + myrow;
+    float *dst = part_A + p * D;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int f0 = 32 * ob + 8 * q + 4 * gl;
+        *reinterpret_cast<f32x4 *>(dst + f0) =
+            f32x4{oacc[ob][4 * q], oacc[ob][4 * q + 1], oacc[ob][4 * q + 2], oacc[ob][4 * q + 3]};
+      }
+    if (gl == 0) {
+      part_ms[2 * p] = m_run;
+      part_ms[2 * p + 1] = s_tot;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// fp32 debug kernel (vector ALU): one wave per query row, tokens streamed four at a time.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attend_f32_kernel(
+    const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
+    const int64_t *__restrict__ toff, int h, int chunk, const float *__restrict__ Xt,
+    const float *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
+    float *__restrict__ part_ms, const int64_t *__restrict__ part_base) {
+  constexpr int E = D / 64;
+  if ((int)blockIdx.x >= *n_items) return;
+  const WorkItem it = items[blockIdx.x];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
+  const int64_t t0 = L0 + (int64_t)it.chunk * chunk;
+  const int64_t t1 = (t0 + chunk < L1) ? t0 + chunk : L1;
+  const int64_t T0 = toff[it.user];
+  const int R = (int)((toff[it.user + 1] - T0) * h);
+  const int64_t rowbase = T0 * h;
+  const int rend = (it.group + 1) * kRowsPerGroup < R ? (it.group + 1) * kRowsPerGroup : R;
+
+  for (int r = it.group * kRowsPerGroup + wave; r < rend; r += 4) {
+    float u[E], a[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      u[e] = U[(rowbase + r) * D + lane + 64 * e];
+      a[e] = 0.f;
+    }
+    float m = -INFINITY, s = 0.f;
+    for (int64_t p = t0; p < t1; p += 4) {
+      float x[4][E], dot[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t pj = (p + j < t1) ? p + j : t1 - 1;
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          x[j][e] = Xt[pj * D + lane + 64 * e];
+          acc = fmaf(u[e], x[j][e], acc);
+        }
+        dot[j] = acc;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dot[j] = (p + j < t1) ? wave_sum(dot[j]) : -INFINITY;
+      const float mx = fmaxf(fmaxf(dot[0], dot[1]), fmaxf(dot[2], dot[3]));
+      const float m_new = fmaxf(m, mx);
+      const float sf = exp2f(m - m_new);
+      s *= sf;
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[e] *= sf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = exp2f(dot[j] - m_new);
+        s += w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] = fmaf(w, x[j][e], a[e]);
+      }
+      m = m_new;
+    }
+    if (it.n_chunks == 1) {
+      const float inv = 1.0f / s;
+#pragma unroll
+      for (int e = 0; e < E; ++e) abar[(rowbase + r) * D + lane + 64 * e] = a[e] * inv;
+    } else {
+      const int64_t pidx = part_base[it.user] + (int64_t)it.chunk * R + r;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part_A[pidx * D + lane + 64 * e] = a[e];
+      if (lane == 0) {
+        part_ms[2 * pidx] = m;
+        part_ms[2 * pidx + 1] = s;
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_path, const int64_t *hoff,
+                                 const int64_t *toff, const void *Xt, const void *U, float *abar,
+                                 const AttnBuffers &b) {
+  const dim3 grid((unsigned)p.max_items), block(256);
+  if (bf16_path)
+    hipLaunchKernelGGL((attend_mfma_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
+                       (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base);
+  else
+    hipLaunchKernelGGL((attend_f32_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
+                       (const float *)Xt, (const float *)U, abar, b.part_A, b.part_ms, b.part_base);
+  return hipGetLastError();
+}
+
+hipError_t attend_split(hipStream_t s, const AttnPlan &p, bool bf16_path, const int64_t *hist_off,
+                        const int64_t *tgt_off, const void *Xt, const void *U, float *abar,
+                        const AttnBuffers &b) {
+  if (p.max_items <= 0) return hipSuccess;
+  switch (p.d) {
+    case 64: return attend_split_d<64>(s, p, bf16_path, hist_off, tgt_off, Xt, U, abar, b);
+    case 128: return attend_split_d<128>(s, p, bf16_path, hist_off, tgt_off, Xt, U, abar, b);
+    case 256: return attend_split_d<256>(s, p, bf16_path, hist_off, tgt_off, Xt, U, abar, b);
+    case 512: return attend_split_d<512>(s, p, bf16_path, hist_off, tgt_off, Xt, U, abar, b);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Merge of split-L partial softmax states (exact: rescale each chunk's sum and accumulator by
+// 2^(m_c - max_c m_c), then divide).  Fixed chunk order, so the result is deterministic.  Users
+// with one chunk were finalised by the attention kernel; users with an empty history get NaN.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(int64_t n_rows, int h, int D,
+                                                      const int32_t *__restrict__ tgt_user,
+                                                      const int32_t *__restrict__ user_nchunks,
+                                                      const int64_t *__restrict__ toff,
+                                                      const int64_t *__restrict__ part_base,
+                                                      const float *__restrict__ part_A,
+                                                      const float *__restrict__ part_ms, float *__restrict__ abar) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int u = tgt_user[row / h];
+  const int nc = user_nchunks[u];
+  if (nc == 1) return;
+  float *dst = abar + row * D;
+  if (nc == 0) {
+    for (int f = lane; f < D; f += 64) dst[f] = NAN;
+    return;
+  }
+  const int64_t R = (toff[u + 1] - toff[u]) * h;
+  const int64_t r = row - toff[u] * h;
+  const int64_t p0 = part_base[u] + r;
+  float mstar = -INFINITY;
+  for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, part_ms[2 * (p0 + c * R)]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float s = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const int64_t p = p0 + c * R;
+    const float w = exp2f(part_ms[2 * p] - mstar);
+    s += part_ms[2 * p + 1] * w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int f = lane + 64 * e;
+      if (f < D) acc[e] += part_A[p * D + f] * w;
+    }
+  }
+  const float inv = 1.0f / s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int f = lane + 64 * e;
+    if (f < D) dst[f] = acc[e] * inv;
+  }
+}
+
+hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_off, float *abar,
+                          const AttnBuffers &b) {
+  const int64_t rows = p.total_T * p.h;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, p.h, p.d,
+                     b.tgt_user, b.user_nchunks, tgt_off, b.part_base, b.part_A, b.part_ms, abar);
+  return hipGetLastError();
+}
+
+}  // namespace stca

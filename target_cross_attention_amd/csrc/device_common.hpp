@@ -1,0 +1,84 @@
+// Device-side helpers shared by the libstca HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace stca {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define STCA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- scalar conversions ------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) { return (bf16)f; }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (bf16)f);
+}
+
+template <typename T> struct elem;
+template <> struct elem<float> {
+  __device__ __forceinline__ static float load(const float *p) { return *p; }
+  __device__ __forceinline__ static void store(float *p, float v) { *p = v; }
+};
+template <> struct elem<bf16> {
+  __device__ __forceinline__ static float load(const bf16 *p) {
+    return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(p));
+  }
+  __device__ __forceinline__ static void store(bf16 *p, float v) { *p = f32_to_bf16(v); }
+};
+
+template <typename T> __device__ __forceinline__ float ld(const T *p) { return elem<T>::load(p); }
+template <typename T> __device__ __forceinline__ void st(T *p, float v) { elem<T>::store(p, v); }
+
+// ---- math --------------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// a * SiLU(g) = a * g / (1 + e^-g), with e^-g = 2^(-g log2 e).  exp2 of a large positive
+// argument gives +inf and rcp(+inf) = 0, so very negative g yields -0 / 0 as it should.
+__device__ __forceinline__ float swiglu_gate(float a, float g) {
+  return a * g * fast_rcp(1.0f + fast_exp2(-g * kLog2e));
+}
+
+// ---- wave (64-lane) reductions -------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Value held by lane (lane ^ 32): swaps the two halves of the wave.
+__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+
+// ---- MFMA ----------------------------------------------------------------------------------
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] B[16x32].
+//   A: lane l holds row (l & 31), 8 k-slots of group (l >> 5).
+//   B: lane l holds column (l & 31), 8 k-slots of group (l >> 5).
+//   D: lane l holds column (l & 31); register i holds row 8*(i>>2) + 4*(l>>5) + (i&3).
+// The k index behind a (group, slot) pair is the same for A and B, so any assignment of
+// logical k to (group, slot) gives the right product as long as A and B use the same one.
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace stca

@@ -1,0 +1,73 @@
+// Internal (non-exported) interfaces between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace stca {
+
+// ---- generic fp32-accumulating kernels (generic.hip) ----------------------------------------
+struct GemmArgs {
+  int M = 0, N = 0, K = 0, batch = 1;
+  const void *A = nullptr;
+  int64_t lda = 0, sA = 0;
+  bool ta_bf16 = false;
+  const void *B = nullptr;
+  int64_t ldb = 0, sB = 0;
+  bool tb_bf16 = false, trans_b = false;
+  void *C = nullptr;
+  int64_t ldc = 0, sC = 0;
+  bool tc_bf16 = false;
+  float alpha = 1.f, beta = 0.f;
+};
+hipError_t gemm(hipStream_t s, const GemmArgs &g);
+hipError_t swiglu_gate_inplace(hipStream_t s, int64_t n, float *A, const float *G);
+hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, int64_t ldy, void *out,
+                          int64_t ldo, bool out_bf16, const float *gamma, const float *beta, float eps);
+
+// ---- fused bf16 MFMA encode (encode_mfma.hip) -----------------------------------------------
+// Re-layout of one FFN's W_u, W_v (d x rd) and W_o (rd x d) into MFMA fragment order.
+size_t encode_packed_bytes(int d, int r);
+hipError_t encode_pack(hipStream_t s, int d, int r, const void *Wu, const void *Wv, const void *Wo,
+                       void *packed);
+// out[n x d] = LN(SwiGLUFFN(X)) (apply_ln) or SwiGLUFFN(X); X bf16 (row stride ldx);
+// out bf16 or fp32 (row stride ldo).
+hipError_t encode_mfma(hipStream_t s, int d, int r, int64_t n_rows, const void *X, int64_t ldx,
+                       const void *packed, void *out, int64_t ldo, bool out_bf16, bool apply_ln,
+                       const float *gamma, const float *beta, float eps);
+
+// ---- ragged split-L attention (attend.hip) --------------------------------------------------
+constexpr int kRowsPerGroup = 128;  // query rows one attention work item covers (4 waves x 32)
+
+struct WorkItem {
+  int32_t user, chunk, group, n_chunks;
+};
+
+struct AttnPlan {
+  int n_users = 0, h = 0, d = 0, chunk = 0;
+  int64_t total_L = 0, total_T = 0;
+  int64_t max_items = 0;      // grid bound
+  int64_t max_part_rows = 0;  // partial-state rows bound
+};
+
+struct AttnBuffers {
+  WorkItem *items = nullptr;
+  int32_t *n_items = nullptr;
+  int32_t *user_nchunks = nullptr;
+  int64_t *part_base = nullptr;
+  int32_t *tgt_user = nullptr;
+  float *part_A = nullptr;   // max_part_rows x d
+  float *part_ms = nullptr;  // max_part_rows x 2  (running max, sum)
+};
+
+hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_off, const int64_t *tgt_off,
+                          const AttnBuffers &b);
+// abar[T*h x d] (fp32): attention-weighted history per (target, head), eq. (13); U (T*h x d) holds
+// u pre-scaled by log2(e)/sqrt(d_h).  Xt and U are bf16 (MFMA path) or fp32 (debug path).
+hipError_t attend_split(hipStream_t s, const AttnPlan &p, bool bf16_path, const int64_t *hist_off,
+                        const int64_t *tgt_off, const void *Xt, const void *U, float *abar,
+                        const AttnBuffers &b);
+hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_off, float *abar,
+                          const AttnBuffers &b);
+
+}  // namespace stca

@@ -1,0 +1,163 @@
+"""C ABI checks that need no GPU: exports, status codes, workspace sizing and the host-side
+argument validation (every error below is returned before any device work is enqueued, so
+placeholder device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import stca_inputs as SI
+from target_cross_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 16-byte aligned placeholder device address (never dereferenced)
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "stca.h")).read()
+    return sorted(set(re.findall(r"STCA_API\s+(?:const\s+)?\w+\s*\*?\s*(stca_\w+)\s*\(", txt)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 14
+    assert set(names) == set(B.EXPORTS)
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert B.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert B.status_string(code) != "unknown status"
+    assert "gfx950" in B.version()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        B._load()
+
+
+def _fake_weights(M, with_wc=True):
+    w = B.WeightsC()
+    for i in range(M):
+        w.hist[i] = B.Ffn(FAKE, FAKE, FAKE, FAKE, FAKE)
+        w.query[i] = B.Ffn(FAKE, FAKE, FAKE, FAKE, FAKE)
+        w.WQ[i] = w.WK[i] = w.WV[i] = w.WO[i] = FAKE
+        w.WC[i] = FAKE if (with_wc and i >= 1) else None
+    return w
+
+
+def _batch(n=4, L=100, T=3, max_L=None, max_T=None):
+    return B.BatchC(n, FAKE, FAKE, n * L, n * T, L if max_L is None else max_L, T if max_T is None else max_T)
+
+
+def _forward(dims, w, batch, X=FAKE, xt=FAKE, Z=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return B.LIB.stca_forward(ctypes.byref(dims) if dims is not None else None, ctypes.byref(w),
+                              ctypes.byref(batch), X, xt, Z, ws, ws_bytes, None)
+
+
+def test_workspace_sizes():
+    cfg = SI.get_config("dense10k")
+    dims = B.dims_for(cfg)
+    b = _batch(n=1024, L=10000, T=16)
+    fw = B.forward_workspace_size(dims, b)
+    aw = B.attend_workspace_size(dims, b)
+    ew = B.encode_workspace_size(dims, 10_240_000)
+    # the forward holds one encoded history (sum L x d bf16) plus the attention workspace
+    assert fw >= 10_240_000 * 256 * 2 + aw
+    assert ew == (4 * 256 // 32) * (3 * 256 // 16) * 1024  # packed weights only
+    assert B.forward_workspace_size(dims, _batch(n=2048, L=10000, T=16)) > fw
+    f32 = B.make_dims(64, 4, 1, 2, "f32")
+    assert B.encode_workspace_size(f32, 256) > 0
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(d=96), -2), (dict(d=0), -2), (dict(h=3), -2), (dict(h=0), -2), (dict(r=0), -2), (dict(r=9), -2),
+    (dict(M=0), -2), (dict(M=9), -2), (dict(dtype=7), -2), (dict(ln_eps=0.0), -2), (dict(attn_chunk=33), -2),
+    (dict(attn_chunk=-32), -2),
+])
+def test_forward_rejects_bad_dims(change, code):
+    kw = dict(d=256, h=8, M=3, r=4, dtype="bf16", ln_eps=1e-5, attn_chunk=0)
+    dt = change.pop("dtype", None)
+    kw.update(change)
+    dims = B.make_dims(**kw)
+    if dt is not None:
+        dims.dtype = dt
+    assert _forward(dims, _fake_weights(3), _batch()) == code
+    assert B.last_error()
+
+
+def test_forward_rejects_bad_pointers_and_sizes():
+    dims = B.make_dims(256, 8, 3, 4)
+    w = _fake_weights(3)
+    b = _batch()
+    assert B.LIB.stca_forward(None, ctypes.byref(w), ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+    assert _forward(dims, w, b, X=None) == -1
+    assert _forward(dims, w, b, Z=None) == -1
+    assert _forward(dims, w, b, X=FAKE + 8) == -4
+    assert _forward(dims, w, b, ws=FAKE + 4) == -4
+    assert _forward(dims, w, b, ws_bytes=1024) == -3
+    assert _forward(dims, w, b, ws=None) == -3
+    w2 = _fake_weights(3, with_wc=False)
+    assert _forward(dims, w2, b) == -1
+    w3 = _fake_weights(3)
+    w3.hist[1] = B.Ffn(FAKE, FAKE, FAKE + 2, FAKE, FAKE)
+    assert _forward(dims, w3, b) == -4
+    w4 = _fake_weights(3)
+    w4.hist[0] = B.Ffn(FAKE, FAKE, FAKE, None, FAKE)  # history LayerNorm needs gamma
+    assert _forward(dims, w4, b) == -1
+    # the layer-1.. query FFN has no LayerNorm unless query_ln: gamma may be NULL there
+    w5 = _fake_weights(3)
+    w5.query[1] = B.Ffn(FAKE, FAKE, FAKE, None, None)
+    assert _forward(dims, w5, b, ws_bytes=1024) == -3  # passes weight checks, fails on workspace
+    dims_qln = B.make_dims(256, 8, 3, 4, query_ln=True)
+    assert _forward(dims_qln, w5, b) == -1
+
+
+def test_forward_rejects_inconsistent_batch():
+    dims = B.make_dims(256, 8, 3, 4)
+    w = _fake_weights(3)
+    assert _forward(dims, w, _batch(max_L=50)) == -1         # max_L * n < total_L
+    assert _forward(dims, w, _batch(max_T=1)) == -1          # max_T * n < total_T
+    assert _forward(dims, w, _batch(max_L=1000)) == -1       # max_L > total_L
+    assert _forward(dims, w, B.BatchC(-1, FAKE, FAKE, 0, 0, 0, 0)) == -1
+    assert _forward(dims, w, B.BatchC(2, None, FAKE, 10, 2, 5, 1)) == -1
+    assert _forward(dims, w, B.BatchC(2, FAKE + 8, FAKE, 10, 2, 5, 1)) == -4
+    assert _forward(dims, w, B.BatchC(0, None, None, 5, 0, 0, 0)) == -1
+
+
+def test_forward_with_no_targets_is_a_no_op():
+    dims = B.make_dims(256, 8, 3, 4)
+    b = B.BatchC(2, FAKE, FAKE, 10, 0, 5, 0)
+    need = B.forward_workspace_size(dims, b)
+    assert _forward(dims, _fake_weights(3), b, ws_bytes=need) == 0
+
+
+def test_encode_and_attend_validation():
+    dims = B.make_dims(128, 8, 2, 2)
+    ffn = B.Ffn(FAKE, FAKE, FAKE, FAKE, FAKE)
+    L = B.LIB
+    assert L.stca_encode(ctypes.byref(dims), ctypes.byref(ffn), -1, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.stca_encode(ctypes.byref(dims), ctypes.byref(ffn), 10, FAKE + 2, FAKE, FAKE, 1 << 30, None) == -4
+    assert L.stca_encode(ctypes.byref(dims), ctypes.byref(ffn), 10, FAKE, FAKE, FAKE, 16, None) == -3
+    assert L.stca_encode(ctypes.byref(dims), ctypes.byref(ffn), 0, FAKE, FAKE, FAKE, 1 << 30, None) == 0
+    w = _fake_weights(2)
+    b = _batch()
+    for layer in (-1, 2):
+        assert L.stca_attend(ctypes.byref(dims), ctypes.byref(w), layer, ctypes.byref(b), FAKE, FAKE, FAKE, FAKE,
+                             1 << 40, None) == -1
+    assert L.stca_attend(ctypes.byref(dims), ctypes.byref(w), 0, ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 64,
+                         None) == -3
+
+
+def test_profiler_lifecycle_without_launches():
+    p = B.Profiler()
+    p.reset()
+    rep = p.read()
+    assert set(rep) == set(B.PHASE_NAMES)
+    assert all(v == (0.0, 0) for v in rep.values())
+    p.close()

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on identical seeded inputs.
+
+Error measure: max over output rows of max_k |gpu - oracle| / max_k |oracle|; bars 2e-2 for the
+bf16 storage path, 1e-4 for the fp32 debug path.
+"""
+import numpy as np
+import pytest
+
+import stca_inputs as SI
+from oracle import stca as O
+from stca_testlib import announce, row_rel, tol_for
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from target_cross_attention_amd import binding
+    return binding
+
+
+DEV = "cuda:0"
+
+
+def run_forward(B, cfg, inp, W, **dims_kw):
+    dw = B.DeviceWeights(W, cfg.dtype, DEV)
+    db = B.DeviceBatch(inp, DEV)
+    Z = B.stca_forward(B.dims_for(cfg, **dims_kw), dw, db)
+    torch.cuda.synchronize()
+    return Z.cpu().numpy()
+
+
+REDUCED = [
+    ("tiny", dict()),
+    ("uniform", dict(n_users=6)),
+    ("ragged", dict(n_users=24)),
+    ("dense10k", dict(n_users=3)),
+    ("stress20k", dict(n_users=2, length=("fixed", 2500))),
+]
+
+
+@pytest.mark.parametrize("key,change", REDUCED, ids=[k for k, _ in REDUCED])
+def test_forward_reduced(B, key, change):
+    cfg = SI.scaled(SI.get_config(key), **change)
+    announce("forward", cfg.key, cfg.dtype, change)
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    Z = run_forward(B, cfg, inp, W)
+    ref = O.forward_batch(inp, W)
+    err = row_rel(Z, ref)
+    print(f"  {key}: users={inp.n_users} L={inp.total_L} T={inp.total_T} err={err:.3e}", flush=True)
+    assert err <= tol_for(cfg)
+
+
+FP32_SHAPES = [
+    ("uniform", dict(n_users=3, dtype="f32")),
+    ("ragged", dict(n_users=10, dtype="f32", length=("lognormal", 300.0, 400.0, 1, 2000))),
+    ("dense10k", dict(n_users=2, dtype="f32", length=("fixed", 1500))),
+    ("stress20k", dict(n_users=1, dtype="f32", length=("fixed", 777), targets=("fixed", 5))),
+]
+
+
+@pytest.mark.parametrize("key,change", FP32_SHAPES, ids=[k for k, _ in FP32_SHAPES])
+def test_forward_fp32_debug_path(B, key, change):
+    cfg = SI.scaled(SI.get_config(key), **change)
+    announce("forward-fp32", cfg.key, change)
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    err = row_rel(run_forward(B, cfg, inp, W), O.forward_batch(inp, W))
+    print(f"  fp32 {key}: err={err:.3e}", flush=True)
+    assert err <= 1e-4
+
+
+# ---------------------------------------------------------------------------------------------
+# the two boundary calls on their own
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("d,r,dtype,n", [(64, 2, "f32", 300), (64, 2, "bf16", 300), (128, 2, "bf16", 1000),
+                                         (256, 4, "bf16", 4133), (512, 4, "bf16", 517), (256, 4, "f32", 517),
+                                         (128, 1, "bf16", 129), (256, 3, "bf16", 31)])
+def test_encode(B, d, r, dtype, n):
+    cfg = SI.scaled(SI.get_config("ragged"), d=d, r=r, h=8, M=1, dtype=dtype, n_users=1, length=("fixed", n),
+                    targets=("fixed", 1))
+    announce("encode", d, r, dtype, n)
+    W = SI.make_weights(cfg, random_ln=True)
+    inp = SI.make_inputs(cfg)
+    dims = B.dims_for(cfg)
+    dw = B.DeviceWeights(W, dtype, DEV)
+    X = B.to_device(inp.X, dtype, DEV)
+    Xt = B.stca_encode(dims, dw.c.hist[0], X)
+    torch.cuda.synchronize()
+    got = Xt.float().cpu().numpy()
+    ref = O.encode(inp.user_X(0), W.Wu[0], W.Wv[0], W.Wo[0], W.gamma[0], W.beta[0])
+    err = row_rel(got, ref)
+    print(f"  encode d={d} r={r} {dtype} n={n}: err={err:.3e}", flush=True)
+    assert err <= (2e-2 if dtype == "bf16" else 1e-4)
+
+
+def _attend_case(B, cfg, inp, W, layer, chunk):
+    """o from stca_attend given the oracle's encoded history and queries (rounded to storage)."""
+    dims = B.dims_for(cfg, attn_chunk=chunk)
+    dw = B.DeviceWeights(W, cfg.dtype, DEV)
+    db = B.DeviceBatch(inp, DEV)
+    Xts, qs, refs = [], [], []
+    for k in range(inp.n_users):
+        tr = {}
+        O.forward_user(inp.user_X(k), inp.user_xt(k), W, cfg.h, cfg.M, trace=tr)
+        Xt = tr["Xt"][layer].astype(np.float32)
+        if cfg.dtype == "bf16":
+            Xt = SI.bf16_round(Xt)
+        q = tr["q"][layer].astype(np.float32)
+        Xts.append(Xt)
+        qs.append(q)
+        refs.append(O.attend_reordered(q, Xt, W.WQ[layer], W.WK[layer], W.WV[layer], W.WO[layer], cfg.h)[0])
+    Xt_d = B.to_device(np.concatenate(Xts), cfg.dtype, DEV)
+    q_d = torch.from_numpy(np.concatenate(qs)).to(DEV)
+    o = B.stca_attend(dims, dw, layer, db, Xt_d, q_d)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), np.concatenate(refs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("chunk", [0, 64, 96, 1024])
+def test_attend_ragged_split(B, dtype, chunk):
+    """Ragged lengths (1 .. ~1500, not multiples of 32), 1..several targets, several chunk sizes
+    so users span one or many split-L chunks and the combine step runs."""
+    cfg = SI.scaled(SI.get_config("ragged"), d=128, h=8, M=2, r=2, n_users=9, dtype=dtype,
+                    length=("lognormal", 200.0, 300.0, 1, 1500))
+    announce("attend", dtype, "chunk", chunk)
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    assert inp.L.min() < 32 and np.any(inp.L % 32 != 0)
+    for layer in (0, 1):
+        got, ref = _attend_case(B, cfg, inp, W, layer, chunk)
+        err = row_rel(got, ref)
+        print(f"  attend {dtype} chunk={chunk} layer={layer}: err={err:.3e}", flush=True)
+        assert err <= (2e-2 if dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("d,h", [(64, 4), (256, 8), (512, 16)])
+def test_attend_many_rows(B, d, h):
+    """m*h query rows above one 128-row group (and not a multiple of 32)."""
+    cfg = SI.scaled(SI.get_config("ragged"), d=d, h=h, M=1, r=2, n_users=2, targets=("fixed", 37 * 8 // h),
+                    length=("fixed", 333))
+    announce("attend-many-rows", d, h)
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    got, ref = _attend_case(B, cfg, inp, W, 0, 0)
+    err = row_rel(got, ref)
+    print(f"  rows={inp.m[0] * h}: err={err:.3e}", flush=True)
+    assert err <= 2e-2
+
+
+# ---------------------------------------------------------------------------------------------
+# edge cases and request-level-batching invariants
+# ---------------------------------------------------------------------------------------------
+def _custom_inputs(cfg, L, m, users_seed=0):
+    """A batch with given per-user lengths / target counts, drawn from the workload's streams."""
+    L = np.asarray(L, np.int64)
+    m = np.asarray(m, np.int64)
+    hoff, toff = SI.offsets(L), SI.offsets(m)
+    bf = cfg.dtype == "bf16"
+    X = np.concatenate([SI.user_history(cfg, 1000 + users_seed + u, max(int(l), 0)) for u, l in enumerate(L)]) \
+        if L.sum() else np.zeros((0, cfg.d), np.float32)
+    xt = SI.targets(cfg, int(m.sum()))
+    if bf:
+        X, xt = SI.bf16_bits(X), SI.bf16_bits(xt)
+    return SI.Inputs(cfg, np.arange(len(L)), L, m, hoff, toff, X, xt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_lengths_and_targets(B, dtype):
+    cfg = SI.scaled(SI.get_config("ragged"), d=128, h=8, M=3, r=2, dtype=dtype)
+    L = [1, 31, 32, 33, 64, 0 + 2, 10000, 65, 1]
+    m = [3, 0, 1, 2, 5, 1, 2, 0, 1]
+    announce("edges", dtype, L, m)
+    inp = _custom_inputs(cfg, L, m)
+    W = SI.make_weights(cfg, random_ln=True, separate_query_ffn=True)
+    for qln in (False, True):
+        Z = run_forward(B, cfg, inp, W, query_ln=qln, attn_chunk=64)
+        ref = O.forward_batch(inp, W, query_ln=qln)
+        err = row_rel(Z, ref)
+        print(f"  {dtype} query_ln={qln}: err={err:.3e}", flush=True)
+        assert err <= tol_for(cfg)
+
+
+def test_single_token_history_gives_projection_of_that_token(B):
+    cfg = SI.scaled(SI.get_config("ragged"), d=256, h=8, M=1, r=4)
+    inp = _custom_inputs(cfg, [1, 1], [4, 2])
+    announce("L=1")
+    W = SI.make_weights(cfg)
+    Z = run_forward(B, cfg, inp, W)
+    for k in range(2):
+        Xt = O.encode(inp.user_X(k), W.Wu[0], W.Wv[0], W.Wo[0], W.gamma[0], W.beta[0])
+        closed = (Xt @ W.WV[0].astype(np.float64)) @ W.WO[0].astype(np.float64)   # alpha = [1]
+        zk = Z[inp.tgt_off[k]:inp.tgt_off[k + 1], 0]
+        assert row_rel(zk, np.repeat(closed, len(zk), 0)) <= 2e-2
+
+
+def test_empty_history_user_gets_nan_and_others_unaffected(B):
+    cfg = SI.scaled(SI.get_config("ragged"), d=128, h=8, M=2, r=2)
+    inp = _custom_inputs(cfg, [50, 0, 70], [2, 3, 1])
+    announce("empty history")
+    W = SI.make_weights(cfg)
+    Z = run_forward(B, cfg, inp, W)
+    assert np.all(np.isnan(Z[2:5]))
+    keep = np.r_[0:2, 5:6]
+    parts = [O.forward_user(inp.user_X(k), inp.user_xt(k), W, cfg.h) for k in (0, 2)]
+    assert row_rel(Z[keep], np.concatenate(parts)) <= 2e-2
+
+
+def test_batching_is_layout_only(B):
+    """A batch of users equals one call per user, and permuting users permutes rows (bitwise, fixed chunk)."""
+    cfg = SI.scaled(SI.get_config("ragged"), d=256, h=8, M=3, r=4, n_users=7)
+    announce("rlb layout")
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    Z = run_forward(B, cfg, inp, W, attn_chunk=256)
+    for k in range(inp.n_users):
+        one = SI.make_inputs(cfg, users=[k])
+        Zk = run_forward(B, cfg, one, W, attn_chunk=256)
+        assert np.array_equal(Zk, Z[inp.tgt_off[k]:inp.tgt_off[k + 1]]), k
+    perm = [3, 0, 6, 1, 5, 2, 4]
+    L = inp.L[perm]
+    m = inp.m[perm]
+    X = np.concatenate([inp.X[inp.hist_off[k]:inp.hist_off[k + 1]] for k in perm])
+    xt = np.concatenate([inp.xt[inp.tgt_off[k]:inp.tgt_off[k + 1]] for k in perm])
+    pinp = SI.Inputs(cfg, np.array(perm), L, m, SI.offsets(L), SI.offsets(m), X, xt)
+    Zp = run_forward(B, cfg, pinp, W, attn_chunk=256)
+    Zref = np.concatenate([Z[inp.tgt_off[k]:inp.tgt_off[k + 1]] for k in perm])
+    assert np.array_equal(Zp, Zref)
+
+
+def test_user_isolation_under_nan(B):
+    cfg = SI.scaled(SI.get_config("ragged"), d=128, h=8, M=2, r=2, n_users=5)
+    announce("isolation")
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    base = run_forward(B, cfg, inp, W, attn_chunk=128)
+    bad = SI.Inputs(cfg, inp.users, inp.L, inp.m, inp.hist_off, inp.tgt_off, inp.X.copy(), inp.xt)
+    a = 2
+    bad.X[inp.hist_off[a] + inp.L[a] // 2] = 0x7FC0  # a bf16 NaN in one token of user a
+    Z = run_forward(B, cfg, bad, W, attn_chunk=128)
+    rows_a = np.arange(inp.tgt_off[a], inp.tgt_off[a + 1])
+    others = np.setdiff1d(np.arange(inp.total_T), rows_a)
+    assert np.all(np.isnan(Z[rows_a]))
+    assert np.array_equal(Z[others], base[others])
+
+
+def test_repeat_runs_are_bitwise_identical(B):
+    cfg = SI.scaled(SI.get_config("dense10k"), n_users=4, length=("fixed", 3000))
+    announce("determinism")
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    dw = B.DeviceWeights(W, cfg.dtype, DEV)
+    db = B.DeviceBatch(inp, DEV)
+    dims = B.dims_for(cfg, attn_chunk=1024)
+    Z1 = B.stca_forward(dims, dw, db).cpu().numpy()
+    Z2 = B.stca_forward(dims, dw, db).cpu().numpy()
+    assert np.array_equal(Z1, Z2)
