@@ -61,6 +61,10 @@ class StcaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libstca.so not built at {LIB_PATH}; run `python -m target_cross_attention_amd.build`")
+    # PyTorch ships its own HIP runtime (same soname, libamdhip64.so.7).  Loading it first makes
+    # the dynamic loader bind libstca to that one copy, so device memory and streams created by
+    # torch are valid in libstca's calls; loading libstca first would bring in a second runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = c_void_p
     sig = {

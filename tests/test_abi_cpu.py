@@ -161,3 +161,11 @@ def test_profiler_lifecycle_without_launches():
     assert set(rep) == set(B.PHASE_NAMES)
     assert all(v == (0.0, 0) for v in rep.values())
     p.close()
+
+
+def test_one_hip_runtime_in_process():
+    """libstca binds to the HIP runtime torch already loaded (one copy per process)."""
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    hsa = {ln.split()[-1] for ln in maps if "libhsa-runtime64" in ln}
+    assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
