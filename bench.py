@@ -21,7 +21,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def log(*a):
