@@ -106,7 +106,8 @@ int auto_chunk(const stca_dims *dm, const stca_batch *b) {
   if (dm->attn_chunk > 0) return dm->attn_chunk;
   // Aim for >= ~2 work items per workgroup slot of the chip, but keep chunks long enough
   // that the partial-state traffic stays small next to the history bytes.
-  const int64_t groups = std::max<int64_t>(1, (b->max_T * dm->h + kRowsPerGroup - 1) / kRowsPerGroup);
+  const int rpg = attn_rows_per_group(dm->d);
+  const int64_t groups = std::max<int64_t>(1, (b->max_T * dm->h + rpg - 1) / rpg);
   const int64_t target_items = 2048;
   int64_t c = (b->total_L * groups + target_items - 1) / target_items;
   c = std::max<int64_t>(c, 512);
@@ -123,7 +124,8 @@ AttnPlan make_plan(const stca_dims *dm, const stca_batch *b) {
   p.chunk = auto_chunk(dm, b);
   p.total_L = b->total_L;
   p.total_T = b->total_T;
-  const int64_t groups = (b->max_T * dm->h + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int rpg = attn_rows_per_group(dm->d);
+  const int64_t groups = (b->max_T * dm->h + rpg - 1) / rpg;
   const int64_t chunks_ceil = (b->total_L + p.chunk - 1) / p.chunk;
   // sum_u ceil(L_u / c) ceil(m_u h / 128) <= (total_L / c + n_users) * ceil(max_T h / 128)
   p.max_items = b->total_T > 0 ? (chunks_ceil + b->n_users) * groups : 0;

@@ -14,6 +14,8 @@
 // otherwise the partial (max, sum, accumulator) triples are merged by attend_combine.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -26,7 +28,7 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // One workgroup; users in blocks of 1024 with a block-wide prefix sum.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64_t *__restrict__ hoff,
-                                                        const int64_t *__restrict__ toff, int h, int chunk,
+                                                        const int64_t *__restrict__ toff, int h, int chunk, int rpg,
                                                         int64_t max_items, WorkItem *__restrict__ items,
                                                         int32_t *__restrict__ n_items,
                                                         int32_t *__restrict__ user_nchunks,
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64
       const int64_t L = hoff[u + 1] - hoff[u];
       const int64_t R = (toff[u + 1] - toff[u]) * h;
       nc = L > 0 ? (int)((L + chunk - 1) / chunk) : 0;
-      ng = (int)((R + kRowsPerGroup - 1) / kRowsPerGroup);
+      ng = (int)((R + rpg - 1) / rpg);
       ni = R > 0 ? (int64_t)nc * ng : 0;
       np = nc > 1 ? (int64_t)nc * R : 0;
       user_nchunks[u] = nc;
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64
 hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_off, const int64_t *tgt_off,
                           const AttnBuffers &b) {
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, p.n_users, hist_off, tgt_off, p.h, p.chunk,
-                     p.max_items, b.items, b.n_items, b.user_nchunks, b.part_base, b.tgt_user);
+                     attn_rows_per_group(p.d), p.max_items, b.items, b.n_items, b.user_nchunks, b.part_base, b.tgt_user);
   return hipGetLastError();
 }
 
@@ -89,10 +91,32 @@ hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_
 //   update  O^T[d x row]  += X~_tile^T[d x tok] P^T[tok x row]  (A from LDS, B = P in registers)
 // The accumulator layout of S^T is, per lane, one query row and 16 tokens; taking the
 // probabilities of registers 8 kk .. 8 kk + 7 as the B operand of k-step kk pairs them with the
-// tokens phi(kk, g, e) = 16 kk + 8 (e>>2) + 4 g + (e&3), which the A operand reads from LDS.
+// tokens phi(kk, g, e) = 16 kk + 8 (e>>2) + 4 g + (e&3), which the A operand reads from LDS with
+// the transposing 64-bit LDS read (ds_read_b64_tr_b16: within each 16-lane group, lane i gets
+// element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3), two per fragment.
 // LDS tile layout: 32 rows x d/8 16-byte chunks, chunk c of row t stored at position
 // c ^ (t & SWZ) so both the row-wise and the column-wise reads spread over the banks.
+// History tiles stream through an NST-deep LDS ring (direct global->LDS loads), keeping
+// (NST-1) tiles in flight per workgroup.
 // ------------------------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+// Swizzle of the history tile: 16-byte chunk c of row t is stored at chunk position c ^ sigma(t).
+// For d >= 128, sigma swaps the two low 2-bit fields of t (bit 4 passes through at d >= 256): a
+// bijection on the row index, so the 16 rows of a row-wise read quarter still hit 16 different
+// chunk positions, while the 8 rows x 4 chunks touched by a transposed read half-wave land on
+// 32 different 8-byte bank pairs.  d = 64 (8 chunks per row) keeps sigma(t) = t & 7.
+template <int D> __device__ __forceinline__ int tile_sigma(int t) {
+  if constexpr (D >= 256) return ((t & 3) << 2) | ((t >> 2) & 3) | (t & 16);
+  else if constexpr (D == 128) return ((t & 3) << 2) | ((t >> 2) & 3);
+  else return t & 7;
+}
+
+// Softmax running-max slack (log2 units): rescale the accumulators only when a row's maximum
+// grows by more than this.  Exact (the same reference maximum normalises numerator and
+// denominator); probabilities stay <= 2^kLazy.
+constexpr float kLazy = 8.0f;
+
 template <int D>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
@@ -103,7 +127,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr int SWZ = (CPR < 32 ? CPR : 32) - 1;  // swizzle mask
   constexpr int NKS = D / 16, NOB = D / 32;
   constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
-  __shared__ bf16x8 tiles[2][32 * CPR];
+  constexpr int LPW = INSTR / 4;                  // per wave
+  constexpr int NST = D <= 256 ? 5 : 4;           // tile ring depth
+  // At d = 512 a wave keeps half of the output features: two waves share a 32-row block
+  // (both compute its scores), so U and the accumulators fit in one wave's registers.
+  constexpr int FH = attn_feature_halves(D);
+  constexpr int NOBW = NOB / FH;                  // output blocks per wave
+  static_assert(INSTR % 4 == 0, "tile loads split evenly over 4 waves");
+  __shared__ bf16x8 tiles[NST][32 * CPR];
 
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
@@ -115,26 +146,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   const int64_t T0 = toff[it.user];
   const int R = (int)((toff[it.user + 1] - T0) * h);
   const int64_t rowbase = T0 * h;
-  const int r0 = it.group * kRowsPerGroup + wave * 32;
+  const int fh = wave % FH;
+  const int r0 = it.group * attn_rows_per_group(D) + (wave / FH) * 32;
   const bool wave_active = r0 < R;
   const int myrow = r0 + col;
   const bool row_ok = myrow < R;
   const int ntiles = (int)((t1 - t0 + 31) / 32);
 
-  auto stage = [&](int k, int b) {
-    const int64_t tb = t0 + 32 * (int64_t)k;
-#pragma unroll
-    for (int j = wave; j < INSTR; j += 4) {
-      const int slot = j * 64 + lane;
-      const int row = slot / CPR, cs = slot % CPR;
-      const int c = cs ^ (row & SWZ);
-      const int64_t tok = (tb + row < t1) ? tb + row : t1 - 1;
-      __builtin_amdgcn_global_load_lds(Xt + tok * D + c * 8, (STCA_LDS void *)&tiles[b][j * 64], 16, 0, 0);
-    }
-  };
-
-  stage(0, 0);
-
+  // U rows as B operands (loaded first so that the tile loads below are the youngest in flight).
   bf16x8 ub[NKS];
   {
     const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + 8 * gl;
@@ -146,37 +165,90 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         ub[ks] = bf16x8{};
     }
   }
-  f32x16 oacc[NOB];
+
+  auto stage = [&](int k, int b) {
+    const int64_t tb = t0 + 32 * (int64_t)k;
 #pragma unroll
-  for (int ob = 0; ob < NOB; ++ob) oacc[ob] = f32x16{};
+    for (int jj = 0; jj < LPW; ++jj) {
+      const int j = wave + 4 * jj;
+      const int slot = j * 64 + lane;
+      const int row = slot / CPR, cs = slot % CPR;
+      const int c = cs ^ tile_sigma<D>(row);
+      const int64_t tok = (tb + row < t1) ? tb + row : t1 - 1;
+      __builtin_amdgcn_global_load_lds(Xt + tok * D + c * 8, (STCA_LDS void *)&tiles[b][j * 64], 16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ntiles) stage(p, p);
+
+  f32x16 oacc[NOBW];
+#pragma unroll
+  for (int ob = 0; ob < NOBW; ++ob) oacc[ob] = f32x16{};
   float m_run = -INFINITY, s_run = 0.f;
-  // Per-lane LDS byte offsets (see the column reads below).
+
+  // Per-lane LDS byte offsets.  Row-wise reads (scores): chunk (2 ks + gl) of row col sits at
+  // (2 ks) ^ rx with rx = gl ^ sigma(col).  Column-wise transposed reads (PV): lane
+  // l = 16 g + 4 j + q points at features 32 ob + 16 (g&1) + 4 q .. +3 of token
+  // tau = 16 kk + 8 s + 4 (g>>1) + j; each address is a per-lane base (one of NTB) plus a
+  // compile-time offset, see tr_offset().
   const uint32_t row_off = (uint32_t)(col * CPR * 16);
-  const uint32_t rx16 = (uint32_t)((gl ^ (col & SWZ)) * 16);
-  uint32_t cbase[2][4];
+  const uint32_t rx16 = (uint32_t)((gl ^ tile_sigma<D>(col)) * 16);
+  constexpr int NTB = D >= 128 ? 8 : 2;
+  uint32_t tbase[NTB];
+  {
+    const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+    const int g2 = g >> 1, g1 = g & 1, q1 = q >> 1, q0 = q & 1;
+    if constexpr (D >= 128) {
+      // chunk (4 ob + 2 g1 + q1) ^ sigma(tau), sigma(tau) = 4 j + 2 s + g2 (+ 16 kk at d >= 256):
+      // low bits (2 g1 + q1) ^ g2 ^ 2 s, high bits ob ^ (4 kk) ^ j.  Base index = 2 (P'&3) + s.
+      const int v1 = (2 * g1 + q1) ^ g2;
 #pragma unroll
-  for (int sgn = 0; sgn < 2; ++sgn)
+      for (int pk = 0; pk < 4; ++pk)
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq)
-      cbase[sgn][kq] = (uint32_t)(64 * CPR * gl + (sgn ? -64 : 64) * gl + 16 * ((col >> 3) ^ kq) + 2 * (col & 7));
+        for (int sh = 0; sh < 2; ++sh)
+          tbase[2 * pk + sh] =
+              (uint32_t)((4 * g2 + j) * CPR * 16 + 64 * (pk ^ j) + 16 * (v1 ^ (2 * sh)) + 8 * q0);
+    } else {
+      const int lo = (2 * g1 + q1) ^ j;
+      const int common = (4 * g2 + j) * CPR * 16 + 16 * lo + 8 * q0;
+      tbase[0] = (uint32_t)(common + 64 * g2);
+      tbase[1] = (uint32_t)(common - 64 * g2);
+    }
+  }
+  // (base index, compile-time byte offset) of the transposed read for (ob, kk, s).
+  auto tr_offset = [](int ob, int kk, int sh, int &bi) -> uint32_t {
+    if constexpr (D >= 128) {
+      const int Pp = ob ^ (D >= 256 ? 4 * kk : 0);
+      bi = 2 * (Pp & 3) + sh;
+      return (uint32_t)((16 * kk + 8 * sh) * CPR * 16 + 64 * (Pp & ~3));
+    } else {
+      const int P = ob ^ ((4 * kk + 2 * sh) & (SWZ >> 2));
+      bi = P & 1;
+      return (uint32_t)((16 * kk + 8 * sh) * CPR * 16 + 64 * P);
+    }
+  };
 
-  for (int k = 0; k < ntiles; ++k) {
-    const int b = k & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile k is in LDS; buffer b^1 is free
-    if (k + 1 < ntiles) stage(k + 1, b ^ 1);
-    if (!wave_active) continue;
-
-    const bf16x8 *tile = tiles[b];
-    const char *tbytes = reinterpret_cast<const char *>(tile);
-    f32x16 sc = f32x16{};
+  // All tile reads go through this LDS-typed base and 32-bit byte offsets (so they stay
+  // ds_read instructions, counted by lgkmcnt only, independent of the tile loads in flight).
+  const STCA_LDS char *lds = (const STCA_LDS char *)&tiles[0][0];
+  constexpr uint32_t kTileBytes = 32 * CPR * 16;
+  // Scores of one tile into two independent accumulation chains (halves of the d reduction).
+  auto scores = [&](uint32_t toff, f32x16 &s0, f32x16 &s1) {
+    uint32_t rx = rx16, rb = toff + row_off;
+    asm volatile("" : "+v"(rx), "+v"(rb));
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      // chunk (2 ks + gl) of row col, stored at (2 ks + gl) ^ (col & SWZ) = (2 ks) ^ rx
-      const uint32_t off = row_off + (((uint32_t)(32 * ks)) ^ rx16);
-      sc = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(tbytes + off), ub[ks], sc);
+      const uint32_t off = rb + (((uint32_t)(32 * ks)) ^ rx);
+      const bf16x8 a = *(const STCA_LDS bf16x8 *)(lds + off);
+      if (ks & 1)
+        s1 = mfma32x32x16(a, ub[ks], ks == 1 ? f32x16{} : s1);
+      else
+        s0 = mfma32x32x16(a, ub[ks], ks == 0 ? f32x16{} : s0);
     }
-    const int64_t rem = t1 - (t0 + 32 * (int64_t)k);
+  };
+  // Raw scores of a tile with `rem` valid tokens -> masked scores and their per-row maximum.
+  auto row_max = [&](f32x16 &sc, int rem) {
     if (rem < 32) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -187,18 +259,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     float mx = sc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx);
-    if (wave_any(m_new > m_run)) {
-      const float sf = fast_exp2(m_run - m_new);
-#pragma unroll
-      for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[ob][i] *= sf;
-      s_run *= sf;
-      m_run = m_new;
-    }
-    bf16x8 pb[2];
+    return fmaxf(mx, swap_halves(mx));
+  };
+  // bf16 probabilities 2^(s - m_run) (B operands of the PV product); their sum goes into s_run.
+  auto probs = [&](const f32x16 &sc, bf16x8 (&pb)[2]) {
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -207,26 +271,103 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       psum += (float)p;
     }
     s_run += psum;
-
-    // Column reads: A operand row = feature f = 32 ob + col, slot (gl, e) = token
-    // tau = 16 kk + 8 (e>>2) + 4 gl + (e&3), element f & 7 of chunk (f >> 3) ^ (tau & SWZ).
-    // (4 ob + (col>>3)) ^ tau splits into 4 (P ^ gl) + ((col>>3) ^ (e&3)) with the compile-time
-    // P = ob ^ ((4 kk + 2 (e>>2)) & (SWZ>>2)), and P ^ gl = P + gl (P even) or P - gl (P odd);
-    // so every address is one of 8 per-lane bases plus an immediate.
+  };
+  // PV product of one tile.
+  auto pv = [&](uint32_t toff, const bf16x8 (&pb)[2], auto FHc) {
+    constexpr int OB0 = decltype(FHc)::value * NOBW;  // first output block of this wave
+    uint32_t bb[NTB];
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob) {
+    for (int i = 0; i < NTB; ++i) {
+      bb[i] = tbase[i] + toff;
+      asm volatile("" : "+v"(bb[i]));
+    }
+#pragma unroll
+    for (int obw = 0; obw < NOBW; ++obw) {
+      const int ob = OB0 + obw;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 xa;
+        s16x4 half[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int P = ob ^ ((4 * kk + 2 * (e >> 2)) & (SWZ >> 2));
-          const uint32_t C = (uint32_t)((16 * kk + 8 * (e >> 2) + (e & 3)) * CPR * 16 + 64 * P);
-          xa[e] = *reinterpret_cast<const bf16 *>(tbytes + (cbase[P & 1][e & 3] + C));
+        for (int sh = 0; sh < 2; ++sh) {
+          int bi = 0;
+          const uint32_t C = tr_offset(ob, kk, sh, bi);
+          half[sh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + bb[bi] + C));
         }
-        oacc[ob] = mfma32x32x16(xa, pb[kk], oacc[ob]);
+        const bf16x8 xa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[obw] = mfma32x32x16(xa, pb[kk], oacc[obw]);
       }
     }
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, (FH > 1 ? 1 : 0)>;
+  auto tile_rem = [&](int k) {
+    const int64_t r = t1 - (t0 + 32 * (int64_t)k);
+    return (int)(r < 32 ? r : 32);
+  };
+  auto tile_off = [&](int k) { return (uint32_t)((k % NST) * kTileBytes); };
+
+  // Pipeline: iteration k computes the scores of tile k+1 (matrix cores) while the vector ALU
+  // turns the scores of tile k into probabilities, then the PV product of tile k.  Tiles k and
+  // k+1 are resident; tiles k+2 .. k+NST-2 are in flight; tile k+NST-1 is staged into the
+  // buffer of tile k-1.  The accumulators are touched only by MFMAs inside the loop: when a
+  // row maximum outgrows the slack the loop is left, the rescale runs, the tile is finished
+  // and the loop resumes.  The running maximum starts at the first tile's.
+  if (NST - 2 < ntiles)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 2)) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 sa = f32x16{}, sb = f32x16{};
+  if (wave_active) {
+    scores(tile_off(0), sa, sb);
+    f32x16 s0 = sa + sb;
+    m_run = row_max(s0, tile_rem(0));
+  }
+  auto tail = [&](int k, const f32x16 &sc, bool has_next) {
+    bf16x8 pb[2];
+    if (has_next) scores(tile_off(k + 1), sa, sb);
+    probs(sc, pb);
+    if constexpr (FH == 1) {
+      pv(tile_off(k), pb, H0{});
+    } else {
+      if (fh == 0)
+        pv(tile_off(k), pb, H0{});
+      else
+        pv(tile_off(k), pb, H1{});
+    }
+  };
+  int k = 0;
+  while (true) {
+    f32x16 sc;
+    float mx = 0.f;
+    for (; k < ntiles; ++k) {
+      const bool has_next = k + 1 < ntiles;
+      if (has_next) {
+        if (k + NST - 2 < ntiles)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 3)) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();  // tile k+1 is in LDS; tile k-1's buffer is free
+      if (k + NST - 1 < ntiles) stage(k + NST - 1, (k + NST - 1) % NST);
+      if (!wave_active) continue;
+      sc = sa + sb;
+      mx = row_max(sc, tile_rem(k));
+      if (wave_any(mx > m_run + kLazy)) break;
+      tail(k, sc, has_next);
+    }
+    if (k >= ntiles) break;
+    // rescale (rare), then finish tile k
+    const float m_new = fmaxf(m_run, mx);
+    const float sf = fast_exp2(m_run - m_new);
+#pragma unroll
+    for (int ob = 0; ob < NOBW; ++ob)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[ob][i] *= sf;
+    s_run *= sf;
+    m_run = m_new;
+    tail(k, sc, k + 1 < ntiles);
+    ++k;
   }
 
   if (!wave_active) return;
@@ -234,9 +375,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   if (!row_ok) return;
   if (it.n_chunks == 1) {
     const float inv = 1.0f / s_tot;
-    float *dst = abar + (rowbase + myrow) * D;
+    float *dst = abar + (rowbase + myrow) * D + fh * (D / FH);
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
+    for (int ob = 0; ob < NOBW; ++ob)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int f0 = 32 * ob + 8 * q + 4 * gl;
@@ -245,16 +386,16 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       }
   } else {
     const int64_t p = part_base[it.user] + (int64_t)it.chunk * R + myrow;
-    float *dst = part_A + p * D;
+    float *dst = part_A + p * D + fh * (D / FH);
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
+    for (int ob = 0; ob < NOBW; ++ob)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int f0 = 32 * ob + 8 * q + 4 * gl;
         *reinterpret_cast<f32x4 *>(dst + f0) =
             f32x4{oacc[ob][4 * q], oacc[ob][4 * q + 1], oacc[ob][4 * q + 2], oacc[ob][4 * q + 3]};
       }
-    if (gl == 0) {
+    if (gl == 0 && fh == 0) {
       part_ms[2 * p] = m_run;
       part_ms[2 * p + 1] = s_tot;
     }
@@ -280,9 +421,10 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
   const int64_t T0 = toff[it.user];
   const int R = (int)((toff[it.user + 1] - T0) * h);
   const int64_t rowbase = T0 * h;
-  const int rend = (it.group + 1) * kRowsPerGroup < R ? (it.group + 1) * kRowsPerGroup : R;
+  const int RG = attn_rows_per_group(D);
+  const int rend = (it.group + 1) * RG < R ? (it.group + 1) * RG : R;
 
-  for (int r = it.group * kRowsPerGroup + wave; r < rend; r += 4) {
+  for (int r = it.group * RG + wave; r < rend; r += 4) {
     float u[E], a[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {

@@ -16,6 +16,8 @@
 //     into LDS with direct global->LDS loads, double-buffered, and shared by the 4 waves;
 //   * the full d-wide output row of each token ends up in two lanes (l, l^32), so the LayerNorm
 //     epilogue is an in-register reduction plus one cross-half exchange.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -29,6 +31,8 @@ template <int D> struct EncShape {
   // is then read by each wave from global memory (L2-resident) instead.
   static constexpr bool WO_GLOBAL = (D > 256);
   static constexpr int FPS_LDS = WO_GLOBAL ? 2 * NKS : FPS;
+  // Three slice buffers fit in LDS up to d = 256 (3 x 48 KiB).
+  static constexpr bool PIPELINED = 3 * FPS_LDS * 1024 <= 160 * 1024;
 };
 
 size_t encode_packed_bytes(int d, int r) { return (size_t)(r * d / 32) * (size_t)(3 * d / 16) * 1024; }
@@ -84,6 +88,9 @@ hipError_t encode_pack(hipStream_t s, int d, int r, const void *Wu, const void *
 // ------------------------------------------------------------------------------------------
 // The fused kernel.
 // ------------------------------------------------------------------------------------------
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
+
 template <int D, bool LN, typename TO>
 __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int n_slices,
                                                              const bf16 *__restrict__ X, int64_t ldx,
@@ -92,7 +99,9 @@ __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int
                                                              const float *__restrict__ gamma,
                                                              const float *__restrict__ beta, float eps) {
   using S = EncShape<D>;
-  __shared__ bf16x8 wbuf[2][S::FPS_LDS][64];
+  // Three slice buffers when they fit: slices s and s+1 are read while s+2 streams in.
+  constexpr int NBUF = S::PIPELINED ? 3 : 2;
+  __shared__ bf16x8 wbuf[NBUF][S::FPS_LDS][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -103,13 +112,17 @@ __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int
   // waves take fragments round-robin.  Each lane moves 16 bytes; the destination of lane i is
   // the fragment base + 16 i.
   auto stage = [&](int s, int b) {
+    static_assert(S::FPS_LDS % 4 == 0, "fragments split evenly over 4 waves");
     const bf16x8 *src = packed + (int64_t)s * S::FPS * 64 + lane;
 #pragma unroll
-    for (int f = wave; f < S::FPS_LDS; f += 4)
+    for (int j = 0; j < S::FPS_LDS / 4; ++j) {
+      const int f = wave + 4 * j;
       __builtin_amdgcn_global_load_lds(src + f * 64, (STCA_LDS void *)&wbuf[b][f][0], 16, 0, 0);
+    }
   };
 
   stage(0, 0);
+  if constexpr (S::PIPELINED) stage(n_slices > 1 ? 1 : 0, 1);
 
   // The wave's 32 tokens as B operands: lane l holds token (l&31), features 16 ks + 8 (l>>5) + 0..7.
   bf16x8 xb[S::NKS];
@@ -128,26 +141,23 @@ __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int
 #pragma unroll
   for (int ob = 0; ob < S::NOB; ++ob) yacc[ob] = f32x16{};
 
-  for (int s = 0; s < n_slices; ++s) {
-    const int b = s & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // slice s is in LDS for every wave; buffer b^1 is no longer read
-    if (s + 1 < n_slices) stage(s + 1, b ^ 1);
-
-    // Up and gate products for hidden features 32 s .. 32 s + 31 (transposed: rows = features).
-    f32x16 accA = f32x16{}, accG = f32x16{};
+  // Up and gate products of one slice (transposed: rows = hidden features, columns = tokens).
+  auto up_gate = [&](int b, f32x16 &accA, f32x16 &accG) {
+    accA = f32x16{};
+    accG = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < S::NKS; ++ks) {
-      const bf16x8 wu = wbuf[b][ks][lane];
-      const bf16x8 wv = wbuf[b][S::NKS + ks][lane];
-      accA = mfma32x32x16(wu, xb[ks], accA);
-      accG = mfma32x32x16(wv, xb[ks], accG);
+      accA = mfma32x32x16(wbuf[b][ks][lane], xb[ks], accA);
+      accG = mfma32x32x16(wbuf[b][S::NKS + ks][lane], xb[ks], accG);
     }
-    // SwiGLU gate in registers -> bf16 B operands of the down product.
-    bf16x8 hb[2];
+  };
+  // SwiGLU gate in registers -> bf16 B operands of the down product.
+  auto gate = [&](const f32x16 &accA, const f32x16 &accG, bf16x8 (&hb)[2]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) hb[i >> 3][i & 7] = f32_to_bf16(swiglu_gate(accA[i], accG[i]));
-    // Down product: Y^T[out x tok] += W_o^T[out x 32] H^T[32 x tok].
+  };
+  // Down product: Y^T[out x tok] += W_o^T[out x 32] H^T[32 x tok].
+  auto down = [&](int s, int b, const bf16x8 (&hb)[2]) {
 #pragma unroll
     for (int ob = 0; ob < S::NOB; ++ob) {
 #pragma unroll
@@ -159,6 +169,180 @@ __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int
           wo = wbuf[b][2 * S::NKS + 2 * ob + kk][lane];
         yacc[ob] = mfma32x32x16(wo, hb[kk], yacc[ob]);
       }
+    }
+  };
+
+  if constexpr (S::PIPELINED) {
+    // Software pipeline over slices with no dependency inside a step.  Step t runs, on the matrix
+    // cores, the up/gate products of slice t+1 and the down product of slice t-1 (whose gate was
+    // computed in step t-1), and on the vector ALU the gate of slice t.  W_u/W_v and W_o slices
+    // live in separate 3-deep LDS rings; a slice is staged two steps before it is read, so each
+    // step waits only for loads issued one step earlier.  The instruction order is pinned
+    // (sched_barrier): fragment reads run kAhead MFMAs ahead through a register ring.
+    constexpr int FUP = 2 * S::NKS, FDN = 2 * S::NOB;
+#ifndef STCA_ENC_RING
+#define STCA_ENC_RING 8
+#endif
+    constexpr int kRing = STCA_ENC_RING, kAhead = STCA_ENC_RING - 2;
+    constexpr int kLoadsUV = FUP / 4, kLoadsO = FDN / 4;  // direct-to-LDS loads per wave
+    static_assert(FUP % 4 == 0 && FDN % 4 == 0, "fragments split evenly over 4 waves");
+    bf16x8 (*wuv)[S::FPS_LDS][64] = wbuf;  // wbuf[b][0 .. FUP)       : W_u/W_v ring (3 slots)
+    // W_o ring lives in wbuf[b][FUP .. FUP + FDN) of the same three slots.
+    auto stage_uv = [&](int t, int b) {
+      const bf16x8 *src = packed + (int64_t)t * S::FPS * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < kLoadsUV; ++j) {
+        const int f = wave + 4 * j;
+        __builtin_amdgcn_global_load_lds(src + f * 64, (STCA_LDS void *)&wuv[b][f][0], 16, 0, 0);
+      }
+    };
+    auto stage_o = [&](int t, int b) {
+      const bf16x8 *src = packed + ((int64_t)t * S::FPS + FUP) * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < kLoadsO; ++j) {
+        const int f = wave + 4 * j;
+        __builtin_amdgcn_global_load_lds(src + f * 64, (STCA_LDS void *)&wuv[b][FUP + f][0], 16, 0, 0);
+      }
+    };
+    // MFMA k of a full step: every third one is a down product (16 of 48 at d = 256).
+    // Fragment source of MFMA k: up k-th (u/v alternating per k-step) or down (ob, kk) ordered
+    // so that MFMAs into the same output block are NOB apart.
+    constexpr int kMM = FUP + FDN;
+    auto is_down = [](int k) { return (k % 3) == 2 && (k / 3) < FDN; };
+    auto up_idx = [](int k) { return k - (k / 3 < FDN ? (k + 1) / 3 : FDN); };
+    auto dn_idx = [](int k) { return k / 3; };
+
+    f32x16 accA, accG;   // up/gate accumulators of the slice in flight
+    bf16x8 hb_prev[2];   // gated slice t-1: B operands of the down product in step t
+    const int S_ = n_slices;
+
+    stage_uv(0, 0);
+    if (S_ > 1) stage_uv(1, 1);
+    if (S_ > 2) stage_uv(2, 2);
+    stage_o(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    up_gate(0, accA, accG);
+    __syncthreads();  // slot 0 of the W_u/W_v ring is restaged in step 0
+
+    // Steady-state step (1 <= t, t + 3 < n_slices) with t % 3 == T3 known at compile time, so
+    // every LDS fragment address is a constant offset from one per-lane base.
+    auto steady = [&](int t, auto T3c) {
+      constexpr int T3 = decltype(T3c)::value;
+      constexpr int BU = (T3 + 1) % 3, BD = (T3 + 2) % 3;
+      stage_uv(t + 3, T3);
+      stage_o(t + 1, (T3 + 1) % 3);
+      auto frag = [&](int k) -> bf16x8 {
+        if (is_down(k)) {
+          const int j = dn_idx(k);
+          return wuv[BD][FUP + 2 * (j % S::NOB) + (j / S::NOB)][lane];
+        }
+        const int i = up_idx(k);
+        return wuv[BU][(i & 1) ? S::NKS + (i >> 1) : (i >> 1)][lane];
+      };
+      float ga[16], gg[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        ga[e] = accA[e];
+        gg[e] = accG[e];
+      }
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int p = 0; p < kAhead; ++p) ring[p] = frag(p);
+      float hv[16];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kMM; ++k) {
+        if (k + kAhead < kMM) ring[(k + kAhead) % kRing] = frag(k + kAhead);
+        if (is_down(k)) {
+          const int j = dn_idx(k);
+          yacc[j % S::NOB] = mfma32x32x16(ring[k % kRing], hb_prev[j / S::NOB], yacc[j % S::NOB]);
+        } else {
+          const int i = up_idx(k);
+          if (i & 1)
+            accG = mfma32x32x16(ring[k % kRing], xb[i >> 1], i == 1 ? f32x16{} : accG);
+          else
+            accA = mfma32x32x16(ring[k % kRing], xb[i >> 1], i == 0 ? f32x16{} : accA);
+        }
+        // gate element e at MFMA 3e (16 elements over the first 48 MFMAs); the empty asm keeps
+        // the optimiser from sinking the arithmetic to its use after the MFMA stream.
+        if (k % 3 == 0 && k / 3 < 16) {
+          hv[k / 3] = swiglu_gate(ga[k / 3], gg[k / 3]);
+          asm volatile("" : "+v"(hv[k / 3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = kMM / 3; e < 16; ++e) hv[e] = swiglu_gate(ga[e], gg[e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) hb_prev[e >> 3][e & 7] = f32_to_bf16(hv[e]);
+      // Data read in step t+1 (W_u/W_v slice t+2, W_o slice t) was staged in step t-1 or before;
+      // this step's loads may stay in flight.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsUV + kLoadsO) : "memory");
+      __syncthreads();
+    };
+    // Any step, plain order (first and last steps).
+    auto general = [&](int t) {
+      const bool has_up = t + 1 < S_, has_down = t >= 1;
+      const bf16x8 *ub = &wuv[(t + 1) % 3][0][lane];
+      const bf16x8 *db = &wuv[(t + 2) % 3][FUP][lane];  // slot of slice t-1
+      if (t + 3 < S_) stage_uv(t + 3, t % 3);
+      if (t + 1 < S_) stage_o(t + 1, (t + 1) % 3);
+      float ga[16], gg[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        ga[e] = accA[e];
+        gg[e] = accG[e];
+      }
+      if (has_up) {
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks) {
+          accA = mfma32x32x16(ub[ks * 64], xb[ks], ks == 0 ? f32x16{} : accA);
+          accG = mfma32x32x16(ub[(S::NKS + ks) * 64], xb[ks], ks == 0 ? f32x16{} : accG);
+        }
+      }
+      if (has_down) {
+#pragma unroll
+        for (int j = 0; j < FDN; ++j)
+          yacc[j % S::NOB] = mfma32x32x16(db[(2 * (j % S::NOB) + (j / S::NOB)) * 64], hb_prev[j / S::NOB],
+                                          yacc[j % S::NOB]);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) hb_prev[e >> 3][e & 7] = f32_to_bf16(swiglu_gate(ga[e], gg[e]));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    general(0);
+    int t = 1;
+    // steady steps t = 1 .. S-4, three at a time starting at t % 3 == 1
+    for (; t + 5 < S_; t += 3) {
+      steady(t, I1{});
+      steady(t + 1, I2{});
+      steady(t + 2, I0{});
+    }
+    for (; t < S_; ++t) general(t);
+    // The down product of the last slice remains.
+    {
+      const bf16x8 *db = &wuv[(S_ - 1) % 3][FUP][lane];
+#pragma unroll
+      for (int j = 0; j < FDN; ++j)
+        yacc[j % S::NOB] = mfma32x32x16(db[(2 * (j % S::NOB) + (j / S::NOB)) * 64], hb_prev[j / S::NOB],
+                                        yacc[j % S::NOB]);
+    }
+  } else {
+    for (int s = 0; s < n_slices; ++s) {
+      const int b = s & 1;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // slice s is in LDS for every wave; buffer b^1 is no longer read
+      if (s + 1 < n_slices) stage(s + 1, b ^ 1);
+      f32x16 accA, accG;
+      up_gate(b, accA, accG);
+      bf16x8 hb[2];
+      gate(accA, accG, hb);
+      down(s, b, hb);
     }
   }
 

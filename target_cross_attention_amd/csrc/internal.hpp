@@ -37,7 +37,10 @@ hipError_t encode_mfma(hipStream_t s, int d, int r, int64_t n_rows, const void *
                        const float *gamma, const float *beta, float eps);
 
 // ---- ragged split-L attention (attend.hip) --------------------------------------------------
-constexpr int kRowsPerGroup = 128;  // query rows one attention work item covers (4 waves x 32)
+// Query rows one attention work item covers: 4 waves x 32 rows, or at d = 512 (where two waves
+// split the output features of a 32-row block) 2 x 32 rows.
+constexpr int attn_feature_halves(int d) { return d > 256 ? 2 : 1; }
+constexpr int attn_rows_per_group(int d) { return 4 * 32 / attn_feature_halves(d); }
 
 struct WorkItem {
   int32_t user, chunk, group, n_chunks;
