@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         s0 = mfma32x32x16(a, ub[ks], ks == 0 ? f32x16{} : s0);
     }
   };
-  // Raw scores of a tile with `rem` valid tokens -> masked scores and their per-row maximum.
+  // Raw scores of a tile with `rem` valid tokens -> masked scores and the maximum over this
+  // lane's 16 tokens (the other 16 tokens of the row are in lane l ^ 32; see half_max).
   auto row_max = [&](f32x16 &sc, int rem) {
     if (rem < 32) {
 #pragma unroll
@@ -259,16 +260,16 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     float mx = sc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-    return fmaxf(mx, swap_halves(mx));
+    return mx;
   };
   // bf16 probabilities 2^(s - m_run) (B operands of the PV product); their sum goes into s_run.
   auto probs = [&](const f32x16 &sc, bf16x8 (&pb)[2]) {
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const bf16 p = f32_to_bf16(fast_exp2(sc[i] - m_run));
-      pb[i >> 3][i & 7] = p;
-      psum += (float)p;
+      const float p = fast_exp2(sc[i] - m_run);
+      pb[i >> 3][i & 7] = f32_to_bf16(p);
+      psum += p;
     }
     s_run += psum;
   };
@@ -321,11 +322,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   if (wave_active) {
     scores(tile_off(0), sa, sb);
     f32x16 s0 = sa + sb;
-    m_run = row_max(s0, tile_rem(0));
+    m_run = half_max(row_max(s0, tile_rem(0)));
   }
-  auto tail = [&](int k, const f32x16 &sc, bool has_next) {
+  auto tail = [&](int k, const f32x16 &sc) {
     bf16x8 pb[2];
-    if (has_next) scores(tile_off(k + 1), sa, sb);
     probs(sc, pb);
     if constexpr (FH == 1) {
       pv(tile_off(k), pb, H0{});
@@ -352,13 +352,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       if (k + NST - 1 < ntiles) stage(k + NST - 1, (k + NST - 1) % NST);
       if (!wave_active) continue;
       sc = sa + sb;
+      if (has_next) scores(tile_off(k + 1), sa, sb);  // in flight during the softmax below
       mx = row_max(sc, tile_rem(k));
       if (wave_any(mx > m_run + kLazy)) break;
-      tail(k, sc, has_next);
+      tail(k, sc);
     }
     if (k >= ntiles) break;
-    // rescale (rare), then finish tile k
-    const float m_new = fmaxf(m_run, mx);
+    // rescale (rare), then finish tile k.  Both halves of a row take the same new maximum.
+    const float m_new = fmaxf(m_run, half_max(mx));
     const float sf = fast_exp2(m_run - m_new);
 #pragma unroll
     for (int ob = 0; ob < NOBW; ++ob)
@@ -366,12 +367,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       for (int i = 0; i < 16; ++i) oacc[ob][i] *= sf;
     s_run *= sf;
     m_run = m_new;
-    tail(k, sc, k + 1 < ntiles);
+    tail(k, sc);
     ++k;
   }
 
   if (!wave_active) return;
-  const float s_tot = s_run + swap_halves(s_run);
+  const float s_tot = half_sum(s_run);
   if (!row_ok) return;
   if (it.n_chunks == 1) {
     const float inv = 1.0f / s_tot;

@@ -65,8 +65,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Value held by lane (lane ^ 32): swaps the two halves of the wave.
-__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+// Reductions across the two 32-lane halves of a wave (lane l with lane l ^ 32).
+__device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+__device__ __forceinline__ float half_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
 
 // ---- MFMA ----------------------------------------------------------------------------------
 // v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] B[16x32].

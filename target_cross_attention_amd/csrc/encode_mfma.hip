@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int
     for (int ob = 0; ob < S::NOB; ++ob)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sum += yacc[ob][i];
-    sum += swap_halves(sum);
+    sum = half_sum(sum);
     mean = sum * (1.0f / D);
     float sq = 0.f;
 #pragma unroll
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int
         const float t = yacc[ob][i] - mean;
         sq += t * t;
       }
-    sq += swap_halves(sq);
+    sq = half_sum(sq);
     inv = 1.0f / sqrtf(sq * (1.0f / D) + eps);
   }
   if (!valid) return;
