@@ -82,4 +82,27 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// ---- global -> LDS staging and workgroup barriers -------------------------------------------
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zeros.  Word 3
+// is the raw (untyped) buffer format of gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from the buffer (byte offset voff + soff) straight into LDS: lane i's bytes
+// land at lds + 16 i, lds being wave-uniform.  The MUBUF form is used rather than the FLAT
+// global form: the compiler treats a pending FLAT access as possibly either kind of memory and
+// then drains every LDS read to zero outstanding, which defeats fragment prefetching.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, STCA_LDS void *lds, uint32_t voff,
+                                           uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+// Workgroup barrier after waiting for all but VM of this wave's vector-memory loads and for all
+// of its LDS operations.  Unlike __syncthreads() it carries no release fence, which would wait
+// for every outstanding LDS-bound load, including those meant to stay in flight across it.
+template <int VM> __device__ __forceinline__ void barrier_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VM) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace stca
