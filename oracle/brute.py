@@ -106,3 +106,17 @@ def forward_user(X, xt, W, h, M=None, query_ln=False, eps=1e-5):
                     q = ln_row(q, Pn["qg"], Pn["qb"], eps)
         Z.append(outs)
     return Z
+
+
+def prediction_token(Z, xt, WZ, Wu, Wv, Wo):
+    """Eq. (9) per target: z = SwiGLUFFN([o^(1) || ... || o^(M) || x_t] W_Z), nested lists.
+
+    ``Z`` is m x M x d (nested lists or an array), ``xt`` m x d, ``WZ`` (M+1)d x d."""
+    WZ, Wu, Wv, Wo = _mat(WZ), _mat(Wu), _mat(Wv), _mat(Wo)
+    out = []
+    for t, x_t in enumerate(_mat(xt)):
+        cat = [float(v) for o in Z[t] for v in o] + x_t
+        d = len(x_t)
+        c = [sum(cat[k] * WZ[k][col] for k in range(len(cat))) for col in range(d)]
+        out.append(ffn_row(c, Wu, Wv, Wo))
+    return out

@@ -33,6 +33,10 @@ Readings taken where the pages are garbled, ambiguous or silent:
   eq. (6) concatenates heads in order.
 * A user must have L_u >= 1 (softmax over no tokens is undefined); a user
   with no targets contributes no output rows.
+* Eq. (9) (prediction token): the SwiGLUFFN there carries no layer index; it is
+  read as an FFN instance of its own, applied without a LayerNorm (none is
+  printed), after the projection by W_Z ((M+1)d x d, row blocks in the order of
+  the concatenation [o^(1) || ... || o^(M) || x_t]).
 """
 from __future__ import annotations
 
@@ -156,6 +160,18 @@ def update_query(o_prev, xt, WC, Wu, Wv, Wo, gamma=None, beta=None, query_ln=Fal
     c = np.concatenate([_f64(o) for o in o_prev] + [_f64(xt)], axis=1) @ _f64(WC)
     y = swiglu_ffn(c, Wu, Wv, Wo)
     return layer_norm(y, gamma, beta, eps) if query_ln else y
+
+
+def prediction_token(Z, xt, WZ, Wu, Wv, Wo):
+    """z = SwiGLUFFN([o^(1) || ... || o^(M) || x_t] W_Z)  ([notes] eq. (9)).
+
+    ``Z`` is m x M x d (eq. (8) per target: the rows o^(1..M)); ``xt`` is m x d;
+    ``WZ`` is (M+1)d x d.  Returns m x d.
+    """
+    Z, xt = _f64(Z), _f64(xt)
+    m, M, d = Z.shape
+    blocks = [Z[:, i, :] for i in range(M)] + [xt]
+    return swiglu_ffn(np.concatenate(blocks, axis=1) @ _f64(WZ), Wu, Wv, Wo)
 
 
 # ----------------------------------------------------------------------------

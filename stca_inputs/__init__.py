@@ -25,6 +25,7 @@ Random streams (numpy PCG64 through ``SeedSequence(seed, spawn_key=...)``):
 * ``(1, u)`` history of user ``u`` (and its duplicate pattern)
 * ``(2,)``   target embeddings x_t for all targets, in user order
 * ``(3,)``   weights, layer-major
+* ``(4,)``   prediction-token weights (W_Z and its SwiGLU FFN)
 
 Values are drawn in float32.  For bf16 workloads every drawn value is rounded
 to the nearest bf16 (ties to even) and kept as a float32 array holding
@@ -36,12 +37,14 @@ fan_in is its number of rows; LayerNorm gamma = 1, beta = 0 unless
 from .configs import CONFIGS, Config, get_config, scaled
 from .generate import (
     Inputs,
+    PredictWeights,
     Weights,
     batch_layout,
     bf16_bits,
     bf16_round,
     bits_to_f32,
     make_inputs,
+    make_predict_weights,
     make_weights,
     offsets,
     user_history,
@@ -49,7 +52,7 @@ from .generate import (
 )
 
 __all__ = [
-    "CONFIGS", "Config", "get_config", "scaled", "Inputs", "Weights",
+    "CONFIGS", "Config", "get_config", "scaled", "Inputs", "PredictWeights", "Weights",
     "batch_layout", "bf16_bits", "bf16_round", "bits_to_f32", "make_inputs",
-    "make_weights", "offsets", "user_history", "targets",
+    "make_predict_weights", "make_weights", "offsets", "user_history", "targets",
 ]

@@ -10,7 +10,7 @@ import numpy as np
 from .configs import Config
 
 # Stream identifiers inside the per-workload SeedSequence.
-_LAYOUT, _HISTORY, _TARGETS, _WEIGHTS = 0, 1, 2, 3
+_LAYOUT, _HISTORY, _TARGETS, _WEIGHTS, _PREDICT = 0, 1, 2, 3, 4
 
 
 def _rng(cfg: Config, *key: int) -> np.random.Generator:
@@ -190,6 +190,31 @@ def make_weights(cfg: Config, random_ln: bool = False, separate_query_ffn: bool 
         W.WO.append(mat(d, d))
         W.WC.append(mat((i + 1) * d, d) if i >= 1 else None)
     return W
+
+
+@dataclass
+class PredictWeights:
+    """Parameters of the prediction token (eq. (9) of the STCA notes page): ``WZ``
+    (M+1)d x d, row blocks in the order [o^(1); ...; o^(M); x_t], and the SwiGLU FFN
+    ``Wu, Wv`` d x rd, ``Wo`` rd x d.  Same storage conventions as ``Weights``."""
+    WZ: np.ndarray
+    Wu: np.ndarray
+    Wv: np.ndarray
+    Wo: np.ndarray
+
+
+def make_predict_weights(cfg: Config) -> PredictWeights:
+    """Draw the prediction-token weights from a stream of their own (the other draws are
+    unchanged), in the order WZ, Wu, Wv, Wo, each N(0, 1/fan_in)."""
+    rng = _rng(cfg, _PREDICT)
+    d, rd = cfg.d, cfg.r * cfg.d
+
+    def mat(rows, cols):
+        w = rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(1.0 / np.sqrt(rows))
+        return _store(cfg, w)
+
+    WZ = mat((cfg.M + 1) * d, d)
+    return PredictWeights(WZ, mat(d, rd), mat(d, rd), mat(rd, d))
 
 
 # ----------------------------------------------------------------------------

@@ -269,3 +269,61 @@ def test_planted_mistakes_are_caught(monkeypatch):
         assert _pins_fail(monkeypatch, name, fn) >= 1, f"planted mistake via {name}/{fn.__name__} not caught"
     assert O.attend_reordered is orig_attend and O.update_query is orig_update
     assert O.layer_norm is orig_ln and O.silu is orig_silu
+
+
+# ----------------------------------------------------------------------------
+# eq. (9): the prediction token
+# ----------------------------------------------------------------------------
+def _swiglu_torch(x, Wu, Wv, Wo):
+    x, Wu, Wv, Wo = (torch.as_tensor(np.asarray(a, np.float64)) for a in (x, Wu, Wv, Wo))
+    return ((x @ Wu) * torch.nn.functional.silu(x @ Wv) @ Wo).numpy()
+
+
+def test_prediction_token_matches_brute_force():
+    cfg = tiny_cfg(d=12, h=3, M=2, r=2, n_users=2, L=5, m=3)
+    W = SI.make_weights(cfg, random_ln=True)
+    P = SI.make_predict_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    Z = O.forward_batch(inp, W)
+    xt = inp.as_f32(inp.xt)
+    z = O.prediction_token(Z, xt, P.WZ, P.Wu, P.Wv, P.Wo)
+    zb = np.array(brute.prediction_token(Z.tolist(), xt, P.WZ, P.Wu, P.Wv, P.Wo))
+    assert z.shape == zb.shape == (inp.total_T, cfg.d)
+    assert rel(z, zb) < 1e-12
+
+
+def test_prediction_token_block_order():
+    """W_Z selecting one block of the concatenation reduces eq. (9) to the FFN of that block."""
+    rng = np.random.default_rng(3)
+    m, M, d, r = 4, 3, 8, 2
+    Z, xt = rand(rng, m, M, d), rand(rng, m, d)
+    Wu, Wv, Wo = rand(rng, d, r * d, scale=0.3), rand(rng, d, r * d, scale=0.3), rand(rng, r * d, d, scale=0.3)
+    for blk in range(M + 1):
+        WZ = np.zeros(((M + 1) * d, d))
+        WZ[blk * d:(blk + 1) * d] = np.eye(d)
+        src = xt if blk == M else Z[:, blk, :]
+        assert rel(O.prediction_token(Z, xt, WZ, Wu, Wv, Wo), _swiglu_torch(src, Wu, Wv, Wo)) < 1e-13
+
+
+def test_prediction_token_planted_mistakes(monkeypatch):
+    orig = O.prediction_token
+
+    def reversed_concat(Z, xt, WZ, Wu, Wv, Wo):
+        Z = np.asarray(Z, np.float64)
+        blocks = [np.asarray(xt, np.float64)] + [Z[:, i, :] for i in range(Z.shape[1])]
+        return O.swiglu_ffn(np.concatenate(blocks, axis=1) @ WZ, Wu, Wv, Wo)
+
+    def gate_on_up(Z, xt, WZ, Wu, Wv, Wo):   # SiLU applied to the W_u branch instead of W_v
+        return orig(Z, xt, WZ, Wv, Wu, Wo)
+
+    for fn in (reversed_concat, gate_on_up):
+        monkeypatch.setattr(O, "prediction_token", fn)
+        caught = 0
+        for test in (test_prediction_token_matches_brute_force, test_prediction_token_block_order):
+            try:
+                test()
+            except AssertionError:
+                caught += 1
+        monkeypatch.undo()
+        assert caught >= 1, fn.__name__
+    assert O.prediction_token is orig
