@@ -148,6 +148,23 @@ def main():
     prof.close()
     assert np.isfinite(Z.sum().item()), "non-finite output"
 
+    # The prediction token of eq. (9) is the next step downstream of the forward (outside the timed
+    # forward): timed on its own, from the forward's Z, on the call's stream.
+    pw = B.DevicePredict(SI.make_predict_weights(cfg), cfg.dtype, dev)
+    zbuf = torch.empty((db.total_T, cfg.d), dtype=torch.float32, device=dev)
+    pws = B.workspace(B.predict_workspace_size(dims, db.total_T), dev)
+    B.stca_predict(dims, pw, Z, db.xt, z=zbuf, ws=pws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_pred = max(a.steps, 5)
+    e0.record(stream)
+    for _ in range(n_pred):
+        B.stca_predict(dims, pw, Z, db.xt, z=zbuf, ws=pws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pred_ms = e0.elapsed_time(e1) / n_pred
+    pred_flops = float(db.total_T) * (2.0 * (cfg.M + 1) * cfg.d * cfg.d + 6.0 * cfg.r * cfg.d * cfg.d)
+    assert np.isfinite(zbuf.sum().item()), "non-finite prediction token"
+
     ms_per_step = dt * 1e3 / a.steps
     tokens_per_s = db.total_L * a.steps / dt
     targets_per_s = db.total_T * a.steps / dt
@@ -197,6 +214,10 @@ def main():
                                "avg_launch_ms": att_avg_s * 1e3, "launches": att_n},
         "targets_per_s": targets_per_s,
         "phase_ms_per_step": {k: v[0] / a.steps for k, v in phases.items()},
+        "prediction_token": {"eq": 9, "rows": db.total_T, "avg_ms": pred_ms, "calls": n_pred,
+                             "targets_per_s": db.total_T / pred_ms * 1e3, "bound": "alu",
+                             "achieved": pred_flops / pred_ms / 1e9, "peak": PEAK_FP32_TFLOPS,
+                             "unit": "TFLOP/s", "frac": pred_flops / pred_ms / 1e9 / PEAK_FP32_TFLOPS},
     }
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle on a user sample)")

@@ -107,6 +107,7 @@ typedef struct {
 STCA_API int stca_encode_workspace_size(const stca_dims *dims, int64_t n_rows, size_t *bytes);
 STCA_API int stca_attend_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
 STCA_API int stca_forward_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
+STCA_API int stca_predict_workspace_size(const stca_dims *dims, int64_t n_targets, size_t *bytes);
 
 /* eq. (2): Xt[n_rows x d] = LN(SwiGLUFFN(X[n_rows x d])) with the weights of `ffn`
  * (gamma/beta required).  X and Xt are dims->dtype.  Rows are independent tokens. */
@@ -124,6 +125,19 @@ STCA_API int stca_attend(const stca_dims *dims, const stca_weights *w, int32_t l
  * Z: total_T x M x d fp32, Z[t][i] = o(i+1) of target t. */
 STCA_API int stca_forward(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
                  const void *xt, float *Z, void *workspace, size_t workspace_bytes, void *stream);
+
+/* eq. (9) of "Make It Long, Keep It Fast" (notes page, section 2.1, prediction head): the
+ * prediction token z = SwiGLUFFN([o(1) || ... || o(M) || x_t] W_Z) of every target.
+ *   WZ:  (M+1)d x d, row-major, dims->dtype; row blocks ordered [o(1); ...; o(M); x_t].
+ *   ffn: the prediction FFN's W_u, W_v (d x rd) and W_o (rd x d), dims->dtype.  No LayerNorm
+ *        follows (none is printed), so gamma/beta are not read and may be NULL.
+ *   Z:   n_targets x M x d fp32 as written by stca_forward (Z[t][i] = o(i+1)).
+ *   xt:  n_targets x d, dims->dtype.
+ *   z:   n_targets x d fp32 (output).
+ * Same conventions as the calls above; n_targets = 0 is a no-op. */
+STCA_API int stca_predict(const stca_dims *dims, const void *WZ, const stca_ffn *ffn, int64_t n_targets,
+                          const float *Z, const void *xt, float *z, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /* ---- per-kernel timing (HIP events on the call's stream) ---------------------------------- */
 typedef struct stca_profiler stca_profiler; /* opaque, host-side; not thread-safe */

@@ -22,7 +22,7 @@ N_PHASES = 7
 
 EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
-    "stca_encode", "stca_attend", "stca_forward", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
 ]
@@ -71,10 +71,12 @@ def _load() -> ctypes.CDLL:
         "stca_encode_workspace_size": [P, c_int64, POINTER(c_size_t)],
         "stca_attend_workspace_size": [P, P, POINTER(c_size_t)],
         "stca_forward_workspace_size": [P, P, POINTER(c_size_t)],
+        "stca_predict_workspace_size": [P, c_int64, POINTER(c_size_t)],
         "stca_encode": [P, P, c_int64, P, P, P, c_size_t, P],
         "stca_attend": [P, P, c_int32, P, P, P, P, P, c_size_t, P],
         "stca_forward": [P, P, P, P, P, P, P, c_size_t, P],
         "stca_forward_profiled": [P, P, P, P, P, P, P, c_size_t, P, P],
+        "stca_predict": [P, P, P, c_int64, P, P, P, P, c_size_t, P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -191,6 +193,18 @@ class DeviceWeights:
             self.c.WC[i] = up(W.WC[i]) if W.WC[i] is not None else None
 
 
+class DevicePredict:
+    """``stca_inputs.PredictWeights`` uploaded in the storage type: ``WZ`` and the ``stca_ffn``
+    struct of the prediction FFN (no LayerNorm parameters)."""
+
+    def __init__(self, P, dtype: str, device="cuda"):
+        self.WZ = to_device(P.WZ, dtype, device)
+        self.Wu = to_device(P.Wu, dtype, device)
+        self.Wv = to_device(P.Wv, dtype, device)
+        self.Wo = to_device(P.Wo, dtype, device)
+        self.ffn = Ffn(self.Wu.data_ptr(), self.Wv.data_ptr(), self.Wo.data_ptr(), None, None)
+
+
 class DeviceBatch:
     """A ``stca_inputs.Inputs`` batch uploaded to the device, plus the ``stca_batch`` struct."""
 
@@ -229,6 +243,12 @@ def forward_workspace_size(dims: Dims, batch: BatchC) -> int:
     n = c_size_t(0)
     _check(LIB.stca_forward_workspace_size(_ref(dims), _ref(batch), ctypes.byref(n)),
            "stca_forward_workspace_size")
+    return n.value
+
+
+def predict_workspace_size(dims: Dims, n_targets: int) -> int:
+    n = c_size_t(0)
+    _check(LIB.stca_predict_workspace_size(_ref(dims), n_targets, ctypes.byref(n)), "stca_predict_workspace_size")
     return n.value
 
 
@@ -277,6 +297,21 @@ def stca_forward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, Z=None, ws=No
                                        _ptr(Z), _ptr(ws), ws.numel(), _stream(stream), profiler.handle)
     _check(st, "stca_forward")
     return Z
+
+
+def stca_predict(dims: Dims, pw: DevicePredict, Z, xt, z=None, ws=None, stream=None):
+    """eq. (9): the prediction token of every target from Z (T x M x d fp32) and x_t (T x d,
+    storage type).  Returns z (T x d float32)."""
+    import torch
+    T = int(Z.shape[0])
+    if z is None:
+        z = torch.empty((T, dims.d), dtype=torch.float32, device=Z.device)
+    if ws is None:
+        ws = workspace(predict_workspace_size(dims, T), Z.device)
+    st = LIB.stca_predict(_ref(dims), _ptr(pw.WZ), _ref(pw.ffn), T, _ptr(Z), _ptr(xt), _ptr(z), _ptr(ws),
+                          ws.numel(), _stream(stream))
+    _check(st, "stca_predict")
+    return z
 
 
 class Profiler:

@@ -281,6 +281,36 @@ int ffn_generic(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t r
   return STCA_OK;
 }
 
+// c[T x d] = [Zb(1) || ... || Zb(nblk) || x_t] W: the first nblk d-wide blocks of each row of Z
+// (row stride ldz, fp32) and x_t (dtype) against the row blocks of W ((nblk+1)d x d, dtype),
+// as two GEMMs so the concatenation is never materialised (eqs. (7) and (9)).
+hipError_t concat_project(hipStream_t s, const stca_dims *dm, int64_t T, const float *Z, int64_t ldz, int nblk,
+                          const void *xt, const void *W, float *c) {
+  const int d = dm->d;
+  const bool bf = dm->dtype == STCA_BF16;
+  GemmArgs g;
+  g.M = (int)T;
+  g.N = d;
+  g.K = nblk * d;
+  g.A = Z;
+  g.lda = ldz;
+  g.B = W;
+  g.ldb = d;
+  g.tb_bf16 = bf;
+  g.C = c;
+  g.ldc = d;
+  hipError_t e = gemm(s, g);
+  if (e != hipSuccess) return e;
+  GemmArgs gx = g;
+  gx.K = d;
+  gx.A = xt;
+  gx.lda = d;
+  gx.ta_bf16 = bf;
+  gx.B = (const char *)W + (size_t)nblk * d * d * esize(dm);
+  gx.beta = 1.f;
+  return gemm(s, gx);
+}
+
 // eq. (2) for all history rows.
 int encode_rows(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t rows, const void *X, void *Xt,
                 const void *packed, const FfnWs &w) {
@@ -469,27 +499,7 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
       return st;
     if (i + 1 < M) {  // eq. (7): q(i+1) = SwiGLUFFN([o(1..i) || x_t] W_C) (+LN)
       Phase ph(prof, s, STCA_PHASE_QUERY);
-      const int nblk = i + 1;  // o blocks already in Z
-      GemmArgs g;
-      g.M = (int)b->total_T;
-      g.N = d;
-      g.K = nblk * d;
-      g.A = Z;
-      g.lda = (int64_t)M * d;
-      g.B = w->WC[i + 1];
-      g.ldb = d;
-      g.tb_bf16 = bf;
-      g.C = fw.c;
-      g.ldc = d;
-      HIP_TRY(gemm(s, g));
-      GemmArgs gx = g;
-      gx.K = d;
-      gx.A = xt;
-      gx.lda = d;
-      gx.ta_bf16 = bf;
-      gx.B = (const char *)w->WC[i + 1] + (size_t)nblk * d * d * esize(dm);
-      gx.beta = 1.f;
-      HIP_TRY(gemm(s, gx));
+      HIP_TRY(concat_project(s, dm, b->total_T, Z, (int64_t)M * d, i + 1, xt, w->WC[i + 1], fw.c));
       if ((st = ffn_generic(s, dm, &w->query[i + 1], b->total_T, fw.c, d, false, fw.q, d, false, dm->query_ln != 0,
                             fw.ffn)) != STCA_OK)
         return st;
@@ -606,6 +616,46 @@ int stca_forward_profiled(const stca_dims *dims, const stca_weights *w, const st
                           const void *xt, float *Z, void *workspace, size_t workspace_bytes, void *stream,
                           stca_profiler *prof) {
   return forward_impl(dims, w, batch, X, xt, Z, workspace, workspace_bytes, stream, prof);
+}
+
+int stca_predict_workspace_size(const stca_dims *dims, int64_t n_targets, size_t *bytes) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if (!bytes) return fail(STCA_E_ARG, "bytes is NULL");
+  if (n_targets < 0) return fail(STCA_E_ARG, "n_targets < 0");
+  Carver c(nullptr);
+  c.take<float>((size_t)std::max<int64_t>(n_targets, 1) * dims->d);
+  FfnWs f;
+  carve_ffn(c, dims, n_targets, f);
+  *bytes = round_up(c.off, 256);
+  return STCA_OK;
+}
+
+int stca_predict(const stca_dims *dims, const void *WZ, const stca_ffn *ffn, int64_t n_targets, const float *Z,
+                 const void *xt, float *z, void *workspace, size_t workspace_bytes, void *stream) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_ffn(ffn, false, "predict")) != STCA_OK) return st;
+  if (!WZ) return fail(STCA_E_ARG, "W_Z is NULL");
+  if (n_targets < 0) return fail(STCA_E_ARG, "n_targets < 0");
+  if (n_targets > INT32_MAX) return fail(STCA_E_ARG, "n_targets = %lld exceeds 2^31 - 1", (long long)n_targets);
+  if (n_targets > 0 && (!Z || !xt || !z)) return fail(STCA_E_ARG, "Z, xt or z is NULL");
+  if (!aligned16(WZ) || !aligned16(Z) || !aligned16(xt) || !aligned16(z))
+    return fail(STCA_E_ALIGN, "W_Z/Z/xt/z not 16-byte aligned");
+  size_t need = 0;
+  stca_predict_workspace_size(dims, n_targets, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(STCA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(STCA_E_ALIGN, "workspace not 16-byte aligned");
+  if (n_targets == 0) return STCA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c(workspace);
+  float *cbuf = c.take<float>((size_t)n_targets * dims->d);
+  FfnWs f;
+  carve_ffn(c, dims, n_targets, f);
+  const int d = dims->d, M = dims->M;
+  HIP_TRY(concat_project(s, dims, n_targets, Z, (int64_t)M * d, M, xt, WZ, cbuf));
+  return ffn_generic(s, dims, ffn, n_targets, cbuf, d, false, z, d, false, false, f);
 }
 
 int stca_profiler_create(stca_profiler **out) {

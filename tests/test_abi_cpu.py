@@ -154,6 +154,34 @@ def test_encode_and_attend_validation():
                          None) == -3
 
 
+def test_predict_validation():
+    dims = B.make_dims(128, 8, 3, 2)
+    ffn = B.Ffn(FAKE, FAKE, FAKE, None, None)   # eq. (9) has no LayerNorm: gamma/beta may be NULL
+    L = B.LIB
+    n = ctypes.c_size_t(0)
+    assert L.stca_predict_workspace_size(ctypes.byref(dims), 1000, ctypes.byref(n)) == 0
+    # c (T x d fp32) plus the generic FFN scratch (two T x rd fp32 blocks)
+    assert n.value >= 1000 * 128 * 4 + 2 * 1000 * 256 * 4
+    assert L.stca_predict_workspace_size(ctypes.byref(dims), -1, ctypes.byref(n)) == -1
+
+    def call(WZ=FAKE, ffn_=ffn, T=10, Z=FAKE, xt=FAKE, z=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.stca_predict(ctypes.byref(dims), WZ, ctypes.byref(ffn_) if ffn_ is not None else None, T, Z, xt, z,
+                              ws, wsb, None)
+    assert call(WZ=None) == -1
+    assert call(ffn_=None) == -1
+    assert call(ffn_=B.Ffn(FAKE, None, FAKE, None, None)) == -1
+    assert call(T=-1) == -1
+    assert call(Z=None) == -1
+    assert call(z=FAKE + 4) == -4
+    assert call(WZ=FAKE + 2) == -4
+    assert call(wsb=64) == -3
+    assert call(T=0) == 0            # no targets: nothing enqueued
+    bad = B.make_dims(128, 8, 3, 2)
+    bad.d = 96
+    assert L.stca_predict(ctypes.byref(bad), FAKE, ctypes.byref(ffn), 10, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                          None) == -2
+
+
 def test_profiler_lifecycle_without_launches():
     p = B.Profiler()
     p.reset()
