@@ -11,6 +11,8 @@ arithmetic).
   sources and the readings taken where the pages are garbled or silent).
 * ``oracle.brute`` -- an independent pure-Python scalar-loop version of the
   same equations, for tiny sizes only; the tests pin ``oracle.stca`` to it.
+* ``oracle.sl``    -- stochastic-length training batches (eqs. (15)-(17), temporal
+  suffix selection, two-step batch load balancing) in integer numpy.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (library routines, closed forms, invariants the pages state, brute force).
@@ -20,6 +22,6 @@ LayerNorm in the query update) are fixed readings, shared with the HIP path
 by definition; no page prints a number that could pin them ("parity unpinned"
 for those readings only).
 """
-from . import brute, stca
+from . import brute, sl, stca
 
-__all__ = ["stca", "brute"]
+__all__ = ["stca", "brute", "sl"]

@@ -26,6 +26,7 @@ Random streams (numpy PCG64 through ``SeedSequence(seed, spawn_key=...)``):
 * ``(2,)``   target embeddings x_t for all targets, in user order
 * ``(3,)``   weights, layer-major
 * ``(4,)``   prediction-token weights (W_Z and its SwiGLU FFN)
+* ``(5,)``   stochastic-length draws (Beta variates, truncation order)
 
 Values are drawn in float32.  For bf16 workloads every drawn value is rounded
 to the nearest bf16 (ties to even) and kept as a float32 array holding
@@ -45,6 +46,7 @@ from .generate import (
     bits_to_f32,
     make_inputs,
     make_predict_weights,
+    make_sl_draws,
     make_weights,
     offsets,
     user_history,
@@ -54,5 +56,5 @@ from .generate import (
 __all__ = [
     "CONFIGS", "Config", "get_config", "scaled", "Inputs", "PredictWeights", "Weights",
     "batch_layout", "bf16_bits", "bf16_round", "bits_to_f32", "make_inputs",
-    "make_predict_weights", "make_weights", "offsets", "user_history", "targets",
+    "make_predict_weights", "make_sl_draws", "make_weights", "offsets", "user_history", "targets",
 ]

@@ -10,7 +10,7 @@ import numpy as np
 from .configs import Config
 
 # Stream identifiers inside the per-workload SeedSequence.
-_LAYOUT, _HISTORY, _TARGETS, _WEIGHTS, _PREDICT = 0, 1, 2, 3, 4
+_LAYOUT, _HISTORY, _TARGETS, _WEIGHTS, _PREDICT, _SL = 0, 1, 2, 3, 4, 5
 
 
 def _rng(cfg: Config, *key: int) -> np.random.Generator:
@@ -215,6 +215,16 @@ def make_predict_weights(cfg: Config) -> PredictWeights:
 
     WZ = mat((cfg.M + 1) * d, d)
     return PredictWeights(WZ, mat(d, rd), mat(d, rd), mat(rd, d))
+
+
+def make_sl_draws(cfg: Config, n: int, alpha: float, beta: float):
+    """The random draws of stochastic-length batching for n sequences, from a stream of their
+    own: s ~ Beta(alpha, beta) per sequence (float64), then a random order of the sequences
+    (int32) for the truncation pass.  The shape parameters are the caller's."""
+    rng = _rng(cfg, _SL)
+    s = rng.beta(alpha, beta, size=n)
+    order = rng.permutation(n).astype(np.int32)
+    return s, order
 
 
 # ----------------------------------------------------------------------------
