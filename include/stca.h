@@ -139,6 +139,47 @@ STCA_API int stca_predict(const stca_dims *dims, const void *WZ, const stca_ffn 
                           const float *Z, const void *xt, float *z, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* ---- stochastic-length training batches -----------------------------------------------------
+ * "Make It Long, Keep It Fast" (notes page, length extrapolation: stochastic length sampling,
+ * eqs. (15)-(17); element selection; batch-level load balancing, two steps).  A training batch
+ * gives each user a random length L_train (a Beta draw mapped by eq. (16), aligned to 8), keeps
+ * the user's most recent L_train history rows (the temporal suffix), truncates sequences so the
+ * batch holds at most B * L_avg tokens, and lays the rows end to end with no padding; the
+ * segment offsets are the index tensor the ragged kernels above take as hist_off. */
+typedef struct {
+  int32_t L_min;   /* shortest training length, >= 1 */
+  int32_t L_max;   /* longest training length, L_min < L_avg < L_max */
+  int32_t L_avg;   /* mean training length; the batch budget is n_users * L_avg tokens */
+  int32_t L_infer; /* histories are first truncated to their most recent L_infer rows, >= 1 */
+} stca_sl_params;
+
+/* eq. (17): the Beta shape beta = alpha (L_max - L_avg) / (L_avg - L_min) that puts the mean of
+ * eq. (16) at L_avg (alpha > 0).  Host only. */
+STCA_API int stca_sl_beta(const stca_sl_params *p, double alpha, double *beta);
+
+/* Host only: the lengths and segment offsets of a stochastic-length batch of n_users users.
+ *   full_len [host]: n_users history lengths (>= 0) of the users' full histories.
+ *   s        [host]: n_users draws in [0, 1] (the caller's Beta(alpha, beta) variates).
+ *   order    [host]: a permutation of 0 .. n_users-1, the order in which sequences are truncated.
+ *   len      [host, out]: n_users training lengths; hist_off [host, out]: n_users + 1 offsets.
+ * Steps: L = L_min + s (L_max - L_min) (eq. (16)); rounded to the nearest multiple of 8 (halves
+ * up) and clamped to [8 ceil(L_min/8), 8 floor(L_max/8)]; capped by min(full_len, L_infer); then,
+ * while the total exceeds n_users * L_avg, sequences are shortened in `order`, each by as much of
+ * the excess as it can give without going below 8 ceil(L_min/8), so the total equals that budget.  Returns STCA_E_ARG on bad
+ * parameters, draws outside [0, 1] or an `order` that is not a permutation. */
+STCA_API int stca_sl_plan(const stca_sl_params *p, int32_t n_users, const int64_t *full_len, const double *s,
+                          const int32_t *order, int64_t *len, int64_t *hist_off);
+
+/* Device: gathers the temporal suffix of every user into X_packed (total x d, dims->dtype, no
+ * padding): packed row hist_off[u] + j is full-history row full_off[u+1] - len[u] + j.
+ *   full_off: n_users + 1 offsets of the full histories in X_full (device);
+ *   hist_off: n_users + 1 offsets of the packed batch (device), as from stca_sl_plan, with
+ *             hist_off[u+1] - hist_off[u] <= full_off[u+1] - full_off[u];
+ *   total:    [host] hist_off[n_users].
+ * Only dims->d and dims->dtype are read.  Asynchronous on `stream`. */
+STCA_API int stca_sl_pack(const stca_dims *dims, int32_t n_users, const int64_t *full_off, const int64_t *hist_off,
+                          int64_t total, const void *X_full, void *X_packed, void *stream);
+
 /* ---- per-kernel timing (HIP events on the call's stream) ---------------------------------- */
 typedef struct stca_profiler stca_profiler; /* opaque, host-side; not thread-safe */
 

@@ -29,9 +29,11 @@ Readings where the pages are silent (shared with the HIP path by definition):
   it: L = min(L_train, available).
 * R3. The random draws (s per sequence; the order in which sequences are truncated) are inputs.
 * R4. Global allocation only truncates: when the sampled total exceeds the budget B * L_avg,
-  sequences are visited in the given random order and each is shortened, in steps of 8 and not
-  below 8 ceil(L_min / 8), until the total equals the budget (budget a multiple of 8).  A total
-  at or under the budget is left as is.
+  sequences are visited in the given random order and each is shortened by as much of the
+  remaining excess as it can give without going below 8 ceil(L_min / 8), so the total equals
+  the budget exactly (the pages ask for exactly B * L_avg tokens; a cut need not be a multiple of
+  8, since lengths capped by a short history are not).  A total at or under the budget is left
+  as is.
 * R5. Compression concatenates sequences in user order; the boundary index is the prefix sum of
   lengths (hist_off), and row r of the compressed view covers tokens [r L_avg, (r+1) L_avg).
 """
@@ -79,7 +81,6 @@ def allocate(L, budget: int, order, L_min: int):
         if excess <= 0:
             break
         cut = min(excess, max(int(L[u]) - floor, 0))
-        cut -= cut % 8
         L[u] -= cut
         excess -= cut
     return L

@@ -22,7 +22,8 @@ N_PHASES = 7
 
 EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
-    "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict",
+    "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
 ]
@@ -52,6 +53,10 @@ class ProfileReport(ctypes.Structure):
     _fields_ = [("ms", c_double * N_PHASES), ("launches", c_int64 * N_PHASES)]
 
 
+class SlParams(ctypes.Structure):
+    _fields_ = [("L_min", c_int32), ("L_max", c_int32), ("L_avg", c_int32), ("L_infer", c_int32)]
+
+
 class StcaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -77,6 +82,9 @@ def _load() -> ctypes.CDLL:
         "stca_forward": [P, P, P, P, P, P, P, c_size_t, P],
         "stca_forward_profiled": [P, P, P, P, P, P, P, c_size_t, P, P],
         "stca_predict": [P, P, P, c_int64, P, P, P, P, c_size_t, P],
+        "stca_sl_beta": [P, ctypes.c_double, POINTER(ctypes.c_double)],
+        "stca_sl_plan": [P, c_int32, P, P, P, P, P],
+        "stca_sl_pack": [P, c_int32, P, P, c_int64, P, P, P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -312,6 +320,38 @@ def stca_predict(dims: Dims, pw: DevicePredict, Z, xt, z=None, ws=None, stream=N
                           ws.numel(), _stream(stream))
     _check(st, "stca_predict")
     return z
+
+
+def sl_beta(params: SlParams, alpha: float) -> float:
+    """eq. (17): the Beta shape that puts the mean training length at L_avg."""
+    b = ctypes.c_double(0.0)
+    _check(LIB.stca_sl_beta(_ref(params), alpha, ctypes.byref(b)), "stca_sl_beta")
+    return b.value
+
+
+def sl_plan(params: SlParams, full_len, s, order):
+    """Host-side stochastic-length plan: (lengths, hist_off) as int64 numpy arrays."""
+    full_len = np.ascontiguousarray(full_len, np.int64)
+    s = np.ascontiguousarray(s, np.float64)
+    order = np.ascontiguousarray(order, np.int32)
+    n = len(full_len)
+    L = np.zeros(n, np.int64)
+    off = np.zeros(n + 1, np.int64)
+    vp = lambda a: a.ctypes.data_as(c_void_p) if a.size else None  # noqa: E731
+    _check(LIB.stca_sl_plan(_ref(params), n, vp(full_len), vp(s), vp(order), vp(L), off.ctypes.data_as(c_void_p)),
+           "stca_sl_plan")
+    return L, off
+
+
+def sl_pack(dims: Dims, full_off, hist_off, total: int, X_full, X_packed=None, stream=None):
+    """Device gather of every user's temporal suffix (full_off/hist_off: device int64 tensors)."""
+    import torch
+    n_users = int(hist_off.numel()) - 1
+    if X_packed is None:
+        X_packed = torch.empty((total, dims.d), dtype=X_full.dtype, device=X_full.device)
+    _check(LIB.stca_sl_pack(_ref(dims), n_users, _ptr(full_off), _ptr(hist_off), total, _ptr(X_full),
+                            _ptr(X_packed), _stream(stream)), "stca_sl_pack")
+    return X_packed
 
 
 class Profiler:

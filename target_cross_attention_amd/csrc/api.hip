@@ -1,4 +1,5 @@
 // libstca C ABI: argument checks, workspace layout, launch sequence.  See include/stca.h.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -656,6 +657,72 @@ int stca_predict(const stca_dims *dims, const void *WZ, const stca_ffn *ffn, int
   const int d = dims->d, M = dims->M;
   HIP_TRY(concat_project(s, dims, n_targets, Z, (int64_t)M * d, M, xt, WZ, cbuf));
   return ffn_generic(s, dims, ffn, n_targets, cbuf, d, false, z, d, false, false, f);
+}
+
+int stca_sl_beta(const stca_sl_params *p, double alpha, double *beta) {
+  if (!p || !beta) return fail(STCA_E_ARG, "params or beta is NULL");
+  if (!(p->L_min >= 1 && p->L_min < p->L_avg && p->L_avg < p->L_max))
+    return fail(STCA_E_ARG, "need 1 <= L_min < L_avg < L_max (got %d, %d, %d)", p->L_min, p->L_avg, p->L_max);
+  if (!(alpha > 0)) return fail(STCA_E_ARG, "alpha must be > 0");
+  *beta = alpha * (double)(p->L_max - p->L_avg) / (double)(p->L_avg - p->L_min);
+  return STCA_OK;
+}
+
+int stca_sl_plan(const stca_sl_params *p, int32_t n_users, const int64_t *full_len, const double *s,
+                 const int32_t *order, int64_t *len, int64_t *hist_off) {
+  double beta;
+  int st;
+  if ((st = stca_sl_beta(p, 1.0, &beta)) != STCA_OK) return st;
+  if (p->L_infer < 1) return fail(STCA_E_ARG, "L_infer must be >= 1");
+  if (n_users < 0) return fail(STCA_E_ARG, "n_users < 0");
+  if (!hist_off) return fail(STCA_E_ARG, "hist_off is NULL");
+  hist_off[0] = 0;
+  if (n_users == 0) return STCA_OK;
+  if (!full_len || !s || !order || !len) return fail(STCA_E_ARG, "full_len, s, order or len is NULL");
+  std::vector<char> seen(n_users, 0);
+  for (int32_t i = 0; i < n_users; ++i) {
+    if (order[i] < 0 || order[i] >= n_users || seen[order[i]]) return fail(STCA_E_ARG, "order is not a permutation");
+    seen[order[i]] = 1;
+    if (!(s[i] >= 0.0 && s[i] <= 1.0)) return fail(STCA_E_ARG, "s[%d] = %g outside [0, 1]", i, s[i]);
+    if (full_len[i] < 0) return fail(STCA_E_ARG, "full_len[%d] < 0", i);
+  }
+  // eq. (16), aligned to 8 (nearest, halves up) and clamped; capped by the available history.
+  const int64_t lo = 8 * ((p->L_min + 7) / 8), hi = 8 * (p->L_max / 8);
+  int64_t total = 0;
+  for (int32_t u = 0; u < n_users; ++u) {
+    const double raw = (double)p->L_min + s[u] * (double)(p->L_max - p->L_min);
+    int64_t L = 8 * (int64_t)floor(raw / 8.0 + 0.5);
+    L = std::min(std::max(L, lo), hi);
+    L = std::min<int64_t>(L, std::min<int64_t>(full_len[u], p->L_infer));
+    len[u] = L;
+    total += L;
+  }
+  // Global length allocation: truncate in the given order until the budget is met exactly.
+  int64_t excess = total - (int64_t)n_users * p->L_avg;
+  for (int32_t i = 0; i < n_users && excess > 0; ++i) {
+    const int32_t u = order[i];
+    const int64_t cut = std::min<int64_t>(excess, std::max<int64_t>(len[u] - lo, 0));
+    len[u] -= cut;
+    excess -= cut;
+  }
+  for (int32_t u = 0; u < n_users; ++u) hist_off[u + 1] = hist_off[u] + len[u];
+  return STCA_OK;
+}
+
+int stca_sl_pack(const stca_dims *dims, int32_t n_users, const int64_t *full_off, const int64_t *hist_off,
+                 int64_t total, const void *X_full, void *X_packed, void *stream) {
+  if (!dims) return fail(STCA_E_ARG, "dims is NULL");
+  if (dims->dtype != STCA_F32 && dims->dtype != STCA_BF16) return fail(STCA_E_DIMS, "unknown dtype %d", dims->dtype);
+  const int64_t row_bytes = (int64_t)dims->d * (dims->dtype == STCA_BF16 ? 2 : 4);
+  if (dims->d < 1 || row_bytes % 16 != 0) return fail(STCA_E_DIMS, "d=%d: rows must be a multiple of 16 bytes", dims->d);
+  if (n_users < 0 || total < 0) return fail(STCA_E_ARG, "n_users or total < 0");
+  if (total > 0 && n_users == 0) return fail(STCA_E_ARG, "total > 0 with no users");
+  if (total == 0) return STCA_OK;
+  if (!full_off || !hist_off || !X_full || !X_packed) return fail(STCA_E_ARG, "NULL pointer");
+  if (!aligned16(X_full) || !aligned16(X_packed) || ((uintptr_t)full_off % 8) || ((uintptr_t)hist_off % 8))
+    return fail(STCA_E_ALIGN, "X buffers need 16-byte, offsets 8-byte alignment");
+  HIP_TRY(sl_pack((hipStream_t)stream, n_users, full_off, hist_off, total, (int)(row_bytes / 16), X_full, X_packed));
+  return STCA_OK;
 }
 
 int stca_profiler_create(stca_profiler **out) {

@@ -73,4 +73,9 @@ hipError_t attend_split(hipStream_t s, const AttnPlan &p, bool bf16_path, const 
 hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_off, float *abar,
                           const AttnBuffers &b);
 
+// ---- stochastic-length batches (sl.hip) -------------------------------------------------------
+// X_packed[total x row16 16-byte chunks] <- the temporal suffix rows of every user of X_full.
+hipError_t sl_pack(hipStream_t s, int n_users, const int64_t *full_off, const int64_t *hist_off, int64_t total,
+                   int row16, const void *X_full, void *X_packed);
+
 }  // namespace stca
