@@ -80,6 +80,78 @@ def cpu_baseline(cfg, W, target_s: float = 12.0, max_users: int = 64):
             "targets_per_s": targets / elapsed}
 
 
+def bench_sl(a, cfg, dev):
+    """Stochastic-length training batch from the workload's full histories: the host plan, the
+    device suffix gather (timed against HBM), then the forward on the packed batch."""
+    from types import SimpleNamespace
+
+    import numpy as np
+    import torch
+
+    import stca_inputs as SI
+    from target_cross_attention_amd import binding as B
+
+    alpha, L_min, L_max, L_avg, L_infer = 0.02, 8, 10000, 2000, 10000
+    prm = B.SlParams(L_min, L_max, L_avg, L_infer)
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    s, order = SI.make_sl_draws(cfg, inp.n_users, alpha, B.sl_beta(prm, alpha))
+    t = time.perf_counter()
+    L, off = B.sl_plan(prm, inp.L, s, order)
+    plan_ms = (time.perf_counter() - t) * 1e3
+    total = int(off[-1])
+    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk)
+    Xf = B.to_device(inp.X, cfg.dtype, dev)
+    del inp.X
+    full_off = torch.from_numpy(inp.hist_off.astype(np.int64)).to(dev)
+    hist_off = torch.from_numpy(off).to(dev)
+    Xp = torch.empty((total, cfg.d), dtype=Xf.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    B.sl_pack(dims, full_off, hist_off, total, int(L.max()), Xf, Xp, stream=stream)
+    n_pack = max(a.steps, 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_pack):
+        B.sl_pack(dims, full_off, hist_off, total, int(L.max()), Xf, Xp, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1) / n_pack
+    del Xf
+    pack_bytes = 2.0 * total * cfg.d * (2 if cfg.dtype == "bf16" else 4)   # read + write each row
+
+    tgt_off = torch.from_numpy(inp.tgt_off.astype(np.int64)).to(dev)
+    xt = B.to_device(inp.xt, cfg.dtype, dev)
+    T = int(inp.tgt_off[-1])
+    batch = SimpleNamespace(X=Xp, xt=xt, total_T=T,
+                            c=B.batch_struct(inp.n_users, hist_off, tgt_off, total, T, int(L.max()), int(inp.m.max())))
+    dw = B.DeviceWeights(W, cfg.dtype, dev)
+    ws = B.workspace(B.forward_workspace_size(dims, batch.c), dev)
+    Z = torch.empty((T, cfg.M, cfg.d), dtype=torch.float32, device=dev)
+    for _ in range(a.warmup):
+        B.stca_forward(dims, dw, batch, Z=Z, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        B.stca_forward(dims, dw, batch, Z=Z, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert np.isfinite(Z.sum().item()), "non-finite output"
+    print(json.dumps({
+        "metric": "STCA fwd history-tokens/s on a stochastic-length batch",
+        "value": total * a.steps / dt, "unit": "history-tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": dt * 1e3 / a.steps, "higher_is_better": True,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"stochastic-length batch from {cfg.description}", "alpha": alpha,
+                   "L_min": L_min, "L_max": L_max, "L_avg": L_avg, "L_infer": L_infer, "users": inp.n_users,
+                   "packed_tokens": total, "budget": inp.n_users * L_avg, "mean_len": float(L.mean()),
+                   "users_at_L_max": int((L >= 8 * (L_max // 8)).sum())},
+        "sl_plan_host_ms": plan_ms,
+        "sl_pack": {"bound": "hbm", "avg_ms": pack_ms, "achieved": pack_bytes / pack_ms / 1e6,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": pack_bytes / pack_ms / 1e6 / PEAK_HBM_GBS,
+                    "algorithmic_bytes_per_launch": pack_bytes},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +161,9 @@ def main():
     ap.add_argument("--users", type=int, default=0, help="override the number of users (0 = workload's)")
     ap.add_argument("--attn-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sl", action="store_true",
+                    help="time a stochastic-length batch built from the workload's histories instead "
+                         "(L_avg 2000, L_max = L_infer = 10000, alpha 0.02)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of STCA, run K device copies of 2 GiB (counter calibration)")
     a = ap.parse_args()
@@ -119,6 +194,8 @@ def main():
     cfg = SI.get_config(a.workload)
     if a.users:
         cfg = SI.scaled(cfg, n_users=a.users)
+    if a.sl:
+        return bench_sl(a, cfg, dev)
     t = time.perf_counter()
     W = SI.make_weights(cfg)
     inp = SI.make_inputs(cfg)

@@ -175,10 +175,11 @@ STCA_API int stca_sl_plan(const stca_sl_params *p, int32_t n_users, const int64_
  *   full_off: n_users + 1 offsets of the full histories in X_full (device);
  *   hist_off: n_users + 1 offsets of the packed batch (device), as from stca_sl_plan, with
  *             hist_off[u+1] - hist_off[u] <= full_off[u+1] - full_off[u];
- *   total:    [host] hist_off[n_users].
+ *   total:    [host] hist_off[n_users];
+ *   max_len:  [host] an upper bound on hist_off[u+1] - hist_off[u] (the largest length of the plan).
  * Only dims->d and dims->dtype are read.  Asynchronous on `stream`. */
 STCA_API int stca_sl_pack(const stca_dims *dims, int32_t n_users, const int64_t *full_off, const int64_t *hist_off,
-                          int64_t total, const void *X_full, void *X_packed, void *stream);
+                          int64_t total, int64_t max_len, const void *X_full, void *X_packed, void *stream);
 
 /* ---- per-kernel timing (HIP events on the call's stream) ---------------------------------- */
 typedef struct stca_profiler stca_profiler; /* opaque, host-side; not thread-safe */

@@ -84,7 +84,7 @@ def _load() -> ctypes.CDLL:
         "stca_predict": [P, P, P, c_int64, P, P, P, P, c_size_t, P],
         "stca_sl_beta": [P, ctypes.c_double, POINTER(ctypes.c_double)],
         "stca_sl_plan": [P, c_int32, P, P, P, P, P],
-        "stca_sl_pack": [P, c_int32, P, P, c_int64, P, P, P],
+        "stca_sl_pack": [P, c_int32, P, P, c_int64, c_int64, P, P, P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -343,13 +343,13 @@ def sl_plan(params: SlParams, full_len, s, order):
     return L, off
 
 
-def sl_pack(dims: Dims, full_off, hist_off, total: int, X_full, X_packed=None, stream=None):
+def sl_pack(dims: Dims, full_off, hist_off, total: int, max_len: int, X_full, X_packed=None, stream=None):
     """Device gather of every user's temporal suffix (full_off/hist_off: device int64 tensors)."""
     import torch
     n_users = int(hist_off.numel()) - 1
     if X_packed is None:
         X_packed = torch.empty((total, dims.d), dtype=X_full.dtype, device=X_full.device)
-    _check(LIB.stca_sl_pack(_ref(dims), n_users, _ptr(full_off), _ptr(hist_off), total, _ptr(X_full),
+    _check(LIB.stca_sl_pack(_ref(dims), n_users, _ptr(full_off), _ptr(hist_off), total, max_len, _ptr(X_full),
                             _ptr(X_packed), _stream(stream)), "stca_sl_pack")
     return X_packed
 

@@ -710,18 +710,21 @@ int stca_sl_plan(const stca_sl_params *p, int32_t n_users, const int64_t *full_l
 }
 
 int stca_sl_pack(const stca_dims *dims, int32_t n_users, const int64_t *full_off, const int64_t *hist_off,
-                 int64_t total, const void *X_full, void *X_packed, void *stream) {
+                 int64_t total, int64_t max_len, const void *X_full, void *X_packed, void *stream) {
   if (!dims) return fail(STCA_E_ARG, "dims is NULL");
   if (dims->dtype != STCA_F32 && dims->dtype != STCA_BF16) return fail(STCA_E_DIMS, "unknown dtype %d", dims->dtype);
   const int64_t row_bytes = (int64_t)dims->d * (dims->dtype == STCA_BF16 ? 2 : 4);
   if (dims->d < 1 || row_bytes % 16 != 0) return fail(STCA_E_DIMS, "d=%d: rows must be a multiple of 16 bytes", dims->d);
-  if (n_users < 0 || total < 0) return fail(STCA_E_ARG, "n_users or total < 0");
-  if (total > 0 && n_users == 0) return fail(STCA_E_ARG, "total > 0 with no users");
+  if (n_users < 0 || total < 0 || max_len < 0) return fail(STCA_E_ARG, "n_users, total or max_len < 0");
+  if (total > 0 && (n_users == 0 || max_len == 0)) return fail(STCA_E_ARG, "total > 0 with no users or max_len 0");
+  if (max_len > total) return fail(STCA_E_ARG, "max_len %lld > total %lld", (long long)max_len, (long long)total);
+  if ((int64_t)n_users > 65535) return fail(STCA_E_ARG, "n_users %d > 65535", n_users);
   if (total == 0) return STCA_OK;
   if (!full_off || !hist_off || !X_full || !X_packed) return fail(STCA_E_ARG, "NULL pointer");
   if (!aligned16(X_full) || !aligned16(X_packed) || ((uintptr_t)full_off % 8) || ((uintptr_t)hist_off % 8))
     return fail(STCA_E_ALIGN, "X buffers need 16-byte, offsets 8-byte alignment");
-  HIP_TRY(sl_pack((hipStream_t)stream, n_users, full_off, hist_off, total, (int)(row_bytes / 16), X_full, X_packed));
+  HIP_TRY(sl_pack((hipStream_t)stream, n_users, full_off, hist_off, total, max_len, (int)(row_bytes / 16), X_full,
+                  X_packed));
   return STCA_OK;
 }
 

@@ -74,8 +74,9 @@ hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_o
                           const AttnBuffers &b);
 
 // ---- stochastic-length batches (sl.hip) -------------------------------------------------------
-// X_packed[total x row16 16-byte chunks] <- the temporal suffix rows of every user of X_full.
+// X_packed (rows of row16 16-byte chunks) <- the temporal suffix rows of every user of X_full;
+// max_len bounds every user's packed length.
 hipError_t sl_pack(hipStream_t s, int n_users, const int64_t *full_off, const int64_t *hist_off, int64_t total,
-                   int row16, const void *X_full, void *X_packed);
+                   int64_t max_len, int row16, const void *X_full, void *X_packed);
 
 }  // namespace stca

@@ -78,10 +78,11 @@ def test_pack_argument_checks():
     dims = B.make_dims(256, 8, 3, 4)
     L = B.LIB
     ref = ctypes.byref
-    assert L.stca_sl_pack(ref(dims), 2, FAKE, FAKE, 0, FAKE, FAKE, None) == 0   # nothing to copy
-    assert L.stca_sl_pack(ref(dims), 2, None, FAKE, 10, FAKE, FAKE, None) == -1
-    assert L.stca_sl_pack(ref(dims), 0, FAKE, FAKE, 10, FAKE, FAKE, None) == -1
-    assert L.stca_sl_pack(ref(dims), 2, FAKE, FAKE, 10, FAKE + 8, FAKE, None) == -4
+    assert L.stca_sl_pack(ref(dims), 2, FAKE, FAKE, 0, 0, FAKE, FAKE, None) == 0   # nothing to copy
+    assert L.stca_sl_pack(ref(dims), 2, None, FAKE, 10, 8, FAKE, FAKE, None) == -1
+    assert L.stca_sl_pack(ref(dims), 0, FAKE, FAKE, 10, 8, FAKE, FAKE, None) == -1
+    assert L.stca_sl_pack(ref(dims), 2, FAKE, FAKE, 10, 11, FAKE, FAKE, None) == -1   # max_len > total
+    assert L.stca_sl_pack(ref(dims), 2, FAKE, FAKE, 10, 8, FAKE + 8, FAKE, None) == -4
     bad = B.make_dims(256, 8, 3, 4)
     bad.d = 4                                                         # 8-byte bf16 rows
-    assert L.stca_sl_pack(ref(bad), 2, FAKE, FAKE, 10, FAKE, FAKE, None) == -2
+    assert L.stca_sl_pack(ref(bad), 2, FAKE, FAKE, 10, 8, FAKE, FAKE, None) == -2
