@@ -95,9 +95,8 @@ hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_
 // the transposing 64-bit LDS read (ds_read_b64_tr_b16: within each 16-lane group, lane i gets
 // element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, j = 0..3), two per fragment.
 // LDS tile layout: 32 rows x d/8 16-byte chunks, chunk c of row t stored at position
-// c ^ (t & SWZ) so both the row-wise and the column-wise reads spread over the banks.
-// History tiles stream through an NST-deep LDS ring (direct global->LDS loads), keeping
-// (NST-1) tiles in flight per workgroup.
+// c ^ sigma(t) so both the row-wise and the column-wise reads spread over the banks.
+// History tiles stream from HBM through registers into a 3-slot LDS ring.
 // ------------------------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
@@ -128,13 +127,17 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr int NKS = D / 16, NOB = D / 32;
   constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
   constexpr int LPW = INSTR / 4;                  // per wave
-  constexpr int NST = D <= 256 ? 5 : 4;           // tile ring depth
+  // Tiles pass through registers into a 3-slot LDS ring: tile k+2 is written while tile k+1's
+  // scores and tile k's PV product read the other two slots, and tile k+3 is fetched from HBM
+  // into the registers it leaves.  (No direct-to-LDS loads: with one in flight the compiler
+  // makes every transposed LDS read wait for all outstanding loads, serialising the pipeline.)
+  constexpr int NSL = 3;
   // At d = 512 a wave keeps half of the output features: two waves share a 32-row block
   // (both compute its scores), so U and the accumulators fit in one wave's registers.
   constexpr int FH = attn_feature_halves(D);
   constexpr int NOBW = NOB / FH;                  // output blocks per wave
   static_assert(INSTR % 4 == 0, "tile loads split evenly over 4 waves");
-  __shared__ bf16x8 tiles[NST][32 * CPR];
+  __shared__ bf16x8 tiles[NSL][32 * CPR];
 
   if ((int)blockIdx.x >= *n_items) return;
   const WorkItem it = items[blockIdx.x];
@@ -166,7 +169,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     }
   }
 
-  auto stage = [&](int k, int b) {
+  // Tile k: wave piece j = wave + 4 jj (1 KiB) holds, at byte 16 i, the 16-byte chunk
+  // (i mod CPR) ^ sigma(row) of history row 32 k + row, row = (64 j + i) / CPR (rows past the
+  // chunk's end repeat its last row; their scores are masked).
+  auto fetch = [&](int k, u32x4 (&rg)[LPW]) {
     const int64_t tb = t0 + 32 * (int64_t)k;
 #pragma unroll
     for (int jj = 0; jj < LPW; ++jj) {
@@ -175,12 +181,30 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       const int row = slot / CPR, cs = slot % CPR;
       const int c = cs ^ tile_sigma<D>(row);
       const int64_t tok = (tb + row < t1) ? tb + row : t1 - 1;
-      __builtin_amdgcn_global_load_lds(Xt + tok * D + c * 8, (STCA_LDS void *)&tiles[b][j * 64], 16, 0, 0);
+      rg[jj] = *reinterpret_cast<const u32x4 *>(Xt + tok * D + c * 8);
     }
   };
+  auto put = [&](int b, const u32x4 (&rg)[LPW]) {
 #pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < ntiles) stage(p, p);
+    for (int jj = 0; jj < LPW; ++jj) {
+      const int j = wave + 4 * jj;
+      tiles[b][j * 64 + lane] = __builtin_bit_cast(bf16x8, rg[jj]);
+    }
+  };
+  // LDS writes of this wave complete, then the workgroup meets; loads in flight stay in flight.
+  auto sync = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  u32x4 rg[LPW];  // the tile between its fetch (one iteration ahead) and its put
+  fetch(0, rg);
+  put(0, rg);
+  if (1 < ntiles) {
+    fetch(1, rg);
+    put(1, rg);
+  }
+  if (2 < ntiles) fetch(2, rg);
 
   f32x16 oacc[NOBW];
 #pragma unroll
@@ -305,19 +329,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     const int64_t r = t1 - (t0 + 32 * (int64_t)k);
     return (int)(r < 32 ? r : 32);
   };
-  auto tile_off = [&](int k) { return (uint32_t)((k % NST) * kTileBytes); };
+  auto tile_off = [&](int k) { return (uint32_t)((k % NSL) * kTileBytes); };
 
   // Pipeline: iteration k computes the scores of tile k+1 (matrix cores) while the vector ALU
   // turns the scores of tile k into probabilities, then the PV product of tile k.  Tiles k and
-  // k+1 are resident; tiles k+2 .. k+NST-2 are in flight; tile k+NST-1 is staged into the
-  // buffer of tile k-1.  The accumulators are touched only by MFMAs inside the loop: when a
-  // row maximum outgrows the slack the loop is left, the rescale runs, the tile is finished
-  // and the loop resumes.  The running maximum starts at the first tile's.
-  if (NST - 2 < ntiles)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 2)) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // k+1 are in LDS; tile k+2 is written from registers into the slot of tile k-1, and tile k+3
+  // is fetched into the registers it leaves.  The accumulators are touched only by MFMAs inside
+  // the loop: when a row maximum outgrows the slack the loop is left, the rescale runs, the
+  // tile is finished and the loop resumes.  The running maximum starts at the first tile's.
+  sync();
   f32x16 sa = f32x16{}, sb = f32x16{};
   if (wave_active) {
     scores(tile_off(0), sa, sb);
@@ -336,27 +356,29 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         pv(tile_off(k), pb, H1{});
     }
   };
+  // One step on tile k.  Returns true when a row maximum outgrew the slack: the caller then
+  // rescales and finishes tile k.
+  auto step = [&](int k, f32x16 &sc, float &mx) -> bool {
+    sync();  // tile k+1 is in LDS; tile k-1's slot is free
+    if (k + 2 < ntiles) {
+      put((k + 2) % NSL, rg);
+      if (k + 3 < ntiles) fetch(k + 3, rg);
+    }
+    if (!wave_active) return false;
+    const bool has_next = k + 1 < ntiles;
+    sc = sa + sb;
+    if (has_next) scores(tile_off(k + 1), sa, sb);  // in flight during the softmax below
+    mx = row_max(sc, tile_rem(k));
+    if (wave_any(mx > m_run + kLazy)) return true;
+    tail(k, sc);
+    return false;
+  };
   int k = 0;
   while (true) {
     f32x16 sc;
     float mx = 0.f;
-    for (; k < ntiles; ++k) {
-      const bool has_next = k + 1 < ntiles;
-      if (has_next) {
-        if (k + NST - 2 < ntiles)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 3)) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __syncthreads();  // tile k+1 is in LDS; tile k-1's buffer is free
-      if (k + NST - 1 < ntiles) stage(k + NST - 1, (k + NST - 1) % NST);
-      if (!wave_active) continue;
-      sc = sa + sb;
-      if (has_next) scores(tile_off(k + 1), sa, sb);  // in flight during the softmax below
-      mx = row_max(sc, tile_rem(k));
-      if (wave_any(mx > m_run + kLazy)) break;
-      tail(k, sc);
-    }
+    for (; k < ntiles; ++k)
+      if (step(k, sc, mx)) break;
     if (k >= ntiles) break;
     // rescale (rare), then finish tile k.  Both halves of a row take the same new maximum.
     const float m_new = fmaxf(m_run, half_max(mx));
