@@ -3,25 +3,24 @@
 // Equations: SwiGLU FFN of eq. (1) with the three-matrix shapes of the STCA review page
 // (section 2.2), followed by the LayerNorm of eq. (2) ("Make It Long, Keep It Fast", section 2.1).
 //
-// Work decomposition for d <= 256 (gfx950, 64-wide waves, v_mfma_f32_32x32x16_bf16):
-//   * a workgroup is 4 waves in 2 pairs; a pair owns 64 history tokens for the whole FFN and each
-//     wave keeps all 64 input rows in registers as MFMA B operands;
+// Work decomposition (gfx950, 64-wide waves, v_mfma_f32_32x32x16_bf16):
+//   * waves work in pairs; a pair owns 32 TB history tokens for the whole FFN and each wave keeps
+//     all of them in registers as MFMA B operands (TB = 32-token blocks per wave);
 //   * rd is walked in steps of 32 hidden features.  In each step wave `role` of a pair computes,
-//     for its 16 hidden features and the pair's 64 tokens, the transposed up and gate products in
+//     for its 16 hidden features and the pair's tokens, the transposed up and gate products in
 //     ONE accumulator per 32 tokens: the A operand stacks the 16 W_u columns (rows 0-15) on the 16
 //     W_v columns (rows 16-31), so accumulator registers i and i+8 of a lane hold the up and gate
 //     value of the same feature and token, and the SwiGLU gate is lane-local;
 //   * the gated values of a lane form exactly one B operand (16 hidden features x 32 tokens) of
-//     the down product; the pair swaps these through LDS (2 KiB per wave and step), and each wave
-//     accumulates half of the d outputs, Y^T[d/2 x 64] += W_o^T[d/2 x 32] H^T[32 x 64];
-//   * every weight fragment read from LDS (1 KiB) therefore feeds two MFMAs, one per 32-token
-//     block, which halves the LDS read traffic per MFMA against a wave that owns 32 tokens;
+//     the down product; the pair swaps these through LDS (1 KiB per wave, block and step), and
+//     each wave accumulates half of the d outputs, Y^T[d/2 x tokens] += W_o^T[d/2 x 32] H^T;
 //   * weights are pre-packed in fragment order (1 KiB = one wave operand), staged step by step
-//     into LDS with direct global->LDS loads two steps ahead, and shared by the 4 waves;
+//     into LDS with direct global->LDS loads and shared by all waves of the workgroup;
 //   * LayerNorm statistics of a token combine the two waves of its pair through LDS.
-// At d = 512 the 64 input rows do not fit in registers; each wave then owns 32 tokens and all d
-// outputs (encode_mfma_kernel below), with W_o read from L2 since a step of weights (96 KiB)
-// cannot be double-buffered in LDS.
+// d <= 256: a workgroup is 8 waves (TB = 1, two per SIMD) or 4 (TB = 2) over 128 tokens, and the
+// whole step (up/gate and down fragments) is staged two steps ahead in a 3-slot ring.  d = 512: a
+// step of weights is 96 KiB, so only the up/gate part is staged (two slots, one step ahead) and
+// each wave loads its down fragments from L2 into registers; 4 waves over 64 tokens.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -34,20 +33,16 @@ size_t encode_packed_bytes(int d, int r) { return (size_t)(r * d / 32) * (size_t
 // ------------------------------------------------------------------------------------------
 // Fragment re-layout.  Step s (hidden features 32s .. 32s+31) holds 3d/16 fragments of 64 lanes x
 // 8 bf16, in order:
-//   up/gate part, 2 d/16 fragments.
-//     pair layout (d <= 256), fragment role * d/16 + ks: lane l, slot e, row = l & 31:
+//   up/gate part, 2 d/16 fragments: fragment role * d/16 + ks: lane l, slot e, row = l & 31:
 //       W_u[16 ks + 8 (l>>5) + e][32 s + 16 role + row]        for row < 16,
 //       W_v[16 ks + 8 (l>>5) + e][32 s + 16 role + row - 16]   for row >= 16;
-//     single-wave layout (d = 512): fragment ks holds W_u, d/16 + ks W_v:
-//       W[16 ks + 8 (l>>5) + e][32 s + (l&31)];
 //   down part, 2 d/32 fragments for (32-wide output block ob, 16-feature block kk):
 //       lane l, slot e = W_o[32 s + phi(kk, l>>5, e)][32 ob + (l&31)],
 //     phi(kk, g, e) = 16 kk + 8 (e>>2) + 4 g + (e&3): the hidden feature whose gated value sits in
 //     slot e of the lane-group-g B operand built from 16-feature block kk.
-//     pair layout: fragment d/8 + (d/32) (kk ^ owner) + ob, owner = ob / (d/64) the role of the wave
-//       that accumulates block ob, so a wave finds its own-feature blocks and its partner-feature
-//       blocks as two runs at power-of-two offsets;
-//     single-wave layout: fragment d/8 + 2 ob + kk.
+//     fragment d/8 + (d/32) (kk ^ owner) + ob, owner = ob / (d/64) the role of the wave that
+//     accumulates block ob, so a wave finds its own-feature blocks and its partner-feature blocks
+//     as two runs at power-of-two offsets.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void encode_pack_kernel(int d, int rd, const uint16_t *__restrict__ Wu,
                                                           const uint16_t *__restrict__ Wv,
@@ -62,24 +57,15 @@ __global__ __launch_bounds__(256) void encode_pack_kernel(int d, int rd, const u
   const int s = (int)(fr / FPS), f = (int)(fr % FPS);
   const int col = lane & 31, g = lane >> 5;
   uint16_t v[8];
-  if (f < 2 * NKS && d <= 256) {
+  if (f < 2 * NKS) {
     const int role = f / NKS, ks = f % NKS;
     const uint16_t *W = col < 16 ? Wu : Wv;
     const int fc = 32 * s + 16 * role + (col & 15);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = W[(int64_t)(16 * ks + 8 * g + e) * rd + fc];
-  } else if (f < 2 * NKS) {
-    const uint16_t *W = (f < NKS) ? Wu : Wv;
-    const int ks = (f < NKS) ? f : f - NKS;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = W[(int64_t)(16 * ks + 8 * g + e) * rd + 32 * s + col];
   } else {
     const int idx = f - 2 * NKS;
-    int ob = idx >> 1, kk = idx & 1;
-    if (d <= 256) {
-      ob = idx % NOB;
-      kk = (idx / NOB) ^ (ob / (NOB / 2));
-    }
+    const int ob = idx % NOB, kk = (idx / NOB) ^ (ob / (NOB / 2));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int phi = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3);
@@ -127,16 +113,27 @@ __host__ __device__ constexpr int pair_up_idx(int g, int fd) { return g - (g / 3
 #endif
 
 // TB = 32-token blocks per wave: TB = 2 gives 4 waves of up to 512 registers (one per SIMD), TB = 1
-// gives 8 waves of up to 256 registers (two per SIMD).  Either way a workgroup covers 128 tokens.
+// gives 8 waves of up to 256 registers (two per SIMD); either way a workgroup covers 128 tokens.
+// At d = 512 (wide) a step of weights is 96 KiB: only the up/gate part goes through LDS (two
+// slots), each wave reads its W_o fragments from L2 into registers at the start of the step, and
+// the workgroup is 4 waves of one 32-token block (64 tokens), one wave per SIMD.
+template <int D, int TB> struct PairLaunch {
+  static constexpr bool kWide = D > 256;
+  static constexpr int NW = kWide ? 4 : 8 / TB;            // waves per workgroup
+  static constexpr int kTokens = (NW / 2) * 32 * TB;       // tokens per workgroup
+};
+
 template <int D, int TB, bool LN, typename TO>
-__global__ __launch_bounds__(64 * (8 / TB), 1) void encode_pair_kernel(int64_t n_rows, int n_steps,
+__global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_kernel(int64_t n_rows, int n_steps,
                                                              const bf16 *__restrict__ X, int64_t ldx,
                                                              const bf16x8 *__restrict__ packed,
                                                              TO *__restrict__ out, int64_t ldo,
                                                              const float *__restrict__ gamma,
                                                              const float *__restrict__ beta, float eps) {
   using S = PairShape<D>;
-  constexpr int NW = 8 / TB;  // waves per workgroup
+  constexpr bool kWide = PairLaunch<D, TB>::kWide;
+  constexpr int NW = PairLaunch<D, TB>::NW;
+  constexpr int kTokens = PairLaunch<D, TB>::kTokens;
   // Direct-to-LDS loads per wave and step: fragments go round-robin over the waves; the barrier
   // wait uses the smallest per-wave count, which waits for at least all loads of older steps.
   constexpr int LUV = (S::FUP + NW - 1) / NW, LO = (S::FDN + NW - 1) / NW;
@@ -147,8 +144,8 @@ __global__ __launch_bounds__(64 * (8 / TB), 1) void encode_pair_kernel(int64_t n
   // another (oN), see the step schedule below.  Every part is an array of its own so that the
   // compiler sees reads of one slot as independent of the loads landing in another and does not
   // wait for those loads.
-  __shared__ bf16x8 uv0[S::FUP][64], uv1[S::FUP][64], uv2[S::FUP][64];
-  __shared__ bf16x8 o0[S::FDN][64], o1[S::FDN][64], o2[S::FDN][64];
+  __shared__ bf16x8 uv0[S::FUP][64], uv1[S::FUP][64], uv2[kWide ? 1 : S::FUP][64];
+  __shared__ bf16x8 o0[kWide ? 1 : S::FDN][64], o1[kWide ? 1 : S::FDN][64], o2[kWide ? 1 : S::FDN][64];
   auto uv_slot = [&](int b) -> const STCA_LDS char * {
     return (const STCA_LDS char *)(b == 0 ? &uv0[0][0] : b == 1 ? &uv1[0][0] : &uv2[0][0]);
   };
@@ -163,7 +160,7 @@ __global__ __launch_bounds__(64 * (8 / TB), 1) void encode_pair_kernel(int64_t n
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int role = wave & 1, partner = wave ^ 1;
   const int col = lane & 31, grp = lane >> 5;
-  const int64_t tok0 = (int64_t)blockIdx.x * 128 + (wave >> 1) * 32 * TB + col;  // block tb: + 32 tb
+  const int64_t tok0 = (int64_t)blockIdx.x * kTokens + (wave >> 1) * 32 * TB + col;  // block tb: + 32 tb
   const int S_ = n_steps;
 
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)n_steps * SLOT);
@@ -265,106 +262,156 @@ __global__ __launch_bounds__(64 * (8 / TB), 1) void encode_pair_kernel(int64_t n
     }
   };
 
-  // Step t: the matrix cores run the up/gate products of step t+1 and the down product of step
-  // t-1 (own block from registers, partner's block from LDS); the vector ALU gates step t.  The
-  // up/gate fragments of step t live in ring slot t % 3, the down fragments of step t in slot
-  // t % 3 as well; step t stages up/gate of t+3 (into the slot step t-1 finished reading) and
-  // down of t+1, so every load has a full step to land before the barrier that precedes its use.
-  stage_uv(0, 0);
-  if (S_ > 1) stage_uv(1, 1);
-  if (S_ > 2) stage_uv(2, 2);
-  stage_o(0, 0);
-  barrier_vm<0>();
-  up_all(0);
-  barrier_vm<0>();  // slot 0's up/gate part is restaged in step 0
-
-  // Any step, plain order (first and last steps).
-  auto general = [&](int t) {
-    const bool has_up = t + 1 < S_, has_down = t >= 1;
-    if (t + 3 < S_) stage_uv(t + 3, t % 3);
-    if (t + 1 < S_) stage_o(t + 1, (t + 1) % 3);
-    if (has_down) swap_in(t - 1);
-    float ga[TB][16];
-    copy_acc(ga);
-    if (has_up) up_all((t + 1) % 3);
-    if (has_down) down_all((t + 2) % 3);
-    bf16x8 h[TB];
-    gate_all(ga, h);
-    swap_out(t, h);
+  if constexpr (kWide) {
+    // Step t: up/gate of step t+1 from LDS slot (t+1) % 2, down of step t-1 with W_o fragments
+    // loaded from L2 at the start of the step, gate of step t; up/gate of t+2 is staged into
+    // the slot step t-1 finished reading and must land by the end of step t.
+    auto down_regs = [&](const bf16x8 (&wo)[2][S::NOBW]) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
-    barrier_vm<0>();
-  };
-
-  // Steady-state step (1 <= t, t + 3 < n_steps) with t % 3 == T3 known at compile time.  The
-  // instruction order is pinned (sched_barrier): fragment reads run kAhead groups ahead through a
-  // register ring, and one gate element is computed every third MFMA.
-  auto steady = [&](int t, auto T3c) {
-    constexpr int T3 = decltype(T3c)::value;
-    constexpr int BU = (T3 + 1) % 3, BD = (T3 + 2) % 3;
-    stage_uv(t + 3, T3);
-    stage_o(t + 1, BU);
-    swap_in(t - 1);
-    auto frag = [&](int g) -> bf16x8 {
-      if (pair_is_down(g, S::FD)) {
-        const int di = g / 3;
-        return frag_at(o_slot(BD), (di < S::NOBW ? own_off : par_off) + (di % S::NOBW) * 1024u);
-      }
-      return frag_at(uv_slot(BU), uv_off + pair_up_idx(g, S::FD) * 1024u);
+      for (int ob = 0; ob < S::NOBW; ++ob)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) yacc[ob][tb] = mfma32x32x16(wo[0][ob], hb_prev[tb], yacc[ob][tb]);
+#pragma unroll
+      for (int ob = 0; ob < S::NOBW; ++ob)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) yacc[ob][tb] = mfma32x32x16(wo[1][ob], hp[tb], yacc[ob][tb]);
     };
-    float ga[TB][16];
-    copy_acc(ga);
-    bf16x8 ring[kRing];
+    auto load_wo = [&](int t, bf16x8 (&wo)[2][S::NOBW]) {
+      const bf16x8 *base = packed + ((int64_t)t * S::FPS + S::FUP + S::NOBW * role) * 64 + lane;
 #pragma unroll
-    for (int p = 0; p < kAhead; ++p) ring[p] = frag(p);
-    float hv[8 * TB];
-    __builtin_amdgcn_sched_barrier(0);
-    constexpr int kMM = TB * S::NG;
+      for (int ob = 0; ob < S::NOBW; ++ob) {
+        wo[0][ob] = base[ob * 64];
+        wo[1][ob] = base[(S::NOB + ob) * 64];
+      }
+    };
+    stage_uv(0, 0);
+    if (S_ > 1) stage_uv(1, 1);
+    barrier_vm<0>();
+    up_all(0);
+    barrier_vm<0>();  // slot 0 is restaged in step 0
+    for (int t = 0; t < S_; ++t) {
+      const bool has_up = t + 1 < S_, has_down = t >= 1;
+      bf16x8 wo[2][S::NOBW];
+      if (has_down) load_wo(t - 1, wo);
+      if (t + 2 < S_) stage_uv(t + 2, t % 2);
+      if (has_down) swap_in(t - 1);
+      float ga[TB][16];
+      copy_acc(ga);
+      if (has_up) up_all((t + 1) % 2);
+      if (has_down) down_regs(wo);
+      bf16x8 h[TB];
+      gate_all(ga, h);
+      swap_out(t, h);
 #pragma unroll
-    for (int k = 0; k < kMM; ++k) {
-      const int g = k / TB, tb = k % TB;
-      if (tb == 0 && g + kAhead < S::NG) ring[(g + kAhead) % kRing] = frag(g + kAhead);
-      if (pair_is_down(g, S::FD)) {
-        const int di = g / 3, ob = di % S::NOBW;
-        yacc[ob][tb] = mfma32x32x16(ring[g % kRing], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[ob][tb]);
-      } else {
-        const int ui = pair_up_idx(g, S::FD);
-        acc[tb] = mfma32x32x16(ring[g % kRing], xb[tb][ui], ui == 0 ? f32x16{} : acc[tb]);
-      }
-      if (k % 3 == 0 && k / 3 < 8 * TB) {
-        const int e = k / 3;
-        hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
-        asm volatile("" : "+v"(hv[e]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
+      barrier_vm<0>();
     }
-#pragma unroll
-    for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
-    bf16x8 h[TB];
-#pragma unroll
-    for (int e = 0; e < 8 * TB; ++e) h[e >> 3][e & 7] = f32_to_bf16(hv[e]);
-    swap_out(t, h);
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
-    // Data read in step t+1 (up/gate of t+2, down of t) was staged in step t-1 or before; this
-    // step's loads may stay in flight.
-    barrier_vm<kStepLoads>();
-  };
+    swap_in(S_ - 1);
+    bf16x8 wo[2][S::NOBW];
+    load_wo(S_ - 1, wo);
+    down_regs(wo);
+  } else {
+    // Step t: the matrix cores run the up/gate products of step t+1 and the down product of step
+    // t-1 (own block from registers, partner's block from LDS); the vector ALU gates step t.  The
+    // up/gate fragments of step t live in ring slot t % 3, the down fragments of step t in slot
+    // t % 3 as well; step t stages up/gate of t+3 (into the slot step t-1 finished reading) and
+    // down of t+1, so every load has a full step to land before the barrier that precedes its use.
+    stage_uv(0, 0);
+    if (S_ > 1) stage_uv(1, 1);
+    if (S_ > 2) stage_uv(2, 2);
+    stage_o(0, 0);
+    barrier_vm<0>();
+    up_all(0);
+    barrier_vm<0>();  // slot 0's up/gate part is restaged in step 0
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  general(0);
-  int t = 1;
-  for (; t + 5 < S_; t += 3) {
-    steady(t, I1{});
-    steady(t + 1, I2{});
-    steady(t + 2, I0{});
+    // Any step, plain order (first and last steps).
+    auto general = [&](int t) {
+      const bool has_up = t + 1 < S_, has_down = t >= 1;
+      if (t + 3 < S_) stage_uv(t + 3, t % 3);
+      if (t + 1 < S_) stage_o(t + 1, (t + 1) % 3);
+      if (has_down) swap_in(t - 1);
+      float ga[TB][16];
+      copy_acc(ga);
+      if (has_up) up_all((t + 1) % 3);
+      if (has_down) down_all((t + 2) % 3);
+      bf16x8 h[TB];
+      gate_all(ga, h);
+      swap_out(t, h);
+  #pragma unroll
+      for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
+      barrier_vm<0>();
+    };
+
+    // Steady-state step (1 <= t, t + 3 < n_steps) with t % 3 == T3 known at compile time.  The
+    // instruction order is pinned (sched_barrier): fragment reads run kAhead groups ahead through a
+    // register ring, and one gate element is computed every third MFMA.
+    auto steady = [&](int t, auto T3c) {
+      constexpr int T3 = decltype(T3c)::value;
+      constexpr int BU = (T3 + 1) % 3, BD = (T3 + 2) % 3;
+      stage_uv(t + 3, T3);
+      stage_o(t + 1, BU);
+      swap_in(t - 1);
+      auto frag = [&](int g) -> bf16x8 {
+        if (pair_is_down(g, S::FD)) {
+          const int di = g / 3;
+          return frag_at(o_slot(BD), (di < S::NOBW ? own_off : par_off) + (di % S::NOBW) * 1024u);
+        }
+        return frag_at(uv_slot(BU), uv_off + pair_up_idx(g, S::FD) * 1024u);
+      };
+      float ga[TB][16];
+      copy_acc(ga);
+      bf16x8 ring[kRing];
+  #pragma unroll
+      for (int p = 0; p < kAhead; ++p) ring[p] = frag(p);
+      float hv[8 * TB];
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int kMM = TB * S::NG;
+  #pragma unroll
+      for (int k = 0; k < kMM; ++k) {
+        const int g = k / TB, tb = k % TB;
+        if (tb == 0 && g + kAhead < S::NG) ring[(g + kAhead) % kRing] = frag(g + kAhead);
+        if (pair_is_down(g, S::FD)) {
+          const int di = g / 3, ob = di % S::NOBW;
+          yacc[ob][tb] = mfma32x32x16(ring[g % kRing], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[ob][tb]);
+        } else {
+          const int ui = pair_up_idx(g, S::FD);
+          acc[tb] = mfma32x32x16(ring[g % kRing], xb[tb][ui], ui == 0 ? f32x16{} : acc[tb]);
+        }
+        if (k % 3 == 0 && k / 3 < 8 * TB) {
+          const int e = k / 3;
+          hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+          asm volatile("" : "+v"(hv[e]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  #pragma unroll
+      for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+      bf16x8 h[TB];
+  #pragma unroll
+      for (int e = 0; e < 8 * TB; ++e) h[e >> 3][e & 7] = f32_to_bf16(hv[e]);
+      swap_out(t, h);
+  #pragma unroll
+      for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
+      // Data read in step t+1 (up/gate of t+2, down of t) was staged in step t-1 or before; this
+      // step's loads may stay in flight.
+      barrier_vm<kStepLoads>();
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    general(0);
+    int t = 1;
+    for (; t + 5 < S_; t += 3) {
+      steady(t, I1{});
+      steady(t + 1, I2{});
+      steady(t + 2, I0{});
+    }
+    for (; t < S_; ++t) general(t);
+    // The down product of the last step remains.
+    swap_in(S_ - 1);
+    down_all((S_ - 1) % 3);
   }
-  for (; t < S_; ++t) general(t);
-  // The down product of the last step remains.
-  swap_in(S_ - 1);
-  down_all((S_ - 1) % 3);
 
   // Epilogue.  Lane l holds tokens tok0 + 32 tb; register i of block ob is output feature
   // 32 (NOBW role + ob) + 8 (i>>2) + 4 (l>>5) + (i&3).  A token's d outputs are spread over
@@ -374,7 +421,7 @@ __global__ __launch_bounds__(64 * (8 / TB), 1) void encode_pair_kernel(int64_t n
   for (int tb = 0; tb < TB; ++tb) mean[tb] = 0.f, inv[tb] = 1.f;
   if constexpr (LN) {
     // Ring slot S_ % 3 is no longer read: it carries the per-wave partial sums.
-    STCA_LDS float *red = (STCA_LDS float *)uv_slot(S_ % 3);  // [stat][wave][tb][col]
+    STCA_LDS float *red = (STCA_LDS float *)uv_slot(kWide ? 0 : S_ % 3);  // [stat][wave][tb][col]
     constexpr int kStat = NW * TB * 32;
     float part[TB];
 #pragma unroll
@@ -442,153 +489,16 @@ __global__ __launch_bounds__(64 * (8 / TB), 1) void encode_pair_kernel(int64_t n
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// The fused kernel, d = 512: one wave owns 32 tokens and all d outputs; W_u/W_v steps are
-// double-buffered in LDS, W_o fragments are read from L2.
-// ------------------------------------------------------------------------------------------
-template <int D> struct WideShape {
-  static constexpr int NKS = D / 16;             // 16-deep k-steps over d (up/gate products)
-  static constexpr int NOB = D / 32;             // 32-wide output blocks (down product)
-  static constexpr int FPS = 2 * NKS + 2 * NOB;  // fragments per 32-feature step of rd
-  static constexpr int FPS_LDS = 2 * NKS;        // fragments staged in LDS per step
-};
-
-template <int D, bool LN, typename TO>
-__global__ __launch_bounds__(256, 1) void encode_mfma_kernel(int64_t n_rows, int n_slices,
-                                                             const bf16 *__restrict__ X, int64_t ldx,
-                                                             const bf16x8 *__restrict__ packed,
-                                                             TO *__restrict__ out, int64_t ldo,
-                                                             const float *__restrict__ gamma,
-                                                             const float *__restrict__ beta, float eps) {
-  using S = WideShape<D>;
-  __shared__ bf16x8 wbuf[2][S::FPS_LDS][64];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 31, grp = lane >> 5;
-  const int64_t tok = (int64_t)blockIdx.x * 128 + wave * 32 + col;
-  const bool valid = tok < n_rows;
-
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)n_slices * S::FPS * 1024u);
-  auto stage = [&](int s, int b) {
-    static_assert(S::FPS_LDS % 4 == 0, "fragments split evenly over 4 waves");
-#pragma unroll
-    for (int j = 0; j < S::FPS_LDS / 4; ++j) {
-      const int f = wave + 4 * j;
-      load_lds16(wrs, (STCA_LDS void *)&wbuf[b][f][0], (uint32_t)(f * 64 + lane) * 16u,
-                 (uint32_t)s * S::FPS * 1024u);
-    }
-  };
-
-  stage(0, 0);
-
-  // The wave's 32 tokens as B operands: lane l holds token (l&31), features 16 ks + 8 (l>>5) + 0..7.
-  bf16x8 xb[S::NKS];
-  {
-    const bf16 *xrow = X + (valid ? tok : 0) * ldx + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < S::NKS; ++ks) {
-      if (valid)
-        xb[ks] = *reinterpret_cast<const bf16x8 *>(xrow + 16 * ks);
-      else
-        xb[ks] = bf16x8{};
-    }
-  }
-
-  f32x16 yacc[S::NOB];
-#pragma unroll
-  for (int ob = 0; ob < S::NOB; ++ob) yacc[ob] = f32x16{};
-
-  for (int s = 0; s < n_slices; ++s) {
-    const int b = s & 1;
-    barrier_vm<0>();  // step s is in LDS for every wave; buffer b^1 is no longer read
-    if (s + 1 < n_slices) stage(s + 1, b ^ 1);
-    // Up and gate products (transposed: rows = hidden features, columns = tokens).
-    f32x16 accA = f32x16{}, accG = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < S::NKS; ++ks) {
-      accA = mfma32x32x16(wbuf[b][ks][lane], xb[ks], accA);
-      accG = mfma32x32x16(wbuf[b][S::NKS + ks][lane], xb[ks], accG);
-    }
-    // SwiGLU gate in registers -> bf16 B operands of the down product.
-    bf16x8 hb[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) hb[i >> 3][i & 7] = f32_to_bf16(swiglu_gate(accA[i], accG[i]));
-    // Down product: Y^T[out x tok] += W_o^T[out x 32] H^T[32 x tok].
-#pragma unroll
-    for (int ob = 0; ob < S::NOB; ++ob) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 wo = packed[((int64_t)s * S::FPS + 2 * S::NKS + 2 * ob + kk) * 64 + lane];
-        yacc[ob] = mfma32x32x16(wo, hb[kk], yacc[ob]);
-      }
-    }
-  }
-
-  // Epilogue.  Lane l holds token (l&31); register i of block ob is output feature
-  // 32 ob + 8 (i>>2) + 4 (l>>5) + (i&3); lane l^32 holds the other half of the row.
-  float mean = 0.f, inv = 1.f;
-  if constexpr (LN) {
-    float sum = 0.f;
-#pragma unroll
-    for (int ob = 0; ob < S::NOB; ++ob)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += yacc[ob][i];
-    sum = half_sum(sum);
-    mean = sum * (1.0f / D);
-    float sq = 0.f;
-#pragma unroll
-    for (int ob = 0; ob < S::NOB; ++ob)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float t = yacc[ob][i] - mean;
-        sq += t * t;
-      }
-    sq = half_sum(sq);
-    inv = 1.0f / sqrtf(sq * (1.0f / D) + eps);
-  }
-  if (!valid) return;
-  TO *orow = out + tok * ldo;
-#pragma unroll
-  for (int ob = 0; ob < S::NOB; ++ob) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f0 = 32 * ob + 8 * q + 4 * grp;
-      float v[4];
-      if constexpr (LN) {
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(gamma + f0);
-        const f32x4 bt = *reinterpret_cast<const f32x4 *>(beta + f0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = (yacc[ob][4 * q + j] - mean) * inv * gm[j] + bt[j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = yacc[ob][4 * q + j];
-      }
-      if constexpr (sizeof(TO) == 2) {
-        bf16x4 p;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = f32_to_bf16(v[j]);
-        *reinterpret_cast<bf16x4 *>(orow + f0) = p;
-      } else {
-        *reinterpret_cast<f32x4 *>(orow + f0) = f32x4{v[0], v[1], v[2], v[3]};
-      }
-    }
-  }
-}
-
 template <int D, bool LN, typename TO>
 static hipError_t launch_encode(hipStream_t s, int r, int64_t n_rows, const void *X, int64_t ldx,
                                 const void *packed, void *out, int64_t ldo, const float *gamma,
                                 const float *beta, float eps) {
-  const int64_t blocks = (n_rows + 127) / 128;
-  if constexpr (D <= 256)
-    hipLaunchKernelGGL((encode_pair_kernel<D, STCA_ENC_TB, LN, TO>), dim3((unsigned)blocks),
-                       dim3(64 * (8 / STCA_ENC_TB)), 0, s, n_rows,
-                       r * D / 32, (const bf16 *)X, ldx, (const bf16x8 *)packed, (TO *)out, ldo, gamma, beta,
-                       eps);
-  else
-    hipLaunchKernelGGL((encode_mfma_kernel<D, LN, TO>), dim3((unsigned)blocks), dim3(256), 0, s, n_rows,
-                       r * D / 32, (const bf16 *)X, ldx, (const bf16x8 *)packed, (TO *)out, ldo, gamma, beta,
-                       eps);
+  constexpr int TB = D > 256 ? 1 : STCA_ENC_TB;
+  using PL = PairLaunch<D, TB>;
+  const int64_t blocks = (n_rows + PL::kTokens - 1) / PL::kTokens;
+  hipLaunchKernelGGL((encode_pair_kernel<D, TB, LN, TO>), dim3((unsigned)blocks), dim3(64 * PL::NW), 0, s,
+                     n_rows, r * D / 32, (const bf16 *)X, ldx, (const bf16x8 *)packed, (TO *)out, ldo, gamma,
+                     beta, eps);
   return hipGetLastError();
 }
 
