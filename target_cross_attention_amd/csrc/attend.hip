@@ -172,16 +172,29 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // Tile k: wave piece j = wave + 4 jj (1 KiB) holds, at byte 16 i, the 16-byte chunk
   // (i mod CPR) ^ sigma(row) of history row 32 k + row, row = (64 j + i) / CPR (rows past the
   // chunk's end repeat its last row; their scores are masked).
-  auto fetch = [&](int k, u32x4 (&rg)[LPW]) {
-    const int64_t tb = t0 + 32 * (int64_t)k;
+  // Per-lane (row, element offset within the tile) of each piece, fixed for the whole item.
+  int frow[LPW];
+  uint32_t foff[LPW];
 #pragma unroll
-    for (int jj = 0; jj < LPW; ++jj) {
-      const int j = wave + 4 * jj;
-      const int slot = j * 64 + lane;
-      const int row = slot / CPR, cs = slot % CPR;
-      const int c = cs ^ tile_sigma<D>(row);
-      const int64_t tok = (tb + row < t1) ? tb + row : t1 - 1;
-      rg[jj] = *reinterpret_cast<const u32x4 *>(Xt + tok * D + c * 8);
+  for (int jj = 0; jj < LPW; ++jj) {
+    const int slot = (wave + 4 * jj) * 64 + lane;
+    const int row = slot / CPR, cs = slot % CPR;
+    frow[jj] = row;
+    foff[jj] = (uint32_t)(row * D + (cs ^ tile_sigma<D>(row)) * 8);
+  }
+  const int64_t len = t1 - t0;
+  auto fetch = [&](int k, u32x4 (&rg)[LPW]) {
+    const bf16 *tile = Xt + (t0 + 32 * (int64_t)k) * D;
+    if (32 * (int64_t)(k + 1) <= len) {
+#pragma unroll
+      for (int jj = 0; jj < LPW; ++jj) rg[jj] = *reinterpret_cast<const u32x4 *>(tile + foff[jj]);
+    } else {  // partial last tile: rows past the end repeat the last row
+      const int rem = (int)(len - 32 * (int64_t)k);
+#pragma unroll
+      for (int jj = 0; jj < LPW; ++jj) {
+        const int back = frow[jj] < rem ? 0 : (frow[jj] - rem + 1) * D;
+        rg[jj] = *reinterpret_cast<const u32x4 *>(tile + (foff[jj] - back));
+      }
     }
   };
   auto put = [&](int b, const u32x4 (&rg)[LPW]) {
@@ -257,7 +270,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // ds_read instructions, counted by lgkmcnt only, independent of the tile loads in flight).
   const STCA_LDS char *lds = (const STCA_LDS char *)&tiles[0][0];
   constexpr uint32_t kTileBytes = 32 * CPR * 16;
-  // Scores of one tile into two independent accumulation chains (halves of the d reduction).
+  // Scores of one tile into two independent accumulation chains (halves of the d reduction);
+  // their sum lands in fresh registers, leaving both chains free for the next tile.
   auto scores = [&](uint32_t toff, f32x16 &s0, f32x16 &s1) {
     uint32_t rx = rx16, rb = toff + row_off;
     asm volatile("" : "+v"(rx), "+v"(rb));
