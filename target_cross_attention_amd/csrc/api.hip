@@ -421,6 +421,7 @@ struct ForwardWs {
   void *Xt = nullptr;
   float *q = nullptr;
   float *c = nullptr;
+  void *cb = nullptr;  // eq. (7) projection in bf16: the MFMA query FFN's input
   FfnWs ffn;
   AttendWs aw;
 };
@@ -433,13 +434,14 @@ size_t carve_forward(void *base, const stca_dims *dm, const stca_batch *b, const
   if (dm->dtype == STCA_BF16) {
     const size_t pb = encode_packed_bytes(dm->d, dm->r);
     for (int i = 0; i < dm->M; ++i) w.packed_hist[i] = c.take<char>(pb);
+    for (int i = 0; i < dm->M; ++i) w.packed_query[i] = c.take<char>(pb);
     (void)wt;
   }
   w.Xt = c.take<char>((size_t)(b->total_L * dm->d) * esize(dm));
   w.q = c.take<float>((size_t)(b->total_T * dm->d));
   w.c = c.take<float>((size_t)(b->total_T * dm->d));
-  const int64_t ffn_rows = dm->dtype == STCA_BF16 ? b->total_T : std::max(b->total_T, b->total_L);
-  carve_ffn(c, dm, ffn_rows, w.ffn);
+  if (dm->dtype == STCA_BF16) w.cb = c.take<char>((size_t)(b->total_T * dm->d) * 2);
+  if (dm->dtype != STCA_BF16) carve_ffn(c, dm, std::max(b->total_T, b->total_L), w.ffn);
   carve_attend(c, dm, b, p, w.aw);
   return round_up(c.off, 256);
 }
@@ -478,14 +480,34 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
       }
       HIP_TRY(encode_pack(s, d, dm->r, w->hist[i].Wu, w->hist[i].Wv, w->hist[i].Wo, fw.packed_hist[i]));
     }
+    // Query FFNs (eqs. (3), (7)) run on the same MFMA kernel; they usually share the history
+    // FFN's weights (reused), otherwise they are packed here.
+    for (int i = 0; i < M; ++i) {
+      void *found = nullptr;
+      for (int j = 0; j < M && !found; ++j)
+        if (same_ffn(w->hist[j], w->query[i])) found = fw.packed_hist[j];
+      for (int j = 0; j < i && !found; ++j)
+        if (same_ffn(w->query[j], w->query[i])) found = fw.packed_query[j];
+      if (found) {
+        fw.packed_query[i] = found;
+        continue;
+      }
+      HIP_TRY(encode_pack(s, d, dm->r, w->query[i].Wu, w->query[i].Wv, w->query[i].Wo, fw.packed_query[i]));
+    }
     HIP_TRY(ph.end());
   }
   HIP_TRY(build_worklist(s, p, b->hist_off, b->tgt_off, fw.aw.ab));
 
   {  // eq. (3): q(1) = LN(SwiGLUFFN(1)(x_t))
     Phase ph(prof, s, STCA_PHASE_QUERY);
-    if ((st = ffn_generic(s, dm, &w->query[0], b->total_T, xt, d, bf, fw.q, d, false, true, fw.ffn)) != STCA_OK)
+    if (bf) {
+      const stca_ffn &f = w->query[0];
+      HIP_TRY(encode_mfma(s, d, dm->r, b->total_T, xt, d, fw.packed_query[0], fw.q, d, false, true, f.gamma, f.beta,
+                          dm->ln_eps));
+    } else if ((st = ffn_generic(s, dm, &w->query[0], b->total_T, xt, d, bf, fw.q, d, false, true, fw.ffn)) !=
+               STCA_OK) {
       return st;
+    }
     HIP_TRY(ph.end());
   }
   for (int i = 0; i < M; ++i) {
@@ -501,9 +523,15 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
     if (i + 1 < M) {  // eq. (7): q(i+1) = SwiGLUFFN([o(1..i) || x_t] W_C) (+LN)
       Phase ph(prof, s, STCA_PHASE_QUERY);
       HIP_TRY(concat_project(s, dm, b->total_T, Z, (int64_t)M * d, i + 1, xt, w->WC[i + 1], fw.c));
-      if ((st = ffn_generic(s, dm, &w->query[i + 1], b->total_T, fw.c, d, false, fw.q, d, false, dm->query_ln != 0,
-                            fw.ffn)) != STCA_OK)
+      if (bf) {  // bf16 input of the MFMA FFN, fp32 output q
+        const stca_ffn &f = w->query[i + 1];
+        HIP_TRY(to_bf16(s, b->total_T * d, fw.c, fw.cb));
+        HIP_TRY(encode_mfma(s, d, dm->r, b->total_T, fw.cb, d, fw.packed_query[i + 1], fw.q, d, false,
+                            dm->query_ln != 0, f.gamma, f.beta, dm->ln_eps));
+      } else if ((st = ffn_generic(s, dm, &w->query[i + 1], b->total_T, fw.c, d, false, fw.q, d, false,
+                                   dm->query_ln != 0, fw.ffn)) != STCA_OK) {
         return st;
+      }
       HIP_TRY(ph.end());
     }
   }

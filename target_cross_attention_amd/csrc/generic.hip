@@ -183,4 +183,22 @@ hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, in
   return hipGetLastError();
 }
 
+// dst[i] = bf16(src[i]) (round to nearest even), four elements per thread.
+__global__ __launch_bounds__(256) void to_bf16_kernel(int64_t n4, const f32x4 *__restrict__ src,
+                                                      bf16x4 *__restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4 v = src[i];
+  dst[i] = bf16x4{f32_to_bf16(v[0]), f32_to_bf16(v[1]), f32_to_bf16(v[2]), f32_to_bf16(v[3])};
+}
+
+hipError_t to_bf16(hipStream_t s, int64_t n, const float *src, void *dst) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, n4, (const f32x4 *)src,
+                     (bf16x4 *)dst);
+  return hipGetLastError();
+}
+
 }  // namespace stca

@@ -24,6 +24,8 @@ hipError_t gemm(hipStream_t s, const GemmArgs &g);
 hipError_t swiglu_gate_inplace(hipStream_t s, int64_t n, float *A, const float *G);
 hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, int64_t ldy, void *out,
                           int64_t ldo, bool out_bf16, const float *gamma, const float *beta, float eps);
+// dst[n] (bf16) = src[n] (fp32) rounded to nearest even; n a multiple of 4.
+hipError_t to_bf16(hipStream_t s, int64_t n, const float *src, void *dst);
 
 // ---- fused bf16 MFMA encode (encode_mfma.hip) -----------------------------------------------
 // Re-layout of one FFN's W_u, W_v (d x rd) and W_o (rd x d) into MFMA fragment order.
