@@ -105,11 +105,12 @@ int check_weights(const stca_dims *dm, const stca_weights *w) {
 // ---- attention plan -------------------------------------------------------------------------
 int auto_chunk(const stca_dims *dm, const stca_batch *b) {
   if (dm->attn_chunk > 0) return dm->attn_chunk;
-  // Aim for >= ~2 work items per workgroup slot of the chip, but keep chunks long enough
-  // that the partial-state traffic stays small next to the history bytes.
+  // Aim for about four work items per compute unit (one resident workgroup each at d >= 256),
+  // enough to balance ragged lengths, while keeping chunks long: every extra chunk of a user
+  // writes and re-reads a partial state (max, sum, m h x d accumulator) through HBM.
   const int rpg = attn_rows_per_group(dm->d);
   const int64_t groups = std::max<int64_t>(1, (b->max_T * dm->h + rpg - 1) / rpg);
-  const int64_t target_items = 2048;
+  const int64_t target_items = 1024;
   int64_t c = (b->total_L * groups + target_items - 1) / target_items;
   c = std::max<int64_t>(c, 512);
   c = std::min<int64_t>(c, std::max<int64_t>(b->max_L, 32));
