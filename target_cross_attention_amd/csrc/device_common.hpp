@@ -52,6 +52,10 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float swiglu_gate(float a, float g) {
   return a * g * fast_rcp(1.0f + fast_exp2(-g * kLog2e));
 }
+// The same gate on pre-scaled inputs a' = -ln2 a, g' = -log2(e) g: a' g' = a g and 2^g' = e^-g.
+__device__ __forceinline__ float swiglu_gate_scaled(float a, float g) {
+  return a * g * fast_rcp(1.0f + fast_exp2(g));
+}
 
 // ---- wave (64-lane) reductions -------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
@@ -101,6 +105,14 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, STCA_LDS vo
 // for every outstanding LDS-bound load, including those meant to stay in flight across it.
 template <int VM> __device__ __forceinline__ void barrier_vm() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VM) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations: vector-memory loads (for
+// instance direct-to-LDS staging meant for a later phase) may stay in flight across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

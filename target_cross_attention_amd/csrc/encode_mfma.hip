@@ -14,13 +14,20 @@
 //   * the gated values of a lane form exactly one B operand (16 hidden features x 32 tokens) of
 //     the down product; the pair swaps these through LDS (1 KiB per wave, block and step), and
 //     each wave accumulates half of the d outputs, Y^T[d/2 x tokens] += W_o^T[d/2 x 32] H^T;
-//   * weights are pre-packed in fragment order (1 KiB = one wave operand), staged step by step
-//     into LDS with direct global->LDS loads and shared by all waves of the workgroup;
-//   * LayerNorm statistics of a token combine the two waves of its pair through LDS.
-// d <= 256: a workgroup is 8 waves (TB = 1, two per SIMD) or 4 (TB = 2) over 128 tokens, and the
-// whole step (up/gate and down fragments) is staged two steps ahead in a 3-slot ring.  d = 512: a
-// step of weights is 96 KiB, so only the up/gate part is staged (two slots, one step ahead) and
-// each wave loads its down fragments from L2 into registers; 4 waves over 64 tokens.
+//   * weights are pre-packed in fragment order (1 KiB = one wave operand); the up/gate columns are
+//     pre-scaled (by -ln 2 and -log2 e) so that the gate needs no scaling multiply; fragments are
+//     staged step by step into LDS with direct global->LDS loads and shared by all waves of the
+//     workgroup, or read by each wave from L2 straight into registers (down fragments at d >= 256);
+//   * LayerNorm statistics of a token combine the two waves of its pair through LDS;
+//   * workgroups are persistent and walk 128-token tiles (64 at d = 512); a tile's rows and
+//     first weight steps are loaded while the previous tile finishes.
+// d <= 256: a workgroup is 8 waves (TB = 1, two per SIMD; d < 256) or 4 (TB = 2, one per SIMD;
+// d = 256) over 128 tokens, whose rows are staged in LDS with coalesced loads and read out in the
+// B-operand layout; the up/gate fragments are staged two steps ahead in a 3-slot ring.  d = 512: a
+// step of weights is 96 KiB, so only the up/gate part is staged (two slots, one step ahead), the
+// rows are loaded straight into registers, and each wave loads its down fragments from L2; 4 waves
+// over 64 tokens.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -60,9 +67,15 @@ __global__ __launch_bounds__(256) void encode_pack_kernel(int d, int rd, const u
   if (f < 2 * NKS) {
     const int role = f / NKS, ks = f % NKS;
     const uint16_t *W = col < 16 ? Wu : Wv;
+    // Pre-scaled so that the kernel's accumulators hold u' = -ln2 u and v' = -log2(e) v: then
+    // u v SiLU(v) = u' v' / (1 + 2^v'), with no scaling multiply in the gate.
+    const float scale = col < 16 ? -0.69314718055994531f : -1.4426950408889634f;
     const int fc = 32 * s + 16 * role + (col & 15);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = W[(int64_t)(16 * ks + 8 * g + e) * rd + fc];
+    for (int e = 0; e < 8; ++e) {
+      const float w = __uint_as_float((uint32_t)W[(int64_t)(16 * ks + 8 * g + e) * rd + fc] << 16);
+      v[e] = f32_to_bf16_bits(w * scale);
+    }
   } else {
     const int idx = f - 2 * NKS;
     const int ob = idx % NOB, kk = (idx / NOB) ^ (ob / (NOB / 2));
@@ -108,12 +121,24 @@ __host__ __device__ constexpr int pair_up_idx(int g, int fd) { return g - (g / 3
 #ifndef STCA_ENC_RING
 #define STCA_ENC_RING 4
 #endif
+// 32-token blocks per wave at d = 256 and at smaller d.
 #ifndef STCA_ENC_TB
-#define STCA_ENC_TB 1
+#define STCA_ENC_TB 2
+#endif
+#ifndef STCA_ENC_TB_SMALL
+#define STCA_ENC_TB_SMALL 1
+#endif
+#ifndef STCA_ENC_GO
+#define STCA_ENC_GO 1
+#endif
+#ifndef STCA_ENC_STAGGER
+#define STCA_ENC_STAGGER 24
 #endif
 
 // TB = 32-token blocks per wave: TB = 2 gives 4 waves of up to 512 registers (one per SIMD), TB = 1
 // gives 8 waves of up to 256 registers (two per SIMD); either way a workgroup covers 128 tokens.
+// At d = 256 TB = 2 reads half as many fragment bytes per MFMA, which saves power: the kernel runs
+// at the chip's power limit, and TB = 2 measured ~1.5% faster than TB = 1 there, slower at d = 128.
 // At d = 512 (wide) a step of weights is 96 KiB: only the up/gate part goes through LDS (two
 // slots), each wave reads its W_o fragments from L2 into registers at the start of the step, and
 // the workgroup is 4 waves of one 32-token block (64 tokens), one wave per SIMD.
@@ -121,6 +146,9 @@ template <int D, int TB> struct PairLaunch {
   static constexpr bool kWide = D > 256;
   static constexpr int NW = kWide ? 4 : 8 / TB;            // waves per workgroup
   static constexpr int kTokens = (NW / 2) * 32 * TB;       // tokens per workgroup
+  // d = 256: the down (W_o) fragments bypass LDS too, streamed from L2 into a register ring half
+  // a step ahead of their use; LDS then carries only the up/gate fragments.
+  static constexpr bool kGO = STCA_ENC_GO && D == 256;
 };
 
 template <int D, int TB, bool LN, typename TO>
@@ -129,15 +157,18 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
                                                              const bf16x8 *__restrict__ packed,
                                                              TO *__restrict__ out, int64_t ldo,
                                                              const float *__restrict__ gamma,
-                                                             const float *__restrict__ beta, float eps) {
+                                                             const float *__restrict__ beta, float eps,
+                                                             int stagger) {
   using S = PairShape<D>;
   constexpr bool kWide = PairLaunch<D, TB>::kWide;
   constexpr int NW = PairLaunch<D, TB>::NW;
   constexpr int kTokens = PairLaunch<D, TB>::kTokens;
+  constexpr bool kGO = PairLaunch<D, TB>::kGO;
+  constexpr bool kNoO = kWide || kGO;  // no down fragments in LDS
   // Direct-to-LDS loads per wave and step: fragments go round-robin over the waves; the barrier
   // wait uses the smallest per-wave count, which waits for at least all loads of older steps.
   constexpr int LUV = (S::FUP + NW - 1) / NW, LO = (S::FDN + NW - 1) / NW;
-  constexpr int kStepLoads = S::FUP / NW + S::FDN / NW;
+  constexpr int kStepLoads = kGO ? S::FD / 2 : S::FUP / NW + S::FDN / NW;
   constexpr int kRing = STCA_ENC_RING, kAhead = STCA_ENC_RING - 1;  // fragment groups in flight
   constexpr uint32_t SLOT = S::FPS * 1024u;                          // bytes of one ring slot
   // Weight ring: slot b holds the up/gate fragments of one step (uvN) and the down fragments of
@@ -145,7 +176,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   // compiler sees reads of one slot as independent of the loads landing in another and does not
   // wait for those loads.
   __shared__ bf16x8 uv0[S::FUP][64], uv1[S::FUP][64], uv2[kWide ? 1 : S::FUP][64];
-  __shared__ bf16x8 o0[kWide ? 1 : S::FDN][64], o1[kWide ? 1 : S::FDN][64], o2[kWide ? 1 : S::FDN][64];
+  __shared__ bf16x8 o0[kNoO ? 1 : S::FDN][64], o1[kNoO ? 1 : S::FDN][64], o2[kNoO ? 1 : S::FDN][64];
   auto uv_slot = [&](int b) -> const STCA_LDS char * {
     return (const STCA_LDS char *)(b == 0 ? &uv0[0][0] : b == 1 ? &uv1[0][0] : &uv2[0][0]);
   };
@@ -154,15 +185,26 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   };
   // Gated activations swapped within a pair: [step parity][wave][32-token block][lane].
   __shared__ bf16x8 hx[2][NW][TB][64];
+  // d <= 256: a tile's rows are staged in LDS, rows 0-63 in ring slot 2 (its up/gate part is
+  // loaded only once the rows have been read) and rows 64-127 in xs.
+  __shared__ bf16x8 xs[kWide ? 1 : S::FUP][64];
 
   // The wave index is uniform: keeping it in a scalar register makes the LDS destinations of the
   // staging loads (M0) scalar arithmetic.
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int role = wave & 1, partner = wave ^ 1;
   const int col = lane & 31, grp = lane >> 5;
-  const int64_t tok0 = (int64_t)blockIdx.x * kTokens + (wave >> 1) * 32 * TB + col;  // block tb: + 32 tb
   const int S_ = n_steps;
 
+  // LayerNorm scale and shift, staged once into LDS (visible after the first barrier) so that the
+  // epilogue does not wait on global loads.
+  __shared__ __attribute__((aligned(16))) float gb[LN ? 2 : 1][LN ? D : 4];
+  if constexpr (LN) {
+    for (int i = threadIdx.x; i < D; i += 64 * NW) {
+      gb[0][i] = gamma[i];
+      gb[1][i] = beta[i];
+    }
+  }
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)n_steps * SLOT);
   auto stage_uv = [&](int t, int b) {
 #pragma unroll
@@ -182,23 +224,106 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
                  (uint32_t)t * SLOT);
     }
   };
+  // The up/gate fragments of the first steps of a tile; at d <= 256 the third goes into slot 2
+  // only after the tile's rows have been read out of it.
+  auto stage_first = [&]() {
+    stage_uv(0, 0);
+    if (S_ > 1) stage_uv(1, 1);
+  };
 
-  // The pair's 32 TB tokens as B operands: lane l holds token tok0 + 32 tb, features
+  // d <= 256: tile rows into LDS with coalesced direct-to-LDS loads.  Row r (2d bytes, d/8
+  // chunks of 16 bytes) occupies positions r d/8 .. r d/8 + d/8 - 1, chunk c at position
+  // r d/8 + (c ^ (r & 7)): eight consecutive rows then put a given chunk in eight different
+  // 128-byte bank windows, so the transposing reads below are free of bank conflicts.  Each load
+  // fills 64 consecutive positions (1 KiB) from whole rows.  Rows past n_rows read as zeros (or
+  // keep stale data): their tokens are independent MFMA columns and are never stored.
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int kXLoads = (kTokens * CPR) / 64;    // 1-KiB loads per tile
+  static_assert(kWide || kXLoads == 2 * S::FUP, "a tile's rows fill ring slot 2 and xs exactly");
+  auto stage_x = [&](int64_t tl) {
+    if constexpr (!kWide) {
+      const int64_t r0 = tl * kTokens;
+      const int64_t rows = n_rows - r0 < kTokens ? n_rows - r0 : kTokens;
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + r0 * ldx, (uint32_t)((rows - 1) * ldx * 2 + 2 * D));
+#pragma unroll
+      for (int j = 0; j < kXLoads / NW; ++j) {
+        const int q = j * NW + wave;
+        const int pos = q * 64 + lane, r = pos / CPR, c = (pos % CPR) ^ (r & 7);
+        STCA_LDS void *dst = q < S::FUP ? (STCA_LDS void *)&uv2[q][0] : (STCA_LDS void *)&xs[q - S::FUP][0];
+        load_lds16(xr, dst, (uint32_t)(r * ldx * 2 + c * 16), 0);
+      }
+    }
+  };
+
+  // The pair's 32 TB tokens of a tile as B operands: lane l holds token tok0 + 32 tb, features
   // 16 ks + 8 (l>>5) + 0..7.
   bf16x8 xb[TB][S::NKS];
+  auto load_x = [&](int64_t tl) {
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    const int64_t tok = tok0 + 32 * tb;
-    const bool valid = tok < n_rows;
-    const bf16 *xrow = X + (valid ? tok : 0) * ldx + 8 * grp;
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t tok = tl * kTokens + (wave >> 1) * 32 * TB + 32 * tb + col;
+      const bool valid = tok < n_rows;
+      const bf16 *xrow = X + (valid ? tok : 0) * ldx + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < S::NKS; ++ks) {
-      if (valid)
-        xb[tb][ks] = *reinterpret_cast<const bf16x8 *>(xrow + 16 * ks);
-      else
-        xb[tb][ks] = bf16x8{};
+      for (int ks = 0; ks < S::NKS; ++ks) {
+        if (valid)
+          xb[tb][ks] = *reinterpret_cast<const bf16x8 *>(xrow + 16 * ks);
+        else
+          xb[tb][ks] = bf16x8{};
+      }
     }
+  };
+
+  // d <= 256: the pair's 32 tokens from the staged rows into the B-operand registers.
+  auto read_x = [&]() {
+    if constexpr (!kWide) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int row = (wave >> 1) * 32 * TB + 32 * tb;  // first row of the block (uniform)
+        const int r = (row & 63) + col;                    // row within its 64-row half
+        const STCA_LDS char *half =
+            row < 64 ? (const STCA_LDS char *)&uv2[0][0] : (const STCA_LDS char *)&xs[0][0];
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks) {
+          const int c = 2 * ks + grp;
+          xb[tb][ks] = *(const STCA_LDS bf16x8 *)(half + (r * CPR + (c ^ (r & 7))) * 16);
+        }
+      }
+    }
+  };
+
+  // Persistent workgroups walk the token tiles tile = blockIdx.x + k gridDim.x.  A tile's rows and
+  // first weight steps are loaded while the previous tile finishes (its last down product,
+  // LayerNorm and stores), so only the first tile waits for them.  Every workgroup does the same
+  // work per tile, so workgroups that start together would stay in lockstep and load and store
+  // in bursts; the first tile therefore starts after a delay that grows with blockIdx.x
+  // (stagger sleep units of 64 cycles for the last workgroup).
+  if (stagger > 0) {
+    const int n = (int)(((int64_t)blockIdx.x * stagger) / (int64_t)gridDim.x);
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
   }
+  const int64_t n_tiles = (n_rows + kTokens - 1) / kTokens;
+  if ((int64_t)blockIdx.x < n_tiles) {
+    if constexpr (kWide)
+      load_x(blockIdx.x);
+    else
+      stage_x(blockIdx.x);
+    stage_first();
+    barrier_vm<0>();
+  }
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  const int64_t tok0 = tile * kTokens + (wave >> 1) * 32 * TB + col;  // block tb: + 32 tb
+  // Issued after the last loads this tile waits for: vector-memory loads complete in order.
+  auto prefetch_next = [&]() {
+    const int64_t nt = tile + gridDim.x;
+    if (nt < n_tiles) {
+      if constexpr (kWide)
+        load_x(nt);
+      else
+        stage_x(nt);
+      stage_first();
+    }
+  };
 
   f32x16 yacc[S::NOBW][TB];
 #pragma unroll
@@ -231,7 +356,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[tb][j] = f32_to_bf16(swiglu_gate(ga[tb][j], ga[tb][j + 8]));
+      for (int j = 0; j < 8; ++j) h[tb][j] = f32_to_bf16(swiglu_gate_scaled(ga[tb][j], ga[tb][j + 8]));
   };
   auto copy_acc = [&](float (&ga)[TB][16]) {
 #pragma unroll
@@ -284,9 +409,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         wo[1][ob] = base[(S::NOB + ob) * 64];
       }
     };
-    stage_uv(0, 0);
-    if (S_ > 1) stage_uv(1, 1);
-    barrier_vm<0>();
+    // The tile's rows and first fragments landed before the barrier that ended the previous tile.
     up_all(0);
     barrier_vm<0>();  // slot 0 is restaged in step 0
     for (int t = 0; t < S_; ++t) {
@@ -309,6 +432,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     swap_in(S_ - 1);
     bf16x8 wo[2][S::NOBW];
     load_wo(S_ - 1, wo);
+    prefetch_next();
     down_regs(wo);
   } else {
     // Step t: the matrix cores run the up/gate products of step t+1 and the down product of step
@@ -316,11 +440,32 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     // up/gate fragments of step t live in ring slot t % 3, the down fragments of step t in slot
     // t % 3 as well; step t stages up/gate of t+3 (into the slot step t-1 finished reading) and
     // down of t+1, so every load has a full step to land before the barrier that precedes its use.
-    stage_uv(0, 0);
-    if (S_ > 1) stage_uv(1, 1);
+    // With kGO the down fragments come from L2 instead: fragment di of step t (di < NOBW: the
+    // wave's own output blocks built from its own features; otherwise from the partner's) is
+    // loaded into a register ring of FD/2 slots, FD/2 down products ahead of its use.
+    constexpr int WR = S::FD / 2;
+    auto wo_frag = [&](int t, int di) -> bf16x8 {
+      const int f = S::FUP + (di < S::NOBW ? 0 : S::NOB) + S::NOBW * role + di % S::NOBW;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)lo, (int)((uint32_t)(t * S::FPS + f) * 1024u), 0);
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    auto down_go = [&](int t) {
+      bf16x8 wo[S::FD];
+#pragma unroll
+      for (int di = 0; di < S::FD; ++di) wo[di] = wo_frag(t, di);
+#pragma unroll
+      for (int di = 0; di < S::FD; ++di)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+          yacc[di % S::NOBW][tb] = mfma32x32x16(wo[di], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[di % S::NOBW][tb]);
+    };
+    bf16x8 wring[WR];
+
+    // The tile's rows and first fragments landed before the barrier that ended the previous tile.
+    read_x();
+    barrier_lds();  // every wave has read its rows out of slot 2
     if (S_ > 2) stage_uv(2, 2);
-    stage_o(0, 0);
-    barrier_vm<0>();
+    if constexpr (!kGO) stage_o(0, 0);
     up_all(0);
     barrier_vm<0>();  // slot 0's up/gate part is restaged in step 0
 
@@ -328,31 +473,44 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     auto general = [&](int t) {
       const bool has_up = t + 1 < S_, has_down = t >= 1;
       if (t + 3 < S_) stage_uv(t + 3, t % 3);
-      if (t + 1 < S_) stage_o(t + 1, (t + 1) % 3);
+      if constexpr (!kGO)
+        if (t + 1 < S_) stage_o(t + 1, (t + 1) % 3);
       if (has_down) swap_in(t - 1);
       float ga[TB][16];
       copy_acc(ga);
       if (has_up) up_all((t + 1) % 3);
-      if (has_down) down_all((t + 2) % 3);
+      if (has_down) {
+        if constexpr (kGO)
+          down_go(t - 1);
+        else
+          down_all((t + 2) % 3);
+      }
       bf16x8 h[TB];
       gate_all(ga, h);
       swap_out(t, h);
   #pragma unroll
       for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
       barrier_vm<0>();
+      // The next step, if steady, finds its first WR down fragments in the ring.
+      if constexpr (kGO)
+        if (t + 1 < S_)
+  #pragma unroll
+          for (int j = 0; j < WR; ++j) wring[j] = wo_frag(t, j);
     };
 
-    // Steady-state step (1 <= t, t + 3 < n_steps) with t % 3 == T3 known at compile time.  The
+    // Steady-state step (1 <= t, t + 1 < n_steps) with t % 3 == T3 known at compile time.  The
     // instruction order is pinned (sched_barrier): fragment reads run kAhead groups ahead through a
     // register ring, and one gate element is computed every third MFMA.
     auto steady = [&](int t, auto T3c) {
       constexpr int T3 = decltype(T3c)::value;
       constexpr int BU = (T3 + 1) % 3, BD = (T3 + 2) % 3;
-      stage_uv(t + 3, T3);
-      stage_o(t + 1, BU);
+      const bool stage = t + 3 < S_;  // the last steps have nothing left to stage
+      if (stage) stage_uv(t + 3, T3);
+      if constexpr (!kGO) stage_o(t + 1, BU);
       swap_in(t - 1);
       auto frag = [&](int g) -> bf16x8 {
         if (pair_is_down(g, S::FD)) {
+          if constexpr (kGO) return bf16x8{};  // not used: down fragments come from wring
           const int di = g / 3;
           return frag_at(o_slot(BD), (di < S::NOBW ? own_off : par_off) + (di % S::NOBW) * 1024u);
         }
@@ -362,30 +520,39 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       copy_acc(ga);
       bf16x8 ring[kRing];
   #pragma unroll
-      for (int p = 0; p < kAhead; ++p) ring[p] = frag(p);
+      for (int p = 0; p < kAhead; ++p)
+        if (!(kGO && pair_is_down(p, S::FD))) ring[p] = frag(p);
       float hv[8 * TB];
       __builtin_amdgcn_sched_barrier(0);
       constexpr int kMM = TB * S::NG;
   #pragma unroll
       for (int k = 0; k < kMM; ++k) {
         const int g = k / TB, tb = k % TB;
-        if (tb == 0 && g + kAhead < S::NG) ring[(g + kAhead) % kRing] = frag(g + kAhead);
+        if (tb == 0 && g + kAhead < S::NG && !(kGO && pair_is_down(g + kAhead, S::FD)))
+          ring[(g + kAhead) % kRing] = frag(g + kAhead);
         if (pair_is_down(g, S::FD)) {
           const int di = g / 3, ob = di % S::NOBW;
-          yacc[ob][tb] = mfma32x32x16(ring[g % kRing], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[ob][tb]);
+          if constexpr (kGO) {
+            yacc[ob][tb] = mfma32x32x16(wring[di % WR], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[ob][tb]);
+            // Refill the slot: the second half of this step's fragments, then the first half of
+            // the next step's.
+            if (tb == TB - 1) wring[di % WR] = di < WR ? wo_frag(t - 1, di + WR) : wo_frag(t, di - WR);
+          } else {
+            yacc[ob][tb] = mfma32x32x16(ring[g % kRing], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[ob][tb]);
+          }
         } else {
           const int ui = pair_up_idx(g, S::FD);
           acc[tb] = mfma32x32x16(ring[g % kRing], xb[tb][ui], ui == 0 ? f32x16{} : acc[tb]);
         }
         if (k % 3 == 0 && k / 3 < 8 * TB) {
           const int e = k / 3;
-          hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+          hv[e] = swiglu_gate_scaled(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
           asm volatile("" : "+v"(hv[e]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
   #pragma unroll
-      for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+      for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate_scaled(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
       bf16x8 h[TB];
   #pragma unroll
       for (int e = 0; e < 8 * TB; ++e) h[e >> 3][e & 7] = f32_to_bf16(hv[e]);
@@ -393,8 +560,13 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   #pragma unroll
       for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
       // Data read in step t+1 (up/gate of t+2, down of t) was staged in step t-1 or before; this
-      // step's loads may stay in flight.
-      barrier_vm<kStepLoads>();
+      // step's loads may stay in flight.  With kGO the loads still in flight are the four down
+      // fragments of the next step, issued after everything else; otherwise a step that staged
+      // nothing drains all loads.
+      if (kGO || stage)
+        barrier_vm<kStepLoads>();
+      else
+        barrier_vm<0>();
     };
 
     using I0 = std::integral_constant<int, 0>;
@@ -402,7 +574,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     using I2 = std::integral_constant<int, 2>;
     general(0);
     int t = 1;
-    for (; t + 5 < S_; t += 3) {
+    for (; t + 3 < S_; t += 3) {
       steady(t, I1{});
       steady(t + 1, I2{});
       steady(t + 2, I0{});
@@ -410,7 +582,20 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     for (; t < S_; ++t) general(t);
     // The down product of the last step remains.
     swap_in(S_ - 1);
-    down_all((S_ - 1) % 3);
+    if constexpr (kGO) {
+      bf16x8 wo[S::FD];
+#pragma unroll
+      for (int di = 0; di < S::FD; ++di) wo[di] = wo_frag(S_ - 1, di);
+      prefetch_next();
+#pragma unroll
+      for (int di = 0; di < S::FD; ++di)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+          yacc[di % S::NOBW][tb] = mfma32x32x16(wo[di], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[di % S::NOBW][tb]);
+    } else {
+      prefetch_next();
+      down_all((S_ - 1) % 3);
+    }
   }
 
   // Epilogue.  Lane l holds tokens tok0 + 32 tb; register i of block ob is output feature
@@ -420,8 +605,10 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) mean[tb] = 0.f, inv[tb] = 1.f;
   if constexpr (LN) {
-    // Ring slot S_ % 3 is no longer read: it carries the per-wave partial sums.
-    STCA_LDS float *red = (STCA_LDS float *)uv_slot(kWide ? 0 : S_ % 3);  // [stat][wave][tb][col]
+    // Swap buffer parity S_ & 1 was last read in step S_ - 1: it carries the per-wave partial
+    // sums.  The ring is being restaged for the next tile, and the prefetch loads may stay in
+    // flight across these barriers.
+    STCA_LDS float *red = (STCA_LDS float *)&hx[S_ & 1][0][0][0];  // [stat][wave][tb][col]
     constexpr int kStat = NW * TB * 32;
     float part[TB];
 #pragma unroll
@@ -434,7 +621,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       part[tb] = half_sum(sum);
       if (grp == 0) red[(wave * TB + tb) * 32 + col] = part[tb];
     }
-    barrier_vm<0>();
+    barrier_lds();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       mean[tb] = (part[tb] + red[(partner * TB + tb) * 32 + col]) * (1.0f / D);
@@ -449,7 +636,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       part[tb] = half_sum(sq);
       if (grp == 0) red[kStat + (wave * TB + tb) * 32 + col] = part[tb];
     }
-    barrier_vm<0>();
+    barrier_lds();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const float var = (part[tb] + red[kStat + (partner * TB + tb) * 32 + col]) * (1.0f / D);
@@ -468,8 +655,8 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         const int f0 = 32 * (S::NOBW * role + ob) + 8 * q + 4 * grp;
         float v[4];
         if constexpr (LN) {
-          const f32x4 gm = *reinterpret_cast<const f32x4 *>(gamma + f0);
-          const f32x4 bt = *reinterpret_cast<const f32x4 *>(beta + f0);
+          const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gb[0][f0]);
+          const f32x4 bt = *reinterpret_cast<const f32x4 *>(&gb[1][f0]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[j] = (yacc[ob][tb][4 * q + j] - mean[tb]) * inv[tb] * gm[j] + bt[j];
         } else {
@@ -487,18 +674,38 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       }
     }
   }
+  barrier_vm<0>();  // the next tile restages the ring and reuses the swap and statistics buffers
+  }
 }
 
 template <int D, bool LN, typename TO>
 static hipError_t launch_encode(hipStream_t s, int r, int64_t n_rows, const void *X, int64_t ldx,
                                 const void *packed, void *out, int64_t ldo, const float *gamma,
                                 const float *beta, float eps) {
-  constexpr int TB = D > 256 ? 1 : STCA_ENC_TB;
+  constexpr int TB = D > 256 ? 1 : D == 256 ? STCA_ENC_TB : STCA_ENC_TB_SMALL;
   using PL = PairLaunch<D, TB>;
-  const int64_t blocks = (n_rows + PL::kTokens - 1) / PL::kTokens;
-  hipLaunchKernelGGL((encode_pair_kernel<D, TB, LN, TO>), dim3((unsigned)blocks), dim3(64 * PL::NW), 0, s,
-                     n_rows, r * D / 32, (const bf16 *)X, ldx, (const bf16x8 *)packed, (TO *)out, ldo, gamma,
-                     beta, eps);
+  auto kern = encode_pair_kernel<D, TB, LN, TO>;
+  // Persistent grid: as many workgroups as fit on the device at once, each walking tiles.
+  static int resident[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (resident[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * PL::NW, 0);
+    if (e != hipSuccess) return e;
+    resident[dev] = std::max(1, cus * per_cu);
+  }
+  const int64_t tiles = (n_rows + PL::kTokens - 1) / PL::kTokens;
+  const int64_t blocks = std::min<int64_t>(tiles, resident[dev]);
+  // Stagger the first tiles over about half a tile's time only when every workgroup has many
+  // tiles to do, so that the start-up delay is amortised.
+  const int stagger = tiles >= 8 * blocks ? STCA_ENC_STAGGER * (r * D / 32) : 0;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PL::NW), 0, s, n_rows, r * D / 32, (const bf16 *)X, ldx,
+                     (const bf16x8 *)packed, (TO *)out, ldo, gamma, beta, eps, stagger);
   return hipGetLastError();
 }
 
