@@ -28,6 +28,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (bf16)f);
 }
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+__device__ __forceinline__ bf16x2 bf16x2_of(float a, float b) { return bf16x2{(bf16)a, (bf16)b}; }
+
 template <typename T> struct elem;
 template <> struct elem<float> {
   __device__ __forceinline__ static float load(const float *p) { return *p; }

@@ -643,33 +643,56 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       inv[tb] = 1.0f / sqrtf(var + eps);
     }
   }
+  // Output: lane l holds features 32 blk + 8 q + 4 (l>>5) + 0..3 of its token (blk = NOBW role + ob).
+  auto normalised = [&](int ob, int tb, int q, float (&v)[4]) {
+    const int f0 = 32 * (S::NOBW * role + ob) + 8 * q + 4 * grp;
+    if constexpr (LN) {
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gb[0][f0]);
+      const f32x4 bt = *reinterpret_cast<const f32x4 *>(&gb[1][f0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (yacc[ob][tb][4 * q + j] - mean[tb]) * inv[tb] * gm[j] + bt[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = yacc[ob][tb][4 * q + j];
+    }
+  };
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int64_t tok = tok0 + 32 * tb;
-    if (tok >= n_rows) continue;
-    TO *orow = out + tok * ldo;
+    const bool valid = tok < n_rows;
+    TO *orow = out + (valid ? tok : 0) * ldo;
 #pragma unroll
     for (int ob = 0; ob < S::NOBW; ++ob) {
+      if constexpr (sizeof(TO) == 2) {
+        // Lanes l and l + 32 hold the same token: one lane swap per dword gives lane l features
+        // 16 qp + 0..7 and lane l + 32 features 16 qp + 8..15, so each store writes 32 contiguous
+        // bytes per row (16 per lane) instead of 16.
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f0 = 32 * (S::NOBW * role + ob) + 8 * q + 4 * grp;
-        float v[4];
-        if constexpr (LN) {
-          const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gb[0][f0]);
-          const f32x4 bt = *reinterpret_cast<const f32x4 *>(&gb[1][f0]);
+        for (int qp = 0; qp < 2; ++qp) {
+          uint32_t w[2][2];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (yacc[ob][tb][4 * q + j] - mean[tb]) * inv[tb] * gm[j] + bt[j];
-        } else {
+          for (int qq = 0; qq < 2; ++qq) {
+            float v[4];
+            normalised(ob, tb, 2 * qp + qq, v);
+            w[qq][0] = __builtin_bit_cast(uint32_t, bf16x2_of(v[0], v[1]));
+            w[qq][1] = __builtin_bit_cast(uint32_t, bf16x2_of(v[2], v[3]));
+          }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = yacc[ob][tb][4 * q + j];
+          for (int dw = 0; dw < 2; ++dw) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(w[0][dw], w[1][dw], false, false);
+            w[0][dw] = sw[0];
+            w[1][dw] = sw[1];
+          }
+          const int f = 32 * (S::NOBW * role + ob) + 16 * qp + 8 * grp;
+          if (valid) *reinterpret_cast<u32x4 *>(orow + f) = u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
         }
-        if constexpr (sizeof(TO) == 2) {
-          bf16x4 pk;
+      } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pk[j] = f32_to_bf16(v[j]);
-          *reinterpret_cast<bf16x4 *>(orow + f0) = pk;
-        } else {
-          *reinterpret_cast<f32x4 *>(orow + f0) = f32x4{v[0], v[1], v[2], v[3]};
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+          normalised(ob, tb, q, v);
+          const int f0 = 32 * (S::NOBW * role + ob) + 8 * q + 4 * grp;
+          if (valid) *reinterpret_cast<f32x4 *>(orow + f0) = f32x4{v[0], v[1], v[2], v[3]};
         }
       }
     }
