@@ -610,7 +610,11 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     // flight across these barriers.
     STCA_LDS float *red = (STCA_LDS float *)&hx[S_ & 1][0][0][0];  // [stat][wave][tb][col]
     constexpr int kStat = NW * TB * 32;
-    float part[TB];
+    // Each wave holds half of a token's d outputs.  It computes the mean and the sum of squared
+    // deviations of its half (two passes over registers), the pair exchanges them once, and the
+    // halves combine exactly: mean = (m_a + m_b) / 2, M2 = M2_a + M2_b + (m_a - m_b)^2 d / 4.  Both
+    // waves evaluate the same symmetric expressions, so they agree bit for bit.
+    float lm[TB], lq[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       float sum = 0.f;
@@ -618,28 +622,29 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       for (int ob = 0; ob < S::NOBW; ++ob)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum += yacc[ob][tb][i];
-      part[tb] = half_sum(sum);
-      if (grp == 0) red[(wave * TB + tb) * 32 + col] = part[tb];
-    }
-    barrier_lds();
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      mean[tb] = (part[tb] + red[(partner * TB + tb) * 32 + col]) * (1.0f / D);
+      lm[tb] = half_sum(sum) * (2.0f / D);
       float sq = 0.f;
 #pragma unroll
       for (int ob = 0; ob < S::NOBW; ++ob)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float dv = yacc[ob][tb][i] - mean[tb];
+          const float dv = yacc[ob][tb][i] - lm[tb];
           sq += dv * dv;
         }
-      part[tb] = half_sum(sq);
-      if (grp == 0) red[kStat + (wave * TB + tb) * 32 + col] = part[tb];
+      lq[tb] = half_sum(sq);
+      if (grp == 0) {
+        red[(wave * TB + tb) * 32 + col] = lm[tb];
+        red[kStat + (wave * TB + tb) * 32 + col] = lq[tb];
+      }
     }
     barrier_lds();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const float var = (part[tb] + red[kStat + (partner * TB + tb) * 32 + col]) * (1.0f / D);
+      const float pm = red[(partner * TB + tb) * 32 + col];
+      const float pq = red[kStat + (partner * TB + tb) * 32 + col];
+      mean[tb] = (lm[tb] + pm) * 0.5f;
+      const float dm = lm[tb] - pm;
+      const float var = (lq[tb] + pq + dm * dm * (0.25f * D)) * (1.0f / D);
       inv[tb] = 1.0f / sqrtf(var + eps);
     }
   }
