@@ -371,7 +371,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     }
   };
   // One step on tile k.  Returns true when a row maximum outgrew the slack: the caller then
-  // rescales and finishes tile k.
+  // rescales and finishes tile k.  The score MFMAs of tile k+1 go one per group, and each group
+  // also turns one score of tile k into its probability (exp2, bf16, running sum) and folds it
+  // into the tile's maximum, so that this vector work runs in the matrix cores' shadow (the
+  // order is pinned: left alone, the compiler issues all MFMAs first).  The probabilities are
+  // computed against the running maximum before the tile's own maximum is known; when that
+  // maximum outgrew the slack they are discarded and the caller recomputes them after the
+  // rescale.  The PV product of tile k follows.
+  constexpr int kRingA = 4, kAheadA = 3;
+  constexpr int NGA = NKS > 16 ? NKS : 16;
   auto step = [&](int k, f32x16 &sc, float &mx) -> bool {
     sync();  // tile k+1 is in LDS; tile k-1's slot is free
     if (k + 2 < ntiles) {
@@ -381,10 +389,57 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     if (!wave_active) return false;
     const bool has_next = k + 1 < ntiles;
     sc = sa + sb;
-    if (has_next) scores(tile_off(k + 1), sa, sb);  // in flight during the softmax below
-    mx = row_max(sc, tile_rem(k));
+    const int rem = tile_rem(k);
+    if (rem < 32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tau = 8 * (i >> 2) + 4 * gl + (i & 3);
+        if (tau >= rem) sc[i] = -INFINITY;
+      }
+    }
+    bf16x8 pb[2];
+    float psum = 0.f;
+    mx = -INFINITY;
+    auto element = [&](int i) {
+      const float p = fast_exp2(sc[i] - m_run);
+      pb[i >> 3][i & 7] = f32_to_bf16(p);
+      psum += p;
+      mx = fmaxf(mx, sc[i]);
+    };
+    if (has_next) {
+      uint32_t rx = rx16, rb = tile_off(k + 1) + row_off;
+      asm volatile("" : "+v"(rx), "+v"(rb));
+      auto frag = [&](int ks) { return *(const STCA_LDS bf16x8 *)(lds + rb + (((uint32_t)(32 * ks)) ^ rx)); };
+      bf16x8 fr[kRingA];
+#pragma unroll
+      for (int q = 0; q < kAheadA; ++q) fr[q] = frag(q);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NGA; ++g) {
+        if (g < NKS) {
+          if (g + kAheadA < NKS) fr[(g + kAheadA) % kRingA] = frag(g + kAheadA);
+          if (g & 1)
+            sb = mfma32x32x16(fr[g % kRingA], ub[g], g == 1 ? f32x16{} : sb);
+          else
+            sa = mfma32x32x16(fr[g % kRingA], ub[g], g == 0 ? f32x16{} : sa);
+        }
+        if (g < 16) element(g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) element(i);
+    }
     if (wave_any(mx > m_run + kLazy)) return true;
-    tail(k, sc);
+    s_run += psum;
+    if constexpr (FH == 1) {
+      pv(tile_off(k), pb, H0{});
+    } else {
+      if (fh == 0)
+        pv(tile_off(k), pb, H0{});
+      else
+        pv(tile_off(k), pb, H1{});
+    }
     return false;
   };
   int k = 0;
