@@ -13,6 +13,8 @@ arithmetic).
   same equations, for tiny sizes only; the tests pin ``oracle.stca`` to it.
 * ``oracle.sl``    -- stochastic-length training batches (eqs. (15)-(17), temporal
   suffix selection, two-step batch load balancing) in integer numpy.
+* ``oracle.litm``  -- local same-ID token merging of a history (TM20K's LITM): grouping
+  in plain Python, merged rows as float64 sums.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (library routines, closed forms, invariants the pages state, brute force).
@@ -22,6 +24,6 @@ LayerNorm in the query update) are fixed readings, shared with the HIP path
 by definition; no page prints a number that could pin them ("parity unpinned"
 for those readings only).
 """
-from . import brute, sl, stca
+from . import brute, litm, sl, stca
 
-__all__ = ["stca", "brute", "sl"]
+__all__ = ["stca", "brute", "sl", "litm"]

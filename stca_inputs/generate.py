@@ -100,13 +100,22 @@ def _duplicate_sources(rng: np.random.Generator, L: int, p: float, window: int) 
         src = nxt
 
 
-def user_history(cfg: Config, u: int, L_u: int) -> np.ndarray:
-    """History embeddings X of user ``u`` (L_u x d, float32, bf16-valued if bf16)."""
+def user_history_ids(cfg: Config, u: int, L_u: int) -> tuple[np.ndarray, np.ndarray]:
+    """History embeddings X of user ``u`` (L_u x d, float32, bf16-valued if bf16) and the item
+    ID of every position: a repeat carries the ID of the token it copies (its resolved source
+    position), any other token a fresh one (its own position).  IDs are user-local."""
     rng = _rng(cfg, _HISTORY, int(u))
     X = rng.standard_normal((int(L_u), cfg.d), dtype=np.float32)
+    src = np.arange(int(L_u), dtype=np.int64)
     if cfg.dup_prob > 0.0:
-        X = X[_duplicate_sources(rng, int(L_u), cfg.dup_prob, cfg.dup_window)]
-    return _store(cfg, X)
+        src = _duplicate_sources(rng, int(L_u), cfg.dup_prob, cfg.dup_window)
+        X = X[src]
+    return _store(cfg, X), src
+
+
+def user_history(cfg: Config, u: int, L_u: int) -> np.ndarray:
+    """History embeddings X of user ``u`` (L_u x d, float32, bf16-valued if bf16)."""
+    return user_history_ids(cfg, u, L_u)[0]
 
 
 def targets(cfg: Config, T: int) -> np.ndarray:
@@ -247,6 +256,7 @@ class Inputs:
     tgt_off: np.ndarray
     X: np.ndarray
     xt: np.ndarray
+    item_id: np.ndarray | None = None   # int64 per history row (make_inputs(with_ids=True))
 
     @property
     def n_users(self) -> int:
@@ -271,11 +281,13 @@ class Inputs:
         return self.as_f32(self.xt[self.tgt_off[k]:self.tgt_off[k + 1]])
 
 
-def make_inputs(cfg: Config, users=None, threads: int | None = None) -> Inputs:
+def make_inputs(cfg: Config, users=None, threads: int | None = None, with_ids: bool = False) -> Inputs:
     """Histories and targets for ``users`` (default: every user of the workload).
 
     A user's draws do not depend on which other users are generated, so a
-    sample of users reproduces exactly the rows of the full batch.
+    sample of users reproduces exactly the rows of the full batch.  With ``with_ids`` the
+    result also carries ``item_id`` (int64 per history row, globally unique per source token:
+    hist_off[k] + the user-local ID of ``user_history_ids``).
     """
     L_all, m_all = batch_layout(cfg)
     users = np.arange(cfg.n_users) if users is None else np.asarray(sorted(set(int(u) for u in users)))
@@ -286,10 +298,13 @@ def make_inputs(cfg: Config, users=None, threads: int | None = None) -> Inputs:
 
     bf16 = cfg.dtype == "bf16"
     X = np.empty((int(hoff[-1]), cfg.d), dtype=np.uint16 if bf16 else np.float32)
+    ids = np.empty(int(hoff[-1]), dtype=np.int64) if with_ids else None
 
     def fill(k):
-        Xu = user_history(cfg, int(users[k]), int(L[k]))
+        Xu, src = user_history_ids(cfg, int(users[k]), int(L[k]))
         X[hoff[k]:hoff[k + 1]] = bf16_bits(Xu) if bf16 else Xu
+        if ids is not None:
+            ids[hoff[k]:hoff[k + 1]] = hoff[k] + src
 
     if threads is None:
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -306,4 +321,4 @@ def make_inputs(cfg: Config, users=None, threads: int | None = None) -> Inputs:
         np.zeros(0, np.int64)
     xt = all_xt[rows.astype(np.int64)]
     xt = bf16_bits(xt) if bf16 else xt
-    return Inputs(cfg, users, L, m, hoff, toff, X, xt)
+    return Inputs(cfg, users, L, m, hoff, toff, X, xt, ids)

@@ -59,3 +59,20 @@ def test_weight_shapes_and_scale():
     assert abs(W.WC[2].std() * np.sqrt(3 * d) - 1.0) < 0.02
     assert W.qWu[1] is W.Wu[1]
     assert np.array_equal(SI.bf16_round(W.WQ[0]), W.WQ[0])
+
+
+def test_item_ids_follow_the_repeats():
+    """Rows sharing an item ID are bitwise copies; asking for IDs changes no draw."""
+    cfg = SI.scaled(SI.get_config("dense10k"), n_users=3)
+    a = SI.make_inputs(cfg)
+    b = SI.make_inputs(cfg, with_ids=True)
+    assert a.item_id is None and np.array_equal(a.X, b.X) and np.array_equal(a.xt, b.xt)
+    ids = b.item_id
+    assert ids.shape == (b.total_L,)
+    first = {}
+    for p, i in enumerate(ids.tolist()):
+        first.setdefault(i, p)
+        assert np.array_equal(b.X[p], b.X[first[i]])
+    assert 0.05 < 1 - len(first) / len(ids) < 0.15        # ~10% repeats in this workload
+    u = SI.make_inputs(SI.get_config("uniform"), users=[0, 1], with_ids=True)
+    assert len(set(u.item_id.tolist())) == u.total_L       # no repeats: all IDs distinct
