@@ -152,6 +152,79 @@ def bench_sl(a, cfg, dev):
     }))
 
 
+def bench_litm(a, cfg, dev):
+    """Local same-ID token merging of the workload's histories (its repeats carry shared item IDs):
+    the host plan, the device merge (timed against HBM), then the forward on the merged batch."""
+    from types import SimpleNamespace
+
+    import numpy as np
+    import torch
+
+    import stca_inputs as SI
+    from target_cross_attention_amd import binding as B
+
+    T_gap = 3
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg, with_ids=True)
+    t = time.perf_counter()
+    mo, go, mem = B.litm_plan(inp.hist_off, inp.item_id, T_gap)
+    plan_ms = (time.perf_counter() - t) * 1e3
+    n_groups = len(go) - 1
+    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk)
+    Xf = B.to_device(inp.X, cfg.dtype, dev)
+    del inp.X
+    god, memd = torch.from_numpy(go).to(dev), torch.from_numpy(mem).to(dev)
+    Xm = torch.empty((n_groups, cfg.d), dtype=Xf.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    B.litm_merge(dims, god, memd, Xf, Xm, stream=stream)
+    n_rep = max(a.steps, 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_rep):
+        B.litm_merge(dims, god, memd, Xf, Xm, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    merge_ms = e0.elapsed_time(e1) / n_rep
+    del Xf
+    row = cfg.d * (2 if cfg.dtype == "bf16" else 4)
+    # every source row read once, every merged row written once, members and group offsets read
+    merge_bytes = float(inp.total_L * row + n_groups * row + inp.total_L * 8 + (n_groups + 1) * 8)
+
+    hist_off = torch.from_numpy(mo).to(dev)
+    tgt_off = torch.from_numpy(inp.tgt_off.astype(np.int64)).to(dev)
+    T = int(inp.tgt_off[-1])
+    Lm = np.diff(mo)
+    batch = SimpleNamespace(X=Xm, xt=B.to_device(inp.xt, cfg.dtype, dev), total_T=T,
+                            c=B.batch_struct(inp.n_users, hist_off, tgt_off, n_groups, T, int(Lm.max()),
+                                             int(inp.m.max())))
+    dw = B.DeviceWeights(W, cfg.dtype, dev)
+    ws = B.workspace(B.forward_workspace_size(dims, batch.c), dev)
+    Z = torch.empty((T, cfg.M, cfg.d), dtype=torch.float32, device=dev)
+    for _ in range(a.warmup):
+        B.stca_forward(dims, dw, batch, Z=Z, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        B.stca_forward(dims, dw, batch, Z=Z, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert np.isfinite(Z.sum().item()), "non-finite output"
+    print(json.dumps({
+        "metric": "STCA fwd history-tokens/s after local same-ID token merging (tokens before merging)",
+        "value": inp.total_L * a.steps / dt, "unit": "history-tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": dt * 1e3 / a.steps, "higher_is_better": True,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"LITM (T = {T_gap}) on {cfg.description}", "users": inp.n_users,
+                   "tokens": inp.total_L, "merged_tokens": n_groups,
+                   "merged_fraction": 1.0 - n_groups / inp.total_L},
+        "merged_tokens_per_s": n_groups * a.steps / dt,
+        "litm_plan_host_ms": plan_ms,
+        "litm_merge": {"bound": "hbm", "avg_ms": merge_ms, "achieved": merge_bytes / merge_ms / 1e6,
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": merge_bytes / merge_ms / 1e6 / PEAK_HBM_GBS,
+                       "algorithmic_bytes_per_launch": merge_bytes},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +237,9 @@ def main():
     ap.add_argument("--sl", action="store_true",
                     help="time a stochastic-length batch built from the workload's histories instead "
                          "(L_avg 2000, L_max = L_infer = 10000, alpha 0.02)")
+    ap.add_argument("--litm", action="store_true",
+                    help="merge same-ID tokens at most 3 positions apart first (host plan, device merge), then "
+                         "time the forward on the merged batch")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of STCA, run K device copies of 2 GiB (counter calibration)")
     a = ap.parse_args()
@@ -196,6 +272,8 @@ def main():
         cfg = SI.scaled(cfg, n_users=a.users)
     if a.sl:
         return bench_sl(a, cfg, dev)
+    if a.litm:
+        return bench_litm(a, cfg, dev)
     t = time.perf_counter()
     W = SI.make_weights(cfg)
     inp = SI.make_inputs(cfg)

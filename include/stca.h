@@ -181,6 +181,36 @@ STCA_API int stca_sl_plan(const stca_sl_params *p, int32_t n_users, const int64_
 STCA_API int stca_sl_pack(const stca_dims *dims, int32_t n_users, const int64_t *full_off, const int64_t *hist_off,
                           int64_t total, int64_t max_len, const void *X_full, void *X_packed, void *stream);
 
+/* ---- local same-ID token merging (LITM) -----------------------------------------------------
+ * "TM20K：老师读全文，学生读缩写" (notes page, section 4.2.1; the threshold T of section 5.4, the
+ * host/device split of section 4.1): tokens of a history that carry the same key (item) ID and
+ * sit at most T positions apart are summed into one token, a local merge rather than a
+ * deduplication of the whole sequence.  Reading of the page where it is silent: positions are
+ * scanned in order and token p joins the group of the latest earlier token of its user with the
+ * same ID when that token is at most T positions back, otherwise it opens a group; a group is
+ * placed at its first token, so merged histories keep the order of first occurrences; tokens of
+ * different users never merge. */
+
+/* Host only.  Groups of a batch of n_users histories.
+ *   hist_off   [host]: n_users + 1 nondecreasing offsets, hist_off[0] = 0 (total = hist_off[n_users]).
+ *   item_id    [host]: total item IDs, one per history row.
+ *   T: largest position gap that still merges (>= 0; 0 merges nothing).
+ *   merged_off [host, out]: n_users + 1 offsets of the merged histories (in groups).
+ *   group_off  [host, out]: n_groups + 1 offsets into members (room for total + 1 entries).
+ *   members    [host, out]: the total source rows, grouped, in position order within a group.
+ *   n_groups   [host, out]: number of groups (merged rows).
+ * Returns STCA_E_ARG on NULL pointers, T < 0, n_users < 0 or offsets that are not as stated. */
+STCA_API int stca_litm_plan(int32_t n_users, const int64_t *hist_off, const int64_t *item_id, int32_t T,
+                            int64_t *merged_off, int64_t *group_off, int64_t *members, int64_t *n_groups);
+
+/* Device: X_merged[g] = sum of the rows X[members[j]], group_off[g] <= j < group_off[g+1], for the
+ * n_groups groups of a plan (group_off, members: device copies of the plan's arrays).  X is
+ * n_rows x d and X_merged n_groups x d, both dims->dtype; sums run in fp32 in member order and
+ * are rounded once to the storage type.  Member indices outside [0, n_rows) are skipped.
+ * 16-byte aligned rows; n_groups = 0 is a no-op. */
+STCA_API int stca_litm_merge(const stca_dims *dims, int64_t n_rows, int64_t n_groups, const int64_t *group_off,
+                             const int64_t *members, const void *X, void *X_merged, void *stream);
+
 /* ---- per-kernel timing (HIP events on the call's stream) ---------------------------------- */
 typedef struct stca_profiler stca_profiler; /* opaque, host-side; not thread-safe */
 

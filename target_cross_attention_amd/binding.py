@@ -23,7 +23,7 @@ N_PHASES = 7
 EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
     "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict",
-    "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_litm_plan", "stca_litm_merge", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
 ]
@@ -85,6 +85,8 @@ def _load() -> ctypes.CDLL:
         "stca_sl_beta": [P, ctypes.c_double, POINTER(ctypes.c_double)],
         "stca_sl_plan": [P, c_int32, P, P, P, P, P],
         "stca_sl_pack": [P, c_int32, P, P, c_int64, c_int64, P, P, P],
+        "stca_litm_plan": [c_int32, P, P, c_int32, P, P, P, POINTER(c_int64)],
+        "stca_litm_merge": [P, c_int64, c_int64, P, P, P, P, P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -352,6 +354,34 @@ def sl_pack(dims: Dims, full_off, hist_off, total: int, max_len: int, X_full, X_
     _check(LIB.stca_sl_pack(_ref(dims), n_users, _ptr(full_off), _ptr(hist_off), total, max_len, _ptr(X_full),
                             _ptr(X_packed), _stream(stream)), "stca_sl_pack")
     return X_packed
+
+
+def litm_plan(hist_off, item_id, T: int):
+    """Host-side LITM grouping: (merged_off, group_off, members) as int64 numpy arrays."""
+    hist_off = np.ascontiguousarray(hist_off, np.int64)
+    item_id = np.ascontiguousarray(item_id, np.int64)
+    n = len(hist_off) - 1
+    total = int(hist_off[-1])
+    merged_off = np.zeros(n + 1, np.int64)
+    group_off = np.zeros(total + 1, np.int64)
+    members = np.zeros(max(total, 1), np.int64)
+    ng = c_int64(0)
+    vp = lambda a: a.ctypes.data_as(c_void_p) if a.size else None  # noqa: E731
+    _check(LIB.stca_litm_plan(n, hist_off.ctypes.data_as(c_void_p), vp(item_id), int(T),
+                              merged_off.ctypes.data_as(c_void_p), group_off.ctypes.data_as(c_void_p),
+                              members.ctypes.data_as(c_void_p), ctypes.byref(ng)), "stca_litm_plan")
+    return merged_off, group_off[:ng.value + 1].copy(), members[:total].copy()
+
+
+def litm_merge(dims: Dims, group_off, members, X, X_merged=None, stream=None):
+    """Device merge of a plan's groups (group_off, members: device int64 tensors)."""
+    import torch
+    n_groups = int(group_off.numel()) - 1
+    if X_merged is None:
+        X_merged = torch.empty((n_groups, dims.d), dtype=X.dtype, device=X.device)
+    _check(LIB.stca_litm_merge(_ref(dims), int(X.shape[0]), n_groups, _ptr(group_off), _ptr(members), _ptr(X),
+                               _ptr(X_merged), _stream(stream)), "stca_litm_merge")
+    return X_merged
 
 
 class Profiler:

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/stca.h"
@@ -754,6 +755,70 @@ int stca_sl_pack(const stca_dims *dims, int32_t n_users, const int64_t *full_off
     return fail(STCA_E_ALIGN, "X buffers need 16-byte, offsets 8-byte alignment");
   HIP_TRY(sl_pack((hipStream_t)stream, n_users, full_off, hist_off, total, max_len, (int)(row_bytes / 16), X_full,
                   X_packed));
+  return STCA_OK;
+}
+
+int stca_litm_plan(int32_t n_users, const int64_t *hist_off, const int64_t *item_id, int32_t T, int64_t *merged_off,
+                   int64_t *group_off, int64_t *members, int64_t *n_groups) {
+  if (n_users < 0) return fail(STCA_E_ARG, "n_users < 0");
+  if (T < 0) return fail(STCA_E_ARG, "T < 0");
+  if (!hist_off || !merged_off || !n_groups) return fail(STCA_E_ARG, "hist_off, merged_off or n_groups is NULL");
+  if (hist_off[0] != 0) return fail(STCA_E_ARG, "hist_off[0] != 0");
+  for (int32_t u = 0; u < n_users; ++u)
+    if (hist_off[u + 1] < hist_off[u]) return fail(STCA_E_ARG, "hist_off decreases at user %d", u);
+  const int64_t total = hist_off[n_users];
+  merged_off[0] = 0;
+  *n_groups = 0;
+  if (total == 0) {
+    for (int32_t u = 0; u < n_users; ++u) merged_off[u + 1] = 0;
+    if (group_off) group_off[0] = 0;
+    return STCA_OK;
+  }
+  if (!item_id || !group_off || !members) return fail(STCA_E_ARG, "item_id, group_off or members is NULL");
+  // Scan in position order: token p joins the group of the latest earlier token of its user with
+  // the same ID if that token is at most T positions back, else it opens a group (groups are
+  // numbered in order of their first token).
+  std::vector<int64_t> gid(total);
+  std::unordered_map<int64_t, int64_t> last;
+  int64_t ng = 0;
+  for (int32_t u = 0; u < n_users; ++u) {
+    last.clear();
+    for (int64_t p = hist_off[u]; p < hist_off[u + 1]; ++p) {
+      auto it = last.find(item_id[p]);
+      if (it != last.end() && p - it->second <= T) {
+        gid[p] = gid[it->second];
+        it->second = p;
+      } else {
+        gid[p] = ng++;
+        last[item_id[p]] = p;
+      }
+    }
+    merged_off[u + 1] = ng;
+  }
+  // Members grouped by group, in position order within a group (counting sort).
+  std::vector<int64_t> fill(ng + 1, 0);
+  for (int64_t p = 0; p < total; ++p) ++fill[gid[p] + 1];
+  for (int64_t g = 0; g < ng; ++g) fill[g + 1] += fill[g];
+  for (int64_t g = 0; g <= ng; ++g) group_off[g] = fill[g];
+  for (int64_t p = 0; p < total; ++p) members[fill[gid[p]]++] = p;
+  *n_groups = ng;
+  return STCA_OK;
+}
+
+int stca_litm_merge(const stca_dims *dims, int64_t n_rows, int64_t n_groups, const int64_t *group_off,
+                    const int64_t *members, const void *X, void *X_merged, void *stream) {
+  if (!dims) return fail(STCA_E_ARG, "dims is NULL");
+  if (dims->dtype != STCA_F32 && dims->dtype != STCA_BF16) return fail(STCA_E_DIMS, "unknown dtype %d", dims->dtype);
+  if (dims->d != 64 && dims->d != 128 && dims->d != 256 && dims->d != 512)
+    return fail(STCA_E_DIMS, "d=%d not in {64, 128, 256, 512}", dims->d);
+  if (n_rows < 0 || n_groups < 0 || n_groups > n_rows) return fail(STCA_E_ARG, "need 0 <= n_groups <= n_rows");
+  if (n_groups > ((int64_t)1 << 33)) return fail(STCA_E_ARG, "n_groups too large for one launch");
+  if (n_groups == 0) return STCA_OK;
+  if (!group_off || !members || !X || !X_merged) return fail(STCA_E_ARG, "NULL pointer");
+  if (!aligned16(X) || !aligned16(X_merged) || ((uintptr_t)group_off % 8) || ((uintptr_t)members % 8))
+    return fail(STCA_E_ALIGN, "X buffers need 16-byte, index arrays 8-byte alignment");
+  HIP_TRY(litm_merge((hipStream_t)stream, dims->dtype == STCA_BF16, dims->d, n_rows, n_groups, group_off, members, X,
+                     X_merged));
   return STCA_OK;
 }
 

@@ -78,6 +78,9 @@ hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_o
 // ---- stochastic-length batches (sl.hip) -------------------------------------------------------
 // X_packed (rows of row16 16-byte chunks) <- the temporal suffix rows of every user of X_full;
 // max_len bounds every user's packed length.
+// Local same-ID token merging: merged row g = sum of rows members[group_off[g] .. group_off[g+1]).
+hipError_t litm_merge(hipStream_t s, bool bf16_rows, int d, int64_t n_rows, int64_t n_groups,
+                      const int64_t *group_off, const int64_t *members, const void *X, void *out);
 hipError_t sl_pack(hipStream_t s, int n_users, const int64_t *full_off, const int64_t *hist_off, int64_t total,
                    int64_t max_len, int row16, const void *X_full, void *X_packed);
 
