@@ -15,6 +15,8 @@ arithmetic).
   suffix selection, two-step batch load balancing) in integer numpy.
 * ``oracle.litm``  -- local same-ID token merging of a history (TM20K's LITM): grouping
   in plain Python, merged rows as float64 sums.
+* ``oracle.grad``  -- gradients of the forward (eqs. (2)-(8)) for an upstream dZ: the chain
+  rule written out in float64, pinned by central finite differences of ``oracle.stca``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 (library routines, closed forms, invariants the pages state, brute force).
@@ -24,6 +26,6 @@ LayerNorm in the query update) are fixed readings, shared with the HIP path
 by definition; no page prints a number that could pin them ("parity unpinned"
 for those readings only).
 """
-from . import brute, litm, sl, stca
+from . import brute, grad, litm, sl, stca
 
-__all__ = ["stca", "brute", "sl", "litm"]
+__all__ = ["stca", "brute", "sl", "litm", "grad"]
