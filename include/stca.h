@@ -139,6 +139,47 @@ STCA_API int stca_predict(const stca_dims *dims, const void *WZ, const stca_ffn 
                           const float *Z, const void *xt, float *z, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* ---- backward pass ---------------------------------------------------------------------------
+ * Gradients of the forward of eqs. (2)-(8) (the training step of "Make It Long, Keep It Fast",
+ * notes page, section 2.2: the stack is trained end to end with the loss of eq. (14), which is
+ * outside this library) for an upstream gradient dZ of its output.  With L = sum(dZ * Z), the
+ * call returns dL/dX, dL/dx_t and dL/dW for every weight slot, in fp32:
+ *   - the history FFN of layer i (hist[i]) and the query FFN of layer i (query[i]) are separate
+ *     slots even where they point at the same matrices; a caller sharing them adds the two;
+ *   - every output is overwritten (not accumulated); gradients of query[i].gamma/beta for i >= 1
+ *     without dims->query_ln are zeros; pointers may be NULL to skip dX, dxt and those unused
+ *     query LayerNorm slots, every other gradient pointer is required;
+ *   - the forward is recomputed inside the call in fp32 from the stored X, x_t and weights
+ *     (dims->dtype storage; no bf16 rounding of intermediates), so results are the fp32
+ *     gradients of the fp32 forward;
+ *   - reductions over rows (tokens, targets) run in a fixed order: results are deterministic.
+ * Memory: the workspace holds the encoded history of every layer in fp32 (M total_L d floats)
+ * and per-target intermediates; see stca_backward_workspace_size. */
+typedef struct {
+  float *dWu, *dWv; /* d x rd */
+  float *dWo;       /* rd x d */
+  float *dgamma, *dbeta; /* d */
+} stca_ffn_grad;
+
+typedef struct {
+  float *dX;  /* total_L x d, or NULL */
+  float *dxt; /* total_T x d, or NULL */
+  stca_ffn_grad hist[STCA_MAX_M];
+  stca_ffn_grad query[STCA_MAX_M];
+  float *dWQ[STCA_MAX_M], *dWK[STCA_MAX_M], *dWV[STCA_MAX_M], *dWO[STCA_MAX_M]; /* d x d */
+  float *dWC[STCA_MAX_M]; /* (i+1)d x d for i >= 1; dWC[0] unused */
+} stca_grads;
+
+STCA_API int stca_backward_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
+
+/* X: total_L x d, xt: total_T x d (dims->dtype), dZ: total_T x M x d fp32 (the layout of Z in
+ * stca_forward), grads: output pointers as described above (device).  Same conventions as the
+ * forward: argument errors before any work, asynchronous on `stream`; a user with an empty
+ * history gets NaN gradients. */
+STCA_API int stca_backward(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
+                           const void *xt, const float *dZ, const stca_grads *grads, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* ---- stochastic-length training batches -----------------------------------------------------
  * "Make It Long, Keep It Fast" (notes page, length extrapolation: stochastic length sampling,
  * eqs. (15)-(17); element selection; batch-level load balancing, two steps).  A training batch

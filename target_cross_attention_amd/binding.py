@@ -23,7 +23,8 @@ N_PHASES = 7
 EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
     "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict",
-    "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_litm_plan", "stca_litm_merge", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_litm_plan", "stca_litm_merge",
+    "stca_backward_workspace_size", "stca_backward", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
 ]
@@ -47,6 +48,16 @@ class WeightsC(ctypes.Structure):
 class BatchC(ctypes.Structure):
     _fields_ = [("n_users", c_int32), ("hist_off", c_void_p), ("tgt_off", c_void_p), ("total_L", c_int64),
                 ("total_T", c_int64), ("max_L", c_int64), ("max_T", c_int64)]
+
+
+class FfnGrad(ctypes.Structure):
+    _fields_ = [("dWu", c_void_p), ("dWv", c_void_p), ("dWo", c_void_p), ("dgamma", c_void_p), ("dbeta", c_void_p)]
+
+
+class GradsC(ctypes.Structure):
+    _fields_ = [("dX", c_void_p), ("dxt", c_void_p), ("hist", FfnGrad * MAX_M), ("query", FfnGrad * MAX_M),
+                ("dWQ", c_void_p * MAX_M), ("dWK", c_void_p * MAX_M), ("dWV", c_void_p * MAX_M),
+                ("dWO", c_void_p * MAX_M), ("dWC", c_void_p * MAX_M)]
 
 
 class ProfileReport(ctypes.Structure):
@@ -87,6 +98,8 @@ def _load() -> ctypes.CDLL:
         "stca_sl_pack": [P, c_int32, P, P, c_int64, c_int64, P, P, P],
         "stca_litm_plan": [c_int32, P, P, c_int32, P, P, P, POINTER(c_int64)],
         "stca_litm_merge": [P, c_int64, c_int64, P, P, P, P, P],
+        "stca_backward_workspace_size": [P, P, POINTER(c_size_t)],
+        "stca_backward": [P, P, P, P, P, P, P, P, c_size_t, P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -382,6 +395,62 @@ def litm_merge(dims: Dims, group_off, members, X, X_merged=None, stream=None):
     _check(LIB.stca_litm_merge(_ref(dims), int(X.shape[0]), n_groups, _ptr(group_off), _ptr(members), _ptr(X),
                                _ptr(X_merged), _stream(stream)), "stca_litm_merge")
     return X_merged
+
+
+GRAD_SLOTS = ["Wu", "Wv", "Wo", "gamma", "beta", "qWu", "qWv", "qWo", "qgamma", "qbeta",
+              "WQ", "WK", "WV", "WO", "WC"]
+
+
+class DeviceGrads:
+    """fp32 device tensors for every gradient of stca_backward, plus the filled ``stca_grads``
+    struct.  ``slot(name)`` lists the per-layer tensors of a slot named as in ``oracle.grad.Grads``
+    (None where the library writes nothing)."""
+
+    def __init__(self, dims: Dims, total_L: int, total_T: int, device="cuda", with_dX=True, with_dxt=True):
+        import torch
+        d, M, rd = dims.d, dims.M, dims.r * dims.d
+        z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=device)  # noqa: E731
+        self.dX = z(max(total_L, 1), d) if with_dX else None
+        self.dxt = z(max(total_T, 1), d) if with_dxt else None
+        self.t = {k: [None] * M for k in GRAD_SLOTS}
+        self.c = GradsC()
+        self.c.dX, self.c.dxt = _ptr(self.dX), _ptr(self.dxt)
+        for i in range(M):
+            for pre, fg in (("", self.c.hist[i]), ("q", self.c.query[i])):
+                self.t[pre + "Wu"][i], self.t[pre + "Wv"][i], self.t[pre + "Wo"][i] = z(d, rd), z(d, rd), z(rd, d)
+                fg.dWu, fg.dWv, fg.dWo = (_ptr(self.t[pre + k][i]) for k in ("Wu", "Wv", "Wo"))
+                if pre == "" or i == 0 or dims.query_ln:
+                    self.t[pre + "gamma"][i], self.t[pre + "beta"][i] = z(d), z(d)
+                    fg.dgamma, fg.dbeta = _ptr(self.t[pre + "gamma"][i]), _ptr(self.t[pre + "beta"][i])
+            for k in ("WQ", "WK", "WV", "WO"):
+                self.t[k][i] = z(d, d)
+                getattr(self.c, "d" + k)[i] = _ptr(self.t[k][i])
+            if i >= 1:
+                self.t["WC"][i] = z((i + 1) * d, d)
+                self.c.dWC[i] = _ptr(self.t["WC"][i])
+
+    def slot(self, name: str):
+        return self.t[name]
+
+
+def backward_workspace_size(dims: Dims, batch: BatchC) -> int:
+    n = c_size_t(0)
+    _check(LIB.stca_backward_workspace_size(_ref(dims), _ref(batch), ctypes.byref(n)),
+           "stca_backward_workspace_size")
+    return n.value
+
+
+def stca_backward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, dZ, grads: DeviceGrads | None = None, ws=None,
+                  stream=None):
+    """Gradients of sum(dZ * Z) for the forward of ``batch`` (dZ: total_T x M x d float32, device).
+    Returns the DeviceGrads holding them."""
+    if grads is None:
+        grads = DeviceGrads(dims, batch.total_L, batch.total_T, batch.X.device)
+    if ws is None:
+        ws = workspace(backward_workspace_size(dims, batch.c), batch.X.device)
+    _check(LIB.stca_backward(_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(dZ),
+                             _ref(grads.c), _ptr(ws), ws.numel(), _stream(stream)), "stca_backward")
+    return grads
 
 
 class Profiler:

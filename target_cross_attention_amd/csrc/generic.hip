@@ -8,12 +8,13 @@
 namespace stca {
 
 // ------------------------------------------------------------------------------------------
-// C = alpha * A B + beta * C, batched over blockIdx.z.  A: M x K (lda), B: K x N (ldb) or,
-// with TRANS_B, B[k][n] = Bt[n * ldb + k].  fp32 accumulation; beta == 0 never reads C.
+// C = alpha * A B + beta * C, batched over blockIdx.z.  A: M x K (lda) or, with TRANS_A,
+// A[m][k] = At[k * lda + m]; B: K x N (ldb) or, with TRANS_B, B[k][n] = Bt[n * ldb + k].  fp32
+// accumulation; beta == 0 never reads C.
 // ------------------------------------------------------------------------------------------
 constexpr int GT = 64, GK = 16;
 
-template <typename TA, typename TB, typename TC, bool TRANS_B>
+template <typename TA, typename TB, typename TC, bool TRANS_B, bool TRANS_A>
 __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, const TA *__restrict__ A,
                                                    int64_t lda, int64_t sA, const TB *__restrict__ B,
                                                    int64_t ldb, int64_t sB, TC *__restrict__ C,
@@ -38,9 +39,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, const TA
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + e * 256;  // 0..1023
-      const int r = idx >> 4, k = idx & 15;
+      const int r = TRANS_A ? (idx & 63) : (idx >> 4), k = TRANS_A ? (idx >> 6) : (idx & 15);
       const int gm = m0 + r, gk = k0 + k;
-      As[k][r] = (gm < M && gk < K) ? ld(A + (int64_t)gm * lda + gk) : 0.f;
+      As[k][r] = (gm < M && gk < K) ? ld(TRANS_A ? A + (int64_t)gk * lda + gm : A + (int64_t)gm * lda + gk) : 0.f;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -89,10 +90,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K, const TA
   }
 }
 
-template <typename TA, typename TB, typename TC, bool TB_T>
+template <typename TA, typename TB, typename TC, bool TB_T, bool TA_T = false>
 static hipError_t gemm_t(hipStream_t s, const GemmArgs &g) {
   dim3 grid((g.N + GT - 1) / GT, (g.M + GT - 1) / GT, g.batch);
-  hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, TB_T>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+  hipLaunchKernelGGL((gemm_kernel<TA, TB, TC, TB_T, TA_T>), grid, dim3(256), 0, s, g.M, g.N, g.K,
                      (const TA *)g.A, g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (TC *)g.C, g.ldc, g.sC,
                      g.alpha, g.beta);
   return hipGetLastError();
@@ -100,7 +101,11 @@ static hipError_t gemm_t(hipStream_t s, const GemmArgs &g) {
 
 hipError_t gemm(hipStream_t s, const GemmArgs &g) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
-  // Dispatch on (A type, B type, C type, transB).
+  // Dispatch on (A type, B type, C type, transB); transposed A only for fp32 outputs.
+  if (g.trans_a) {
+    if (g.tc_bf16 || g.tb_bf16 || g.trans_b) return hipErrorInvalidValue;
+    return g.ta_bf16 ? gemm_t<bf16, float, float, false, true>(s, g) : gemm_t<float, float, float, false, true>(s, g);
+  }
 #define STCA_GEMM_CASE(ta, tb, tc, TA_, TB_, TC_)                                             \
   if (g.ta_bf16 == ta && g.tb_bf16 == tb && g.tc_bf16 == tc)                                   \
     return g.trans_b ? gemm_t<TA_, TB_, TC_, true>(s, g) : gemm_t<TA_, TB_, TC_, false>(s, g);

@@ -14,7 +14,7 @@ struct GemmArgs {
   bool ta_bf16 = false;
   const void *B = nullptr;
   int64_t ldb = 0, sB = 0;
-  bool tb_bf16 = false, trans_b = false;
+  bool tb_bf16 = false, trans_b = false, trans_a = false;
   void *C = nullptr;
   int64_t ldc = 0, sC = 0;
   bool tc_bf16 = false;
@@ -83,5 +83,33 @@ hipError_t litm_merge(hipStream_t s, bool bf16_rows, int d, int64_t n_rows, int6
                       const int64_t *group_off, const int64_t *members, const void *X, void *out);
 hipError_t sl_pack(hipStream_t s, int n_users, const int64_t *full_off, const int64_t *hist_off, int64_t total,
                    int64_t max_len, int row16, const void *X_full, void *X_packed);
+
+// ---- backward pieces (backward.hip); all fp32 ------------------------------------------------
+hipError_t fill_f32(hipStream_t s, int64_t n, float *y, float v);
+// out[i] (+)= sum over k of parts[k n + i], in k order (deterministic split-K reduction).
+hipError_t sum_parts(hipStream_t s, int64_t n, int nparts, const float *parts, float *out, bool accumulate);
+// The same over a rows x cols block: parts are contiguous blocks, out has row stride ldo.
+hipError_t sum_parts2d(hipStream_t s, int64_t rows, int cols, int nparts, const float *parts, float *out,
+                       int64_t ldo, bool accumulate);
+// out[c] += sum over rows of A[r][c], in two fixed-order stages through parts (max_parts x cols).
+hipError_t colsum(hipStream_t s, int64_t rows, int cols, const float *A, int64_t lda, float *parts, int max_parts,
+                  float *out);
+hipError_t swiglu_fwd(hipStream_t s, int64_t n, const float *A, const float *G, float *H);
+hipError_t swiglu_bwd(hipStream_t s, int64_t n, const float *dH, const float *A, const float *G, float *dA,
+                      float *dG);
+// dY (rows x d) and Pg = dout * xhat (rows x d) from the pre-LN rows Y; d <= 512.
+hipError_t ln_bwd(hipStream_t s, int64_t rows, int d, const float *dout, int64_t ldd, const float *Y, int64_t ldy,
+                  const float *gamma, float eps, float *dY, float *Pg);
+hipError_t rowdot(hipStream_t s, int64_t rows, int d, const float *A, const float *B, float *out);
+hipError_t copy_rows(hipStream_t s, int64_t rows, int d, const float *x, int64_t ldx, float *y, int64_t ldy);
+// Attention of the (target, head) rows over their user's history, fp32; U unscaled, scale 1/sqrt(d_h).
+hipError_t attn_rows_fwd(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off, const int64_t *tgt_off,
+                         int64_t T, const float *Xt, const float *U, float scale, float *abar, float *lse);
+hipError_t attn_rows_bwd_query(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off,
+                               const int64_t *tgt_off, int64_t T, const float *Xt, const float *U,
+                               const float *dabar, const float *lse, const float *D, float scale, float *du);
+hipError_t attn_rows_bwd_keys(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off,
+                              const int64_t *tgt_off, int64_t L, const float *Xt, const float *U,
+                              const float *dabar, const float *lse, const float *D, float scale, float *dXt);
 
 }  // namespace stca

@@ -197,3 +197,48 @@ def test_one_hip_runtime_in_process():
     hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     hsa = {ln.split()[-1] for ln in maps if "libhsa-runtime64" in ln}
     assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
+
+
+def _fake_grads(M, query_ln=False):
+    g = B.GradsC()
+    g.dX = g.dxt = FAKE
+    for i in range(M):
+        g.hist[i] = B.FfnGrad(FAKE, FAKE, FAKE, FAKE, FAKE)
+        ln = FAKE if (i == 0 or query_ln) else None
+        g.query[i] = B.FfnGrad(FAKE, FAKE, FAKE, ln, ln)
+        g.dWQ[i] = g.dWK[i] = g.dWV[i] = g.dWO[i] = FAKE
+        g.dWC[i] = FAKE if i >= 1 else None
+    return g
+
+
+def _backward(dims, w, batch, g, X=FAKE, xt=FAKE, dZ=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return B.LIB.stca_backward(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(batch), X, xt, dZ,
+                               ctypes.byref(g) if g is not None else None, ws, ws_bytes, None)
+
+
+def test_backward_validation():
+    dims = B.make_dims(256, 8, 3, 4)
+    w, batch, g = _fake_weights(3), _batch(), _fake_grads(3)
+    need = B.backward_workspace_size(dims, batch)
+    # M x total_L x d fp32 encoded histories dominate the workspace
+    assert need >= 3 * 400 * 256 * 4
+    assert _backward(B.make_dims(96, 8, 3, 4), w, batch, g) == -2
+    assert _backward(dims, w, batch, None) == -1
+    bad = _fake_grads(3)
+    bad.dWC[2] = None
+    assert _backward(dims, w, batch, bad) == -1
+    bad = _fake_grads(3)
+    bad.query[1] = B.FfnGrad(FAKE, None, FAKE, None, None)
+    assert _backward(dims, w, batch, bad) == -1
+    bad = _fake_grads(3)
+    bad.hist[2] = B.FfnGrad(FAKE, FAKE, FAKE, FAKE, FAKE + 8)
+    assert _backward(dims, w, batch, bad) == -4
+    # the query LayerNorm slots of layers >= 1 are needed once eq. (7) applies the LayerNorm
+    ln = B.make_dims(256, 8, 3, 4, query_ln=True)
+    assert _backward(ln, w, batch, _fake_grads(3)) == -1
+    assert _backward(dims, w, batch, g, X=None) == -1
+    assert _backward(dims, w, batch, g, dZ=FAKE + 4) == -4
+    assert _backward(dims, w, batch, g, ws=None) == -3
+    assert _backward(dims, w, batch, g, ws_bytes=need - 1) == -3
+    assert _backward(dims, _fake_weights(3, with_wc=False), batch, g) == -1
+    assert _backward(dims, w, B.BatchC(4, FAKE, FAKE, 400, 1 << 23, 100, 1 << 21), g) == -1

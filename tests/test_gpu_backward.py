@@ -1,0 +1,130 @@
+"""GPU parity of stca_backward against ``oracle.grad`` (float64 chain rule, pinned by finite
+differences of the forward oracle in test_oracle_grad.py) on identical seeded inputs.
+
+Both sides differentiate the same function of the same stored values (bf16 workloads: the
+bf16-rounded X, x_t and weights); the library computes in fp32 throughout, the oracle in
+float64.  Bar: for every gradient tensor, max |gpu - oracle| / max |oracle| <= 1e-4.  Where it
+comes from: each gradient is a short chain (<= 4 layers x ~10 products) of fp32 sums; at these
+sizes a sum runs over at most ~1500 terms, whose relative error is of order sqrt(K) u in the mean
+and K u at worst (u = 2^-24: 2e-6 .. 9e-5), and no step divides by a small quantity (LayerNorm
+rows have unit scale, far from rstd = 1/sqrt(eps)).  A wrong term (a dropped softmax centring,
+a transposed operand, a missing LayerNorm mean) gives errors of order 1e-2 .. 1.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import stca_inputs as SI
+from oracle import grad as G
+from stca_testlib import announce
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+GRAD_TOL = 1e-4
+SLOTS = ["Wu", "Wv", "Wo", "gamma", "beta", "qWu", "qWv", "qWo", "qgamma", "qbeta", "WQ", "WK", "WV", "WO", "WC"]
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from target_cross_attention_amd import binding
+    return binding
+
+
+def tensor_rel(g, o) -> float:
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    if o.size == 0:
+        return 0.0
+    den = max(float(np.max(np.abs(o))), 1e-30)
+    r = float(np.max(np.abs(g - o))) / den
+    return float("inf") if np.isnan(r) else r
+
+
+def without_targets(inp, drop):
+    """The batch with the users at positions ``drop`` given no targets (their histories stay)."""
+    m = inp.m.copy()
+    keep_rows = []
+    for k in range(inp.n_users):
+        if k in drop:
+            m[k] = 0
+        else:
+            keep_rows.extend(range(inp.tgt_off[k], inp.tgt_off[k + 1]))
+    return dataclasses.replace(inp, m=m, tgt_off=SI.offsets(m), xt=inp.xt[np.asarray(keep_rows, np.int64)])
+
+
+def run_case(B, cfg, inp, W, query_ln=False, seed=5):
+    dims = B.dims_for(cfg, query_ln=query_ln)
+    dZ = np.random.default_rng(seed).standard_normal((inp.total_T, cfg.M, cfg.d)).astype(np.float32)
+    dw = B.DeviceWeights(W, cfg.dtype, DEV)
+    db = B.DeviceBatch(inp, DEV)
+    grads = B.stca_backward(dims, dw, db, torch.from_numpy(dZ).to(DEV))
+    torch.cuda.synchronize()
+    ref = G.backward_batch(inp, W, dZ.astype(np.float64), query_ln=query_ln)
+    errs = {"dX": tensor_rel(grads.dX[:inp.total_L].cpu().numpy(), ref.dX),
+            "dxt": tensor_rel(grads.dxt[:inp.total_T].cpu().numpy(), ref.dxt)}
+    for name in SLOTS:
+        for i, t in enumerate(grads.slot(name)):
+            want = getattr(ref, name)[i]
+            if t is None:
+                assert want is None or not np.any(want), (name, i)   # unused slot: zero in the oracle
+                continue
+            errs[f"{name}[{i}]"] = tensor_rel(t.cpu().numpy(), want)
+    worst = max(errs, key=errs.get)
+    print(f"  users={inp.n_users} L={inp.total_L} T={inp.total_T} worst {worst}={errs[worst]:.3e}", flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= GRAD_TOL}
+    assert not bad, bad
+    return errs
+
+
+CASES = [
+    ("tiny", dict(), False, False),
+    ("tiny", dict(M=3, n_users=3, length=("fixed", 40), targets=("fixed", 3)), True, True),
+    ("uniform", dict(n_users=3, length=("fixed", 200)), False, False),
+    ("ragged", dict(n_users=5, length=("lognormal", 150.0, 200.0, 16, 600)), False, True),
+    ("ragged", dict(n_users=4, dtype="f32", length=("lognormal", 100.0, 150.0, 16, 400)), True, False),
+    ("stress20k", dict(n_users=2, M=2, length=("fixed", 150), targets=("fixed", 3)), False, False),
+]
+
+
+@pytest.mark.parametrize("key,change,query_ln,separate", CASES,
+                         ids=[f"{k}-{i}" for i, (k, *_) in enumerate(CASES)])
+def test_backward_matches_oracle(B, key, change, query_ln, separate):
+    cfg = SI.scaled(SI.get_config(key), **change)
+    announce("backward", cfg.key, cfg.dtype, change, "query_ln" if query_ln else "", "separate" if separate else "")
+    W = SI.make_weights(cfg, random_ln=True, separate_query_ffn=separate)
+    run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln)
+
+
+def test_backward_short_histories_and_targetless_users(B):
+    """Many users with 1..40 history rows (the key-side kernel's rows straddle users) and some
+    users without targets (their history gets zero gradient)."""
+    cfg = SI.scaled(SI.get_config("ragged"), n_users=23, M=2, length=("lognormal", 4.0, 8.0, 1, 40))
+    announce("backward-short", cfg.key)
+    inp = without_targets(SI.make_inputs(cfg), {0, 5, 6, 22})
+    W = SI.make_weights(cfg, random_ln=True)
+    run_case(B, cfg, inp, W)
+
+
+def test_backward_no_targets_gives_zero(B):
+    cfg = SI.scaled(SI.get_config("tiny"), n_users=2, M=2)
+    inp = without_targets(SI.make_inputs(cfg), {0, 1})
+    announce("backward-no-targets", cfg.key)
+    dims = B.dims_for(cfg)
+    dw = B.DeviceWeights(SI.make_weights(cfg), cfg.dtype, DEV)
+    db = B.DeviceBatch(inp, DEV)
+    grads = B.DeviceGrads(dims, inp.total_L, 0, DEV)
+    for t in [grads.dX] + [x for k in SLOTS for x in grads.slot(k) if x is not None]:
+        t.fill_(7.0)                                  # every output is overwritten
+    B.stca_backward(dims, dw, db, torch.zeros((1, cfg.M, cfg.d), device=DEV), grads)
+    torch.cuda.synchronize()
+    assert float(grads.dX.abs().max()) == 0.0
+    for k in SLOTS:
+        for x in grads.slot(k):
+            if x is not None:
+                assert float(x.abs().max()) == 0.0, k
