@@ -225,6 +225,106 @@ def bench_litm(a, cfg, dev):
     }))
 
 
+def bench_backward(a, cfg, dev):
+    """One training step's backward on the training-shaped ragged batch: stca_backward for an
+    upstream dZ of the forward (the forward is recomputed inside the call), timed per phase with
+    HIP events on the call's stream."""
+    import numpy as np
+    import torch
+
+    import stca_inputs as SI
+    from target_cross_attention_amd import binding as B
+
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    log(f"inputs {cfg.key}: {inp.n_users} users, {inp.total_L} history tokens, {inp.total_T} targets")
+    dims = B.dims_for(cfg)
+    dw = B.DeviceWeights(W, cfg.dtype, dev)
+    db = B.DeviceBatch(inp, dev)
+    del inp.X
+    dZ = torch.from_numpy(np.random.default_rng(11).standard_normal((db.total_T, cfg.M, cfg.d), np.float32)).to(dev)
+    grads = B.DeviceGrads(dims, db.total_L, db.total_T, dev)
+    ws = B.workspace(B.backward_workspace_size(dims, db.c), dev)
+    stream = torch.cuda.current_stream()
+    log(f"backward workspace {ws.numel() / 2**30:.2f} GiB; warmup {a.warmup}")
+    for _ in range(a.warmup):
+        B.stca_backward(dims, dw, db, dZ, grads, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    log(f"timing {a.steps} steps")
+    prof = B.Profiler()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        B.stca_backward(dims, dw, db, dZ, grads, ws=ws, stream=stream, profiler=prof)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    phases = prof.read()
+    prof.close()
+    assert np.isfinite(grads.dX.sum().item()), "non-finite gradient"
+    L, T, d, r, M, h = db.total_L, db.total_T, cfg.d, cfg.r, cfg.M, cfg.h
+    pairs = float((db.inp.L * db.inp.m).sum()) * h
+    # Dominant phase: the derivative of eq. (2) over the history rows, one per layer.  Algorithmic
+    # FLOP per history token: the recomputed A = x W_u, G = x W_v, Y = H W_o (6 r d^2) and the
+    # products dW_o, dH, dW_u, dW_v, dx (12 r d^2), 2 FLOP per multiply-add.
+    enc_ms, enc_n = phases["bwd_encode"]
+    enc_avg_s = enc_ms / max(enc_n, 1) / 1e3
+    enc_flops = 18.0 * r * d * d * L
+    achieved = enc_flops / enc_avg_s / 1e12
+    att_layer_ms = phases["bwd_attend"][0] / a.steps / M   # 4d FLOP per pair forward, 8d backward
+    out = {
+        "metric": "STCA backward history-tokens/s (gradients of every weight, X and x_t)",
+        "value": L * a.steps / dt, "unit": "history-tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": dt * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded; training-shaped ragged batch)",
+        "config": {"workload": cfg.description, "key": cfg.key, "users": db.inp.n_users, "history_tokens": L,
+                   "targets": T, "storage": cfg.dtype},
+        "roofline": {"kernel": "encode backward (fp32 GEMMs on the vector ALU + SwiGLU/LayerNorm derivatives)",
+                     "bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": enc_flops, "avg_launch_ms": enc_avg_s * 1e3,
+                     "launches": enc_n},
+        "attention_backward": {"kernels": "softmax statistics + query-side + key-side derivative",
+                               "ms_per_layer": att_layer_ms, "pairs_per_layer": pairs, "bound": "alu",
+                               "achieved": 12.0 * d * pairs / (att_layer_ms / 1e3) / 1e12,
+                               "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"},
+        "phase_ms_per_step": {k: v[0] / a.steps for k, v in phases.items() if k.startswith("bwd")},
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (gradient oracle on a user sample)")
+        out["cpu_baseline"] = cpu_baseline_backward(cfg, W)
+    print(json.dumps(out))
+
+
+def cpu_baseline_backward(cfg, W, target_s: float = 12.0, max_users: int = 64):
+    """The gradient oracle, as it stands, on users of the same workload until ~target_s of CPU work."""
+    import numpy as np
+    import stca_inputs as SI
+    from oracle import grad as G
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    L, m = SI.batch_layout(cfg)
+    rng = np.random.default_rng(3)
+    tokens = users = 0
+    elapsed = 0.0
+    t0 = time.perf_counter()
+    for u in range(min(cfg.n_users, max_users)):
+        inp = SI.make_inputs(cfg, users=[u], threads=1)
+        dZ = rng.standard_normal((inp.total_T, cfg.M, cfg.d))
+        ts = time.perf_counter()
+        G.backward_batch(inp, W, dZ)
+        elapsed += time.perf_counter() - ts
+        tokens += int(L[u])
+        users += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    return {"value": tokens / elapsed, "unit": "history-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{users} of {cfg.n_users} users ({tokens} history tokens), numpy float64 per-user "
+                      f"backward (oracle.grad), {elapsed:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +340,8 @@ def main():
     ap.add_argument("--litm", action="store_true",
                     help="merge same-ID tokens at most 3 positions apart first (host plan, device merge), then "
                          "time the forward on the merged batch")
+    ap.add_argument("--backward", action="store_true",
+                    help="time stca_backward instead (default workload: the training-shaped ragged batch)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of STCA, run K device copies of 2 GiB (counter calibration)")
     a = ap.parse_args()
@@ -267,6 +369,8 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "copies": a.calib_copy}))
         return
 
+    if a.backward and a.workload == "dense10k":
+        a.workload = "ragged"
     cfg = SI.get_config(a.workload)
     if a.users:
         cfg = SI.scaled(cfg, n_users=a.users)
@@ -274,6 +378,8 @@ def main():
         return bench_sl(a, cfg, dev)
     if a.litm:
         return bench_litm(a, cfg, dev)
+    if a.backward:
+        return bench_backward(a, cfg, dev)
     t = time.perf_counter()
     W = SI.make_weights(cfg)
     inp = SI.make_inputs(cfg)

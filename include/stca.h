@@ -263,6 +263,10 @@ enum {
   STCA_PHASE_ATTEND,     /* split-L attention over the history (one launch per layer) */
   STCA_PHASE_COMBINE,    /* merge of split-L partial softmax states */
   STCA_PHASE_PROJECT,    /* (alpha X~) W_V and W_O, eqs. (13), (6) */
+  STCA_PHASE_BWD_RECOMPUTE, /* backward: fp32 encode of the history for every layer, eq. (2) */
+  STCA_PHASE_BWD_ATTEND,    /* backward: softmax statistics, query- and key-side derivative kernels */
+  STCA_PHASE_BWD_ENCODE,    /* backward: derivative of eq. (2) over the history rows (per layer) */
+  STCA_PHASE_BWD_TARGET,    /* backward: every per-target step (query path, projections, W_C) */
   STCA_N_PHASES
 };
 
@@ -280,6 +284,11 @@ STCA_API int stca_profiler_read(stca_profiler *p, stca_profile_report *out);
 STCA_API int stca_forward_profiled(const stca_dims *dims, const stca_weights *w, const stca_batch *batch,
                           const void *X, const void *xt, float *Z, void *workspace,
                           size_t workspace_bytes, void *stream, stca_profiler *prof);
+
+/* stca_backward with an event pair recorded around every phase (prof may be NULL). */
+STCA_API int stca_backward_profiled(const stca_dims *dims, const stca_weights *w, const stca_batch *batch,
+                                    const void *X, const void *xt, const float *dZ, const stca_grads *grads,
+                                    void *workspace, size_t workspace_bytes, void *stream, stca_profiler *prof);
 
 /* ---- diagnostics ---------------------------------------------------------------------------- */
 STCA_API const char *stca_status_string(int status);

@@ -16,15 +16,17 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstca.so"
 MAX_M = 8
 
 F32, BF16 = 0, 1
-(PHASE_PACK, PHASE_ENCODE, PHASE_QUERY, PHASE_UPROJ, PHASE_ATTEND, PHASE_COMBINE, PHASE_PROJECT) = range(7)
-PHASE_NAMES = ["pack", "encode", "query", "uproj", "attend", "combine", "project"]
-N_PHASES = 7
+(PHASE_PACK, PHASE_ENCODE, PHASE_QUERY, PHASE_UPROJ, PHASE_ATTEND, PHASE_COMBINE, PHASE_PROJECT,
+ PHASE_BWD_RECOMPUTE, PHASE_BWD_ATTEND, PHASE_BWD_ENCODE, PHASE_BWD_TARGET) = range(11)
+PHASE_NAMES = ["pack", "encode", "query", "uproj", "attend", "combine", "project",
+               "bwd_recompute", "bwd_attend", "bwd_encode", "bwd_target"]
+N_PHASES = 11
 
 EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
     "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict",
     "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_litm_plan", "stca_litm_merge",
-    "stca_backward_workspace_size", "stca_backward", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_backward_workspace_size", "stca_backward", "stca_backward_profiled", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
 ]
@@ -100,6 +102,7 @@ def _load() -> ctypes.CDLL:
         "stca_litm_merge": [P, c_int64, c_int64, P, P, P, P, P],
         "stca_backward_workspace_size": [P, P, POINTER(c_size_t)],
         "stca_backward": [P, P, P, P, P, P, P, P, c_size_t, P],
+        "stca_backward_profiled": [P, P, P, P, P, P, P, P, c_size_t, P, P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -441,15 +444,19 @@ def backward_workspace_size(dims: Dims, batch: BatchC) -> int:
 
 
 def stca_backward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, dZ, grads: DeviceGrads | None = None, ws=None,
-                  stream=None):
+                  stream=None, profiler=None):
     """Gradients of sum(dZ * Z) for the forward of ``batch`` (dZ: total_T x M x d float32, device).
     Returns the DeviceGrads holding them."""
     if grads is None:
         grads = DeviceGrads(dims, batch.total_L, batch.total_T, batch.X.device)
     if ws is None:
         ws = workspace(backward_workspace_size(dims, batch.c), batch.X.device)
-    _check(LIB.stca_backward(_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(dZ),
-                             _ref(grads.c), _ptr(ws), ws.numel(), _stream(stream)), "stca_backward")
+    args = (_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(dZ), _ref(grads.c), _ptr(ws),
+            ws.numel(), _stream(stream))
+    if profiler is None:
+        _check(LIB.stca_backward(*args), "stca_backward")
+    else:
+        _check(LIB.stca_backward_profiled(*args, profiler.handle), "stca_backward")
     return grads
 
 

@@ -725,7 +725,8 @@ int check_grads(const stca_dims *dm, const stca_grads *g) {
 }
 
 int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b, const void *X, const void *xt,
-                  const float *dZ, const stca_grads *g, void *ws, size_t ws_bytes, hipStream_t s) {
+                  const float *dZ, const stca_grads *g, void *ws, size_t ws_bytes, hipStream_t s,
+                  stca_profiler *prof) {
   int st;
   if ((st = check_dims(dm)) != STCA_OK) return st;
   if ((st = check_batch(b)) != STCA_OK) return st;
@@ -767,6 +768,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
   if (T == 0) return STCA_OK;  // no target, no gradient
 
   // ---- forward, keeping what the backward needs ----------------------------------------------
+  // Per-target steps are timed as STCA_PHASE_BWD_TARGET, the per-history-row ones by their phases.
   auto qffn_in = [&](int i) -> const void * { return i == 0 ? xt : (const void *)bw.qin[i]; };
   auto q_forward = [&](int i) -> int {  // eq. (3) (i = 0) or eq. (7): q(i) from its FFN input
     const stca_ffn &f = w->query[i];
@@ -779,13 +781,22 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
       HIP_TRY(copy_rows(s, T, d, bw.qY[i], d, bw.q[i], d));
     return STCA_OK;
   };
-  if ((st = q_forward(0)) != STCA_OK) return st;
+  {
+    Phase ph(prof, s, STCA_PHASE_BWD_TARGET);
+    if ((st = q_forward(0)) != STCA_OK) return st;
+    HIP_TRY(ph.end());
+  }
   FfnWs enc;
   enc.A = bw.eA;
   enc.G = bw.eG;
   for (int i = 0; i < M; ++i) {
     float *Xt = bw.Xt + (size_t)i * L * d;
-    if ((st = ffn_generic(s, dm, &w->hist[i], L, X, d, bf, Xt, d, false, true, enc)) != STCA_OK) return st;  // eq. (2)
+    {
+      Phase ph(prof, s, STCA_PHASE_BWD_RECOMPUTE);
+      if ((st = ffn_generic(s, dm, &w->hist[i], L, X, d, bf, Xt, d, false, true, enc)) != STCA_OK) return st;  // eq. (2)
+      HIP_TRY(ph.end());
+    }
+    Phase pt(prof, s, STCA_PHASE_BWD_TARGET);
     HIP_TRY(mm(s, (int)T, d, d, bw.q[i], d, false, w->WQ[i], d, bf, false, bw.P[i], d, 0.f));  // P = q W_Q
     GemmArgs u;  // u_j = P_j W_K,j^T (eq. (13)), unscaled
     u.M = (int)T;
@@ -804,7 +815,14 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     u.ldc = (int64_t)h * d;
     u.sC = d;
     HIP_TRY(gemm(s, u));
-    HIP_TRY(attn_rows_fwd(s, d, h, b->n_users, b->hist_off, b->tgt_off, T, Xt, bw.U[i], sc, bw.abar[i], bw.lse[i]));
+    HIP_TRY(pt.end());
+    {
+      Phase ph(prof, s, STCA_PHASE_BWD_ATTEND);
+      HIP_TRY(attn_rows_fwd(s, d, h, b->n_users, b->hist_off, b->tgt_off, T, Xt, bw.U[i], sc, bw.abar[i],
+                            bw.lse[i]));
+      HIP_TRY(ph.end());
+    }
+    Phase pt2(prof, s, STCA_PHASE_BWD_TARGET);
     GemmArgs v;  // heads_j = abar_j W_V,j
     v.M = (int)T;
     v.N = dh;
@@ -827,6 +845,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
       HIP_TRY(concat_project(s, dm, T, bw.Z, (int64_t)M * d, i + 1, xt, w->WC[i + 1], bw.qin[i + 1]));
       if ((st = q_forward(i + 1)) != STCA_OK) return st;
     }
+    HIP_TRY(pt2.end());
   }
 
   // ---- backward, last layer first -------------------------------------------------------------
@@ -853,6 +872,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     return STCA_OK;
   };
   for (int i = M - 1; i >= 0; --i) {
+    Phase pt(prof, s, STCA_PHASE_BWD_TARGET);
     if (i + 1 < M && (st = q_backward(i + 1)) != STCA_OK) return st;
     const float *Xt = bw.Xt + (size_t)i * L * d;
     const float *dO = bw.dO + (size_t)i * d;
@@ -883,10 +903,16 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     da.sC = d;
     HIP_TRY(gemm(s, da));
     HIP_TRY(rowdot(s, T * h, d, bw.dabar, bw.abar[i], bw.Dv));
-    HIP_TRY(attn_rows_bwd_query(s, d, h, b->n_users, b->hist_off, b->tgt_off, T, Xt, bw.U[i], bw.dabar, bw.lse[i],
-                                bw.Dv, sc, bw.du));
-    HIP_TRY(attn_rows_bwd_keys(s, d, h, b->n_users, b->hist_off, b->tgt_off, L, Xt, bw.U[i], bw.dabar, bw.lse[i],
-                               bw.Dv, sc, bw.dXt));
+    HIP_TRY(pt.end());
+    {
+      Phase ph(prof, s, STCA_PHASE_BWD_ATTEND);
+      HIP_TRY(attn_rows_bwd_query(s, d, h, b->n_users, b->hist_off, b->tgt_off, T, Xt, bw.U[i], bw.dabar,
+                                  bw.lse[i], bw.Dv, sc, bw.du));
+      HIP_TRY(attn_rows_bwd_keys(s, d, h, b->n_users, b->hist_off, b->tgt_off, L, Xt, bw.U[i], bw.dabar,
+                                 bw.lse[i], bw.Dv, sc, bw.dXt));
+      HIP_TRY(ph.end());
+    }
+    Phase pt2(prof, s, STCA_PHASE_BWD_TARGET);
     GemmArgs dp;  // dP_j = du_j W_K,j
     dp.M = (int)T;
     dp.N = dh;
@@ -909,7 +935,9 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
         return st;
     if ((st = wgrad(s, d, d, T, bw.q[i], d, false, bw.dP, d, g->dWQ[i], d, bw.parts)) != STCA_OK) return st;
     HIP_TRY(mm(s, (int)T, d, d, bw.dP, d, false, w->WQ[i], d, bf, true, bw.dq, d, 0.f));
+    HIP_TRY(pt2.end());
     // eq. (2): LayerNorm and SwiGLU FFN of every history row, in row chunks
+    Phase pe(prof, s, STCA_PHASE_BWD_ENCODE);
     const size_t xes = esize(dm);
     for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
       const int64_t n = std::min<int64_t>(bw.rows, L - r0);
@@ -920,8 +948,12 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
                              bw.parts)) != STCA_OK)
         return st;
     }
+    HIP_TRY(pe.end());
   }
-  return q_backward(0);
+  Phase pt(prof, s, STCA_PHASE_BWD_TARGET);
+  if ((st = q_backward(0)) != STCA_OK) return st;
+  HIP_TRY(pt.end());
+  return STCA_OK;
 }
 
 }  // namespace
@@ -1086,7 +1118,13 @@ int stca_backward_workspace_size(const stca_dims *dims, const stca_batch *batch,
 int stca_backward(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
                   const void *xt, const float *dZ, const stca_grads *grads, void *workspace, size_t workspace_bytes,
                   void *stream) {
-  return backward_impl(dims, w, batch, X, xt, dZ, grads, workspace, workspace_bytes, (hipStream_t)stream);
+  return backward_impl(dims, w, batch, X, xt, dZ, grads, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
+}
+
+int stca_backward_profiled(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
+                           const void *xt, const float *dZ, const stca_grads *grads, void *workspace,
+                           size_t workspace_bytes, void *stream, stca_profiler *prof) {
+  return backward_impl(dims, w, batch, X, xt, dZ, grads, workspace, workspace_bytes, (hipStream_t)stream, prof);
 }
 
 int stca_sl_beta(const stca_sl_params *p, double alpha, double *beta) {

@@ -128,3 +128,52 @@ def test_backward_no_targets_gives_zero(B):
         for x in grads.slot(k):
             if x is not None:
                 assert float(x.abs().max()) == 0.0, k
+
+
+def test_backward_full_size_ragged_sampled(B):
+    """The whole training-shaped batch (512 users, ~1M history tokens, the size the backward bench
+    times) in one call.  Every gradient is linear in dZ and a user's dX and dx_t depend only on its
+    own dZ, so: (a) with dZ random everywhere, the dX / dx_t rows of sampled users equal the oracle
+    run on those users alone; (b) with dZ zero outside the sampled users, every weight gradient
+    equals the oracle's over those users and every other dX / dx_t row is exactly zero.  Bar 1e-3:
+    the weight-gradient sums here run over up to ~2e4 nonzero rows (sqrt(K) u ~ 1e-5 in the mean)."""
+    cfg = SI.get_config("ragged")
+    announce("backward-fullsize", cfg.key)
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    L = inp.L
+    sample = sorted({0, int(np.argmax(L)), inp.n_users - 1})
+    dims = B.dims_for(cfg)
+    dw = B.DeviceWeights(W, cfg.dtype, DEV)
+    db = B.DeviceBatch(inp, DEV)
+    rng = np.random.default_rng(9)
+    dZ = rng.standard_normal((inp.total_T, cfg.M, cfg.d)).astype(np.float32)
+    ga = B.stca_backward(dims, dw, db, torch.from_numpy(dZ).to(DEV))
+    mask = np.zeros(inp.total_T, bool)
+    for k in sample:
+        mask[inp.tgt_off[k]:inp.tgt_off[k + 1]] = True
+    gb = B.stca_backward(dims, dw, db, torch.from_numpy(dZ * mask[:, None, None]).to(DEV))
+    torch.cuda.synchronize()
+    sub = SI.make_inputs(cfg, users=sample)
+    ref = G.backward_batch(sub, W, dZ[mask].astype(np.float64))
+    errs = {}
+    hrows = np.concatenate([np.arange(inp.hist_off[k], inp.hist_off[k + 1]) for k in sample])
+    trows = np.nonzero(mask)[0]
+    for tag, g in (("a", ga), ("b", gb)):
+        dX = g.dX[:inp.total_L].cpu().numpy()
+        dxt = g.dxt[:inp.total_T].cpu().numpy()
+        errs[f"{tag}:dX"] = tensor_rel(dX[hrows], ref.dX)
+        errs[f"{tag}:dxt"] = tensor_rel(dxt[trows], ref.dxt)
+        if tag == "b":
+            other = np.ones(inp.total_L, bool)
+            other[hrows] = False
+            assert not np.any(dX[other]) and not np.any(dxt[~mask])
+    for name in SLOTS:
+        for i, t in enumerate(gb.slot(name)):
+            if t is not None:
+                errs[f"{name}[{i}]"] = tensor_rel(t.cpu().numpy(), getattr(ref, name)[i])
+    worst = max(errs, key=errs.get)
+    print(f"  users={inp.n_users} L={inp.total_L} T={inp.total_T} sampled={sample} (L={L[sample].tolist()}) "
+          f"worst {worst}={errs[worst]:.3e}", flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= 1e-3}
+    assert not bad, bad
