@@ -99,8 +99,176 @@ static hipError_t gemm_t(hipStream_t s, const GemmArgs &g) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// The same product on fp32 matrix cores (v_mfma_f32_32x32x2_f32: exact fp32 products, fp32
+// accumulation), for fp32 outputs.  128 x 128 output tile per workgroup, four waves of 64 x 64
+// (2 x 2 MFMA blocks of 32 x 32), k in steps of 16 through double-buffered LDS tiles stored
+// k-contiguous ([row][k], rows padded to 20 floats so the 16-byte fragment reads of 8 lanes fall in
+// distinct banks).  Within a step, lane group g = lane / 32 of MFMA j covers k = 8 g + j, so a
+// lane's 8 operands of a step are two 16-byte LDS reads.  Operands are read from global memory
+// 4 consecutive elements at a time along their contiguous dimension (rows of A, or of At with
+// TRANS_A; of Bt with TRANS_B, or of B): that dimension's length and leading dimension must be
+// multiples of 4 and the base 16-byte (fp32) or 8-byte (bf16) aligned (see mfma_ok).
+// ------------------------------------------------------------------------------------------
+constexpr int MT = 128, MK = 16, MKP = 20;
+
+template <typename T> struct vec4_of;
+template <> struct vec4_of<float> {
+  __device__ __forceinline__ static f32x4 load(const float *p) { return *(const f32x4 *)p; }
+};
+template <> struct vec4_of<bf16> {
+  __device__ __forceinline__ static f32x4 load(const bf16 *p) {
+    const u32x2 w = *(const u32x2 *)p;
+    return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+                 __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+  }
+};
+
+// One operand tile (128 rows x 16 k) of a K-step, in registers between its global load and its
+// LDS store.  KCONT: the operand's k index is contiguous in memory (element (row, k) at
+// P[row * ld + k]); otherwise rows are (element (row, k) at P[k * ld + row]).
+template <typename T, bool KCONT> struct TileLoader {
+  f32x4 v[2];
+  __device__ __forceinline__ void load(const T *__restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
+                                       int tid) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (KCONT) {
+        const int r = (tid >> 2) + 64 * e, k = k0 + (tid & 3) * 4;
+        v[e] = (r0 + r < rows && k < K) ? vec4_of<T>::load(P + (int64_t)(r0 + r) * ld + k) : f32x4{0, 0, 0, 0};
+      } else {
+        const int k = k0 + (tid >> 5) + 8 * e, r = r0 + (tid & 31) * 4;
+        v[e] = (k < K && r < rows) ? vec4_of<T>::load(P + (int64_t)k * ld + r) : f32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float (*S)[MKP], int tid) const {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (KCONT) {
+        *(f32x4 *)&S[(tid >> 2) + 64 * e][(tid & 3) * 4] = v[e];
+      } else {
+        const int k = (tid >> 5) + 8 * e, r = (tid & 31) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[r + i][k] = v[e][i];
+      }
+    }
+  }
+};
+
+template <typename TA, typename TB, bool TRANS_B, bool TRANS_A>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, const TA *__restrict__ A, int64_t lda,
+                                                        int64_t sA, const TB *__restrict__ B, int64_t ldb,
+                                                        int64_t sB, float *__restrict__ C, int64_t ldc, int64_t sC,
+                                                        float alpha, float beta) {
+  __shared__ __attribute__((aligned(16))) float As[2][MT][MKP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][MT][MKP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * MT, n0 = blockIdx.x * MT;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
+  TileLoader<TA, !TRANS_A> la;  // A (row m, k): k-contiguous unless transposed
+  TileLoader<TB, TRANS_B> lb;   // B as (row n, k): k-contiguous only when transposed
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, g8 = (lane >> 5) * 8, lr = lane & 31;
+  la.load(A, lda, M, K, m0, 0, tid);
+  lb.load(B, ldb, N, K, n0, 0, tid);
+  la.store(As[0], tid);
+  lb.store(Bs[0], tid);
+  __syncthreads();
+  const int steps = (K + MK - 1) / MK;
+  for (int st = 0; st < steps; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < steps;
+    if (more) {
+      la.load(A, lda, M, K, m0, (st + 1) * MK, tid);
+      lb.load(B, ldb, N, K, n0, (st + 1) * MK, tid);
+    }
+    f32x4 a[2][2], b[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a[i][0] = *(const f32x4 *)&As[cur][wm + 32 * i + lr][g8];
+      a[i][1] = *(const f32x4 *)&As[cur][wm + 32 * i + lr][g8 + 4];
+      b[i][0] = *(const f32x4 *)&Bs[cur][wn + 32 * i + lr][g8];
+      b[i][1] = *(const f32x4 *)&Bs[cur][wn + 32 * i + lr][g8 + 4];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[bi][j >> 2][j & 3], b[bj][j >> 2][j & 3],
+                                                             acc[bi][bj], 0, 0, 0);
+    if (more) {
+      la.store(As[cur ^ 1], tid);
+      lb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+  // D layout: lane holds column lr; register e holds row 8 (e >> 2) + 4 (lane >> 5) + (e & 3).
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int col = n0 + wn + 32 * bj + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm + 32 * bi + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row >= M) continue;
+        float *p = C + (int64_t)row * ldc + col;
+        float v = alpha * acc[bi][bj][e];
+        if (beta != 0.f) v += beta * *p;
+        *p = v;
+      }
+    }
+}
+
+template <typename TA, typename TB, bool TB_T, bool TA_T>
+static hipError_t gemm_mfma_t(hipStream_t s, const GemmArgs &g) {
+  dim3 grid((g.N + MT - 1) / MT, (g.M + MT - 1) / MT, g.batch);
+  hipLaunchKernelGGL((gemm_mfma_kernel<TA, TB, TB_T, TA_T>), grid, dim3(256), 0, s, g.M, g.N, g.K, (const TA *)g.A,
+                     g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (float *)g.C, g.ldc, g.sC, g.alpha, g.beta);
+  return hipGetLastError();
+}
+
+// Whether the matrix-core form applies: fp32 output, enough 128 x 128 tiles to fill the chip, and
+// vector-aligned operands along their contiguous dimension.
+static bool mfma_ok(const GemmArgs &g) {
+  if (g.tc_bf16) return false;
+  const int64_t tiles = (int64_t)((g.N + MT - 1) / MT) * ((g.M + MT - 1) / MT) * g.batch;
+  if (tiles < 128 || g.K < 64) return false;
+  auto fits = [](const void *p, bool is_bf16, int64_t ld, int64_t stride, int64_t contiguous_len) {
+    const uintptr_t align = is_bf16 ? 8 : 16;
+    return ((uintptr_t)p % align) == 0 && ld % 4 == 0 && stride % 4 == 0 && contiguous_len % 4 == 0;
+  };
+  const int64_t a_len = g.trans_a ? g.M : g.K, b_len = g.trans_b ? g.K : g.N;
+  return fits(g.A, g.ta_bf16, g.lda, g.sA, a_len) && fits(g.B, g.tb_bf16, g.ldb, g.sB, b_len);
+}
+
+static hipError_t gemm_mfma(hipStream_t s, const GemmArgs &g) {
+#define STCA_MFMA_CASE(TA_, TB_)                                                                       \
+  if (g.trans_a) return g.trans_b ? gemm_mfma_t<TA_, TB_, true, true>(s, g) : gemm_mfma_t<TA_, TB_, false, true>(s, g); \
+  return g.trans_b ? gemm_mfma_t<TA_, TB_, true, false>(s, g) : gemm_mfma_t<TA_, TB_, false, false>(s, g);
+  if (g.ta_bf16 && g.tb_bf16) { STCA_MFMA_CASE(bf16, bf16) }
+  if (g.ta_bf16) { STCA_MFMA_CASE(bf16, float) }
+  if (g.tb_bf16) { STCA_MFMA_CASE(float, bf16) }
+  STCA_MFMA_CASE(float, float)
+#undef STCA_MFMA_CASE
+}
+
 hipError_t gemm(hipStream_t s, const GemmArgs &g) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  if (mfma_ok(g)) return gemm_mfma(s, g);
   // Dispatch on (A type, B type, C type, transB); transposed A only for fp32 outputs.
   if (g.trans_a) {
     if (g.tc_bf16 || g.tb_bf16 || g.trans_b) return hipErrorInvalidValue;

@@ -89,6 +89,9 @@ CASES = [
     ("ragged", dict(n_users=5, length=("lognormal", 150.0, 200.0, 16, 600)), False, True),
     ("ragged", dict(n_users=4, dtype="f32", length=("lognormal", 100.0, 150.0, 16, 400)), True, False),
     ("stress20k", dict(n_users=2, M=2, length=("fixed", 150), targets=("fixed", 3)), False, False),
+    # large enough that the encode products run on the fp32 matrix-core GEMM (>= 128 output tiles)
+    ("ragged", dict(n_users=40, length=("lognormal", 150.0, 200.0, 16, 600)), False, False),
+    ("stress20k", dict(n_users=2, M=2, length=("fixed", 600), targets=("fixed", 3)), False, True),
 ]
 
 
