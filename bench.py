@@ -270,7 +270,9 @@ def bench_backward(a, cfg, dev):
     enc_avg_s = enc_ms / max(enc_n, 1) / 1e3
     enc_flops = 18.0 * r * d * d * L
     achieved = enc_flops / enc_avg_s / 1e12
-    att_layer_ms = phases["bwd_attend"][0] / a.steps / M   # 4d FLOP per pair forward, 8d backward
+    # Per (target, head, history token) pair: the scores twice (statistics, then again for alpha), abar,
+    # dA, du and the two products of dX~, each 2d FLOP.
+    att_layer_ms = phases["bwd_attend"][0] / a.steps / M
     out = {
         "metric": "STCA backward history-tokens/s (gradients of every weight, X and x_t)",
         "value": L * a.steps / dt, "unit": "history-tokens/s", "n_gpus": 1, "steps": a.steps,
@@ -283,9 +285,9 @@ def bench_backward(a, cfg, dev):
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
                      "algorithmic_flops_per_launch": enc_flops, "avg_launch_ms": enc_avg_s * 1e3,
                      "launches": enc_n},
-        "attention_backward": {"kernels": "softmax statistics + query-side + key-side derivative",
-                               "ms_per_layer": att_layer_ms, "pairs_per_layer": pairs, "bound": "alu",
-                               "achieved": 12.0 * d * pairs / (att_layer_ms / 1e3) / 1e12,
+        "attention_backward": {"kernels": "ragged per-user fp32 matrix-core products + softmax/dS row passes",
+                               "ms_per_layer": att_layer_ms, "pairs_per_layer": pairs, "bound": "mfma",
+                               "achieved": 14.0 * d * pairs / (att_layer_ms / 1e3) / 1e12,
                                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"},
         "phase_ms_per_step": {k: v[0] / a.steps for k, v in phases.items() if k.startswith("bwd")},
     }

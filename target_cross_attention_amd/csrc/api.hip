@@ -556,8 +556,17 @@ struct BackwardWs {
   float *dheads = nullptr, *dabar = nullptr, *Dv = nullptr, *du = nullptr, *dP = nullptr;
   float *eA = nullptr, *eG = nullptr, *eH = nullptr, *eY = nullptr, *edY = nullptr, *ePg = nullptr;
   float *parts = nullptr;
+  float *S = nullptr, *S2 = nullptr;  // every user's score matrix (R_u x Lp_u), twice
+  RaggedDesc *desc = nullptr;         // 3 n_users product descriptors
   int64_t rows = 0;         // history rows per encode-backward chunk
 };
+
+// Upper bound on sum_u R_u Lp_u (R_u = m_u h query rows, Lp_u = L_u rounded up to 4):
+// sum_u m_u L_u <= min(max_T total_L, max_L total_T), plus 3 per target for the rounding.
+int64_t score_elems(const stca_dims *dm, const stca_batch *b) {
+  const int64_t ml = std::min(b->max_T * b->total_L, b->max_L * b->total_T);
+  return (int64_t)dm->h * (ml + 3 * b->total_T);
+}
 
 size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, BackwardWs &w) {
   Carver c(base);
@@ -598,6 +607,9 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   w.edY = c.take<float>((size_t)(w.rows * d));
   w.ePg = c.take<float>((size_t)(w.rows * d));
   w.parts = c.take<float>((size_t)kWgradParts * std::max<int64_t>(d * rd, M * d * d));
+  w.S = c.take<float>((size_t)score_elems(dm, b));
+  w.S2 = c.take<float>((size_t)score_elems(dm, b));
+  w.desc = c.take<RaggedDesc>((size_t)std::max(3 * b->n_users, 1));
   return round_up(c.off, 256);
 }
 
@@ -766,6 +778,19 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     if (i >= 1) HIP_TRY(fill_f32(s, (int64_t)(i + 1) * d * d, g->dWC[i], 0.f));
   }
   if (T == 0) return STCA_OK;  // no target, no gradient
+  HIP_TRY(ragged_plan(s, b->n_users, b->hist_off, b->tgt_off, h, d, bw.desc));
+  const int64_t T_rows = b->max_T * h, max_L = b->max_L;  // bounds of the ragged products' sizes
+  auto rg = [](const float *A, const float *B, float *C, float alpha, float beta, bool ta, bool tb) {
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.trans_a = ta;
+    g.trans_b = tb;
+    return g;
+  };
 
   // ---- forward, keeping what the backward needs ----------------------------------------------
   // Per-target steps are timed as STCA_PHASE_BWD_TARGET, the per-history-row ones by their phases.
@@ -818,8 +843,10 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     HIP_TRY(pt.end());
     {
       Phase ph(prof, s, STCA_PHASE_BWD_ATTEND);
-      HIP_TRY(attn_rows_fwd(s, d, h, b->n_users, b->hist_off, b->tgt_off, T, Xt, bw.U[i], sc, bw.abar[i],
-                            bw.lse[i]));
+      HIP_TRY(gemm_ragged(s, rg(bw.U[i], Xt, bw.S, 1.f, 0.f, false, true), bw.desc, b->n_users, T_rows, max_L));
+      HIP_TRY(ragged_rows(s, 0, T * h, h, b->n_users, b->tgt_off, bw.desc, bw.S, nullptr, sc, bw.lse[i], nullptr));
+      HIP_TRY(gemm_ragged(s, rg(bw.S, Xt, bw.abar[i], 1.f, 0.f, false, false), bw.desc + b->n_users, b->n_users,
+                          T_rows, d));
       HIP_TRY(ph.end());
     }
     Phase pt2(prof, s, STCA_PHASE_BWD_TARGET);
@@ -904,12 +931,16 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     HIP_TRY(gemm(s, da));
     HIP_TRY(rowdot(s, T * h, d, bw.dabar, bw.abar[i], bw.Dv));
     HIP_TRY(pt.end());
-    {
+    {  // alpha again (saved lse), dA = dabar X~^T, dS, then du and dX~ (eq. (13))
       Phase ph(prof, s, STCA_PHASE_BWD_ATTEND);
-      HIP_TRY(attn_rows_bwd_query(s, d, h, b->n_users, b->hist_off, b->tgt_off, T, Xt, bw.U[i], bw.dabar,
-                                  bw.lse[i], bw.Dv, sc, bw.du));
-      HIP_TRY(attn_rows_bwd_keys(s, d, h, b->n_users, b->hist_off, b->tgt_off, L, Xt, bw.U[i], bw.dabar,
-                                 bw.lse[i], bw.Dv, sc, bw.dXt));
+      const RaggedDesc *d_s = bw.desc, *d_row = bw.desc + b->n_users, *d_key = bw.desc + 2 * b->n_users;
+      HIP_TRY(gemm_ragged(s, rg(bw.U[i], Xt, bw.S, 1.f, 0.f, false, true), d_s, b->n_users, T_rows, max_L));
+      HIP_TRY(ragged_rows(s, 1, T * h, h, b->n_users, b->tgt_off, d_s, bw.S, nullptr, sc, bw.lse[i], nullptr));
+      HIP_TRY(gemm_ragged(s, rg(bw.dabar, Xt, bw.S2, 1.f, 0.f, false, true), d_s, b->n_users, T_rows, max_L));
+      HIP_TRY(ragged_rows(s, 2, T * h, h, b->n_users, b->tgt_off, d_s, bw.S, bw.S2, sc, nullptr, bw.Dv));
+      HIP_TRY(gemm_ragged(s, rg(bw.S2, Xt, bw.du, sc, 0.f, false, false), d_row, b->n_users, T_rows, d));
+      HIP_TRY(gemm_ragged(s, rg(bw.S, bw.dabar, bw.dXt, 1.f, 0.f, true, false), d_key, b->n_users, max_L, d));
+      HIP_TRY(gemm_ragged(s, rg(bw.S2, bw.U[i], bw.dXt, sc, 1.f, true, false), d_key, b->n_users, max_L, d));
       HIP_TRY(ph.end());
     }
     Phase pt2(prof, s, STCA_PHASE_BWD_TARGET);

@@ -263,11 +263,14 @@ hipError_t copy_rows(hipStream_t s, int64_t rows, int d, const float *x, int64_t
   return hipGetLastError();
 }
 
-// ---- attention over a user's history, fp32 (eq. (13) and its derivative) ---------------------
-// Query rows r = t h + j (target t, head j) with u_r = U[r] (unscaled: the score of history row k
-// is scale * u_r . X~_k, scale = 1/sqrt(d_h)); history rows of target t's user are hist_off[u] ..
-// hist_off[u+1]-1.  Each wave takes up to RW heads of one target (so all its rows share a user);
-// lane l holds features l + 64 e, e < DPL = d / 64.
+// ---- attention over a user's history as ragged products (eq. (13) and its derivative) --------
+// Query rows r = t h + j (target t, head j), u_r = U[r] unscaled (scores are scale * u_r . X~_k with
+// scale = 1/sqrt(d_h)).  User u owns R_u = m_u h query rows and L_u history rows; its score matrix
+// S_u (R_u x Lp_u, Lp_u = L_u rounded up to 4, padding columns kept at zero) sits at element sbase_u
+// of a buffer holding all users' matrices back to back.  Three descriptor shapes per user:
+//   0: S-shape  (R x L, k = d):   S = U X~^T, dA = dabar X~^T          (B transposed)
+//   1: row-shape (R x d, k = L):  abar = alpha X~, du = dS X~
+//   2: key-shape (L x d, k = R):  dX~ = alpha^T dabar + dS^T U          (A transposed)
 
 // Largest u in [0, n) with off[u] <= x (off nondecreasing, off[0] = 0 <= x < off[n]).
 __device__ __forceinline__ int segment_of(const int64_t *__restrict__ off, int n, int64_t x) {
@@ -279,235 +282,102 @@ __device__ __forceinline__ int segment_of(const int64_t *__restrict__ off, int n
   return lo;
 }
 
-template <int DPL>
-__device__ __forceinline__ void load_row(float (&v)[DPL], const float *__restrict__ p, int lane) {
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) v[e] = p[lane + 64 * e];
-}
-
-template <int DPL>
-__device__ __forceinline__ float dot_row(const float (&a)[DPL], const float (&b)[DPL]) {
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) s = fmaf(a[e], b[e], s);
-  return s;
-}
-
-// Softmax statistics and weighted history: abar_r = sum_k alpha_rk X~_k, lse_r = log sum_k e^{s_rk}.
-template <int DPL, int RW>
-__global__ __launch_bounds__(256) void attn_fwd_rows_kernel(int64_t T, int h, int n_users,
-                                                            const int64_t *__restrict__ hist_off,
-                                                            const int64_t *__restrict__ tgt_off,
-                                                            const float *__restrict__ Xt, const float *__restrict__ U,
-                                                            float scale, float *__restrict__ abar,
-                                                            float *__restrict__ lse) {
-  constexpr int d = 64 * DPL;
-  const int lane = threadIdx.x & 63;
-  const int groups = (h + RW - 1) / RW;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t t = gw / groups;
-  if (t >= T) return;
-  const int j0 = (int)(gw % groups) * RW;
-  const int u = segment_of(tgt_off, n_users, t);
-  const int64_t k0 = hist_off[u], k1 = hist_off[u + 1];
-  float q[RW][DPL], acc[RW][DPL], m[RW], l[RW];
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int j = j0 + rr < h ? j0 + rr : h - 1;
-    load_row<DPL>(q[rr], U + (t * h + j) * d, lane);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[rr][e] = 0.f;
-    m[rr] = -INFINITY;
-    l[rr] = 0.f;
-  }
-  for (int64_t k = k0; k < k1; ++k) {
-    float x[DPL];
-    load_row<DPL>(x, Xt + k * d, lane);
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      const float s = scale * wave_sum(dot_row<DPL>(q[rr], x));
-      const float mn = fmaxf(m[rr], s);
-      const float c = expf(m[rr] - mn), p = expf(s - mn);
-      l[rr] = l[rr] * c + p;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[rr][e] = fmaf(acc[rr][e], c, p * x[e]);
-      m[rr] = mn;
+// One workgroup: users in blocks of 1024 with a block-wide prefix sum of R_u Lp_u.
+__global__ __launch_bounds__(1024) void ragged_plan_kernel(int n_users, const int64_t *__restrict__ hoff,
+                                                           const int64_t *__restrict__ toff, int h, int d,
+                                                           RaggedDesc *__restrict__ descs) {
+  __shared__ int64_t sc[1024];
+  const int tid = threadIdx.x;
+  int64_t carry = 0;
+  for (int base = 0; base < n_users; base += 1024) {
+    const int u = base + tid;
+    int64_t R = 0, L = 0, Lp = 0, L0 = 0, T0 = 0;
+    if (u < n_users) {
+      L0 = hoff[u];
+      T0 = toff[u];
+      L = hoff[u + 1] - L0;
+      R = (toff[u + 1] - T0) * h;
+      Lp = (L + 3) & ~(int64_t)3;
     }
-  }
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    if (j0 + rr >= h) continue;
-    const int64_t r = t * h + j0 + rr;
-    const float inv = 1.0f / l[rr];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) abar[r * d + lane + 64 * e] = acc[rr][e] * inv;
-    if (lane == 0) lse[r] = m[rr] + logf(l[rr]);
-  }
-}
-
-// du_r = scale sum_k dS_rk X~_k with alpha_rk = exp(scale u_r . X~_k - lse_r),
-// dS_rk = alpha_rk (dabar_r . X~_k - D_r), D_r = dabar_r . abar_r.
-template <int DPL, int RW>
-__global__ __launch_bounds__(256) void attn_bwd_query_kernel(int64_t T, int h, int n_users,
-                                                             const int64_t *__restrict__ hist_off,
-                                                             const int64_t *__restrict__ tgt_off,
-                                                             const float *__restrict__ Xt, const float *__restrict__ U,
-                                                             const float *__restrict__ dabar,
-                                                             const float *__restrict__ lse,
-                                                             const float *__restrict__ D, float scale,
-                                                             float *__restrict__ du) {
-  constexpr int d = 64 * DPL;
-  const int lane = threadIdx.x & 63;
-  const int groups = (h + RW - 1) / RW;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t t = gw / groups;
-  if (t >= T) return;
-  const int j0 = (int)(gw % groups) * RW;
-  const int u = segment_of(tgt_off, n_users, t);
-  const int64_t k0 = hist_off[u], k1 = hist_off[u + 1];
-  float q[RW][DPL], g[RW][DPL], acc[RW][DPL], ls[RW], Dr[RW];
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    const int j = j0 + rr < h ? j0 + rr : h - 1;
-    const int64_t r = t * h + j;
-    load_row<DPL>(q[rr], U + r * d, lane);
-    load_row<DPL>(g[rr], dabar + r * d, lane);
-    ls[rr] = lse[r];
-    Dr[rr] = D[r];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[rr][e] = 0.f;
-  }
-  for (int64_t k = k0; k < k1; ++k) {
-    float x[DPL];
-    load_row<DPL>(x, Xt + k * d, lane);
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-      const float a = wave_sum(dot_row<DPL>(q[rr], x)), b = wave_sum(dot_row<DPL>(g[rr], x));
-      const float ds = expf(scale * a - ls[rr]) * (b - Dr[rr]);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[rr][e] = fmaf(ds, x[e], acc[rr][e]);
+    const int64_t cnt = R * Lp;
+    sc[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int64_t a = tid >= off ? sc[tid - off] : 0;
+      __syncthreads();
+      sc[tid] += a;
+      __syncthreads();
     }
-  }
-#pragma unroll
-  for (int rr = 0; rr < RW; ++rr) {
-    if (j0 + rr >= h) continue;
-    const int64_t r = t * h + j0 + rr;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) du[r * d + lane + 64 * e] = scale * acc[rr][e];
-  }
-}
-
-// dX~_k = sum over the (t, j) rows of k's user of alpha_rk dabar_r + scale dS_rk u_r.
-// A wave takes RK consecutive history rows (which may belong to up to RK users).
-template <int DPL, int RK>
-__global__ __launch_bounds__(256) void attn_bwd_keys_kernel(int64_t L, int h, int n_users,
-                                                            const int64_t *__restrict__ hist_off,
-                                                            const int64_t *__restrict__ tgt_off,
-                                                            const float *__restrict__ Xt, const float *__restrict__ U,
-                                                            const float *__restrict__ dabar,
-                                                            const float *__restrict__ lse,
-                                                            const float *__restrict__ D, float scale,
-                                                            float *__restrict__ dXt) {
-  constexpr int d = 64 * DPL;
-  const int lane = threadIdx.x & 63;
-  const int64_t k0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RK;
-  if (k0 >= L) return;
-  float x[RK][DPL], acc[RK][DPL];
-  int usr[RK];
-#pragma unroll
-  for (int kk = 0; kk < RK; ++kk) {
-    const int64_t k = k0 + kk < L ? k0 + kk : L - 1;
-    load_row<DPL>(x[kk], Xt + k * d, lane);
-    usr[kk] = k0 + kk < L ? segment_of(hist_off, n_users, k) : -1;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[kk][e] = 0.f;
-  }
-  for (int first = 0; first < RK;) {  // the rows of one user at a time (users grow with k)
-    const int u = usr[first];
-    if (u < 0) break;
-    int last = first;
-    while (last + 1 < RK && usr[last + 1] == u) ++last;
-    const int64_t r0 = tgt_off[u] * h, r1 = tgt_off[u + 1] * h;
-    for (int64_t r = r0; r < r1; ++r) {
-      float q[DPL], g[DPL];
-      load_row<DPL>(q, U + r * d, lane);
-      load_row<DPL>(g, dabar + r * d, lane);
-      const float ls = lse[r], Dr = D[r];
-#pragma unroll
-      for (int kk = 0; kk < RK; ++kk) {
-        if (kk < first || kk > last) continue;
-        const float a = wave_sum(dot_row<DPL>(q, x[kk])), b = wave_sum(dot_row<DPL>(g, x[kk]));
-        const float al = expf(scale * a - ls), ds = scale * al * (b - Dr);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[kk][e] = fmaf(al, g[e], fmaf(ds, q[e], acc[kk][e]));
-      }
+    if (u < n_users) {
+      const int64_t sbase = carry + sc[tid] - cnt, qrow = T0 * h * d, hrow = L0 * d;
+      descs[u] = RaggedDesc{(int32_t)R, (int32_t)L, d, 0, qrow, d, hrow, d, sbase, Lp};
+      descs[n_users + u] = RaggedDesc{(int32_t)R, d, (int32_t)L, 0, sbase, Lp, hrow, d, qrow, d};
+      descs[2 * n_users + u] = RaggedDesc{(int32_t)L, d, (int32_t)R, 0, sbase, Lp, qrow, d, hrow, d};
     }
-    first = last + 1;
-  }
-#pragma unroll
-  for (int kk = 0; kk < RK; ++kk) {
-    if (k0 + kk >= L) continue;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) dXt[(k0 + kk) * d + lane + 64 * e] = acc[kk][e];
+    carry += sc[1023];
+    __syncthreads();
   }
 }
 
-template <int DPL>
-static hipError_t attn_bwd_launch(hipStream_t s, int which, int64_t T, int64_t L, int h, int n_users,
-                                  const int64_t *hist_off, const int64_t *tgt_off, const float *Xt, const float *U,
-                                  const float *dabar, float *abar, float *lse, const float *D, float scale,
-                                  float *out) {
-  constexpr int RW = DPL >= 8 ? 2 : 4, RK = 4;
-  if (which == 2) {
-    const int64_t waves = (L + RK - 1) / RK;
-    if (waves == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_bwd_keys_kernel<DPL, RK>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, L, h,
-                       n_users, hist_off, tgt_off, Xt, U, dabar, lse, D, scale, out);
-    return hipGetLastError();
-  }
-  const int64_t waves = T * ((h + RW - 1) / RW);
-  if (waves == 0) return hipSuccess;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (which == 0)
-    hipLaunchKernelGGL((attn_fwd_rows_kernel<DPL, RW>), grid, dim3(256), 0, s, T, h, n_users, hist_off, tgt_off, Xt,
-                       U, scale, abar, lse);
-  else
-    hipLaunchKernelGGL((attn_bwd_query_kernel<DPL, RW>), grid, dim3(256), 0, s, T, h, n_users, hist_off, tgt_off, Xt,
-                       U, dabar, lse, D, scale, out);
+hipError_t ragged_plan(hipStream_t s, int n_users, const int64_t *hist_off, const int64_t *tgt_off, int h, int d,
+                       RaggedDesc *descs) {
+  if (n_users <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ragged_plan_kernel, dim3(1), dim3(1024), 0, s, n_users, hist_off, tgt_off, h, d, descs);
   return hipGetLastError();
 }
 
-static hipError_t attn_bwd_dispatch(hipStream_t s, int which, int d, int64_t T, int64_t L, int h, int n_users,
-                                    const int64_t *hist_off, const int64_t *tgt_off, const float *Xt, const float *U,
-                                    const float *dabar, float *abar, float *lse, const float *D, float scale,
-                                    float *out) {
-  switch (d) {
-    case 64: return attn_bwd_launch<1>(s, which, T, L, h, n_users, hist_off, tgt_off, Xt, U, dabar, abar, lse, D, scale, out);
-    case 128: return attn_bwd_launch<2>(s, which, T, L, h, n_users, hist_off, tgt_off, Xt, U, dabar, abar, lse, D, scale, out);
-    case 256: return attn_bwd_launch<4>(s, which, T, L, h, n_users, hist_off, tgt_off, Xt, U, dabar, abar, lse, D, scale, out);
-    case 512: return attn_bwd_launch<8>(s, which, T, L, h, n_users, hist_off, tgt_off, Xt, U, dabar, abar, lse, D, scale, out);
-    default: return hipErrorInvalidValue;
+// Per query row (one wave): MODE 0 computes lse_r = log sum_k e^{scale S_rk} and replaces S_r by
+// alpha_r = exp(scale S_r - lse_r); MODE 1 does the replacement with the given lse_r; MODE 2 turns
+// dA_r (in S2) into dS_r = alpha_r (dA_r - D_r).  Padding columns become zero.
+template <int MODE>
+__global__ __launch_bounds__(256) void ragged_rows_kernel(int64_t rows, int h, int n_users,
+                                                          const int64_t *__restrict__ tgt_off,
+                                                          const RaggedDesc *__restrict__ sdesc, float *__restrict__ S,
+                                                          float *__restrict__ S2, float scale, float *__restrict__ lse,
+                                                          const float *__restrict__ D) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int u = segment_of(tgt_off, n_users, r / h);
+  const RaggedDesc dsc = sdesc[u];
+  const int64_t L = dsc.N, Lp = dsc.ldc;
+  const int64_t off = dsc.c_off + (r - tgt_off[u] * h) * Lp;
+  float *row = S + off;
+  if (MODE == 2) {
+    float *drow = S2 + off;
+    const float Dr = D[r];
+    for (int64_t k = lane; k < Lp; k += 64) drow[k] = k < L ? row[k] * (drow[k] - Dr) : 0.f;
+    return;
   }
+  float l;
+  if (MODE == 0) {
+    float mx = -INFINITY;
+    for (int64_t k = lane; k < L; k += 64) mx = fmaxf(mx, scale * row[k]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int64_t k = lane; k < L; k += 64) sum += expf(scale * row[k] - mx);
+    l = mx + logf(wave_sum(sum));
+    if (lane == 0) lse[r] = l;
+  } else {
+    l = lse[r];
+  }
+  for (int64_t k = lane; k < Lp; k += 64) row[k] = k < L ? expf(scale * row[k] - l) : 0.f;
 }
 
-hipError_t attn_rows_fwd(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off, const int64_t *tgt_off,
-                         int64_t T, const float *Xt, const float *U, float scale, float *abar, float *lse) {
-  return attn_bwd_dispatch(s, 0, d, T, 0, h, n_users, hist_off, tgt_off, Xt, U, nullptr, abar, lse, nullptr, scale,
-                           nullptr);
-}
-
-hipError_t attn_rows_bwd_query(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off,
-                               const int64_t *tgt_off, int64_t T, const float *Xt, const float *U,
-                               const float *dabar, const float *lse, const float *D, float scale, float *du) {
-  return attn_bwd_dispatch(s, 1, d, T, 0, h, n_users, hist_off, tgt_off, Xt, U, dabar, nullptr, (float *)lse, D,
-                           scale, du);
-}
-
-hipError_t attn_rows_bwd_keys(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off,
-                              const int64_t *tgt_off, int64_t L, const float *Xt, const float *U,
-                              const float *dabar, const float *lse, const float *D, float scale, float *dXt) {
-  return attn_bwd_dispatch(s, 2, d, 0, L, h, n_users, hist_off, tgt_off, Xt, U, dabar, nullptr, (float *)lse, D,
-                           scale, dXt);
+hipError_t ragged_rows(hipStream_t s, int mode, int64_t rows, int h, int n_users, const int64_t *tgt_off,
+                       const RaggedDesc *sdesc, float *S, float *S2, float scale, float *lse, const float *D) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (mode == 0)
+    hipLaunchKernelGGL(ragged_rows_kernel<0>, grid, dim3(256), 0, s, rows, h, n_users, tgt_off, sdesc, S, S2, scale,
+                       lse, D);
+  else if (mode == 1)
+    hipLaunchKernelGGL(ragged_rows_kernel<1>, grid, dim3(256), 0, s, rows, h, n_users, tgt_off, sdesc, S, S2, scale,
+                       lse, D);
+  else
+    hipLaunchKernelGGL(ragged_rows_kernel<2>, grid, dim3(256), 0, s, rows, h, n_users, tgt_off, sdesc, S, S2, scale,
+                       lse, D);
+  return hipGetLastError();
 }
 
 }  // namespace stca

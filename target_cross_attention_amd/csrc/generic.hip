@@ -156,18 +156,35 @@ template <typename T, bool KCONT> struct TileLoader {
   }
 };
 
-template <typename TA, typename TB, bool TRANS_B, bool TRANS_A>
+// RAGGED: blockIdx.z picks a descriptor (one per user of a ragged batch) that gives the product's
+// sizes, element offsets and leading dimensions; blocks outside that user's tiles return at once.
+template <typename TA, typename TB, bool TRANS_B, bool TRANS_A, bool RAGGED>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, const TA *__restrict__ A, int64_t lda,
                                                         int64_t sA, const TB *__restrict__ B, int64_t ldb,
                                                         int64_t sB, float *__restrict__ C, int64_t ldc, int64_t sC,
-                                                        float alpha, float beta) {
+                                                        float alpha, float beta,
+                                                        const RaggedDesc *__restrict__ descs) {
   __shared__ __attribute__((aligned(16))) float As[2][MT][MKP];
   __shared__ __attribute__((aligned(16))) float Bs[2][MT][MKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * MT, n0 = blockIdx.x * MT;
-  A += (int64_t)blockIdx.z * sA;
-  B += (int64_t)blockIdx.z * sB;
-  C += (int64_t)blockIdx.z * sC;
+  if constexpr (RAGGED) {
+    const RaggedDesc dsc = descs[blockIdx.z];
+    M = dsc.M;
+    N = dsc.N;
+    K = dsc.K;
+    if (m0 >= M || n0 >= N) return;
+    A += dsc.a_off;
+    lda = dsc.lda;
+    B += dsc.b_off;
+    ldb = dsc.ldb;
+    C += dsc.c_off;
+    ldc = dsc.ldc;
+  } else {
+    A += (int64_t)blockIdx.z * sA;
+    B += (int64_t)blockIdx.z * sB;
+    C += (int64_t)blockIdx.z * sC;
+  }
   TileLoader<TA, !TRANS_A> la;  // A (row m, k): k-contiguous unless transposed
   TileLoader<TB, TRANS_B> lb;   // B as (row n, k): k-contiguous only when transposed
   f32x16 acc[2][2];
@@ -236,9 +253,40 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, con
 template <typename TA, typename TB, bool TB_T, bool TA_T>
 static hipError_t gemm_mfma_t(hipStream_t s, const GemmArgs &g) {
   dim3 grid((g.N + MT - 1) / MT, (g.M + MT - 1) / MT, g.batch);
-  hipLaunchKernelGGL((gemm_mfma_kernel<TA, TB, TB_T, TA_T>), grid, dim3(256), 0, s, g.M, g.N, g.K, (const TA *)g.A,
-                     g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (float *)g.C, g.ldc, g.sC, g.alpha, g.beta);
+  hipLaunchKernelGGL((gemm_mfma_kernel<TA, TB, TB_T, TA_T, false>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                     (const TA *)g.A, g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (float *)g.C, g.ldc, g.sC, g.alpha,
+                     g.beta, nullptr);
   return hipGetLastError();
+}
+
+// Ragged fp32 products: g gives the operand types, transposes, base pointers, alpha and beta; the
+// sizes, offsets and leading dimensions of product z come from descs[z] (z < n), every one at most
+// max_m x max_n.  Operands are fp32; every leading dimension and offset a multiple of 4 elements and
+// the bases 16-byte aligned, as the vector loads need.
+hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs, int n, int64_t max_m,
+                       int64_t max_n) {
+  if (n <= 0 || max_m <= 0 || max_n <= 0) return hipSuccess;
+  if (g.ta_bf16 || g.tb_bf16 || g.tc_bf16 || (g.trans_a && g.trans_b)) return hipErrorInvalidValue;
+  if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return hipErrorInvalidValue;
+  const int64_t gx = (max_n + MT - 1) / MT, gy = (max_m + MT - 1) / MT;
+  if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
+  for (int z0 = 0; z0 < n; z0 += 65535) {  // grid z holds at most 65535 products
+    dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)(n - z0 < 65535 ? n - z0 : 65535));
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, 0, 0, 0, (const float *)g.A, (int64_t)0, (int64_t)0,
+                         (const float *)g.B, (int64_t)0, (int64_t)0, (float *)g.C, (int64_t)0, (int64_t)0, g.alpha,
+                         g.beta, descs + z0);
+    };
+    if (g.trans_a)
+      go(gemm_mfma_kernel<float, float, false, true, true>);
+    else if (g.trans_b)
+      go(gemm_mfma_kernel<float, float, true, false, true>);
+    else
+      go(gemm_mfma_kernel<float, float, false, false, true>);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Whether the matrix-core form applies: fp32 output, enough 128 x 128 tiles to fill the chip, and

@@ -21,6 +21,13 @@ struct GemmArgs {
   float alpha = 1.f, beta = 0.f;
 };
 hipError_t gemm(hipStream_t s, const GemmArgs &g);
+// One product of a ragged batch: sizes, element offsets from the base pointers, leading dimensions.
+struct RaggedDesc {
+  int32_t M, N, K, pad;
+  int64_t a_off, lda, b_off, ldb, c_off, ldc;
+};
+hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs, int n, int64_t max_m,
+                       int64_t max_n);
 hipError_t swiglu_gate_inplace(hipStream_t s, int64_t n, float *A, const float *G);
 hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, int64_t ldy, void *out,
                           int64_t ldo, bool out_bf16, const float *gamma, const float *beta, float eps);
@@ -102,14 +109,12 @@ hipError_t ln_bwd(hipStream_t s, int64_t rows, int d, const float *dout, int64_t
                   const float *gamma, float eps, float *dY, float *Pg);
 hipError_t rowdot(hipStream_t s, int64_t rows, int d, const float *A, const float *B, float *out);
 hipError_t copy_rows(hipStream_t s, int64_t rows, int d, const float *x, int64_t ldx, float *y, int64_t ldy);
-// Attention of the (target, head) rows over their user's history, fp32; U unscaled, scale 1/sqrt(d_h).
-hipError_t attn_rows_fwd(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off, const int64_t *tgt_off,
-                         int64_t T, const float *Xt, const float *U, float scale, float *abar, float *lse);
-hipError_t attn_rows_bwd_query(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off,
-                               const int64_t *tgt_off, int64_t T, const float *Xt, const float *U,
-                               const float *dabar, const float *lse, const float *D, float scale, float *du);
-hipError_t attn_rows_bwd_keys(hipStream_t s, int d, int h, int n_users, const int64_t *hist_off,
-                              const int64_t *tgt_off, int64_t L, const float *Xt, const float *U,
-                              const float *dabar, const float *lse, const float *D, float scale, float *dXt);
+// Attention over each user's history as ragged products (see backward.hip): descriptors of the three
+// product shapes (3 n_users entries), and the row passes over the users' score matrices
+// (mode 0: softmax with lse out, 1: softmax with lse in, 2: dS = alpha (dA - D) into S2).
+hipError_t ragged_plan(hipStream_t s, int n_users, const int64_t *hist_off, const int64_t *tgt_off, int h, int d,
+                       RaggedDesc *descs);
+hipError_t ragged_rows(hipStream_t s, int mode, int64_t rows, int h, int n_users, const int64_t *tgt_off,
+                       const RaggedDesc *sdesc, float *S, float *S2, float scale, float *lse, const float *D);
 
 }  // namespace stca
