@@ -541,8 +541,8 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
 }
 
 // ---- backward (gradients of eqs. (2)-(8)) ------------------------------------------------------
-constexpr int kWgradParts = 16;    // split-K blocks of one weight gradient
-constexpr int kColsumParts = 128;  // row blocks of one column sum
+constexpr int kWgradParts = 64;    // split-K blocks of one weight gradient
+constexpr int kLnBlocks = 256;     // row blocks of the LayerNorm derivative (partial column sums)
 
 struct BackwardWs {
   float *Xt = nullptr;      // M x total_L x d: encoded history of every layer (fp32)
@@ -552,9 +552,9 @@ struct BackwardWs {
   float *qin[STCA_MAX_M] = {}, *qA[STCA_MAX_M] = {}, *qG[STCA_MAX_M] = {}, *qY[STCA_MAX_M] = {};
   float *q[STCA_MAX_M] = {}, *P[STCA_MAX_M] = {}, *U[STCA_MAX_M] = {}, *lse[STCA_MAX_M] = {};
   float *abar[STCA_MAX_M] = {}, *heads[STCA_MAX_M] = {};
-  float *dq = nullptr, *qH = nullptr, *qdA = nullptr, *qdG = nullptr, *qdY = nullptr, *qPg = nullptr, *dc = nullptr;
+  float *dq = nullptr, *qH = nullptr, *qdA = nullptr, *qdG = nullptr, *qdY = nullptr, *dc = nullptr;
   float *dheads = nullptr, *dabar = nullptr, *Dv = nullptr, *du = nullptr, *dP = nullptr;
-  float *eA = nullptr, *eG = nullptr, *eH = nullptr, *eY = nullptr, *edY = nullptr, *ePg = nullptr;
+  float *eA = nullptr, *eG = nullptr, *eH = nullptr, *eY = nullptr, *edY = nullptr;
   float *parts = nullptr;
   float *S = nullptr, *S2 = nullptr;  // every user's score matrix (R_u x Lp_u), twice
   RaggedDesc *desc = nullptr;         // 3 n_users product descriptors
@@ -592,7 +592,6 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   w.qdA = c.take<float>((size_t)(T * rd));
   w.qdG = c.take<float>((size_t)(T * rd));
   w.qdY = c.take<float>((size_t)(T * d));
-  w.qPg = c.take<float>((size_t)(T * d));
   w.dc = c.take<float>((size_t)(T * d));
   w.dheads = c.take<float>((size_t)(T * d));
   w.dabar = c.take<float>((size_t)(T * h * d));
@@ -605,7 +604,6 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   w.eH = c.take<float>((size_t)(w.rows * rd));
   w.eY = c.take<float>((size_t)(w.rows * d));
   w.edY = c.take<float>((size_t)(w.rows * d));
-  w.ePg = c.take<float>((size_t)(w.rows * d));
   w.parts = c.take<float>((size_t)kWgradParts * std::max<int64_t>(d * rd, M * d * d));
   w.S = c.take<float>((size_t)score_elems(dm, b));
   w.S2 = c.take<float>((size_t)score_elems(dm, b));
@@ -689,15 +687,13 @@ int ffn_saved(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t n, 
 // dx (n x d) written (or added, when accumulate) through the products dA W_u^T + dG W_v^T.
 int ffn_backward(hipStream_t s, const stca_dims *dm, const stca_ffn *f, const stca_ffn_grad &g, bool with_ln,
                  int64_t n, const void *x, bool x_bf16, const float *A, const float *G, float *H, const float *Y,
-                 const float *dout, float *dY, float *Pg, float *dx, bool accumulate, float *parts) {
+                 const float *dout, float *dY, float *dx, bool accumulate, float *parts) {
   const int d = dm->d, rd = dm->r * dm->d;
   const bool wb = dm->dtype == STCA_BF16;
   int st;
   const float *dy = dout;
   if (with_ln) {
-    HIP_TRY(ln_bwd(s, n, d, dout, d, Y, d, f->gamma, dm->ln_eps, dY, Pg));
-    HIP_TRY(colsum(s, n, d, Pg, d, parts, kColsumParts, g.dgamma));
-    HIP_TRY(colsum(s, n, d, dout, d, parts, kColsumParts, g.dbeta));
+    HIP_TRY(ln_bwd(s, n, d, dout, d, Y, d, f->gamma, dm->ln_eps, dY, g.dgamma, g.dbeta, parts, kLnBlocks));
     dy = dY;
   }
   if ((st = wgrad(s, rd, d, n, H, rd, false, dy, d, g.dWo, d, parts)) != STCA_OK) return st;
@@ -884,7 +880,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     HIP_TRY(swiglu_fwd(s, T * rd, bw.qA[i], bw.qG[i], bw.qH));
     float *dx = i == 0 ? g->dxt : bw.dc;
     if ((st2 = ffn_backward(s, dm, &f, g->query[i], with_ln, T, qffn_in(i), i == 0 && bf, bw.qA[i], bw.qG[i], bw.qH,
-                            bw.qY[i], bw.dq, bw.qdY, bw.qPg, dx, i == 0, bw.parts)) != STCA_OK)
+                            bw.qY[i], bw.dq, bw.qdY, dx, i == 0, bw.parts)) != STCA_OK)
       return st2;
     if (i == 0) return STCA_OK;
     // c = [o(1) .. o(i) || x_t] W_C(i): gradients of W_C, of every earlier o and of x_t.
@@ -975,7 +971,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
       const void *Xc = (const char *)X + (size_t)r0 * d * xes;
       if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, bw.eA, bw.eG, bw.eH, bw.eY)) != STCA_OK) return st;
       if ((st = ffn_backward(s, dm, &w->hist[i], g->hist[i], true, n, Xc, bf, bw.eA, bw.eG, bw.eH, bw.eY,
-                             bw.dXt + (size_t)r0 * d, bw.edY, bw.ePg, g->dX ? g->dX + (size_t)r0 * d : nullptr, true,
+                             bw.dXt + (size_t)r0 * d, bw.edY, g->dX ? g->dX + (size_t)r0 * d : nullptr, true,
                              bw.parts)) != STCA_OK)
         return st;
     }

@@ -52,32 +52,6 @@ hipError_t sum_parts(hipStream_t s, int64_t n, int nparts, const float *parts, f
   return sum_parts2d(s, 1, (int)n, nparts, parts, out, n, accumulate);
 }
 
-// Column sums in two fixed-order stages: parts[b][c] = sum of rows b*rows_per .. of column c.
-__global__ __launch_bounds__(256) void colsum_parts_kernel(int64_t rows, int cols, const float *__restrict__ A,
-                                                           int64_t lda, int64_t rows_per, float *__restrict__ parts) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
-  const int64_t r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
-  float acc = 0.f;
-  for (int64_t r = r0; r < r1; ++r) acc += A[r * lda + c];
-  parts[(int64_t)blockIdx.y * cols + c] = acc;
-}
-
-hipError_t colsum(hipStream_t s, int64_t rows, int cols, const float *A, int64_t lda, float *parts, int max_parts,
-                  float *out) {
-  if (rows <= 0) return hipSuccess;
-  int nparts = (int)((rows + 255) / 256);
-  if (nparts > max_parts) nparts = max_parts;
-  const int64_t per = (rows + nparts - 1) / nparts;
-  nparts = (int)((rows + per - 1) / per);
-  hipLaunchKernelGGL(colsum_parts_kernel, dim3((unsigned)((cols + 255) / 256), (unsigned)nparts), dim3(256), 0, s,
-                     rows, cols, A, lda, per, parts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return sum_parts(s, cols, nparts, parts, out, true);
-}
-
 // ---- SwiGLU: H = A * G * sigmoid(G) and its derivative ----------------------------------------
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(int64_t n, const float *__restrict__ A,
                                                          const float *__restrict__ G, float *__restrict__ H) {
@@ -111,121 +85,91 @@ hipError_t swiglu_bwd(hipStream_t s, int64_t n, const float *dH, const float *A,
   return hipGetLastError();
 }
 
-// ---- LayerNorm derivative: one wave per row (d <= 512) -----------------------------------------
+// ---- LayerNorm derivative (d <= 512) ------------------------------------------------------------
 // From the pre-LN rows Y: xh = (y - mean) rstd; dxh = dout gamma;
-// dY = rstd (dxh - mean(dxh) - xh mean(dxh xh)); Pg = dout xh (rows summed later into dgamma).
-__global__ __launch_bounds__(256) void ln_bwd_kernel(int64_t rows, int d, const float *__restrict__ dout,
+// dY = rstd (dxh - mean(dxh) - xh mean(dxh xh)).  A workgroup takes `per` consecutive rows (its four
+// waves one row at a time) and also sums, per column, dout xh and dout over its rows: those partial
+// sums of dgamma and dbeta go to parts[blk][c] and parts[nblk + blk][c], added later in block order.
+__global__ __launch_bounds__(256) void ln_bwd_kernel(int64_t rows, int d, int64_t per, const float *__restrict__ dout,
                                                      int64_t ldd, const float *__restrict__ Y, int64_t ldy,
                                                      const float *__restrict__ gamma, float eps,
-                                                     float *__restrict__ dY, float *__restrict__ Pg) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float y[8], g[8];
-  float sum = 0.f;
+                                                     float *__restrict__ dY, float *__restrict__ parts) {
+  __shared__ float red[4][2][512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * per, r1 = r0 + per < rows ? r0 + per : rows;
+  float pg[8], pb[8], gm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = lane + 64 * e;
-    y[e] = c < d ? Y[row * ldy + c] : 0.f;
-    sum += y[e];
+    pg[e] = pb[e] = 0.f;
+    gm[e] = c < d ? gamma[c] : 0.f;
   }
-  const float mean = wave_sum(sum) / (float)d;
-  float q = 0.f;
+  for (int64_t row = r0 + wave; row < r1; row += 4) {
+    float y[8], g[8];
+    float sum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = lane + 64 * e;
-    const float t = c < d ? y[e] - mean : 0.f;
-    q += t * t;
-  }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
-  float s1 = 0.f, s2 = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const int c = lane + 64 * e;
+      y[e] = c < d ? Y[row * ldy + c] : 0.f;
+      sum += y[e];
+    }
+    const float mean = wave_sum(sum) / (float)d;
+    float q = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = lane + 64 * e;
-    if (c < d) {
-      const float xh = (y[e] - mean) * rstd, go = dout[row * ldd + c];
-      g[e] = go * gamma[c];
-      s1 += g[e];
-      s2 += g[e] * xh;
-      Pg[row * d + c] = go * xh;
-      y[e] = xh;
-    } else {
-      g[e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      const int c = lane + 64 * e;
+      const float t = c < d ? y[e] - mean : 0.f;
+      q += t * t;
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = lane + 64 * e;
+      if (c < d) {
+        const float xh = (y[e] - mean) * rstd, go = dout[row * ldd + c];
+        g[e] = go * gm[e];
+        s1 += g[e];
+        s2 += g[e] * xh;
+        pg[e] = fmaf(go, xh, pg[e]);
+        pb[e] += go;
+        y[e] = xh;
+      } else {
+        g[e] = 0.f;
+      }
+    }
+    const float m1 = wave_sum(s1) / (float)d, m2 = wave_sum(s2) / (float)d;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = lane + 64 * e;
+      if (c < d) dY[row * d + c] = rstd * (g[e] - m1 - y[e] * m2);
     }
   }
-  const float m1 = wave_sum(s1) / (float)d, m2 = wave_sum(s2) / (float)d;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int c = lane + 64 * e;
-    if (c < d) dY[row * d + c] = rstd * (g[e] - m1 - y[e] * m2);
+    red[wave][0][lane + 64 * e] = pg[e];
+    red[wave][1][lane + 64 * e] = pb[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    parts[(int64_t)blockIdx.x * d + c] = red[0][0][c] + red[1][0][c] + red[2][0][c] + red[3][0][c];
+    parts[(int64_t)(gridDim.x + blockIdx.x) * d + c] = red[0][1][c] + red[1][1][c] + red[2][1][c] + red[3][1][c];
   }
 }
 
 hipError_t ln_bwd(hipStream_t s, int64_t rows, int d, const float *dout, int64_t ldd, const float *Y, int64_t ldy,
-                  const float *gamma, float eps, float *dY, float *Pg) {
+                  const float *gamma, float eps, float *dY, float *dgamma, float *dbeta, float *parts,
+                  int max_blocks) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, d, dout, ldd, Y, ldy,
-                     gamma, eps, dY, Pg);
-  return hipGetLastError();
-}
-
-// ---- attention softmax and its derivative (rows of S are one query row each) -------------------
-// Per row r (one wave): with s = scale * S[r][:], lse = max + log(sum exp(s - max)); S[r][:] is
-// replaced by alpha = exp(s - lse).
-__global__ __launch_bounds__(256) void softmax_rows_kernel(int R, int L, float *__restrict__ S, int64_t lds,
-                                                           float scale, float *__restrict__ lse) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= R) return;
-  float *row = S + (int64_t)r * lds;
-  float mx = -INFINITY;
-  for (int k = lane; k < L; k += 64) mx = fmaxf(mx, scale * row[k]);
-  mx = wave_max(mx);
-  float sum = 0.f;
-  for (int k = lane; k < L; k += 64) sum += expf(scale * row[k] - mx);
-  const float l = mx + logf(wave_sum(sum));
-  for (int k = lane; k < L; k += 64) row[k] = expf(scale * row[k] - l);
-  if (lane == 0) lse[r] = l;
-}
-
-hipError_t softmax_rows(hipStream_t s, int R, int L, float *S, int64_t lds, float scale, float *lse) {
-  if (R <= 0 || L <= 0) return hipSuccess;
-  hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, R, L, S, lds, scale, lse);
-  return hipGetLastError();
-}
-
-// S[r][k] <- exp(scale * S[r][k] - lse[r]) (the saved softmax).
-__global__ __launch_bounds__(256) void softmax_apply_kernel(int R, int L, float *__restrict__ S, int64_t lds,
-                                                            float scale, const float *__restrict__ lse) {
-  const int64_t n = (int64_t)R * L;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int r = (int)(i / L), k = (int)(i % L);
-    S[(int64_t)r * lds + k] = expf(scale * S[(int64_t)r * lds + k] - lse[r]);
-  }
-}
-
-hipError_t softmax_apply(hipStream_t s, int R, int L, float *S, int64_t lds, float scale, const float *lse) {
-  if (R <= 0 || L <= 0) return hipSuccess;
-  hipLaunchKernelGGL(softmax_apply_kernel, dim3(grid_for((int64_t)R * L)), dim3(256), 0, s, R, L, S, lds, scale, lse);
-  return hipGetLastError();
-}
-
-// dS[r][k] = alpha[r][k] (dA[r][k] - D[r]), in place over dA.
-__global__ __launch_bounds__(256) void softmax_bwd_kernel(int R, int L, const float *__restrict__ alpha,
-                                                          float *__restrict__ dA, int64_t ld,
-                                                          const float *__restrict__ D) {
-  const int64_t n = (int64_t)R * L;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int r = (int)(i / L), k = (int)(i % L);
-    const int64_t o = (int64_t)r * ld + k;
-    dA[o] = alpha[o] * (dA[o] - D[r]);
-  }
-}
-
-hipError_t softmax_bwd(hipStream_t s, int R, int L, const float *alpha, float *dA, int64_t ld, const float *D) {
-  if (R <= 0 || L <= 0) return hipSuccess;
-  hipLaunchKernelGGL(softmax_bwd_kernel, dim3(grid_for((int64_t)R * L)), dim3(256), 0, s, R, L, alpha, dA, ld, D);
-  return hipGetLastError();
+  int64_t per = (rows + max_blocks - 1) / max_blocks;
+  per = per < 16 ? 16 : per;
+  const int nblk = (int)((rows + per - 1) / per);
+  hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)nblk), dim3(256), 0, s, rows, d, per, dout, ldd, Y, ldy, gamma, eps,
+                     dY, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = sum_parts(s, d, nblk, parts, dgamma, true)) != hipSuccess) return e;
+  return sum_parts(s, d, nblk, parts + (int64_t)nblk * d, dbeta, true);
 }
 
 // out[r] = sum_c A[r][c] B[r][c] (one wave per row).

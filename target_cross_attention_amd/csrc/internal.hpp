@@ -98,15 +98,15 @@ hipError_t sum_parts(hipStream_t s, int64_t n, int nparts, const float *parts, f
 // The same over a rows x cols block: parts are contiguous blocks, out has row stride ldo.
 hipError_t sum_parts2d(hipStream_t s, int64_t rows, int cols, int nparts, const float *parts, float *out,
                        int64_t ldo, bool accumulate);
-// out[c] += sum over rows of A[r][c], in two fixed-order stages through parts (max_parts x cols).
-hipError_t colsum(hipStream_t s, int64_t rows, int cols, const float *A, int64_t lda, float *parts, int max_parts,
-                  float *out);
 hipError_t swiglu_fwd(hipStream_t s, int64_t n, const float *A, const float *G, float *H);
 hipError_t swiglu_bwd(hipStream_t s, int64_t n, const float *dH, const float *A, const float *G, float *dA,
                       float *dG);
-// dY (rows x d) and Pg = dout * xhat (rows x d) from the pre-LN rows Y; d <= 512.
+// LayerNorm derivative from the pre-LN rows Y (d <= 512): dY (rows x d) written; dgamma and dbeta
+// (d each) accumulated through per-block partial sums in parts (2 max_blocks x d floats), added in
+// block order.
 hipError_t ln_bwd(hipStream_t s, int64_t rows, int d, const float *dout, int64_t ldd, const float *Y, int64_t ldy,
-                  const float *gamma, float eps, float *dY, float *Pg);
+                  const float *gamma, float eps, float *dY, float *dgamma, float *dbeta, float *parts,
+                  int max_blocks);
 hipError_t rowdot(hipStream_t s, int64_t rows, int d, const float *A, const float *B, float *out);
 hipError_t copy_rows(hipStream_t s, int64_t rows, int d, const float *x, int64_t ldx, float *y, int64_t ldy);
 // Attention over each user's history as ragged products (see backward.hip): descriptors of the three
