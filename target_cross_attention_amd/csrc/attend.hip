@@ -8,9 +8,9 @@
 // the request-level-batching reuse.
 //
 // Work item = (user, chunk of the history, group of up to 128 query rows).  A workgroup streams
-// its chunk through LDS in 32-token tiles (direct global->LDS loads, double-buffered); each of
-// its 4 waves owns 32 query rows and keeps, per row, a running max, a running sum and the
-// fp32 accumulator of alpha X~ (online softmax).  A user with one chunk is finalised in place;
+// its chunk through LDS in 32-token tiles (fetched into registers three tiles ahead, written into a
+// 3-slot LDS ring); each of its 4 waves owns 32 query rows and keeps, per row, a running max, a
+// running sum and the fp32 accumulator of alpha X~ (online softmax).  A user with one chunk is finalised in place;
 // otherwise the partial (max, sum, accumulator) triples are merged by attend_combine.
 #include <math.h>
 
