@@ -330,8 +330,8 @@ def cpu_baseline_backward(cfg, W, target_s: float = 12.0, max_users: int = 64):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense10k")
     ap.add_argument("--users", type=int, default=0, help="override the number of users (0 = workload's)")
     ap.add_argument("--attn-chunk", type=int, default=0)
@@ -402,11 +402,15 @@ def main():
     prof = B.Profiler()
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(a.steps):
+    ev[0].record(stream)
+    for k in range(a.steps):
         B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=stream, profiler=prof)
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_ms = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(a.steps))
     phases = prof.read()
     prof.close()
     assert np.isfinite(Z.sum().item()), "non-finite output"
@@ -457,6 +461,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": step_ms[len(step_ms) // 2],
+        "ms_per_step_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -85,6 +85,21 @@ hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_
   return hipGetLastError();
 }
 
+// Work item of this workgroup.  Workgroups are dealt to the chip's 8 XCDs round-robin by index, and
+// each XCD has its own L2; item ranges are therefore handed out per XCD (XCD x = blockIdx mod 8 takes
+// the x-th eighth of the list, in order), so the row groups of one user, which stream the same
+// history chunk, run on one XCD and share its L2.  Returns false for workgroups with no item.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool my_item(const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items,
+                                        WorkItem &it) {
+  const int n = *n_items, b = (int)blockIdx.x;
+  const int x = b % kXcds, j = b / kXcds, q = n / kXcds, rem = n % kXcds;
+  const int cnt = q + (x < rem ? 1 : 0), base = x * q + (x < rem ? x : rem);
+  if (j >= cnt) return false;
+  it = items[base + j];
+  return true;
+}
+
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16 for both contractions).
 //   scores  S^T[tok x row] = X~_tile[tok x d] U^T[d x row]      (A from LDS, B = U in registers)
@@ -139,8 +154,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   static_assert(INSTR % 4 == 0, "tile loads split evenly over 4 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
 
-  if ((int)blockIdx.x >= *n_items) return;
-  const WorkItem it = items[blockIdx.x];
+  WorkItem it;
+  if (!my_item(items, n_items, it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, gl = lane >> 5;
   const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
@@ -504,8 +519,8 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
     const float *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
     float *__restrict__ part_ms, const int64_t *__restrict__ part_base) {
   constexpr int E = D / 64;
-  if ((int)blockIdx.x >= *n_items) return;
-  const WorkItem it = items[blockIdx.x];
+  WorkItem it;
+  if (!my_item(items, n_items, it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
   const int64_t t0 = L0 + (int64_t)it.chunk * chunk;
