@@ -1,7 +1,8 @@
-// Plain fp32-accumulating kernels: a tiled GEMM, the SwiGLU gate, row LayerNorm.
-// They carry the fp32 debug path and the small per-target projections of the bf16 path
-// (eqs. (3), (6), (7) and the u-projection of eq. (13)), whose work is a few d x d
-// products per target, negligible next to the per-history-token work.
+// fp32-accumulating kernels: a tiled GEMM in two forms (vector ALU; fp32 matrix cores, also for
+// ragged per-user batches), the SwiGLU gate, row LayerNorm, bf16 conversion.  They carry the fp32
+// debug path, the small per-target projections of the bf16 path (eqs. (3), (6), (7) and the
+// u-projection of eq. (13), a few d x d products per target, negligible next to the
+// per-history-token work) and every product of the backward pass.
 #include "device_common.hpp"
 #include "internal.hpp"
 
