@@ -147,12 +147,16 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // into the registers it leaves.  (No direct-to-LDS loads: with one in flight the compiler
   // makes every transposed LDS read wait for all outstanding loads, serialising the pipeline.)
   constexpr int NSL = 3;
-  // At d = 512 a wave keeps half of the output features: two waves share a 32-row block
-  // (both compute its scores), so U and the accumulators fit in one wave's registers.
+  // At d = 512 a wave keeps half of the output features: two waves (wave, wave ^ 1) share a
+  // 32-row block, each computes the scores over its half of d, and the pair adds the two partial
+  // score tiles through LDS; U and the accumulators then fit in one wave's registers.
   constexpr int FH = attn_feature_halves(D);
   constexpr int NOBW = NOB / FH;                  // output blocks per wave
+  constexpr int NKW = NKS / FH;                   // score k-steps per wave
   static_assert(INSTR % 4 == 0, "tile loads split evenly over 4 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
+  // Partial score tiles of the pairs (FH = 2): [tile parity][wave][register quad][lane].
+  __shared__ f32x4 exch[FH > 1 ? 2 : 1][FH > 1 ? 4 : 1][4][64];
 
   WorkItem it;
   if (!my_item(items, n_items, it)) return;
@@ -171,12 +175,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   const bool row_ok = myrow < R;
   const int ntiles = (int)((t1 - t0 + 31) / 32);
 
-  // U rows as B operands (loaded first so that the tile loads below are the youngest in flight).
-  bf16x8 ub[NKS];
+  // U rows as B operands (loaded first so that the tile loads below are the youngest in flight):
+  // this wave's k-steps fh NKW .. fh NKW + NKW - 1 of the score reduction.
+  bf16x8 ub[NKW];
   {
-    const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + 8 * gl;
+    const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + 8 * gl + 16 * NKW * fh;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKW; ++ks) {
       if (row_ok)
         ub[ks] = *reinterpret_cast<const bf16x8 *>(urow + 16 * ks);
       else
@@ -287,11 +292,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr uint32_t kTileBytes = 32 * CPR * 16;
   // Scores of one tile into two independent accumulation chains (halves of the d reduction);
   // their sum lands in fresh registers, leaving both chains free for the next tile.
+  // This wave's k-steps start 32 NKW fh bytes into a row; the swizzle (rx16 < 512) never reaches
+  // that bit, so the offset adds outside the XOR.
+  const uint32_t kofs = (uint32_t)(32 * NKW * fh);
   auto scores = [&](uint32_t toff, f32x16 &s0, f32x16 &s1) {
-    uint32_t rx = rx16, rb = toff + row_off;
+    uint32_t rx = rx16, rb = toff + row_off + kofs;
     asm volatile("" : "+v"(rx), "+v"(rb));
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKW; ++ks) {
       const uint32_t off = rb + (((uint32_t)(32 * ks)) ^ rx);
       const bf16x8 a = *(const STCA_LDS bf16x8 *)(lds + off);
       if (ks & 1)
@@ -367,11 +375,43 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // the loop: when a row maximum outgrows the slack the loop is left, the rescale runs, the
   // tile is finished and the loop resumes.  The running maximum starts at the first tile's.
   sync();
+  // Pairs (FH = 2): publish this wave's partial score tile of tile k; after the next workgroup
+  // barrier the partner adds it (both waves then hold bit-identical scores: a + b = b + a).
+  auto publish = [&](int k, const f32x16 &part) {
+    if constexpr (FH > 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        exch[k & 1][wave][q][lane] = f32x4{part[4 * q], part[4 * q + 1], part[4 * q + 2], part[4 * q + 3]};
+    }
+  };
+  auto with_partner = [&](int k, f32x16 own) {
+    if constexpr (FH > 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 o = exch[k & 1][wave ^ 1][q][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) own[4 * q + e] += o[e];
+      }
+    }
+    return own;
+  };
   f32x16 sa = f32x16{}, sb = f32x16{};
-  if (wave_active) {
-    scores(tile_off(0), sa, sb);
-    f32x16 s0 = sa + sb;
-    m_run = half_max(row_max(s0, tile_rem(0)));
+  if constexpr (FH == 1) {
+    if (wave_active) {
+      scores(tile_off(0), sa, sb);
+      f32x16 s0 = sa + sb;
+      m_run = half_max(row_max(s0, tile_rem(0)));
+    }
+  } else {
+    if (wave_active) {
+      scores(tile_off(0), sa, sb);
+      publish(0, sa + sb);
+    }
+    sync();
+    if (wave_active) {
+      f32x16 s0 = with_partner(0, sa + sb);
+      m_run = half_max(row_max(s0, tile_rem(0)));
+    }
   }
   auto tail = [&](int k, const f32x16 &sc) {
     bf16x8 pb[2];
@@ -394,7 +434,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // maximum outgrew the slack they are discarded and the caller recomputes them after the
   // rescale.  The PV product of tile k follows.
   constexpr int kRingA = 4, kAheadA = 3;
-  constexpr int NGA = NKS > 16 ? NKS : 16;
+  constexpr int NGA = NKW > 16 ? NKW : 16;
   auto step = [&](int k, f32x16 &sc, float &mx) -> bool {
     sync();  // tile k+1 is in LDS; tile k-1's slot is free
     if (k + 2 < ntiles) {
@@ -403,7 +443,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     }
     if (!wave_active) return false;
     const bool has_next = k + 1 < ntiles;
-    sc = sa + sb;
+    sc = with_partner(k, sa + sb);
     const int rem = tile_rem(k);
     if (rem < 32) {
 #pragma unroll
@@ -422,7 +462,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       mx = fmaxf(mx, sc[i]);
     };
     if (has_next) {
-      uint32_t rx = rx16, rb = tile_off(k + 1) + row_off;
+      uint32_t rx = rx16, rb = tile_off(k + 1) + row_off + kofs;
       asm volatile("" : "+v"(rx), "+v"(rb));
       auto frag = [&](int ks) { return *(const STCA_LDS bf16x8 *)(lds + rb + (((uint32_t)(32 * ks)) ^ rx)); };
       bf16x8 fr[kRingA];
@@ -431,8 +471,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < NGA; ++g) {
-        if (g < NKS) {
-          if (g + kAheadA < NKS) fr[(g + kAheadA) % kRingA] = frag(g + kAheadA);
+        if (g < NKW) {
+          if (g + kAheadA < NKW) fr[(g + kAheadA) % kRingA] = frag(g + kAheadA);
           if (g & 1)
             sb = mfma32x32x16(fr[g % kRingA], ub[g], g == 1 ? f32x16{} : sb);
           else
@@ -454,6 +494,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         pv(tile_off(k), pb, H0{});
       else
         pv(tile_off(k), pb, H1{});
+      if (has_next) publish(k + 1, sa + sb);
     }
     return false;
   };
@@ -474,6 +515,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     s_run *= sf;
     m_run = m_new;
     tail(k, sc);
+    if (k + 1 < ntiles) publish(k + 1, sa + sb);  // step k returned before publishing
     ++k;
   }
 

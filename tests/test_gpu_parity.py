@@ -125,13 +125,14 @@ def _attend_case(B, cfg, inp, W, layer, chunk):
     return o.cpu().numpy(), np.concatenate(refs)
 
 
+@pytest.mark.parametrize("d,h", [(128, 8), (512, 16)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("chunk", [0, 64, 96, 1024])
-def test_attend_ragged_split(B, dtype, chunk):
+def test_attend_ragged_split(B, dtype, chunk, d, h):
     """Ragged lengths (1 .. ~1500, not multiples of 32), 1..several targets, several chunk sizes
     so users span one or many split-L chunks and the combine step runs."""
-    cfg = SI.scaled(SI.get_config("ragged"), d=128, h=8, M=2, r=2, dtype=dtype)
-    announce("attend", dtype, "chunk", chunk)
+    cfg = SI.scaled(SI.get_config("ragged"), d=d, h=h, M=2, r=2, dtype=dtype)
+    announce("attend", d, dtype, "chunk", chunk)
     W = SI.make_weights(cfg)
     inp = _custom_inputs(cfg, [1, 17, 31, 32, 33, 95, 200, 1000, 1499], [2, 1, 3, 0, 1, 4, 2, 5, 3])
     for layer in (0, 1):
@@ -139,6 +140,37 @@ def test_attend_ragged_split(B, dtype, chunk):
         err = row_rel(got, ref)
         print(f"  attend {dtype} chunk={chunk} layer={layer}: err={err:.3e}", flush=True)
         assert err <= (2e-2 if dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("d,h,chunk", [(128, 8, 0), (256, 8, 0), (512, 16, 0), (512, 16, 96)])
+def test_attend_growing_scores(B, d, h, chunk):
+    """Histories whose scores grow along the sequence (row k of X~ scaled by 1 + k/64: a row's
+    maximum climbs from ~4 to ~40 in log2 units, outgrowing the kernel's running maximum by its
+    2^8 slack dozens of times per user), so every rescale path runs, including those of the
+    two-wave score split at d = 512 and of several chunks per user.  The bf16 bar still holds:
+    rounding u to bf16 (as the bf16 path does) costs ~9e-3 here, more than on unscaled rows,
+    because the softmax concentrates on few tokens; steeper growth (1 + k/16) costs ~2.4e-2 from
+    that rounding alone."""
+    cfg = SI.scaled(SI.get_config("ragged"), d=d, h=h, M=1, r=2)
+    announce("attend-growing", d, h, chunk)
+    W = SI.make_weights(cfg)
+    inp = _custom_inputs(cfg, [40, 300, 700], [3, 2, 4])
+    dims = B.dims_for(cfg, attn_chunk=chunk)
+    rng = np.random.default_rng(d)
+    Xts, qs, refs = [], [], []
+    for k in range(inp.n_users):
+        L = int(inp.L[k])
+        Xt = SI.bf16_round((rng.standard_normal((L, d)) * (1.0 + np.arange(L) / 64.0)[:, None]).astype(np.float32))
+        q = rng.standard_normal((int(inp.m[k]), d)).astype(np.float32)
+        Xts.append(Xt)
+        qs.append(q)
+        refs.append(O.attend_reordered(q, Xt, W.WQ[0], W.WK[0], W.WV[0], W.WO[0], h)[0])
+    o = B.stca_attend(dims, B.DeviceWeights(W, cfg.dtype, DEV), 0, B.DeviceBatch(inp, DEV),
+                      B.to_device(np.concatenate(Xts), cfg.dtype, DEV), torch.from_numpy(np.concatenate(qs)).to(DEV))
+    torch.cuda.synchronize()
+    err = row_rel(o.cpu().numpy(), np.concatenate(refs))
+    print(f"  growing d={d} chunk={chunk}: err={err:.3e}", flush=True)
+    assert err <= 2e-2
 
 
 @pytest.mark.parametrize("d,h", [(64, 4), (256, 8), (512, 16)])
