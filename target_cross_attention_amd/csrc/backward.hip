@@ -35,6 +35,7 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(int64_t rows, int cols, 
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float *o = out + (i / cols) * ldo + (i % cols);
     float acc = accumulate ? *o : 0.f;
+#pragma unroll 8
     for (int k = 0; k < nparts; ++k) acc += parts[(int64_t)k * n + i];
     *o = acc;
   }
@@ -104,15 +105,29 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int64_t rows, int d, int64_
     pg[e] = pb[e] = 0.f;
     gm[e] = c < d ? gamma[c] : 0.f;
   }
-  for (int64_t row = r0 + wave; row < r1; row += 4) {
-    float y[8], g[8];
-    float sum = 0.f;
+  // Rows one ahead: the next row's Y and dout are loaded while this row is reduced.
+  float ny[8], ngo[8];
+  auto load_row = [&](int64_t row) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = lane + 64 * e;
-      y[e] = c < d ? Y[row * ldy + c] : 0.f;
-      sum += y[e];
+      const bool ok = row < r1 && c < d;
+      ny[e] = ok ? Y[row * ldy + c] : 0.f;
+      ngo[e] = ok ? dout[row * ldd + c] : 0.f;
     }
+  };
+  load_row(r0 + wave);
+  for (int64_t row = r0 + wave; row < r1; row += 4) {
+    float y[8], go_[8], g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[e] = ny[e];
+      go_[e] = ngo[e];
+    }
+    load_row(row + 4);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum += y[e];
     const float mean = wave_sum(sum) / (float)d;
     float q = 0.f;
 #pragma unroll
@@ -127,7 +142,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int64_t rows, int d, int64_
     for (int e = 0; e < 8; ++e) {
       const int c = lane + 64 * e;
       if (c < d) {
-        const float xh = (y[e] - mean) * rstd, go = dout[row * ldd + c];
+        const float xh = (y[e] - mean) * rstd, go = go_[e];
         g[e] = go * gm[e];
         s1 += g[e];
         s2 += g[e] * xh;
