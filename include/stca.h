@@ -153,8 +153,9 @@ STCA_API int stca_predict(const stca_dims *dims, const void *WZ, const stca_ffn 
  *     (dims->dtype storage; no bf16 rounding of intermediates), so results are the fp32
  *     gradients of the fp32 forward;
  *   - reductions over rows (tokens, targets) run in a fixed order: results are deterministic.
- * Memory: the workspace holds the encoded history of every layer in fp32 (M total_L d floats)
- * and per-target intermediates; see stca_backward_workspace_size. */
+ * Memory: the workspace holds the encoded history of every layer in fp32 (M total_L d floats),
+ * two buffers of per-user attention scores (h min(max_T total_L, max_L total_T) + 3 h total_T floats
+ * each) and per-target intermediates; stca_backward_workspace_size gives the exact figure. */
 typedef struct {
   float *dWu, *dWv; /* d x rd */
   float *dWo;       /* rd x d */
