@@ -292,15 +292,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr uint32_t kTileBytes = 32 * CPR * 16;
   // Scores of one tile into two independent accumulation chains (halves of the d reduction);
   // their sum lands in fresh registers, leaving both chains free for the next tile.
-  // This wave's k-steps start 32 NKW fh bytes into a row; the swizzle (rx16 < 512) never reaches
-  // that bit, so the offset adds outside the XOR.
+  // This wave's k-steps start 32 NKW fh bytes into a row.  The swizzle acts on the chunk index
+  // (bits 4.. of the byte offset), which that start may share, so it stays inside the XOR.
   const uint32_t kofs = (uint32_t)(32 * NKW * fh);
   auto scores = [&](uint32_t toff, f32x16 &s0, f32x16 &s1) {
-    uint32_t rx = rx16, rb = toff + row_off + kofs;
+    uint32_t rx = rx16, rb = toff + row_off;
     asm volatile("" : "+v"(rx), "+v"(rb));
 #pragma unroll
     for (int ks = 0; ks < NKW; ++ks) {
-      const uint32_t off = rb + (((uint32_t)(32 * ks)) ^ rx);
+      const uint32_t off = rb + (((uint32_t)(32 * ks) + kofs) ^ rx);
       const bf16x8 a = *(const STCA_LDS bf16x8 *)(lds + off);
       if (ks & 1)
         s1 = mfma32x32x16(a, ub[ks], ks == 1 ? f32x16{} : s1);
@@ -462,9 +462,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       mx = fmaxf(mx, sc[i]);
     };
     if (has_next) {
-      uint32_t rx = rx16, rb = tile_off(k + 1) + row_off + kofs;
+      uint32_t rx = rx16, rb = tile_off(k + 1) + row_off;
       asm volatile("" : "+v"(rx), "+v"(rb));
-      auto frag = [&](int ks) { return *(const STCA_LDS bf16x8 *)(lds + rb + (((uint32_t)(32 * ks)) ^ rx)); };
+      auto frag = [&](int ks) { return *(const STCA_LDS bf16x8 *)(lds + rb + (((uint32_t)(32 * ks) + kofs) ^ rx)); };
       bf16x8 fr[kRingA];
 #pragma unroll
       for (int q = 0; q < kAheadA; ++q) fr[q] = frag(q);
