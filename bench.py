@@ -415,6 +415,20 @@ def main():
     prof.close()
     assert np.isfinite(Z.sum().item()), "non-finite output"
 
+    # The same forward replayed from a HIP graph (stca_forward_graph_create): identical kernels with
+    # the per-call host work and launch gaps removed; reported beside the eager figure.
+    graph = B.ForwardGraph(dims, dw, db, ws=ws)
+    graph.launch(stream)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(a.steps):
+        graph.launch(stream)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / a.steps
+    assert torch.equal(graph.Z, Z), "graph replay differs from the eager forward"
+    graph.close()
+
     # The prediction token of eq. (9) is the next step downstream of the forward (outside the timed
     # forward): timed on its own, from the forward's Z, on the call's stream.
     pw = B.DevicePredict(SI.make_predict_weights(cfg), cfg.dtype, dev)
@@ -482,6 +496,8 @@ def main():
                                "mfma_tflops": att_flops / att_avg_s / 1e12,
                                "avg_launch_ms": att_avg_s * 1e3, "launches": att_n},
         "targets_per_s": targets_per_s,
+        "graph_replay": {"ms_per_step": graph_ms, "history_tokens_per_s": db.total_L / graph_ms * 1e3,
+                         "replays": a.steps},
         "phase_ms_per_step": {k: v[0] / a.steps for k, v in phases.items() if not k.startswith("bwd")},
         "prediction_token": {"eq": 9, "rows": db.total_T, "avg_ms": pred_ms, "calls": n_pred,
                              "targets_per_s": db.total_T / pred_ms * 1e3, "bound": "alu",

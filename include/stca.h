@@ -291,6 +291,23 @@ STCA_API int stca_backward_profiled(const stca_dims *dims, const stca_weights *w
                                     const void *X, const void *xt, const float *dZ, const stca_grads *grads,
                                     void *workspace, size_t workspace_bytes, void *stream, stca_profiler *prof);
 
+/* ---- graph replay of the forward -------------------------------------------------------------
+ * A forward over a small batch is a few dozen short kernels, and launch overhead dominates it.
+ * stca_forward_graph_create records one stca_forward with exactly these arguments (the device
+ * pointers and the batch sizes are baked in) as a HIP graph; stca_graph_launch replays it on
+ * `stream`.  A replay reads whatever the buffers hold at that time, so new inputs of the same
+ * shapes in the same buffers need no new graph.  The graph owns driver resources (released by
+ * stca_graph_destroy), not device memory: the workspace stays the caller's and must stay valid
+ * and unused by other work while a replay runs.  Argument errors are returned as by
+ * stca_forward, before anything is recorded.  Capture happens on a stream of the library's own;
+ * nothing runs on the device until the first launch. */
+typedef struct stca_graph stca_graph; /* opaque, host-side */
+STCA_API int stca_forward_graph_create(const stca_dims *dims, const stca_weights *w, const stca_batch *batch,
+                                       const void *X, const void *xt, float *Z, void *workspace,
+                                       size_t workspace_bytes, stca_graph **out);
+STCA_API int stca_graph_launch(stca_graph *g, void *stream);
+STCA_API int stca_graph_destroy(stca_graph *g); /* NULL is a no-op */
+
 /* ---- diagnostics ---------------------------------------------------------------------------- */
 STCA_API const char *stca_status_string(int status);
 STCA_API const char *stca_last_error(void); /* thread-local detail of the last failure in this thread */

@@ -26,7 +26,8 @@ EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
     "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict",
     "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_litm_plan", "stca_litm_merge",
-    "stca_backward_workspace_size", "stca_backward", "stca_backward_profiled", "stca_profiler_create", "stca_profiler_destroy",
+    "stca_backward_workspace_size", "stca_backward", "stca_backward_profiled",
+    "stca_forward_graph_create", "stca_graph_launch", "stca_graph_destroy", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
 ]
@@ -103,6 +104,9 @@ def _load() -> ctypes.CDLL:
         "stca_backward_workspace_size": [P, P, POINTER(c_size_t)],
         "stca_backward": [P, P, P, P, P, P, P, P, c_size_t, P],
         "stca_backward_profiled": [P, P, P, P, P, P, P, P, c_size_t, P, P],
+        "stca_forward_graph_create": [P, P, P, P, P, P, P, c_size_t, POINTER(c_void_p)],
+        "stca_graph_launch": [P, P],
+        "stca_graph_destroy": [P],
         "stca_profiler_create": [POINTER(c_void_p)],
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
@@ -458,6 +462,40 @@ def stca_backward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, dZ, grads: D
     else:
         _check(LIB.stca_backward_profiled(*args, profiler.handle), "stca_backward")
     return grads
+
+
+class ForwardGraph:
+    """A recorded stca_forward (stca_forward_graph_create) over fixed buffers: ``launch()`` replays
+    it on a stream.  Keeps the batch, weights, output and workspace tensors alive."""
+
+    def __init__(self, dims: Dims, w: DeviceWeights, batch: DeviceBatch, Z=None, ws=None):
+        import torch
+        if Z is None:
+            Z = torch.empty((batch.total_T, dims.M, dims.d), dtype=torch.float32, device=batch.X.device)
+        if ws is None:
+            ws = workspace(forward_workspace_size(dims, batch.c), batch.X.device)
+        self.keep = (dims, w, batch)
+        self.Z, self.ws = Z, ws
+        h = c_void_p()
+        _check(LIB.stca_forward_graph_create(_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt),
+                                             _ptr(Z), _ptr(ws), ws.numel(), ctypes.byref(h)),
+               "stca_forward_graph_create")
+        self.handle = h
+
+    def launch(self, stream=None):
+        _check(LIB.stca_graph_launch(self.handle, _stream(stream)), "stca_graph_launch")
+        return self.Z
+
+    def close(self):
+        if self.handle:
+            LIB.stca_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class Profiler:

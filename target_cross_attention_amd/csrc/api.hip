@@ -198,6 +198,11 @@ struct stca_profiler {
   std::vector<Mark> marks;
 };
 
+struct stca_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
 namespace {
 
 struct Phase {
@@ -1284,6 +1289,66 @@ int stca_litm_merge(const stca_dims *dims, int64_t n_rows, int64_t n_groups, con
     return fail(STCA_E_ALIGN, "X buffers need 16-byte, index arrays 8-byte alignment");
   HIP_TRY(litm_merge((hipStream_t)stream, dims->dtype == STCA_BF16, dims->d, n_rows, n_groups, group_off, members, X,
                      X_merged));
+  return STCA_OK;
+}
+
+int stca_forward_graph_create(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
+                              const void *xt, float *Z, void *workspace, size_t workspace_bytes, stca_graph **out) {
+  if (!out) return fail(STCA_E_ARG, "out is NULL");
+  *out = nullptr;
+  int st;
+  // Argument checks first, on a dry run that records nothing.
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_batch(batch)) != STCA_OK) return st;
+  if ((st = check_weights(dims, w)) != STCA_OK) return st;
+  size_t need = 0;
+  if ((st = stca_forward_workspace_size(dims, batch, &need)) != STCA_OK) return st;
+  if (!workspace || workspace_bytes < need)
+    return fail(STCA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if (batch->total_L > 0 && !X) return fail(STCA_E_ARG, "X is NULL");
+  if (batch->total_T > 0 && (!xt || !Z)) return fail(STCA_E_ARG, "xt or Z is NULL");
+  if (!aligned16(X) || !aligned16(xt) || !aligned16(Z) || !aligned16(workspace))
+    return fail(STCA_E_ALIGN, "X/xt/Z/workspace not 16-byte aligned");
+  // Capture on a stream of our own (default priority), then instantiate.
+  hipStream_t cs = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    st = forward_impl(dims, w, batch, X, xt, Z, workspace, workspace_bytes, cs, nullptr);
+    const hipError_t e2 = hipStreamEndCapture(cs, &graph);
+    if (st == STCA_OK && e2 != hipSuccess) e = e2;
+  }
+  hipStreamDestroy(cs);
+  if (e != hipSuccess) {
+    if (graph) hipGraphDestroy(graph);
+    return fail(STCA_E_HIP, "graph capture failed: %s", hipGetErrorString(e));
+  }
+  if (st != STCA_OK) {
+    if (graph) hipGraphDestroy(graph);
+    return st;
+  }
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(graph);
+    return fail(STCA_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  }
+  *out = new stca_graph{graph, exec};
+  return STCA_OK;
+}
+
+int stca_graph_launch(stca_graph *g, void *stream) {
+  if (!g) return fail(STCA_E_ARG, "graph is NULL");
+  HIP_TRY(hipGraphLaunch(g->exec, (hipStream_t)stream));
+  return STCA_OK;
+}
+
+int stca_graph_destroy(stca_graph *g) {
+  if (!g) return STCA_OK;
+  if (g->exec) hipGraphExecDestroy(g->exec);
+  if (g->graph) hipGraphDestroy(g->graph);
+  delete g;
   return STCA_OK;
 }
 

@@ -242,3 +242,25 @@ def test_backward_validation():
     assert _backward(dims, w, batch, g, ws_bytes=need - 1) == -3
     assert _backward(dims, _fake_weights(3, with_wc=False), batch, g) == -1
     assert _backward(dims, w, B.BatchC(4, FAKE, FAKE, 400, 1 << 23, 100, 1 << 21), g) == -1
+
+
+def test_forward_graph_validation():
+    """Graph capture checks its arguments before recording anything (no device work here)."""
+    dims = B.make_dims(256, 8, 2, 4)
+    w, batch = _fake_weights(2), _batch()
+    out = ctypes.c_void_p()
+    g = B.LIB.stca_forward_graph_create
+    assert g(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(batch), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+    assert g(ctypes.byref(B.make_dims(96, 8, 2, 4)), ctypes.byref(w), ctypes.byref(batch), FAKE, FAKE, FAKE, FAKE,
+             1 << 40, ctypes.byref(out)) == -2
+    assert g(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(batch), FAKE, FAKE, FAKE, FAKE, 16,
+             ctypes.byref(out)) == -3
+    assert g(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(batch), None, FAKE, FAKE, FAKE, 1 << 40,
+             ctypes.byref(out)) == -1
+    assert g(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(batch), FAKE, FAKE, FAKE + 4, FAKE, 1 << 40,
+             ctypes.byref(out)) == -4
+    assert g(ctypes.byref(dims), ctypes.byref(_fake_weights(2, with_wc=False)), ctypes.byref(batch), FAKE, FAKE,
+             FAKE, FAKE, 1 << 40, ctypes.byref(out)) == -1
+    assert out.value is None
+    assert B.LIB.stca_graph_destroy(None) == 0
+    assert B.LIB.stca_graph_launch(None, None) == -1
