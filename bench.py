@@ -500,7 +500,7 @@ def main():
                          "replays": a.steps},
         "phase_ms_per_step": {k: v[0] / a.steps for k, v in phases.items() if not k.startswith("bwd")},
         "prediction_token": {"eq": 9, "rows": db.total_T, "avg_ms": pred_ms, "calls": n_pred,
-                             "targets_per_s": db.total_T / pred_ms * 1e3, "bound": "alu",
+                             "targets_per_s": db.total_T / pred_ms * 1e3, "bound": "mfma",
                              "achieved": pred_flops / pred_ms / 1e9, "peak": PEAK_FP32_TFLOPS,
                              "unit": "TFLOP/s", "frac": pred_flops / pred_ms / 1e9 / PEAK_FP32_TFLOPS},
     }
