@@ -244,7 +244,8 @@ def bench_backward(a, cfg, dev):
     del inp.X
     dZ = torch.from_numpy(np.random.default_rng(11).standard_normal((db.total_T, cfg.M, cfg.d), np.float32)).to(dev)
     grads = B.DeviceGrads(dims, db.total_L, db.total_T, dev)
-    ws = B.workspace(B.backward_workspace_size(dims, db.c), dev)
+    keep = not a.no_keep
+    ws = B.workspace(B.backward_workspace_size(dims, db.c, keep), dev)
     stream = torch.cuda.current_stream()
     log(f"backward workspace {ws.numel() / 2**30:.2f} GiB; warmup {a.warmup}")
     for _ in range(a.warmup):
@@ -264,11 +265,12 @@ def bench_backward(a, cfg, dev):
     L, T, d, r, M, h = db.total_L, db.total_T, cfg.d, cfg.r, cfg.M, cfg.h
     pairs = float((db.inp.L * db.inp.m).sum()) * h
     # Dominant phase: the derivative of eq. (2) over the history rows, one per layer.  Algorithmic
-    # FLOP per history token: the recomputed A = x W_u, G = x W_v, Y = H W_o (6 r d^2) and the
-    # products dW_o, dH, dW_u, dW_v, dx (12 r d^2), 2 FLOP per multiply-add.
+    # FLOP per history token: the products dW_o, dH, dW_u, dW_v, dx (12 r d^2, 2 FLOP per
+    # multiply-add), plus with the minimum workspace the recomputed A = x W_u, G = x W_v and
+    # Y = H W_o (6 r d^2).
     enc_ms, enc_n = phases["bwd_encode"]
     enc_avg_s = enc_ms / max(enc_n, 1) / 1e3
-    enc_flops = 18.0 * r * d * d * L
+    enc_flops = (12.0 if keep else 18.0) * r * d * d * L
     achieved = enc_flops / enc_avg_s / 1e12
     # Per (target, head, history token) pair: the scores twice (statistics, then again for alpha), abar,
     # dA, du and the two products of dX~, each 2d FLOP.
@@ -279,7 +281,9 @@ def bench_backward(a, cfg, dev):
         "warmup": a.warmup, "ms_per_step": dt * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded; training-shaped ragged batch)",
         "config": {"workload": cfg.description, "key": cfg.key, "users": db.inp.n_users, "history_tokens": L,
-                   "targets": T, "storage": cfg.dtype},
+                   "targets": T, "storage": cfg.dtype,
+                   "workspace": ("keep (encode intermediates kept from the recompute)" if keep else "minimum"),
+                   "workspace_gib": ws.numel() / 2**30},
         "roofline": {"kernel": "encode backward (fp32 matrix-core GEMMs + SwiGLU/LayerNorm derivatives)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
@@ -344,6 +348,8 @@ def main():
                          "time the forward on the merged batch")
     ap.add_argument("--backward", action="store_true",
                     help="time stca_backward instead (default workload: the training-shaped ragged batch)")
+    ap.add_argument("--no-keep", action="store_true",
+                    help="with --backward: the minimum workspace (recompute the encode's intermediates)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of STCA, run K device copies of 2 GiB (counter calibration)")
     a = ap.parse_args()

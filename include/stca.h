@@ -172,6 +172,11 @@ typedef struct {
 } stca_grads;
 
 STCA_API int stca_backward_workspace_size(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
+/* A larger workspace, at least this size, lets stca_backward keep the history FFN's intermediates from its
+ * forward recompute (A = X W_u, G = X W_v and the pre-LayerNorm rows of every layer: 4 M total_L (2 rd + d)
+ * bytes more) instead of computing them a second time for the derivative of eq. (2).  Same results up to
+ * fp32 rounding order; the call picks the mode from workspace_bytes. */
+STCA_API int stca_backward_workspace_size_keep(const stca_dims *dims, const stca_batch *batch, size_t *bytes);
 
 /* X: total_L x d, xt: total_T x d (dims->dtype), dZ: total_T x M x d fp32 (the layout of Z in
  * stca_forward), grads: output pointers as described above (device).  Same conventions as the

@@ -26,7 +26,7 @@ EXPORTS = [
     "stca_encode_workspace_size", "stca_attend_workspace_size", "stca_forward_workspace_size",
     "stca_predict_workspace_size", "stca_encode", "stca_attend", "stca_forward", "stca_predict",
     "stca_sl_beta", "stca_sl_plan", "stca_sl_pack", "stca_litm_plan", "stca_litm_merge",
-    "stca_backward_workspace_size", "stca_backward", "stca_backward_profiled",
+    "stca_backward_workspace_size", "stca_backward_workspace_size_keep", "stca_backward", "stca_backward_profiled",
     "stca_forward_graph_create", "stca_graph_launch", "stca_graph_destroy", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
     "stca_last_error", "stca_version",
@@ -102,6 +102,7 @@ def _load() -> ctypes.CDLL:
         "stca_litm_plan": [c_int32, P, P, c_int32, P, P, P, POINTER(c_int64)],
         "stca_litm_merge": [P, c_int64, c_int64, P, P, P, P, P],
         "stca_backward_workspace_size": [P, P, POINTER(c_size_t)],
+        "stca_backward_workspace_size_keep": [P, P, POINTER(c_size_t)],
         "stca_backward": [P, P, P, P, P, P, P, P, c_size_t, P],
         "stca_backward_profiled": [P, P, P, P, P, P, P, P, c_size_t, P, P],
         "stca_forward_graph_create": [P, P, P, P, P, P, P, c_size_t, POINTER(c_void_p)],
@@ -440,21 +441,23 @@ class DeviceGrads:
         return self.t[name]
 
 
-def backward_workspace_size(dims: Dims, batch: BatchC) -> int:
+def backward_workspace_size(dims: Dims, batch: BatchC, keep: bool = False) -> int:
+    """Workspace bytes of stca_backward; with ``keep`` the larger size that keeps the encode's
+    intermediates from the forward recompute."""
     n = c_size_t(0)
-    _check(LIB.stca_backward_workspace_size(_ref(dims), _ref(batch), ctypes.byref(n)),
-           "stca_backward_workspace_size")
+    fn = LIB.stca_backward_workspace_size_keep if keep else LIB.stca_backward_workspace_size
+    _check(fn(_ref(dims), _ref(batch), ctypes.byref(n)), "stca_backward_workspace_size")
     return n.value
 
 
 def stca_backward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, dZ, grads: DeviceGrads | None = None, ws=None,
-                  stream=None, profiler=None):
+                  stream=None, profiler=None, keep: bool = False):
     """Gradients of sum(dZ * Z) for the forward of ``batch`` (dZ: total_T x M x d float32, device).
     Returns the DeviceGrads holding them."""
     if grads is None:
         grads = DeviceGrads(dims, batch.total_L, batch.total_T, batch.X.device)
     if ws is None:
-        ws = workspace(backward_workspace_size(dims, batch.c), batch.X.device)
+        ws = workspace(backward_workspace_size(dims, batch.c, keep), batch.X.device)
     args = (_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(dZ), _ref(grads.c), _ptr(ws),
             ws.numel(), _stream(stream))
     if profiler is None:

@@ -564,6 +564,9 @@ struct BackwardWs {
   float *S = nullptr, *S2 = nullptr;  // every user's score matrix (R_u x Lp_u), twice
   RaggedDesc *desc = nullptr;         // 3 n_users product descriptors
   int64_t rows = 0;         // history rows per encode-backward chunk
+  // With a workspace of the "keep" size: A = X W_u, G = X W_v (M x total_L x rd) and the pre-LN rows
+  // Y (M x total_L x d) of every layer, kept from the forward recompute for the encode backward.
+  float *kA = nullptr, *kG = nullptr, *kY = nullptr;
 };
 
 // Upper bound on sum_u R_u Lp_u (R_u = m_u h query rows, Lp_u = L_u rounded up to 4):
@@ -573,7 +576,7 @@ int64_t score_elems(const stca_dims *dm, const stca_batch *b) {
   return (int64_t)dm->h * (ml + 3 * b->total_T);
 }
 
-size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, BackwardWs &w) {
+size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, BackwardWs &w, bool keep) {
   Carver c(base);
   const int64_t L = b->total_L, T = b->total_T, d = dm->d, h = dm->h, rd = (int64_t)dm->r * dm->d, M = dm->M;
   w.Xt = c.take<float>((size_t)(M * L * d));
@@ -613,6 +616,11 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   w.S = c.take<float>((size_t)score_elems(dm, b));
   w.S2 = c.take<float>((size_t)score_elems(dm, b));
   w.desc = c.take<RaggedDesc>((size_t)std::max(3 * b->n_users, 1));
+  if (keep) {
+    w.kA = c.take<float>((size_t)(M * L * rd));
+    w.kG = c.take<float>((size_t)(M * L * rd));
+    w.kY = c.take<float>((size_t)(M * L * d));
+  }
   return round_up(c.off, 256);
 }
 
@@ -752,11 +760,12 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
   if (b->n_users > 0 && b->total_T > 0 && b->total_L / std::max<int64_t>(1, b->n_users) > ((int64_t)1 << 40))
     return fail(STCA_E_ARG, "history too long");
   BackwardWs bw;
-  const size_t need = carve_backward(nullptr, dm, b, bw);
+  const size_t need = carve_backward(nullptr, dm, b, bw, false);
   if (!ws || ws_bytes < need)
     return fail(STCA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(STCA_E_ALIGN, "workspace not 16-byte aligned");
-  carve_backward(ws, dm, b, bw);
+  const bool keep = ws_bytes >= carve_backward(nullptr, dm, b, bw, true);
+  carve_backward(ws, dm, b, bw, keep);
 
   const int d = dm->d, h = dm->h, dh = d / h, M = dm->M, rd = dm->r * dm->d;
   const int64_t L = b->total_L, T = b->total_T;
@@ -819,7 +828,20 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     float *Xt = bw.Xt + (size_t)i * L * d;
     {
       Phase ph(prof, s, STCA_PHASE_BWD_RECOMPUTE);
-      if ((st = ffn_generic(s, dm, &w->hist[i], L, X, d, bf, Xt, d, false, true, enc)) != STCA_OK) return st;  // eq. (2)
+      if (keep) {  // eq. (2) in chunks, keeping A, G and the pre-LN rows
+        for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
+          const int64_t n = std::min<int64_t>(bw.rows, L - r0);
+          float *A = bw.kA + ((size_t)i * L + r0) * rd, *G = bw.kG + ((size_t)i * L + r0) * rd;
+          float *Y = bw.kY + ((size_t)i * L + r0) * d;
+          if ((st = ffn_saved(s, dm, &w->hist[i], n, (const char *)X + (size_t)r0 * d * esize(dm), bf, A, G, bw.eH,
+                              Y)) != STCA_OK)
+            return st;
+          HIP_TRY(layernorm_rows(s, n, d, Y, d, Xt + (size_t)r0 * d, d, false, w->hist[i].gamma, w->hist[i].beta,
+                                 dm->ln_eps));
+        }
+      } else if ((st = ffn_generic(s, dm, &w->hist[i], L, X, d, bf, Xt, d, false, true, enc)) != STCA_OK) {
+        return st;  // eq. (2)
+      }
       HIP_TRY(ph.end());
     }
     Phase pt(prof, s, STCA_PHASE_BWD_TARGET);
@@ -974,8 +996,16 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
       const int64_t n = std::min<int64_t>(bw.rows, L - r0);
       const void *Xc = (const char *)X + (size_t)r0 * d * xes;
-      if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, bw.eA, bw.eG, bw.eH, bw.eY)) != STCA_OK) return st;
-      if ((st = ffn_backward(s, dm, &w->hist[i], g->hist[i], true, n, Xc, bf, bw.eA, bw.eG, bw.eH, bw.eY,
+      float *A = bw.eA, *G = bw.eG, *Y = bw.eY;
+      if (keep) {  // kept from the recompute: only H = A * SiLU(G) is formed again (G is consumed below)
+        A = bw.kA + ((size_t)i * L + r0) * rd;
+        G = bw.kG + ((size_t)i * L + r0) * rd;
+        Y = bw.kY + ((size_t)i * L + r0) * d;
+        HIP_TRY(swiglu_fwd(s, n * rd, A, G, bw.eH));
+      } else if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, A, G, bw.eH, Y)) != STCA_OK) {
+        return st;
+      }
+      if ((st = ffn_backward(s, dm, &w->hist[i], g->hist[i], true, n, Xc, bf, A, G, bw.eH, Y,
                              bw.dXt + (size_t)r0 * d, bw.edY, g->dX ? g->dX + (size_t)r0 * d : nullptr, true,
                              bw.parts)) != STCA_OK)
         return st;
@@ -1143,7 +1173,17 @@ int stca_backward_workspace_size(const stca_dims *dims, const stca_batch *batch,
   if ((st = check_batch(batch)) != STCA_OK) return st;
   if (!bytes) return fail(STCA_E_ARG, "bytes is NULL");
   BackwardWs bw;
-  *bytes = carve_backward(nullptr, dims, batch, bw);
+  *bytes = carve_backward(nullptr, dims, batch, bw, false);
+  return STCA_OK;
+}
+
+int stca_backward_workspace_size_keep(const stca_dims *dims, const stca_batch *batch, size_t *bytes) {
+  int st;
+  if ((st = check_dims(dims)) != STCA_OK) return st;
+  if ((st = check_batch(batch)) != STCA_OK) return st;
+  if (!bytes) return fail(STCA_E_ARG, "bytes is NULL");
+  BackwardWs bw;
+  *bytes = carve_backward(nullptr, dims, batch, bw, true);
   return STCA_OK;
 }
 

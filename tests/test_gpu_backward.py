@@ -58,12 +58,12 @@ def without_targets(inp, drop):
     return dataclasses.replace(inp, m=m, tgt_off=SI.offsets(m), xt=inp.xt[np.asarray(keep_rows, np.int64)])
 
 
-def run_case(B, cfg, inp, W, query_ln=False, seed=5):
+def run_case(B, cfg, inp, W, query_ln=False, seed=5, keep=False):
     dims = B.dims_for(cfg, query_ln=query_ln)
     dZ = np.random.default_rng(seed).standard_normal((inp.total_T, cfg.M, cfg.d)).astype(np.float32)
     dw = B.DeviceWeights(W, cfg.dtype, DEV)
     db = B.DeviceBatch(inp, DEV)
-    grads = B.stca_backward(dims, dw, db, torch.from_numpy(dZ).to(DEV))
+    grads = B.stca_backward(dims, dw, db, torch.from_numpy(dZ).to(DEV), keep=keep)
     torch.cuda.synchronize()
     ref = G.backward_batch(inp, W, dZ.astype(np.float64), query_ln=query_ln)
     errs = {"dX": tensor_rel(grads.dX[:inp.total_L].cpu().numpy(), ref.dX),
@@ -102,6 +102,17 @@ def test_backward_matches_oracle(B, key, change, query_ln, separate):
     announce("backward", cfg.key, cfg.dtype, change, "query_ln" if query_ln else "", "separate" if separate else "")
     W = SI.make_weights(cfg, random_ln=True, separate_query_ffn=separate)
     run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln)
+
+
+@pytest.mark.parametrize("key,change,query_ln,separate", [CASES[1], CASES[3], CASES[6]],
+                         ids=["tiny-M3", "ragged-small", "ragged-40"])
+def test_backward_keep_workspace(B, key, change, query_ln, separate):
+    """The larger workspace that keeps the encode's intermediates from the forward recompute gives
+    the same gradients (the same bar against the oracle)."""
+    cfg = SI.scaled(SI.get_config(key), **change)
+    announce("backward-keep", cfg.key, cfg.dtype, change)
+    W = SI.make_weights(cfg, random_ln=True, separate_query_ffn=separate)
+    run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln, keep=True)
 
 
 def test_backward_short_histories_and_targetless_users(B):
