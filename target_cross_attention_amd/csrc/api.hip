@@ -567,6 +567,9 @@ struct BackwardWs {
   // With a workspace of the "keep" size: A = X W_u, G = X W_v (M x total_L x rd) and the pre-LN rows
   // Y (M x total_L x d) of every layer, kept from the forward recompute for the encode backward.
   float *kA = nullptr, *kG = nullptr, *kY = nullptr;
+  // bf16 storage: W_u^T and W_v^T (rd x d each) of every layer's history FFN, the k-contiguous B operands
+  // of the bf16 matrix-core products A = X W_u, G = X W_v.
+  void *WuT[STCA_MAX_M] = {}, *WvT[STCA_MAX_M] = {};
 };
 
 // Upper bound on sum_u R_u Lp_u (R_u = m_u h query rows, Lp_u = L_u rounded up to 4):
@@ -616,6 +619,11 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   w.S = c.take<float>((size_t)score_elems(dm, b));
   w.S2 = c.take<float>((size_t)score_elems(dm, b));
   w.desc = c.take<RaggedDesc>((size_t)std::max(3 * b->n_users, 1));
+  if (dm->dtype == STCA_BF16)
+    for (int i = 0; i < M; ++i) {
+      w.WuT[i] = c.take<char>((size_t)(d * rd) * 2);
+      w.WvT[i] = c.take<char>((size_t)(d * rd) * 2);
+    }
   if (keep) {
     w.kA = c.take<float>((size_t)(M * L * rd));
     w.kG = c.take<float>((size_t)(M * L * rd));
@@ -685,12 +693,18 @@ hipError_t mm(hipStream_t s, int m, int n, int k, const void *A, int64_t lda, bo
 }
 
 // eq. (1) on n rows with its intermediates kept: A = x W_u, G = x W_v, H = A * SiLU(G), Y = H W_o.
+// With bf16 x and the transposed weights WuT/WvT (rd x d, bf16) A and G run on the bf16 matrix cores.
 int ffn_saved(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t n, const void *x, bool x_bf16,
-              float *A, float *G, float *H, float *Y) {
+              float *A, float *G, float *H, float *Y, const void *WuT = nullptr, const void *WvT = nullptr) {
   const int d = dm->d, rd = dm->r * dm->d;
   const bool wb = dm->dtype == STCA_BF16;
-  HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wu, rd, wb, false, A, rd, 0.f));
-  HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wv, rd, wb, false, G, rd, 0.f));
+  if (x_bf16 && wb && WuT && WvT) {
+    HIP_TRY(gemm_bf16_nt(s, (int)n, rd, d, x, d, WuT, d, A, rd));
+    HIP_TRY(gemm_bf16_nt(s, (int)n, rd, d, x, d, WvT, d, G, rd));
+  } else {
+    HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wu, rd, wb, false, A, rd, 0.f));
+    HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wv, rd, wb, false, G, rd, 0.f));
+  }
   HIP_TRY(swiglu_fwd(s, n * rd, A, G, H));
   HIP_TRY(mm(s, (int)n, d, rd, H, rd, false, f->Wo, d, wb, false, Y, d, 0.f));
   return STCA_OK;
@@ -789,6 +803,11 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
   }
   if (T == 0) return STCA_OK;  // no target, no gradient
   HIP_TRY(ragged_plan(s, b->n_users, b->hist_off, b->tgt_off, h, d, bw.desc));
+  if (bf)
+    for (int i = 0; i < M; ++i) {
+      HIP_TRY(transpose_bf16(s, d, rd, w->hist[i].Wu, bw.WuT[i]));
+      HIP_TRY(transpose_bf16(s, d, rd, w->hist[i].Wv, bw.WvT[i]));
+    }
   const int64_t T_rows = b->max_T * h, max_L = b->max_L;  // bounds of the ragged products' sizes
   auto rg = [](const float *A, const float *B, float *C, float alpha, float beta, bool ta, bool tb) {
     GemmArgs g;
@@ -821,26 +840,24 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     if ((st = q_forward(0)) != STCA_OK) return st;
     HIP_TRY(ph.end());
   }
-  FfnWs enc;
-  enc.A = bw.eA;
-  enc.G = bw.eG;
   for (int i = 0; i < M; ++i) {
     float *Xt = bw.Xt + (size_t)i * L * d;
     {
       Phase ph(prof, s, STCA_PHASE_BWD_RECOMPUTE);
-      if (keep) {  // eq. (2) in chunks, keeping A, G and the pre-LN rows
-        for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
-          const int64_t n = std::min<int64_t>(bw.rows, L - r0);
-          float *A = bw.kA + ((size_t)i * L + r0) * rd, *G = bw.kG + ((size_t)i * L + r0) * rd;
-          float *Y = bw.kY + ((size_t)i * L + r0) * d;
-          if ((st = ffn_saved(s, dm, &w->hist[i], n, (const char *)X + (size_t)r0 * d * esize(dm), bf, A, G, bw.eH,
-                              Y)) != STCA_OK)
-            return st;
-          HIP_TRY(layernorm_rows(s, n, d, Y, d, Xt + (size_t)r0 * d, d, false, w->hist[i].gamma, w->hist[i].beta,
-                                 dm->ln_eps));
+      // eq. (2) in row chunks; with the keep workspace A, G and the pre-LN rows stay for the backward
+      for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
+        const int64_t n = std::min<int64_t>(bw.rows, L - r0);
+        float *A = bw.eA, *G = bw.eG, *Y = bw.eY;
+        if (keep) {
+          A = bw.kA + ((size_t)i * L + r0) * rd;
+          G = bw.kG + ((size_t)i * L + r0) * rd;
+          Y = bw.kY + ((size_t)i * L + r0) * d;
         }
-      } else if ((st = ffn_generic(s, dm, &w->hist[i], L, X, d, bf, Xt, d, false, true, enc)) != STCA_OK) {
-        return st;  // eq. (2)
+        if ((st = ffn_saved(s, dm, &w->hist[i], n, (const char *)X + (size_t)r0 * d * esize(dm), bf, A, G, bw.eH, Y,
+                            bw.WuT[i], bw.WvT[i])) != STCA_OK)
+          return st;
+        HIP_TRY(layernorm_rows(s, n, d, Y, d, Xt + (size_t)r0 * d, d, false, w->hist[i].gamma, w->hist[i].beta,
+                               dm->ln_eps));
       }
       HIP_TRY(ph.end());
     }
@@ -1002,7 +1019,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
         G = bw.kG + ((size_t)i * L + r0) * rd;
         Y = bw.kY + ((size_t)i * L + r0) * d;
         HIP_TRY(swiglu_fwd(s, n * rd, A, G, bw.eH));
-      } else if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, A, G, bw.eH, Y)) != STCA_OK) {
+      } else if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, A, G, bw.eH, Y, bw.WuT[i], bw.WvT[i])) != STCA_OK) {
         return st;
       }
       if ((st = ffn_backward(s, dm, &w->hist[i], g->hist[i], true, n, Xc, bf, A, G, bw.eH, Y,

@@ -338,6 +338,115 @@ hipError_t gemm(hipStream_t s, const GemmArgs &g) {
 }
 
 // ------------------------------------------------------------------------------------------
+// C[M x N] (fp32) = A[M x K] Bt[N x K]^T with bf16 A and Bt, on v_mfma_f32_32x32x16_bf16.  Products of
+// two bf16 values are exact in fp32 and the accumulation is fp32, so this matches the fp32 forms up
+// to summation order.  128 x 128 tiles, four waves of 64 x 64, k in steps of 32 through
+// double-buffered k-contiguous LDS tiles (rows padded to 40 bf16 so 16-byte fragment reads spread
+// over the banks); in a 16-deep MFMA step lane group g covers k = 8 g .. 8 g + 7 of both operands.
+// K, lda and ldb multiples of 8, bases 16-byte aligned.
+// ------------------------------------------------------------------------------------------
+constexpr int BT = 128, BK = 32, BKP = 40;
+
+__global__ __launch_bounds__(256) void gemm_bf16_nt_kernel(int M, int N, int K, const bf16 *__restrict__ A,
+                                                           int64_t lda, const bf16 *__restrict__ Bt, int64_t ldb,
+                                                           float *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BT][BKP];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BT][BKP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * BT, n0 = blockIdx.x * BT;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, g8 = (lane >> 5) * 8, lr = lane & 31;
+  bf16x8 ra[2], rb[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = (tid >> 2) + 64 * e, k = k0 + (tid & 3) * 8;
+      ra[e] = (m0 + r < M && k < K) ? *(const bf16x8 *)(A + (int64_t)(m0 + r) * lda + k) : bf16x8{};
+      rb[e] = (n0 + r < N && k < K) ? *(const bf16x8 *)(Bt + (int64_t)(n0 + r) * ldb + k) : bf16x8{};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = (tid >> 2) + 64 * e, c = (tid & 3) * 8;
+      *(bf16x8 *)&As[buf][r][c] = ra[e];
+      *(bf16x8 *)&Bs[buf][r][c] = rb[e];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  load(0);
+  store(0);
+  __syncthreads();
+  const int steps = (K + BK - 1) / BK;
+  for (int st = 0; st < steps; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < steps;
+    if (more) load((st + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *(const bf16x8 *)&As[cur][wm + 32 * i + lr][16 * kk + g8];
+        b[i] = *(const bf16x8 *)&Bs[cur][wn + 32 * i + lr][16 * kk + g8];
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32x32x16(a[bi], b[bj], acc[bi][bj]);
+    }
+    if (more) store(cur ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int col = n0 + wn + 32 * bj + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm + 32 * bi + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row < M) C[(int64_t)row * ldc + col] = acc[bi][bj][e];
+      }
+    }
+}
+
+hipError_t gemm_bf16_nt(hipStream_t s, int M, int N, int K, const void *A, int64_t lda, const void *Bt, int64_t ldb,
+                        float *C, int64_t ldc) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 8 || lda % 8 || ldb % 8 || (((uintptr_t)A | (uintptr_t)Bt) & 15)) return hipErrorInvalidValue;
+  const int64_t gy = (M + BT - 1) / BT;
+  if (gy > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_bf16_nt_kernel, dim3((unsigned)((N + BT - 1) / BT), (unsigned)gy), dim3(256), 0, s, M, N,
+                     K, (const bf16 *)A, lda, (const bf16 *)Bt, ldb, C, ldc);
+  return hipGetLastError();
+}
+
+// out[c][r] = in[r][c] for a rows x cols bf16 matrix (row-major in and out).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(int rows, int cols, const uint16_t *__restrict__ in,
+                                                             uint16_t *__restrict__ out) {
+  const int64_t n = (int64_t)rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t c = i / rows, r = i % rows;  // output index i = c * rows + r
+    out[i] = in[r * cols + c];
+  }
+}
+
+hipError_t transpose_bf16(hipStream_t s, int rows, int cols, const void *in, void *out) {
+  const int64_t n = (int64_t)rows * cols;
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows, cols,
+                     (const uint16_t *)in, (uint16_t *)out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // SwiGLU gate in place: A[i] <- A[i] * SiLU(G[i])   (eq. (1))
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gate_kernel(int64_t n, float *__restrict__ A,

@@ -29,6 +29,12 @@ struct RaggedDesc {
 hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs, int n, int64_t max_m,
                        int64_t max_n);
 hipError_t swiglu_gate_inplace(hipStream_t s, int64_t n, float *A, const float *G);
+// C[M x N] (fp32) = A[M x K] Bt[N x K]^T, A and Bt bf16 (exact products, fp32 accumulation) on bf16
+// matrix cores; K, lda, ldb multiples of 8, bases 16-byte aligned.
+hipError_t gemm_bf16_nt(hipStream_t s, int M, int N, int K, const void *A, int64_t lda, const void *Bt, int64_t ldb,
+                        float *C, int64_t ldc);
+// out (cols x rows) = in (rows x cols)^T, bf16.
+hipError_t transpose_bf16(hipStream_t s, int rows, int cols, const void *in, void *out);
 hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, int64_t ldy, void *out,
                           int64_t ldo, bool out_bf16, const float *gamma, const float *beta, float eps);
 // dst[n] (bf16) = src[n] (fp32) rounded to nearest even; n a multiple of 4.
