@@ -137,8 +137,8 @@ template <typename T, bool KCONT> struct TileLoader {
       if (KCONT) {
         const int r = (tid >> 2) + 64 * e, k = k0 + (tid & 3) * 4;
         v[e] = (r0 + r < rows && k < K) ? vec4_of<T>::load(P + (int64_t)(r0 + r) * ld + k) : f32x4{0, 0, 0, 0};
-      } else {
-        const int k = k0 + (tid >> 5) + 8 * e, r = r0 + (tid & 31) * 4;
+      } else {  // a 2 (k) x 4 (rows) block per thread: k = 2 (tid >> 5) + e, rows 4 (tid & 31) ..
+        const int k = k0 + 2 * (tid >> 5) + e, r = r0 + (tid & 31) * 4;
         v[e] = (k < K && r < rows) ? vec4_of<T>::load(P + (int64_t)k * ld + r) : f32x4{0, 0, 0, 0};
       }
     }
@@ -148,10 +148,13 @@ template <typename T, bool KCONT> struct TileLoader {
     for (int e = 0; e < 2; ++e) {
       if (KCONT) {
         *(f32x4 *)&S[(tid >> 2) + 64 * e][(tid & 3) * 4] = v[e];
-      } else {
-        const int k = (tid >> 5) + 8 * e, r = (tid & 31) * 4;
+      } else if (e == 0) {  // transposed in registers: row r + i gets (k, k + 1) as one 8-byte store
+        const int k = 2 * (tid >> 5), r = (tid & 31) * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[r + i][k] = v[e][i];
+        for (int i = 0; i < 4; ++i) {
+          typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+          *(f32x2 *)&S[r + i][k] = f32x2{v[0][i], v[1][i]};
+        }
       }
     }
   }
