@@ -85,6 +85,7 @@ def run_case(B, cfg, inp, W, query_ln=False, seed=5, keep=False):
 CASES = [
     ("tiny", dict(), False, False),
     ("tiny", dict(M=3, n_users=3, length=("fixed", 40), targets=("fixed", 3)), True, True),
+    ("tiny", dict(M=4, n_users=2, length=("fixed", 33), targets=("fixed", 2), dtype="bf16"), False, True),
     ("uniform", dict(n_users=3, length=("fixed", 200)), False, False),
     ("ragged", dict(n_users=5, length=("lognormal", 150.0, 200.0, 16, 600)), False, True),
     ("ragged", dict(n_users=4, dtype="f32", length=("lognormal", 100.0, 150.0, 16, 400)), True, False),
@@ -104,7 +105,7 @@ def test_backward_matches_oracle(B, key, change, query_ln, separate):
     run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln)
 
 
-@pytest.mark.parametrize("key,change,query_ln,separate", [CASES[1], CASES[3], CASES[6]],
+@pytest.mark.parametrize("key,change,query_ln,separate", [CASES[1], CASES[4], CASES[7]],
                          ids=["tiny-M3", "ragged-small", "ragged-40"])
 def test_backward_keep_workspace(B, key, change, query_ln, separate):
     """The larger workspace that keeps the encode's intermediates from the forward recompute gives
