@@ -1,10 +1,15 @@
-"""STCA forward benchmark on one MI355X.
+"""STCA benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense10k] [--no-cpu-baseline]
+    python bench.py --backward [--workload ragged] [--no-keep]
+    python bench.py --sl | --litm
 
-One step = one stca_forward over the whole batch: M history encodes, the query path and M
-split-L attention passes.  Inputs are seeded synthetic data resident in HBM before timing.
-Prints one JSON line (history tokens per second, whole job).
+Default mode: one step = one stca_forward over the whole batch (M history encodes, the query path
+and M split-L attention passes).  Inputs are seeded synthetic data resident in HBM before timing.
+Prints one JSON line (history tokens per second, whole job) with the roofline of the dominant
+kernel (the encode), the attention's, the oracle timed on the host, the graph-replay time and the
+prediction token of eq. (9).  --backward times stca_backward on the training-shaped batch, --sl a
+stochastic-length batch and --litm a batch after local same-ID token merging.
 """
 from __future__ import annotations
 
