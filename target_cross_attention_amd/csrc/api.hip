@@ -546,7 +546,7 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
 }
 
 // ---- backward (gradients of eqs. (2)-(8)) ------------------------------------------------------
-constexpr int kWgradParts = 64;    // split-K blocks of one weight gradient
+constexpr int kWgradParts = 32;    // split-K blocks of one weight gradient
 constexpr int kLnBlocks = 256;     // row blocks of the LayerNorm derivative (partial column sums)
 
 struct BackwardWs {
