@@ -2,7 +2,8 @@
 stca_forward on the same buffers.  Both run the same kernels in the same order on the same data,
 so every replay must reproduce the eager output bit for bit; the eager output itself is checked
 against the oracle by the parity tests.  Replays are interleaved with other eager work, and the
-inputs are rewritten in place between replays (a replay reads the buffers as they are then)."""
+inputs are rewritten in place between replays (a replay reads the buffers as they are then).  Also:
+forwards on two streams at once, each with its own workspace, against the same forwards in turn."""
 import numpy as np
 import pytest
 
@@ -75,3 +76,31 @@ def test_graph_of_batch_without_targets(B):
     graph.launch()
     torch.cuda.synchronize()
     graph.close()
+
+
+def test_concurrent_forwards_on_two_streams(B):
+    """The library keeps no mutable state: two forwards of different batches, each with its own
+    workspace, enqueued on two streams at once give the same bits as one after the other."""
+    announce("two-streams")
+    cfg_a = SI.scaled(SI.get_config("ragged"), n_users=6, length=("lognormal", 400.0, 500.0, 1, 2000))
+    cfg_b = SI.scaled(SI.get_config("uniform"), n_users=5, length=("fixed", 700))
+    runs = []
+    for cfg in (cfg_a, cfg_b):
+        W = SI.make_weights(cfg)
+        inp = SI.make_inputs(cfg)
+        dims = B.dims_for(cfg)
+        dw, db = B.DeviceWeights(W, cfg.dtype, DEV), B.DeviceBatch(inp, DEV)
+        ref = B.stca_forward(dims, dw, db).clone()
+        torch.cuda.synchronize()
+        ws = B.workspace(B.forward_workspace_size(dims, db.c), DEV)
+        runs.append((dims, dw, db, ref, ws))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full_like(r[3], float("nan")) for r in runs]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (dims, dw, db, ref, ws), st, Z in zip(runs, streams, outs):
+            with torch.cuda.stream(st):
+                B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=st)
+    torch.cuda.synchronize()
+    for (dims, dw, db, ref, ws), Z in zip(runs, outs):
+        assert torch.equal(Z, ref)
