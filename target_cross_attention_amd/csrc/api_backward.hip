@@ -138,7 +138,7 @@ int wgrad(hipStream_t s, int Mr, int Nc, int64_t K, const void *A, int64_t lda, 
   return STCA_OK;
 }
 
-// C[m x n] (+)= alpha A B^T-or-B with the generic kernel (small helper for the products below).
+// C[m x n] = A B (or A B^T with trans_b) + beta C through the generic GEMM (a helper for the products below).
 hipError_t mm(hipStream_t s, int m, int n, int k, const void *A, int64_t lda, bool a_bf16, const void *B,
               int64_t ldb, bool b_bf16, bool trans_b, float *C, int64_t ldc, float beta) {
   GemmArgs g;
@@ -237,8 +237,6 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
   if (b->total_T > 0 && (!xt || !dZ)) return fail(STCA_E_ARG, "xt or dZ is NULL");
   if (!aligned16(X) || !aligned16(xt) || !aligned16(dZ)) return fail(STCA_E_ALIGN, "X/xt/dZ not 16-byte aligned");
   if (b->total_T > (int64_t)1 << 22) return fail(STCA_E_ARG, "total_T %lld exceeds 2^22", (long long)b->total_T);
-  if (b->n_users > 0 && b->total_T > 0 && b->total_L / std::max<int64_t>(1, b->n_users) > ((int64_t)1 << 40))
-    return fail(STCA_E_ARG, "history too long");
   BackwardWs bw;
   const size_t need = carve_backward(nullptr, dm, b, bw, false);
   if (!ws || ws_bytes < need)
