@@ -143,9 +143,11 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
   constexpr int LPW = INSTR / 4;                  // per wave
   // Tiles pass through registers into a 3-slot LDS ring: tile k+2 is written while tile k+1's
-  // scores and tile k's PV product read the other two slots, and tile k+3 is fetched from HBM
-  // into the registers it leaves.  (No direct-to-LDS loads: with one in flight the compiler
-  // makes every transposed LDS read wait for all outstanding loads, serialising the pipeline.)
+  // scores and tile k's PV product read the other two slots, and tile k+2+NB is fetched from HBM
+  // into the registers it leaves.  NB register sets keep NB tiles in flight per wave: with one,
+  // the loads have a single iteration to arrive and the loaded HBM latency sets the pace.  (No
+  // direct-to-LDS loads: with one in flight the compiler makes every transposed LDS read wait
+  // for all outstanding loads, serialising the pipeline.)
   constexpr int NSL = 3;
   // At d = 512 a wave keeps half of the output features: two waves (wave, wave ^ 1) share a
   // 32-row block, each computes the scores over its half of d, and the pair adds the two partial
@@ -153,6 +155,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr int FH = attn_feature_halves(D);
   constexpr int NOBW = NOB / FH;                  // output blocks per wave
   constexpr int NKW = NKS / FH;                   // score k-steps per wave
+  constexpr int NB = D <= 256 ? 2 : 1;          // register sets (d = 512 has no registers to spare)
   static_assert(INSTR % 4 == 0, "tile loads split evenly over 4 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
   // Partial score tiles of the pairs (FH = 2): [tile parity][wave][register quad][lane].
@@ -230,14 +233,23 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  u32x4 rg[LPW];  // the tile between its fetch (one iteration ahead) and its put
-  fetch(0, rg);
-  put(0, rg);
+  // Tile j >= 2 waits in register set (j - 2) mod NB between its fetch and its put.  Every
+  // iteration fetches, also past the last tile (it re-reads the last one, from cache): loads
+  // issued on some paths only would make the compiler's count of loads in flight conservative
+  // at the join, and each put would then wait for every outstanding load.
+  u32x4 rgb[NB][LPW];
+  fetch(0, rgb[0]);
+  put(0, rgb[0]);
   if (1 < ntiles) {
-    fetch(1, rg);
-    put(1, rg);
+    fetch(1, rgb[0]);
+    put(1, rgb[0]);
   }
-  if (2 < ntiles) fetch(2, rg);
+  if constexpr (NB > 1) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) fetch(min(2 + b, ntiles - 1), rgb[b]);
+  } else if (2 < ntiles) {
+    fetch(2, rgb[0]);
+  }
 
   f32x16 oacc[NOBW];
 #pragma unroll
@@ -370,10 +382,13 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
 
   // Pipeline: iteration k computes the scores of tile k+1 (matrix cores) while the vector ALU
   // turns the scores of tile k into probabilities, then the PV product of tile k.  Tiles k and
-  // k+1 are in LDS; tile k+2 is written from registers into the slot of tile k-1, and tile k+3
-  // is fetched into the registers it leaves.  The accumulators are touched only by MFMAs inside
-  // the loop: when a row maximum outgrows the slack the loop is left, the rescale runs, the
-  // tile is finished and the loop resumes.  The running maximum starts at the first tile's.
+  // k+1 are in LDS; tile k+2 is written from registers into the slot of tile k-1, and tile
+  // k+2+NB is fetched into the registers it leaves.  The loop is unrolled NB times so that each
+  // step names its register set statically.  The accumulators are touched only by MFMAs inside
+  // the loop: when a row maximum outgrows the slack the loop is left, the rescale runs and the
+  // tile is finished.  Every path back into the loop arrives after a step on the last register
+  // set, so the compiler sees the same loads in flight, in the same order, on each of them.
+  // The running maximum starts at the first tile's.
   sync();
   // Pairs (FH = 2): publish this wave's partial score tile of tile k; after the next workgroup
   // barrier the partner adds it (both waves then hold bit-identical scores: a + b = b + a).
@@ -425,21 +440,25 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         pv(tile_off(k), pb, H1{});
     }
   };
-  // One step on tile k.  Returns true when a row maximum outgrew the slack: the caller then
-  // rescales and finishes tile k.  The score MFMAs of tile k+1 go one per group, and each group
-  // also turns one score of tile k into its probability (exp2, bf16, running sum) and folds it
-  // into the tile's maximum, so that this vector work runs in the matrix cores' shadow (the
-  // order is pinned: left alone, the compiler issues all MFMAs first).  The probabilities are
-  // computed against the running maximum before the tile's own maximum is known; when that
-  // maximum outgrew the slack they are discarded and the caller recomputes them after the
-  // rescale.  The PV product of tile k follows.
+  // One step on tile k, with register set BI.  Returns true when a row maximum outgrew the
+  // slack: the caller then rescales and finishes tile k.  The score MFMAs of tile k+1 go one per
+  // group, and each group also turns one score of tile k into its probability (exp2, bf16,
+  // running sum) and folds it into the tile's maximum, so that this vector work runs in the
+  // matrix cores' shadow (the order is pinned: left alone, the compiler issues all MFMAs
+  // first).  The probabilities are computed against the running maximum before the tile's own
+  // maximum is known; when that maximum outgrew the slack they are discarded and the caller
+  // recomputes them after the rescale.  The PV product of tile k follows.
   constexpr int kRingA = 4, kAheadA = 3;
   constexpr int NGA = NKW > 16 ? NKW : 16;
-  auto step = [&](int k, f32x16 &sc, float &mx) -> bool {
+  auto step = [&](int k, auto BI, f32x16 &sc, float &mx) -> bool {
+    constexpr int b = decltype(BI)::value;
     sync();  // tile k+1 is in LDS; tile k-1's slot is free
-    if (k + 2 < ntiles) {
-      put((k + 2) % NSL, rg);
-      if (k + 3 < ntiles) fetch(k + 3, rg);
+    if constexpr (NB > 1) {
+      if (k + 2 < ntiles) put((k + 2) % NSL, rgb[b]);
+      fetch(min(k + 2 + NB, ntiles - 1), rgb[b]);
+    } else if (k + 2 < ntiles) {  // one set: its put waits for the newest loads in any case
+      put((k + 2) % NSL, rgb[b]);
+      if (k + 3 < ntiles) fetch(k + 3, rgb[b]);
     }
     if (!wave_active) return false;
     const bool has_next = k + 1 < ntiles;
@@ -498,14 +517,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     }
     return false;
   };
-  int k = 0;
-  while (true) {
-    f32x16 sc;
-    float mx = 0.f;
-    for (; k < ntiles; ++k)
-      if (step(k, sc, mx)) break;
-    if (k >= ntiles) break;
-    // rescale (rare), then finish tile k.  Both halves of a row take the same new maximum.
+  // Rescale (rare), then finish tile k.  Both halves of a row take the same new maximum.
+  auto rescale_finish = [&](int k, const f32x16 &sc, float mx) {
     const float m_new = fmaxf(m_run, half_max(mx));
     const float sf = fast_exp2(m_run - m_new);
 #pragma unroll
@@ -515,8 +528,47 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     s_run *= sf;
     m_run = m_new;
     tail(k, sc);
-    if (k + 1 < ntiles) publish(k + 1, sa + sb);  // step k returned before publishing
-    ++k;
+    if (k + 1 < ntiles) publish(k + 1, sa + sb);  // the step returned before publishing
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, (NB > 1 ? 1 : 0)>;
+  int k = 0;
+  if constexpr (NB > 1) {
+    while (k < ntiles) {  // k is even here, and register set 1 holds the newest loads
+      f32x16 sc;
+      float mx = 0.f;
+      int hk = -1;
+      for (;;) {  // the back edge follows a step on set 1 only
+        if (step(k, B0{}, sc, mx)) {
+          hk = k;
+          break;
+        }
+        if (k + 1 >= ntiles) break;
+        if (step(k + 1, B1{}, sc, mx)) {
+          hk = k + 1;
+          break;
+        }
+        k += 2;
+        if (k >= ntiles) break;
+      }
+      if (hk < 0) break;
+      rescale_finish(hk, sc, mx);
+      if (hk == k) {  // stopped on set 0: tile k+1 runs on set 1 before the loop is re-entered
+        if (k + 1 >= ntiles) break;
+        if (step(k + 1, B1{}, sc, mx)) rescale_finish(k + 1, sc, mx);
+      }
+      k += 2;
+    }
+  } else {
+    while (true) {
+      f32x16 sc;
+      float mx = 0.f;
+      for (; k < ntiles; ++k)
+        if (step(k, B0{}, sc, mx)) break;
+      if (k >= ntiles) break;
+      rescale_finish(k, sc, mx);
+      ++k;
+    }
   }
 
   if (!wave_active) return;
