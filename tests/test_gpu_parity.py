@@ -125,12 +125,14 @@ def _attend_case(B, cfg, inp, W, layer, chunk):
     return o.cpu().numpy(), np.concatenate(refs)
 
 
-@pytest.mark.parametrize("d,h", [(128, 8), (512, 16)])
+@pytest.mark.parametrize("d,h", [(128, 8), (256, 8), (512, 16)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("chunk", [0, 64, 96, 1024])
 def test_attend_ragged_split(B, dtype, chunk, d, h):
     """Ragged lengths (1 .. ~1500, not multiples of 32), 1..several targets, several chunk sizes
-    so users span one or many split-L chunks and the combine step runs."""
+    so users span one or many split-L chunks and the combine step runs.  Chunks of 64 and 96
+    tokens give work items of 1, 2 and 3 tiles: an odd or even count, shorter than the kernel's
+    tile prefetch distance."""
     cfg = SI.scaled(SI.get_config("ragged"), d=d, h=h, M=2, r=2, dtype=dtype)
     announce("attend", d, dtype, "chunk", chunk)
     W = SI.make_weights(cfg)
