@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
 
   WorkItem it;
   if (!my_item(items, n_items, it)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, gl = lane >> 5;
   const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
   const int64_t t0 = L0 + (int64_t)it.chunk * chunk;
@@ -171,7 +171,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   const int64_t T0 = toff[it.user];
   const int R = (int)((toff[it.user + 1] - T0) * h);
   const int64_t rowbase = T0 * h;
-  const int fh = wave % FH;
+  // The wave index is uniform (readfirstlane), so control flow on it stays scalar; fh is taken
+  // from threadIdx.x instead, because with a scalar fh the compiler spills at d = 512.
+  const int fh = (int)(threadIdx.x >> 6) % FH;
   const int r0 = it.group * attn_rows_per_group(D) + (wave / FH) * 32;
   const bool wave_active = r0 < R;
   const int myrow = r0 + col;
