@@ -156,6 +156,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   constexpr int NOBW = NOB / FH;                  // output blocks per wave
   constexpr int NKW = NKS / FH;                   // score k-steps per wave
   constexpr int NB = D <= 256 ? 2 : 1;          // register sets (d = 512 has no registers to spare)
+  constexpr int NCH = FH > 1 ? 2 : 1;           // score accumulation chains
   static_assert(INSTR % 4 == 0, "tile loads split evenly over 4 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
   // Partial score tiles of the pairs (FH = 2): [tile parity][wave][register quad][lane].
@@ -304,8 +305,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // ds_read instructions, counted by lgkmcnt only, independent of the tile loads in flight).
   const STCA_LDS char *lds = (const STCA_LDS char *)&tiles[0][0];
   constexpr uint32_t kTileBytes = 32 * CPR * 16;
-  // Scores of one tile into two independent accumulation chains (halves of the d reduction);
-  // their sum lands in fresh registers, leaving both chains free for the next tile.
+  // Scores of one tile into NCH accumulation chains.  One chain (d <= 256) saves the per-step sum
+  // of two accumulators and its copies; at d = 512 the k-steps alternate between two chains,
+  // whose sum lands in fresh registers, leaving both free for the next tile.
   // This wave's k-steps start 32 NKW fh bytes into a row.  The swizzle acts on the chunk index
   // (bits 4.. of the byte offset), which that start may share, so it stays inside the XOR.
   const uint32_t kofs = (uint32_t)(32 * NKW * fh);
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     for (int ks = 0; ks < NKW; ++ks) {
       const uint32_t off = rb + (((uint32_t)(32 * ks) + kofs) ^ rx);
       const bf16x8 a = *(const STCA_LDS bf16x8 *)(lds + off);
-      if (ks & 1)
+      if (NCH > 1 && (ks & 1))
         s1 = mfma32x32x16(a, ub[ks], ks == 1 ? f32x16{} : s1);
       else
         s0 = mfma32x32x16(a, ub[ks], ks == 0 ? f32x16{} : s0);
@@ -413,20 +415,24 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     return own;
   };
   f32x16 sa = f32x16{}, sb = f32x16{};
+  auto score_tile = [&]() {
+    if constexpr (NCH > 1) return sa + sb;
+    else return sa;
+  };
   if constexpr (FH == 1) {
     if (wave_active) {
       scores(tile_off(0), sa, sb);
-      f32x16 s0 = sa + sb;
+      f32x16 s0 = score_tile();
       m_run = half_max(row_max(s0, tile_rem(0)));
     }
   } else {
     if (wave_active) {
       scores(tile_off(0), sa, sb);
-      publish(0, sa + sb);
+      publish(0, score_tile());
     }
     sync();
     if (wave_active) {
-      f32x16 s0 = with_partner(0, sa + sb);
+      f32x16 s0 = with_partner(0, score_tile());
       m_run = half_max(row_max(s0, tile_rem(0)));
     }
   }
@@ -464,7 +470,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     }
     if (!wave_active) return false;
     const bool has_next = k + 1 < ntiles;
-    sc = with_partner(k, sa + sb);
+    sc = with_partner(k, score_tile());
     const int rem = tile_rem(k);
     if (rem < 32) {
 #pragma unroll
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       for (int g = 0; g < NGA; ++g) {
         if (g < NKW) {
           if (g + kAheadA < NKW) fr[(g + kAheadA) % kRingA] = frag(g + kAheadA);
-          if (g & 1)
+          if (NCH > 1 && (g & 1))
             sb = mfma32x32x16(fr[g % kRingA], ub[g], g == 1 ? f32x16{} : sb);
           else
             sa = mfma32x32x16(fr[g % kRingA], ub[g], g == 0 ? f32x16{} : sa);
@@ -515,7 +521,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         pv(tile_off(k), pb, H0{});
       else
         pv(tile_off(k), pb, H1{});
-      if (has_next) publish(k + 1, sa + sb);
+      if (has_next) publish(k + 1, score_tile());
     }
     return false;
   };
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     s_run *= sf;
     m_run = m_new;
     tail(k, sc);
-    if (k + 1 < ntiles) publish(k + 1, sa + sb);  // the step returned before publishing
+    if (k + 1 < ntiles) publish(k + 1, score_tile());  // the step returned before publishing
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, (NB > 1 ? 1 : 0)>;
