@@ -376,6 +376,45 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       }
     }
   };
+  // The same product with its operands read ahead (one wave per row block, d >= 128): the reads
+  // for the first PVA output blocks are issued when the step starts, so they land during the
+  // score phase, and each later block's reads go out PVA blocks before its MFMAs.
+  constexpr bool PVPRE = FH == 1 && D >= 128;
+  constexpr int PVA = 2;
+  uint32_t pvb[NTB];
+  bf16x8 xr[PVA + 1][2];
+  auto xt_frag = [&](int ob, int kk) {
+    s16x4 half[2];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      int bi = 0;
+      const uint32_t C = tr_offset(ob, kk, sh, bi);
+      half[sh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + pvb[bi] + C));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv_start = [&](uint32_t toff) {
+#pragma unroll
+    for (int i = 0; i < NTB; ++i) {
+      pvb[i] = tbase[i] + toff;
+      asm volatile("" : "+v"(pvb[i]));
+    }
+#pragma unroll
+    for (int ob = 0; ob < PVA; ++ob)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) xr[ob][kk] = xt_frag(ob, kk);
+  };
+  auto pv_finish = [&](const bf16x8 (&pb)[2]) {
+#pragma unroll
+    for (int ob = 0; ob < NOBW; ++ob) {
+      if (ob + PVA < NOBW)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) xr[(ob + PVA) % (PVA + 1)][kk] = xt_frag(ob + PVA, kk);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) oacc[ob] = mfma32x32x16(xr[ob % (PVA + 1)][kk], pb[kk], oacc[ob]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, (FH > 1 ? 1 : 0)>;
   auto tile_rem = [&](int k) {
@@ -495,6 +534,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       bf16x8 fr[kRingA];
 #pragma unroll
       for (int q = 0; q < kAheadA; ++q) fr[q] = frag(q);
+      if constexpr (PVPRE) pv_start(tile_off(k));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < NGA; ++g) {
@@ -509,12 +549,15 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      if constexpr (PVPRE) pv_start(tile_off(k));
 #pragma unroll
       for (int i = 0; i < 16; ++i) element(i);
     }
     if (wave_any(mx > m_run + kLazy)) return true;
     s_run += psum;
-    if constexpr (FH == 1) {
+    if constexpr (PVPRE) {
+      pv_finish(pb);
+    } else if constexpr (FH == 1) {
       pv(tile_off(k), pb, H0{});
     } else {
       if (fh == 0)
