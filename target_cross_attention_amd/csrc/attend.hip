@@ -236,10 +236,11 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // Tile j >= 2 waits in register set (j - 2) mod NB between its fetch and its put.  Every
-  // iteration fetches, also past the last tile (it re-reads the last one, from cache): loads
-  // issued on some paths only would make the compiler's count of loads in flight conservative
-  // at the join, and each put would then wait for every outstanding load.
+  // Tile j >= 2 waits in register set (j - 2) mod NB between its fetch and its put.  With two
+  // sets every iteration fetches, also past the last tile (it re-reads the last one, from
+  // cache): loads issued on some paths only would make the compiler's count of loads in flight
+  // conservative at the join, and each put would then wait for every outstanding load.  With
+  // one set the put waits for the newest loads anyway, and the fetches stop at the last tile.
   u32x4 rgb[NB][LPW];
   fetch(0, rgb[0]);
   put(0, rgb[0]);
