@@ -241,6 +241,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   // cache): loads issued on some paths only would make the compiler's count of loads in flight
   // conservative at the join, and each put would then wait for every outstanding load.  With
   // one set the put waits for the newest loads anyway, and the fetches stop at the last tile.
+  // The re-reads past the end are never consumed; the wave's end waits for them (s_endpgm
+  // waits for all outstanding memory operations), so no register is written after it.
   u32x4 rgb[NB][LPW];
   fetch(0, rgb[0]);
   put(0, rgb[0]);
