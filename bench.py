@@ -360,8 +360,8 @@ def main():
     a = ap.parse_args()
 
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the forward shards by user with no exchange; multi-GPU is not built)"}))
+        print(json.dumps({"error": "the STCA path here runs on one GPU; --gpus must be 1 "
+                          "(the forward would shard by user with no exchange; no multi-GPU path exists)"}))
         sys.exit(2)
 
     import numpy as np
