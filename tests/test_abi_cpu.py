@@ -264,3 +264,17 @@ def test_forward_graph_validation():
     assert out.value is None
     assert B.LIB.stca_graph_destroy(None) == 0
     assert B.LIB.stca_graph_launch(None, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: a request for several exits with status 2 and says why, before
+    touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
