@@ -54,6 +54,18 @@ def measured_traffic(workload: str, kernel: str, src_files):
     return e.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, W, target_s: float = 12.0, max_users: int = 64):
     """The oracle, as it stands, on users of the same workload until ~target_s of CPU work."""
     import numpy as np
@@ -80,6 +92,7 @@ def cpu_baseline(cfg, W, target_s: float = 12.0, max_users: int = 64):
         if time.perf_counter() - t0 >= target_s:
             break
     return {"value": tokens / elapsed, "unit": "history-tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{users} of {cfg.n_users} users ({tokens} history tokens, {targets} targets), "
                       f"numpy float64 per-user forward, {elapsed:.1f} s",
             "targets_per_s": targets / elapsed}
@@ -332,6 +345,7 @@ def cpu_baseline_backward(cfg, W, target_s: float = 12.0, max_users: int = 64):
         if time.perf_counter() - t0 >= target_s:
             break
     return {"value": tokens / elapsed, "unit": "history-tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{users} of {cfg.n_users} users ({tokens} history tokens), numpy float64 per-user "
                       f"backward (oracle.grad), {elapsed:.1f} s"}
 

@@ -27,9 +27,13 @@
  *     valid once the stream has reached the call's end.  No call synchronises the device.
  *   - Every argument error the host can see is returned as a negative stca_status BEFORE any
  *     work is enqueued.  A failed launch returns STCA_E_HIP (stca_last_error() has the detail).
- *   - Offsets are caller contract, not checked on the device: hist_off/tgt_off start at 0, are
- *     nondecreasing and end at total_L/total_T.  A user with no targets is allowed; a user with
- *     an empty history (softmax over no tokens is undefined) gets NaN outputs for its targets.
+ *   - Offsets are caller contract: hist_off/tgt_off start at 0, are nondecreasing, end at
+ *     total_L/total_T, and no user exceeds max_L history rows or max_T targets.  A user with no
+ *     targets is allowed; a user with an empty history (softmax over no tokens is undefined) gets
+ *     NaN outputs for its targets.  The ragged kernels check the offsets on the device before they
+ *     use them: a batch that breaks the contract makes stca_forward / stca_attend write NaN to
+ *     every output row (stca_backward: meaningless gradients) rather than touch memory outside
+ *     their buffers.  stca_validate_batch reports which condition a batch breaks.
  */
 #ifndef STCA_H
 #define STCA_H
@@ -61,8 +65,9 @@ typedef enum {
 typedef enum { STCA_F32 = 0, STCA_BF16 = 1 } stca_dtype;
 
 /* Model sizes.  Supported: d in {64, 128, 256, 512}; h divides d; 1 <= r <= 8; 1 <= M <= STCA_MAX_M.
- * dtype STCA_BF16 runs the MFMA path (bf16 storage, fp32 accumulation); STCA_F32 runs the fp32
- * debug path (fp32 everywhere, plain vector ALU). */
+ * dtype STCA_BF16 runs the MFMA path (bf16 storage, bf16 matrix-core products, fp32 accumulation);
+ * STCA_F32 runs the fp32 debug path: fp32 storage, products and accumulation throughout, the
+ * larger products on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), the rest on the vector ALU. */
 typedef struct {
   int32_t d, h, M, r;
   int32_t dtype;      /* stca_dtype */
@@ -312,6 +317,21 @@ STCA_API int stca_forward_graph_create(const stca_dims *dims, const stca_weights
                                        size_t workspace_bytes, stca_graph **out);
 STCA_API int stca_graph_launch(stca_graph *g, void *stream);
 STCA_API int stca_graph_destroy(stca_graph *g); /* NULL is a no-op */
+
+/* ---- batch check (debug) -----------------------------------------------------------------------
+ * Checks the device offsets of `batch` against its host fields and writes to *result (a device
+ * int32) the OR of the conditions it breaks, 0 for a batch that meets the contract.  Asynchronous
+ * on `stream`; read *result after the stream has reached the call.  Host argument errors are
+ * returned before any work, as for the other calls. */
+enum {
+  STCA_BATCH_BAD_START = 1,       /* hist_off[0] or tgt_off[0] is not 0 */
+  STCA_BATCH_BAD_END = 2,         /* hist_off[n_users] != total_L or tgt_off[n_users] != total_T */
+  STCA_BATCH_DECREASING = 4,      /* an offset array decreases */
+  STCA_BATCH_OVER_MAX_L = 8,      /* a user has more than max_L history rows */
+  STCA_BATCH_OVER_MAX_T = 16,     /* a user has more than max_T targets */
+  STCA_BATCH_EMPTY_HISTORY = 32   /* a user with targets has no history (allowed: NaN outputs) */
+};
+STCA_API int stca_validate_batch(const stca_batch *batch, int32_t *result, void *stream);
 
 /* ---- diagnostics ---------------------------------------------------------------------------- */
 STCA_API const char *stca_status_string(int status);

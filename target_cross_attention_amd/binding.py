@@ -29,7 +29,7 @@ EXPORTS = [
     "stca_backward_workspace_size", "stca_backward_workspace_size_keep", "stca_backward", "stca_backward_profiled",
     "stca_forward_graph_create", "stca_graph_launch", "stca_graph_destroy", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
-    "stca_last_error", "stca_version",
+    "stca_last_error", "stca_version", "stca_validate_batch",
 ]
 
 
@@ -112,6 +112,7 @@ def _load() -> ctypes.CDLL:
         "stca_profiler_destroy": [P],
         "stca_profiler_reset": [P],
         "stca_profiler_read": [P, P],
+        "stca_validate_batch": [P, P, P],
         "stca_status_string": [c_int],
         "stca_last_error": [],
         "stca_version": [],
@@ -177,6 +178,16 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _on(stream):
+    """Context in which tensors the binding allocates for a call (outputs, workspaces) belong to the
+    call's stream: torch's caching allocator ties a block to the stream current at allocation and
+    reuses it on that stream once freed, so a workspace dropped after an asynchronous call on a
+    non-current stream is never handed to other work before that call has finished."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 # ----------------------------------------------------------------------------------------------
 # device-resident inputs
 # ----------------------------------------------------------------------------------------------
@@ -184,10 +195,10 @@ def to_device(a: np.ndarray, dtype: str, device):
     """Host array -> device tensor in the storage type: uint16 bf16 patterns or float32."""
     import torch
     if dtype == "bf16":
-        if a.dtype != np.uint16:
-            from stca_inputs import bf16_bits
-            a = bf16_bits(a)
-        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+        if a.dtype == np.uint16:  # already bf16 bit patterns
+            return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+        # torch's float32 -> bfloat16 conversion rounds to nearest even
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
@@ -292,10 +303,11 @@ def stca_encode(dims: Dims, ffn: Ffn, X, Xt=None, ws=None, stream=None):
     """eq. (2) for every row of X (device tensor, storage dtype).  Returns Xt."""
     import torch
     n = X.shape[0]
-    if Xt is None:
-        Xt = torch.empty_like(X)
-    if ws is None:
-        ws = workspace(encode_workspace_size(dims, n), X.device)
+    with _on(stream):
+        if Xt is None:
+            Xt = torch.empty_like(X)
+        if ws is None:
+            ws = workspace(encode_workspace_size(dims, n), X.device)
     _check(LIB.stca_encode(_ref(dims), _ref(ffn), n, _ptr(X), _ptr(Xt), _ptr(ws), ws.numel(), _stream(stream)),
            "stca_encode")
     return Xt
@@ -304,10 +316,11 @@ def stca_encode(dims: Dims, ffn: Ffn, X, Xt=None, ws=None, stream=None):
 def stca_attend(dims: Dims, w: DeviceWeights, layer: int, batch: DeviceBatch, Xt, q, o=None, ws=None, stream=None):
     """eqs. (13), (6) for one layer.  q: total_T x d float32 (device).  Returns o (total_T x d)."""
     import torch
-    if o is None:
-        o = torch.empty((batch.total_T, dims.d), dtype=torch.float32, device=q.device)
-    if ws is None:
-        ws = workspace(attend_workspace_size(dims, batch.c), q.device)
+    with _on(stream):
+        if o is None:
+            o = torch.empty((batch.total_T, dims.d), dtype=torch.float32, device=q.device)
+        if ws is None:
+            ws = workspace(attend_workspace_size(dims, batch.c), q.device)
     _check(LIB.stca_attend(_ref(dims), _ref(w.c), layer, _ref(batch.c), _ptr(Xt), _ptr(q), _ptr(o), _ptr(ws),
                            ws.numel(), _stream(stream)), "stca_attend")
     return o
@@ -316,10 +329,11 @@ def stca_attend(dims: Dims, w: DeviceWeights, layer: int, batch: DeviceBatch, Xt
 def stca_forward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, Z=None, ws=None, stream=None, profiler=None):
     """eqs. (2)-(8) for the whole batch.  Returns Z (total_T x M x d float32)."""
     import torch
-    if Z is None:
-        Z = torch.empty((batch.total_T, dims.M, dims.d), dtype=torch.float32, device=batch.X.device)
-    if ws is None:
-        ws = workspace(forward_workspace_size(dims, batch.c), batch.X.device)
+    with _on(stream):
+        if Z is None:
+            Z = torch.empty((batch.total_T, dims.M, dims.d), dtype=torch.float32, device=batch.X.device)
+        if ws is None:
+            ws = workspace(forward_workspace_size(dims, batch.c), batch.X.device)
     if profiler is None:
         st = LIB.stca_forward(_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(Z),
                               _ptr(ws), ws.numel(), _stream(stream))
@@ -335,14 +349,26 @@ def stca_predict(dims: Dims, pw: DevicePredict, Z, xt, z=None, ws=None, stream=N
     storage type).  Returns z (T x d float32)."""
     import torch
     T = int(Z.shape[0])
-    if z is None:
-        z = torch.empty((T, dims.d), dtype=torch.float32, device=Z.device)
-    if ws is None:
-        ws = workspace(predict_workspace_size(dims, T), Z.device)
+    with _on(stream):
+        if z is None:
+            z = torch.empty((T, dims.d), dtype=torch.float32, device=Z.device)
+        if ws is None:
+            ws = workspace(predict_workspace_size(dims, T), Z.device)
     st = LIB.stca_predict(_ref(dims), _ptr(pw.WZ), _ref(pw.ffn), T, _ptr(Z), _ptr(xt), _ptr(z), _ptr(ws),
                           ws.numel(), _stream(stream))
     _check(st, "stca_predict")
     return z
+
+
+def validate_batch(batch: DeviceBatch, stream=None) -> int:
+    """stca_validate_batch: the STCA_BATCH_* bits the batch's offsets break (0 = consistent).
+    Waits for the stream to reach the check."""
+    import torch
+    with _on(stream):
+        res = torch.full((4,), -1, dtype=torch.int32, device=batch.hist_off.device)
+    _check(LIB.stca_validate_batch(_ref(batch.c), _ptr(res), _stream(stream)), "stca_validate_batch")
+    (stream or torch.cuda.current_stream()).synchronize()
+    return int(res[0].item())
 
 
 def sl_beta(params: SlParams, alpha: float) -> float:
@@ -370,8 +396,9 @@ def sl_pack(dims: Dims, full_off, hist_off, total: int, max_len: int, X_full, X_
     """Device gather of every user's temporal suffix (full_off/hist_off: device int64 tensors)."""
     import torch
     n_users = int(hist_off.numel()) - 1
-    if X_packed is None:
-        X_packed = torch.empty((total, dims.d), dtype=X_full.dtype, device=X_full.device)
+    with _on(stream):
+        if X_packed is None:
+            X_packed = torch.empty((total, dims.d), dtype=X_full.dtype, device=X_full.device)
     _check(LIB.stca_sl_pack(_ref(dims), n_users, _ptr(full_off), _ptr(hist_off), total, max_len, _ptr(X_full),
                             _ptr(X_packed), _stream(stream)), "stca_sl_pack")
     return X_packed
@@ -398,8 +425,9 @@ def litm_merge(dims: Dims, group_off, members, X, X_merged=None, stream=None):
     """Device merge of a plan's groups (group_off, members: device int64 tensors)."""
     import torch
     n_groups = int(group_off.numel()) - 1
-    if X_merged is None:
-        X_merged = torch.empty((n_groups, dims.d), dtype=X.dtype, device=X.device)
+    with _on(stream):
+        if X_merged is None:
+            X_merged = torch.empty((n_groups, dims.d), dtype=X.dtype, device=X.device)
     _check(LIB.stca_litm_merge(_ref(dims), int(X.shape[0]), n_groups, _ptr(group_off), _ptr(members), _ptr(X),
                                _ptr(X_merged), _stream(stream)), "stca_litm_merge")
     return X_merged
@@ -454,10 +482,11 @@ def stca_backward(dims: Dims, w: DeviceWeights, batch: DeviceBatch, dZ, grads: D
                   stream=None, profiler=None, keep: bool = False):
     """Gradients of sum(dZ * Z) for the forward of ``batch`` (dZ: total_T x M x d float32, device).
     Returns the DeviceGrads holding them."""
-    if grads is None:
-        grads = DeviceGrads(dims, batch.total_L, batch.total_T, batch.X.device)
-    if ws is None:
-        ws = workspace(backward_workspace_size(dims, batch.c, keep), batch.X.device)
+    with _on(stream):
+        if grads is None:
+            grads = DeviceGrads(dims, batch.total_L, batch.total_T, batch.X.device)
+        if ws is None:
+            ws = workspace(backward_workspace_size(dims, batch.c, keep), batch.X.device)
     args = (_ref(dims), _ref(w.c), _ref(batch.c), _ptr(batch.X), _ptr(batch.xt), _ptr(dZ), _ref(grads.c), _ptr(ws),
             ws.numel(), _stream(stream))
     if profiler is None:

@@ -117,6 +117,8 @@ AttnPlan make_plan(const stca_dims *dm, const stca_batch *b) {
   p.chunk = auto_chunk(dm, b);
   p.total_L = b->total_L;
   p.total_T = b->total_T;
+  p.max_L = b->max_L;
+  p.max_T = b->max_T;
   const int rpg = attn_rows_per_group(dm->d);
   const int64_t groups = (b->max_T * dm->h + rpg - 1) / rpg;
   const int64_t chunks_ceil = (b->total_L + p.chunk - 1) / p.chunk;
@@ -846,6 +848,16 @@ int stca_profiler_read(stca_profiler *p, stca_profile_report *out) {
     out->ms[m.phase] += ms;
     out->launches[m.phase] += 1;
   }
+  return STCA_OK;
+}
+
+int stca_validate_batch(const stca_batch *batch, int32_t *result, void *stream) {
+  int st;
+  if ((st = check_batch(batch)) != STCA_OK) return st;
+  if (!result) return fail(STCA_E_ARG, "result is NULL");
+  if (((uintptr_t)result & 3u) != 0) return fail(STCA_E_ALIGN, "result not 4-byte aligned");
+  HIP_TRY(validate_batch((hipStream_t)stream, batch->n_users, batch->hist_off, batch->tgt_off, batch->total_L,
+                         batch->total_T, batch->max_L, batch->max_T, result));
   return STCA_OK;
 }
 

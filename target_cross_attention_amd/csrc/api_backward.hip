@@ -266,7 +266,8 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     if (i >= 1) HIP_TRY(fill_f32(s, (int64_t)(i + 1) * d * d, g->dWC[i], 0.f));
   }
   if (T == 0) return STCA_OK;  // no target, no gradient
-  HIP_TRY(ragged_plan(s, b->n_users, b->hist_off, b->tgt_off, h, d, bw.desc));
+  HIP_TRY(ragged_plan(s, b->n_users, b->hist_off, b->tgt_off, h, d, b->total_L, b->total_T, b->max_L, b->max_T,
+                      score_elems(dm, b), bw.desc));
   if (bf)
     for (int i = 0; i < M; ++i) {
       HIP_TRY(transpose_bf16(s, d, rd, w->hist[i].Wu, bw.WuT[i]));

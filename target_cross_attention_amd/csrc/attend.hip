@@ -23,21 +23,97 @@ namespace stca {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// One workgroup: the OR of every user's violations into *result.
+__global__ __launch_bounds__(1024) void validate_kernel(int n_users, const int64_t *__restrict__ hoff,
+                                                        const int64_t *__restrict__ toff, int64_t total_L,
+                                                        int64_t total_T, int64_t max_L, int64_t max_T,
+                                                        int32_t *__restrict__ result) {
+  __shared__ int acc;
+  if (threadIdx.x == 0) acc = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int u = threadIdx.x; u < n_users; u += 1024)
+    bad |= offsets_violation(u, n_users, hoff, toff, total_L, total_T, max_L, max_T);
+  if (bad) atomicOr(&acc, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) *result = acc;
+}
+
+hipError_t validate_batch(hipStream_t s, int n_users, const int64_t *hist_off, const int64_t *tgt_off, int64_t total_L,
+                          int64_t total_T, int64_t max_L, int64_t max_T, int32_t *result) {
+  hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(1024), 0, s, n_users, hist_off, tgt_off, total_L, total_T, max_L,
+                     max_T, result);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------------
 // Work list: the segment index tensor turned into (user, chunk, row group) items.
-// One workgroup; users in blocks of 1024 with a block-wide prefix sum.
+// One workgroup; users in blocks of 1024 with a block-wide prefix sum.  The offsets are checked
+// first (an empty history is allowed: its targets get NaN); if they break the batch's stated
+// totals or bounds, or the items or partial rows would exceed what the workspace holds, nothing
+// is listed, n_items[1] records the violation and the combine writes NaN to every output row, so
+// no kernel writes outside its buffers.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64_t *__restrict__ hoff,
                                                         const int64_t *__restrict__ toff, int h, int chunk, int rpg,
-                                                        int64_t max_items, WorkItem *__restrict__ items,
-                                                        int32_t *__restrict__ n_items,
+                                                        int64_t total_L, int64_t total_T, int64_t max_L,
+                                                        int64_t max_T, int64_t max_items, int64_t max_part_rows,
+                                                        WorkItem *__restrict__ items, int32_t *__restrict__ n_items,
                                                         int32_t *__restrict__ user_nchunks,
                                                         int64_t *__restrict__ part_base,
                                                         int32_t *__restrict__ tgt_user) {
   __shared__ int64_t sc_i[1024];
   __shared__ int64_t sc_p[1024];
+  __shared__ int bad_all;
   const int tid = threadIdx.x;
+  if (tid == 0) bad_all = 0;
+  __syncthreads();
+  {
+    int bad = 0;
+    for (int u = tid; u < n_users; u += 1024)
+      bad |= offsets_violation(u, n_users, hoff, toff, total_L, total_T, max_L, max_T) & ~kBatchEmptyHistory;
+    if (bad) atomicOr(&bad_all, bad);
+  }
+  __syncthreads();
+  // Item and partial-row totals against the workspace bounds (implied by the checks above; kept so
+  // that a wrong bound derivation can never turn into an out-of-bounds write).
   int64_t carry_i = 0, carry_p = 0;
+  for (int base = 0; base < n_users && bad_all == 0; base += 1024) {
+    const int u = base + tid;
+    int64_t ni = 0, np = 0;
+    if (u < n_users) {
+      const int64_t L = hoff[u + 1] - hoff[u];
+      const int64_t R = (toff[u + 1] - toff[u]) * h;
+      const int64_t nc = L > 0 ? (L + chunk - 1) / chunk : 0;
+      ni = R > 0 ? nc * ((R + rpg - 1) / rpg) : 0;
+      np = nc > 1 ? nc * R : 0;
+    }
+    sc_i[tid] = ni;
+    sc_p[tid] = np;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+      if (tid < off) {
+        sc_i[tid] += sc_i[tid + off];
+        sc_p[tid] += sc_p[tid + off];
+      }
+      __syncthreads();
+    }
+    carry_i += sc_i[0];
+    carry_p += sc_p[0];
+    __syncthreads();
+  }
+  if (tid == 0 && bad_all == 0 && (carry_i > max_items || carry_p > max_part_rows)) bad_all = kBatchOverflow;
+  __syncthreads();
+  if (bad_all != 0) {
+    if (tid == 0) {
+      n_items[0] = 0;
+      n_items[1] = bad_all;
+    }
+    return;
+  }
+
+  carry_i = 0;
+  carry_p = 0;
   for (int base = 0; base < n_users; base += 1024) {
     const int u = base + tid;
     int64_t ni = 0, np = 0;
@@ -68,20 +144,23 @@ __global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64
       int64_t k = carry_i + sc_i[tid] - ni;
       if (ni > 0)
         for (int c = 0; c < nc; ++c)
-          for (int g = 0; g < ng; ++g, ++k)
-            if (k < max_items) items[k] = WorkItem{u, c, g, nc};
+          for (int g = 0; g < ng; ++g, ++k) items[k] = WorkItem{u, c, g, nc};
     }
     carry_i += sc_i[1023];
     carry_p += sc_p[1023];
     __syncthreads();
   }
-  if (tid == 0) *n_items = (int32_t)(carry_i < max_items ? carry_i : max_items);
+  if (tid == 0) {
+    n_items[0] = (int32_t)carry_i;
+    n_items[1] = 0;
+  }
 }
 
 hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_off, const int64_t *tgt_off,
                           const AttnBuffers &b) {
   hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, p.n_users, hist_off, tgt_off, p.h, p.chunk,
-                     attn_rows_per_group(p.d), p.max_items, b.items, b.n_items, b.user_nchunks, b.part_base, b.tgt_user);
+                     attn_rows_per_group(p.d), p.total_L, p.total_T, p.max_L, p.max_T, p.max_items, p.max_part_rows,
+                     b.items, b.n_items, b.user_nchunks, b.part_base, b.tgt_user);
   return hipGetLastError();
 }
 
@@ -766,6 +845,7 @@ hipError_t attend_split(hipStream_t s, const AttnPlan &p, bool bf16_path, const 
 // with one chunk were finalised by the attention kernel; users with an empty history get NaN.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(int64_t n_rows, int h, int D,
+                                                      const int32_t *__restrict__ status,
                                                       const int32_t *__restrict__ tgt_user,
                                                       const int32_t *__restrict__ user_nchunks,
                                                       const int64_t *__restrict__ toff,
@@ -775,10 +855,14 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t n_rows, int h, int
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;
+  float *dst = abar + row * D;
+  if (status[1] != 0) {  // the work list found inconsistent offsets: no row was computed
+    for (int f = lane; f < D; f += 64) dst[f] = NAN;
+    return;
+  }
   const int u = tgt_user[row / h];
   const int nc = user_nchunks[u];
   if (nc == 1) return;
-  float *dst = abar + row * D;
   if (nc == 0) {
     for (int f = lane; f < D; f += 64) dst[f] = NAN;
     return;
@@ -813,7 +897,7 @@ hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_o
   const int64_t rows = p.total_T * p.h;
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, p.h, p.d,
-                     b.tgt_user, b.user_nchunks, tgt_off, b.part_base, b.part_A, b.part_ms, abar);
+                     b.n_items, b.tgt_user, b.user_nchunks, tgt_off, b.part_base, b.part_A, b.part_ms, abar);
   return hipGetLastError();
 }
 

@@ -241,47 +241,77 @@ __device__ __forceinline__ int segment_of(const int64_t *__restrict__ off, int n
   return lo;
 }
 
-// One workgroup: users in blocks of 1024 with a block-wide prefix sum of R_u Lp_u.
+// One workgroup: users in blocks of 1024 with a block-wide prefix sum of R_u Lp_u.  The offsets are
+// checked against the batch's totals and bounds first (as the forward's work list does); if they
+// break them, or the score matrices would not fit the max_scores elements of the workspace, every
+// descriptor is written empty (no product or row pass then touches memory through it) and the
+// results of the call are meaningless: stca_validate_batch reports such batches.
 __global__ __launch_bounds__(1024) void ragged_plan_kernel(int n_users, const int64_t *__restrict__ hoff,
                                                            const int64_t *__restrict__ toff, int h, int d,
+                                                           int64_t total_L, int64_t total_T, int64_t max_L,
+                                                           int64_t max_T, int64_t max_scores,
                                                            RaggedDesc *__restrict__ descs) {
   __shared__ int64_t sc[1024];
+  __shared__ int bad_all;
   const int tid = threadIdx.x;
-  int64_t carry = 0;
-  for (int base = 0; base < n_users; base += 1024) {
-    const int u = base + tid;
-    int64_t R = 0, L = 0, Lp = 0, L0 = 0, T0 = 0;
-    if (u < n_users) {
-      L0 = hoff[u];
-      T0 = toff[u];
-      L = hoff[u + 1] - L0;
-      R = (toff[u + 1] - T0) * h;
-      Lp = (L + 3) & ~(int64_t)3;
-    }
-    const int64_t cnt = R * Lp;
-    sc[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int64_t a = tid >= off ? sc[tid - off] : 0;
+  if (tid == 0) bad_all = 0;
+  __syncthreads();
+  {
+    int bad = 0;
+    for (int u = tid; u < n_users; u += 1024)
+      bad |= offsets_violation(u, n_users, hoff, toff, total_L, total_T, max_L, max_T) & ~kBatchEmptyHistory;
+    if (bad) atomicOr(&bad_all, bad);
+  }
+  __syncthreads();
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool write = pass == 1;
+    int64_t carry = 0;
+    for (int base = 0; base < n_users; base += 1024) {
+      const int u = base + tid;
+      int64_t R = 0, L = 0, Lp = 0, L0 = 0, T0 = 0;
+      if (u < n_users && bad_all == 0) {
+        L0 = hoff[u];
+        T0 = toff[u];
+        L = hoff[u + 1] - L0;
+        R = (toff[u + 1] - T0) * h;
+        Lp = (L + 3) & ~(int64_t)3;
+      }
+      const int64_t cnt = R * Lp;
+      sc[tid] = cnt;
       __syncthreads();
-      sc[tid] += a;
+      for (int off = 1; off < 1024; off <<= 1) {
+        const int64_t a = tid >= off ? sc[tid - off] : 0;
+        __syncthreads();
+        sc[tid] += a;
+        __syncthreads();
+      }
+      if (write && u < n_users) {
+        if (bad_all == 0) {
+          const int64_t sbase = carry + sc[tid] - cnt, qrow = T0 * h * d, hrow = L0 * d;
+          descs[u] = RaggedDesc{(int32_t)R, (int32_t)L, d, 0, qrow, d, hrow, d, sbase, Lp};
+          descs[n_users + u] = RaggedDesc{(int32_t)R, d, (int32_t)L, 0, sbase, Lp, hrow, d, qrow, d};
+          descs[2 * n_users + u] = RaggedDesc{(int32_t)L, d, (int32_t)R, 0, sbase, Lp, qrow, d, hrow, d};
+        } else {
+          const RaggedDesc empty{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};  // zero sizes and strides
+          descs[u] = descs[n_users + u] = descs[2 * n_users + u] = empty;
+        }
+      }
+      carry += sc[1023];
       __syncthreads();
     }
-    if (u < n_users) {
-      const int64_t sbase = carry + sc[tid] - cnt, qrow = T0 * h * d, hrow = L0 * d;
-      descs[u] = RaggedDesc{(int32_t)R, (int32_t)L, d, 0, qrow, d, hrow, d, sbase, Lp};
-      descs[n_users + u] = RaggedDesc{(int32_t)R, d, (int32_t)L, 0, sbase, Lp, hrow, d, qrow, d};
-      descs[2 * n_users + u] = RaggedDesc{(int32_t)L, d, (int32_t)R, 0, sbase, Lp, qrow, d, hrow, d};
+    if (!write) {
+      if (tid == 0 && carry > max_scores) bad_all |= kBatchOverflow;
+      __syncthreads();
     }
-    carry += sc[1023];
-    __syncthreads();
   }
 }
 
 hipError_t ragged_plan(hipStream_t s, int n_users, const int64_t *hist_off, const int64_t *tgt_off, int h, int d,
+                       int64_t total_L, int64_t total_T, int64_t max_L, int64_t max_T, int64_t max_scores,
                        RaggedDesc *descs) {
   if (n_users <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ragged_plan_kernel, dim3(1), dim3(1024), 0, s, n_users, hist_off, tgt_off, h, d, descs);
+  hipLaunchKernelGGL(ragged_plan_kernel, dim3(1), dim3(1024), 0, s, n_users, hist_off, tgt_off, h, d, total_L, total_T,
+                     max_L, max_T, max_scores, descs);
   return hipGetLastError();
 }
 

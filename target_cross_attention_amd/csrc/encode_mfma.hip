@@ -713,22 +713,18 @@ static hipError_t launch_encode(hipStream_t s, int r, int64_t n_rows, const void
   constexpr int TB = D > 256 ? 1 : D == 256 ? STCA_ENC_TB : STCA_ENC_TB_SMALL;
   using PL = PairLaunch<D, TB>;
   auto kern = encode_pair_kernel<D, TB, LN, TO>;
-  // Persistent grid: as many workgroups as fit on the device at once, each walking tiles.
-  static int resident[64] = {};
-  int dev = 0;
+  // Persistent grid: as many workgroups as fit on the device at once, each walking tiles.  The
+  // count is queried on every call (host-only, no device work), so no state is kept between calls.
+  int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (resident[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * PL::NW, 0);
-    if (e != hipSuccess) return e;
-    resident[dev] = std::max(1, cus * per_cu);
-  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * PL::NW, 0);
+  if (e != hipSuccess) return e;
+  const int64_t resident = std::max(1, cus * per_cu);
   const int64_t tiles = (n_rows + PL::kTokens - 1) / PL::kTokens;
-  const int64_t blocks = std::min<int64_t>(tiles, resident[dev]);
+  const int64_t blocks = std::min<int64_t>(tiles, resident);
   // Stagger the first tiles over about half a tile's time only when every workgroup has many
   // tiles to do, so that the start-up delay is amortised.
   const int stagger = tiles >= 8 * blocks ? STCA_ENC_STAGGER * (r * D / 32) : 0;

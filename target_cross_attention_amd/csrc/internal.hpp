@@ -64,13 +64,37 @@ struct WorkItem {
 struct AttnPlan {
   int n_users = 0, h = 0, d = 0, chunk = 0;
   int64_t total_L = 0, total_T = 0;
+  int64_t max_L = 0, max_T = 0;   // the batch's stated per-user bounds
   int64_t max_items = 0;      // grid bound
   int64_t max_part_rows = 0;  // partial-state rows bound
 };
 
+// Violations of the batch contract, as found on the device (the bits of stca_validate_batch; the
+// work list adds kBatchOverflow when its own totals exceed the workspace bounds).
+constexpr int kBatchBadStart = 1, kBatchBadEnd = 2, kBatchDecreasing = 4, kBatchOverMaxL = 8, kBatchOverMaxT = 16,
+              kBatchEmptyHistory = 32, kBatchOverflow = 64;
+
+// Offset checks.  The ragged kernels size their grids, work list and partial-state buffers from the
+// host-side totals and bounds of the batch; offsets that disagree with them would make those
+// kernels write out of bounds.  offsets_violation() gives the broken conditions of user u as a
+// STCA_BATCH_* bit mask (0 = consistent).
+__device__ __forceinline__ int offsets_violation(int u, int n_users, const int64_t *__restrict__ hoff,
+                                                 const int64_t *__restrict__ toff, int64_t total_L, int64_t total_T,
+                                                 int64_t max_L, int64_t max_T) {
+  const int64_t h0 = hoff[u], h1 = hoff[u + 1], t0 = toff[u], t1 = toff[u + 1];
+  int bad = 0;
+  if (u == 0 && (h0 != 0 || t0 != 0)) bad |= kBatchBadStart;
+  if (u == n_users - 1 && (h1 != total_L || t1 != total_T)) bad |= kBatchBadEnd;
+  if (h1 < h0 || t1 < t0) bad |= kBatchDecreasing;
+  if (h1 - h0 > max_L) bad |= kBatchOverMaxL;
+  if (t1 - t0 > max_T) bad |= kBatchOverMaxT;
+  if (h1 == h0 && t1 > t0) bad |= kBatchEmptyHistory;
+  return bad;
+}
+
 struct AttnBuffers {
   WorkItem *items = nullptr;
-  int32_t *n_items = nullptr;
+  int32_t *n_items = nullptr;  // [0] items listed, [1] violation bits (0: the batch is consistent)
   int32_t *user_nchunks = nullptr;
   int64_t *part_base = nullptr;
   int32_t *tgt_user = nullptr;
@@ -80,6 +104,9 @@ struct AttnBuffers {
 
 hipError_t build_worklist(hipStream_t s, const AttnPlan &p, const int64_t *hist_off, const int64_t *tgt_off,
                           const AttnBuffers &b);
+// *result = OR over users of the violated conditions (kBatch* bits), 0 for a consistent batch.
+hipError_t validate_batch(hipStream_t s, int n_users, const int64_t *hist_off, const int64_t *tgt_off, int64_t total_L,
+                          int64_t total_T, int64_t max_L, int64_t max_T, int32_t *result);
 // abar[T*h x d] (fp32): attention-weighted history per (target, head), eq. (13); U (T*h x d) holds
 // u pre-scaled by log2(e)/sqrt(d_h).  Xt and U are bf16 (MFMA path) or fp32 (debug path).
 hipError_t attend_split(hipStream_t s, const AttnPlan &p, bool bf16_path, const int64_t *hist_off,
@@ -119,6 +146,7 @@ hipError_t copy_rows(hipStream_t s, int64_t rows, int d, const float *x, int64_t
 // product shapes (3 n_users entries), and the row passes over the users' score matrices
 // (mode 0: softmax with lse out, 1: softmax with lse in, 2: dS = alpha (dA - D) into S2).
 hipError_t ragged_plan(hipStream_t s, int n_users, const int64_t *hist_off, const int64_t *tgt_off, int h, int d,
+                       int64_t total_L, int64_t total_T, int64_t max_L, int64_t max_T, int64_t max_scores,
                        RaggedDesc *descs);
 hipError_t ragged_rows(hipStream_t s, int mode, int64_t rows, int h, int n_users, const int64_t *tgt_off,
                        const RaggedDesc *sdesc, float *S, float *S2, float scale, float *lse, const float *D);

@@ -1,0 +1,161 @@
+"""CPU check of the split-L attention kernel's LDS tile layout (attend.hip).
+
+The kernel stages each 32-token history tile in LDS with a swizzle (16-byte chunk c of row t at
+chunk position c ^ sigma(t)) and reads it twice: row-wise with 16-byte reads (the A operand of the
+scores, 8 consecutive features of one token per lane) and column-wise with the transposing 8-byte
+read ds_read_b64_tr_b16 (the A operand of the PV product, 8 tokens of one feature per lane).  This
+test re-states, in Python, the kernel's address arithmetic (the tile fill of fetch/put, the row-wise
+offsets of scores(), the per-lane bases and offsets of tbase/tr_offset) and checks, for every d the
+kernel supports, that
+
+* every lane of every read receives exactly the (token, feature) elements its MFMA operand needs
+  (v_mfma_f32_32x32x16_bf16: A row = lane & 31, k-slot e of lane group g = lane >> 5), with the
+  transposing read modelled by its probed lane layout: within each 16-lane group, lane i receives
+  element i mod 4 of the 8-byte chunks addressed by lanes 4 j + i // 4, j = 0..3;
+* the reads are free of bank conflicts under the model the layout was designed for: 64 banks of
+  4 bytes, the lanes that together fetch 256 bytes (16 lanes of a 16-byte read, 32 lanes of an
+  8-byte read) served in one pass, so their dwords must fall into 64 different banks.  This holds
+  for d >= 128, the sizes the workloads use.  At d = 64 (rows of 128 bytes, swizzle t & 7) rows t
+  and t + 8 of a pass share banks: the reads there are correct but 2-way conflicting, which the
+  test records rather than hides.
+
+A mistake in the swizzle or in an address formula fails one of the two checks.
+"""
+import pytest
+
+BANKS, PER_PASS = 64, 256   # banks of 4 bytes, bytes served per pass
+
+
+def sigma(D, t):
+    if D >= 256:
+        return ((t & 3) << 2) | ((t >> 2) & 3) | (t & 16)
+    if D == 128:
+        return ((t & 3) << 2) | ((t >> 2) & 3)
+    return t & 7
+
+
+def lds_contents(D):
+    """byte address -> (token, feature) of the bf16 element stored there, after the tile fill:
+    wave w's load jj brings 1 KiB, lane l's 16 bytes at LDS position (w + 4 jj) * 64 + l, read
+    from tile element offset row * D + (cs ^ sigma(row)) * 8, slot = position, row = slot // CPR,
+    cs = slot % CPR."""
+    CPR = D // 8
+    INSTR = 32 * D * 2 // 1024
+    LPW = INSTR // 4
+    mem = {}
+    for w in range(4):
+        for jj in range(LPW):
+            for lane in range(64):
+                slot = (w + 4 * jj) * 64 + lane
+                row, cs = slot // CPR, slot % CPR
+                foff = row * D + (cs ^ sigma(D, row)) * 8
+                pos = (w + 4 * jj) * 64 + lane
+                for e in range(8):
+                    tok, feat = divmod(foff + e, D)
+                    mem[pos * 16 + 2 * e] = (tok, feat)
+    assert len(mem) == 32 * D, "the tile fill covers every element once"
+    assert sorted(set(mem.values())) == [(t, f) for t in range(32) for f in range(D)]
+    return mem
+
+
+def banks_distinct(addrs_bytes, banks_n=BANKS):
+    """addrs_bytes: list of (start byte, length) for the lanes served together."""
+    banks = []
+    for a, n in addrs_bytes:
+        assert a % 4 == 0 and n % 4 == 0
+        banks += [((a // 4) + i) % banks_n for i in range(n // 4)]
+    return len(banks) == len(set(banks)) == banks_n
+
+
+def conflict_free(addr, nbytes):
+    lanes = PER_PASS // nbytes
+    return all(banks_distinct([(addr[l], nbytes) for l in range(p, p + lanes)], BANKS) for p in range(0, 64, lanes))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+def test_rowwise_score_reads(D):
+    CPR = D // 8
+    FH = 2 if D > 256 else 1
+    NKS = D // 16
+    NKW = NKS // FH
+    mem = lds_contents(D)
+    for fh in range(FH):
+        kofs = 32 * NKW * fh
+        for ks in range(NKW):
+            addr = []
+            for lane in range(64):
+                col, gl = lane & 31, lane >> 5
+                rx16 = (gl ^ sigma(D, col)) * 16
+                row_off = col * CPR * 16
+                off = row_off + (((32 * ks) + kofs) ^ rx16)
+                addr.append(off)
+                # A operand of the scores: row = token col, k-slots = features 16 k + 8 gl + e
+                k = fh * NKW + ks
+                for e in range(8):
+                    assert mem[off + 2 * e] == (col, 16 * k + 8 * gl + e), (D, fh, ks, lane, e)
+            assert conflict_free(addr, 16) == (D >= 128), (D, fh, ks)
+
+
+def tr_addresses(D, ob, kk, sh):
+    """Per-lane byte address of the transposing read (ob, kk, sh), from tbase and tr_offset."""
+    CPR = D // 8
+    SWZ = (CPR if CPR < 32 else 32) - 1
+    out = []
+    for lane in range(64):
+        g, j, q = lane >> 4, (lane >> 2) & 3, lane & 3
+        g2, g1, q1, q0 = g >> 1, g & 1, q >> 1, q & 1
+        if D >= 128:
+            v1 = (2 * g1 + q1) ^ g2
+            tbase = [0] * 8
+            for pk in range(4):
+                for s in range(2):
+                    tbase[2 * pk + s] = (4 * g2 + j) * CPR * 16 + 64 * (pk ^ j) + 16 * (v1 ^ (2 * s)) + 8 * q0
+            Pp = ob ^ (4 * kk if D >= 256 else 0)
+            bi = 2 * (Pp & 3) + sh
+            C = (16 * kk + 8 * sh) * CPR * 16 + 64 * (Pp & ~3)
+        else:
+            lo = (2 * g1 + q1) ^ j
+            common = (4 * g2 + j) * CPR * 16 + 16 * lo + 8 * q0
+            tbase = [common + 64 * g2, common - 64 * g2]
+            P = ob ^ ((4 * kk + 2 * sh) & (SWZ >> 2))
+            bi = P & 1
+            C = (16 * kk + 8 * sh) * CPR * 16 + 64 * P
+        out.append(tbase[bi] + C)
+    return out
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+def test_transposed_pv_reads(D):
+    NOB = D // 32
+    mem = lds_contents(D)
+    for ob in range(NOB):
+        for kk in range(2):
+            halves = []
+            for sh in range(2):
+                addr = tr_addresses(D, ob, kk, sh)
+                got = []
+                for lane in range(64):
+                    grp, i = lane >> 4, lane & 15
+                    vals = []
+                    for j in range(4):
+                        src = addr[16 * grp + 4 * j + i // 4]
+                        vals.append(mem[src + 2 * (i % 4)])
+                    got.append(vals)
+                halves.append(got)
+                assert conflict_free(addr, 8) == (D >= 128), (D, ob, kk, sh)
+            for lane in range(64):
+                xa = halves[0][lane] + halves[1][lane]
+                g = lane >> 5
+                for e in range(8):
+                    tok = 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3)
+                    assert xa[e] == (tok, 32 * ob + (lane & 31)), (D, ob, kk, lane, e, xa[e])
+
+
+def test_a_wrong_swizzle_is_caught():
+    """The bank check has teeth: without the swizzle the column-wise reads conflict."""
+    D, CPR = 256, 32
+    addr = []
+    for lane in range(32):   # one pass of 8-byte reads down a column of the unswizzled tile
+        tok = lane // 4 + 8 * (lane % 4 // 2)
+        addr.append(tok * CPR * 16 + 8 * (lane % 2))
+    assert not banks_distinct([(a, 8) for a in addr], BANKS)

@@ -125,7 +125,7 @@ def _attend_case(B, cfg, inp, W, layer, chunk):
     return o.cpu().numpy(), np.concatenate(refs)
 
 
-@pytest.mark.parametrize("d,h", [(128, 8), (256, 8), (512, 16)])
+@pytest.mark.parametrize("d,h", [(64, 4), (128, 8), (256, 8), (512, 16)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("chunk", [0, 64, 96, 1024])
 def test_attend_ragged_split(B, dtype, chunk, d, h):
@@ -144,7 +144,8 @@ def test_attend_ragged_split(B, dtype, chunk, d, h):
         assert err <= (2e-2 if dtype == "bf16" else 1e-4)
 
 
-@pytest.mark.parametrize("d,h,chunk", [(128, 8, 0), (256, 8, 0), (512, 16, 0), (512, 16, 96)])
+@pytest.mark.parametrize("d,h,chunk", [(64, 4, 0), (64, 4, 96), (128, 8, 0), (256, 8, 0), (512, 16, 0),
+                                         (512, 16, 96)])
 def test_attend_growing_scores(B, d, h, chunk):
     """Histories whose scores grow along the sequence (row k of X~ scaled by 1 + k/64: a row's
     maximum climbs from ~4 to ~40 in log2 units, outgrowing the kernel's running maximum by its
