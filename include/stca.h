@@ -18,8 +18,10 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all memory; the library
- *     allocates nothing, keeps no global mutable state and is reentrant.  Device pointers must be
- *     16-byte aligned (STCA_E_ALIGN otherwise).
+ *     allocates nothing and is reentrant.  Its only global state is the fixed scratch array of
+ *     stca_attend_noalloc (64 MiB per GPU, in the library's code object) and, on the host, that
+ *     array's per-device address, looked up once under a lock.  Device pointers must be 16-byte
+ *     aligned (STCA_E_ALIGN otherwise).
  *   - Matrices are row-major.  Storage type of X, x_t, X~ and of every weight matrix is
  *     dims->dtype (fp32 or bf16); LayerNorm gamma/beta, q, o and Z are always fp32.  All
  *     arithmetic accumulates in fp32.
@@ -125,6 +127,17 @@ STCA_API int stca_encode(const stca_dims *dims, const stca_ffn *ffn, int64_t n_r
 STCA_API int stca_attend(const stca_dims *dims, const stca_weights *w, int32_t layer, const stca_batch *batch,
                 const void *Xt, const float *q, float *o, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/* stca_attend without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same kernels
+ * work in a fixed scratch array of 64 MiB per GPU that the library's code object holds, so the call
+ * makes no allocation of any kind.  A batch whose stca_attend_workspace_size exceeds 64 MiB is
+ * refused with STCA_E_WORKSPACE before any work.  Every call on one GPU uses that GPU's one array:
+ * calls that overlap on a GPU (on different streams or host threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array needs clearing between calls
+ * (each call writes every scratch value before it reads it).  Otherwise as stca_attend. */
+STCA_API int stca_attend_noalloc(const stca_dims *dims, const stca_weights *w, int32_t layer,
+                                 const stca_batch *batch, const void *Xt, const float *q, float *o, void *stream);
 
 /* eqs. (2)-(8): the whole stack.  X: total_L x d, xt: total_T x d (dims->dtype);
  * Z: total_T x M x d fp32, Z[t][i] = o(i+1) of target t. */

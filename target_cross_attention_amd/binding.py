@@ -29,7 +29,7 @@ EXPORTS = [
     "stca_backward_workspace_size", "stca_backward_workspace_size_keep", "stca_backward", "stca_backward_profiled",
     "stca_forward_graph_create", "stca_graph_launch", "stca_graph_destroy", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
-    "stca_last_error", "stca_version", "stca_validate_batch",
+    "stca_last_error", "stca_version", "stca_validate_batch", "stca_attend_noalloc",
 ]
 
 
@@ -113,6 +113,7 @@ def _load() -> ctypes.CDLL:
         "stca_profiler_reset": [P],
         "stca_profiler_read": [P, P],
         "stca_validate_batch": [P, P, P],
+        "stca_attend_noalloc": [P, P, c_int32, P, P, P, P, P],
         "stca_status_string": [c_int],
         "stca_last_error": [],
         "stca_version": [],
@@ -323,6 +324,14 @@ def stca_attend(dims: Dims, w: DeviceWeights, layer: int, batch: DeviceBatch, Xt
             ws = workspace(attend_workspace_size(dims, batch.c), q.device)
     _check(LIB.stca_attend(_ref(dims), _ref(w.c), layer, _ref(batch.c), _ptr(Xt), _ptr(q), _ptr(o), _ptr(ws),
                            ws.numel(), _stream(stream)), "stca_attend")
+    return o
+
+
+def stca_attend_noalloc(dims: Dims, w: DeviceWeights, layer: int, batch: DeviceBatch, Xt, q, o, stream=None):
+    """stca_attend in the library's fixed scratch array (no workspace, no allocation); o is the
+    caller's (total_T x d float32, device).  Returns o."""
+    _check(LIB.stca_attend_noalloc(_ref(dims), _ref(w.c), layer, _ref(batch.c), _ptr(Xt), _ptr(q), _ptr(o),
+                                   _stream(stream)), "stca_attend_noalloc")
     return o
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -467,6 +468,34 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
   return STCA_OK;
 }
 
+// ---- scratch of the allocation-free attention call (stca_attend_noalloc) -----------------------
+// One fixed array per GPU, part of the library's code object: the runtime places it in each
+// device's memory when it loads the library there, and it stays until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device address is taken once
+// per device with hipGetSymbolAddress, with that device current, and only that address is used.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (its first call on a device looks it up).
+int noalloc_scratch(void **out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(STCA_E_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(STCA_E_HIP, "hipGetSymbolAddress gave no address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return STCA_OK;
+}
+
 }  // namespace stca_abi
 
 // A recorded forward (stca_forward_graph_create): the HIP graph and its executable instance.
@@ -571,6 +600,21 @@ int stca_attend(const stca_dims *dims, const stca_weights *w, int32_t layer, con
   hipStream_t s = (hipStream_t)stream;
   HIP_TRY(build_worklist(s, p, batch->hist_off, batch->tgt_off, aw.ab));
   return attend_layer(s, dims, w, layer, batch, p, Xt, q, o, dims->d, aw, nullptr);
+}
+
+int stca_attend_noalloc(const stca_dims *dims, const stca_weights *w, int32_t layer, const stca_batch *batch,
+                        const void *Xt, const float *q, float *o, void *stream) {
+  size_t need = 0;
+  int st = stca_attend_workspace_size(dims, batch, &need);
+  if (st != STCA_OK) return st;
+  if (need > kNoallocScratchBytes)
+    return fail(STCA_E_WORKSPACE,
+                "batch needs %zu bytes of scratch, more than the %zu of the allocation-free call; use stca_attend "
+                "with a workspace",
+                need, kNoallocScratchBytes);
+  void *ptr = nullptr;
+  if ((st = noalloc_scratch(&ptr)) != STCA_OK) return st;
+  return stca_attend(dims, w, layer, batch, Xt, q, o, ptr, kNoallocScratchBytes, stream);
 }
 
 int stca_forward(const stca_dims *dims, const stca_weights *w, const stca_batch *batch, const void *X,
