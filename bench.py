@@ -9,7 +9,10 @@ and M split-L attention passes).  Inputs are seeded synthetic data resident in H
 Prints one JSON line (history tokens per second, whole job) with the roofline of the dominant
 kernel (the encode), the attention's, the oracle timed on the host, the graph-replay time and the
 prediction token of eq. (9).  --backward times stca_backward on the training-shaped batch, --sl a
-stochastic-length batch and --litm a batch after local same-ID token merging.
+stochastic-length batch and --litm a batch after local same-ID token merging.  --flush-cache evicts
+the 256 MB Infinity Cache (a 512 MiB write) before every timed forward and times each forward
+alone.  --vendor-gemm times the vendor library's bf16 GEMMs (torch.matmul) at the encode's shapes
+instead, as a ceiling reference for the fused encode.
 """
 from __future__ import annotations
 
@@ -52,6 +55,17 @@ def measured_traffic(workload: str, kernel: str, src_files):
     if not e or e.get("source_hash") != kernel_source_hash(src_files):
         return None
     return e.get("bytes_per_launch")
+
+
+INFINITY_CACHE_BYTES = 256 << 20   # MI355X last-level cache (MALL)
+DENSE10K_METRIC = "STCA fwd history-tokens/s at L=10k; achieved HBM GB/s & MFMA % of peak"
+
+
+def metric_for(cfg) -> str:
+    """The dense-inference workload carries the headline metric; every other workload names itself."""
+    if cfg.key == "dense10k":
+        return DENSE10K_METRIC
+    return f"STCA fwd history-tokens/s ({cfg.key} workload)"
 
 
 def cpu_model() -> str:
@@ -350,6 +364,131 @@ def cpu_baseline_backward(cfg, W, target_s: float = 12.0, max_users: int = 64):
                       f"backward (oracle.grad), {elapsed:.1f} s"}
 
 
+# Kernels whose HBM traffic the bench line reports: role -> (name fragment, source files).
+TRAFFIC_KERNELS = {"encode": ("encode_", ["encode_mfma.hip", "device_common.hpp"]),
+                   "attend": ("attend_mfma_kernel", ["attend.hip", "device_common.hpp"])}
+
+
+def _counter_rows(d: str, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc run's counter_collection.csv under d."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, cfetch_dir: str, cwrite_dir: str,
+                    copy_bytes: int = 2 << 30):
+    """Markdown table of HBM bytes per dispatch from two counter passes (FETCH_SIZE, WRITE_SIZE, KiB
+    per dispatch), each scaled by what the same counter reads for a plain device copy of copy_bytes
+    (bench.py --calib-copy); records the encode's and the attention's bytes per launch in
+    profiles/hbm_traffic.txt with the current source hash of each kernel."""
+    from collections import defaultdict
+
+    def per_kernel(rows):
+        acc = defaultdict(list)
+        for k, v in rows:
+            acc[k].append(v)
+        return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
+
+    def calib(d, counter):
+        vals = [v for k, v in _counter_rows(d, counter) if "copyBuffer" in k]
+        return copy_bytes / (max(vals) * 1024.0)   # the 2 GiB copies are the largest copy dispatches
+
+    fs, ws = calib(cfetch_dir, "FETCH_SIZE"), calib(cwrite_dir, "WRITE_SIZE")
+    fetch = per_kernel(_counter_rows(fetch_dir, "FETCH_SIZE"))
+    write = per_kernel(_counter_rows(write_dir, "WRITE_SIZE"))
+    lines = [f"Calibration: a {copy_bytes >> 30} GiB device copy gives bytes = FETCH_SIZE x 1024 x {fs:.3f} and "
+             f"WRITE_SIZE x 1024 x {ws:.3f}.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read GB (scaled) | HBM write GB (scaled) |",
+             "|---|---|---|---|---|---|"]
+    for k in sorted(fetch, key=lambda k: -fetch[k][1]):
+        n, fv = fetch[k]
+        wv = write.get(k, (0, 0.0))[1]
+        lines.append(f"| `{k[:80]}` | {n} | {fv:.0f} | {wv:.0f} | {fv * 1024 * fs / 1e9:.3f} | "
+                     f"{wv * 1024 * ws / 1e9:.3f} |")
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec["_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE passes scaled by a device copy of "
+                    "known size (bench.py --traffic-summary); valid only while the kernel source hash matches")
+    entry = rec.setdefault(workload, {})
+    for role, (frag, files) in TRAFFIC_KERNELS.items():
+        cands = [k for k in fetch if frag in k]
+        if not cands:
+            continue
+        k = max(cands, key=lambda k: fetch[k][1])
+        b = fetch[k][1] * 1024 * fs + write.get(k, (0, 0.0))[1] * 1024 * ws
+        entry[role] = {"kernel": k[:80], "bytes_per_launch": int(b), "source_hash": kernel_source_hash(files)}
+        lines.append(f"\n{role}: `{k[:80]}`: {b / 1e9:.3f} GB per launch")
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+
+
+def bench_vendor_gemm(a, dev):
+    """torch.matmul (hipBLASLt) bf16 GEMMs at the encode's shapes for the workload (1 Mi history
+    rows: up and gate as one [rows x d] x [d x 2rd] product, the down product [rows x rd] x [rd x d])
+    and at a large square shape, as a ceiling reference for the fused encode.  GEMMs only: the
+    vendor path would still need the gate and LayerNorm kernels."""
+    import torch
+
+    import stca_inputs as SI
+    cfg = SI.get_config(a.workload)
+    rows = 1 << 20
+    d, rd = cfg.d, cfg.r * cfg.d
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(m, n):
+        return torch.randn(m, n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    def timed(A, Bm, reps):
+        C = A @ Bm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(A, Bm, out=C)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = 2.0 * A.shape[0] * A.shape[1] * Bm.shape[1]
+        return {"shape": f"[{A.shape[0]} x {A.shape[1]}] x [{Bm.shape[0]} x {Bm.shape[1]}]", "avg_ms": ms,
+                "tflops": fl / ms / 1e9, "frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+
+    reps = max(a.steps, 10)
+    X, Wuv = rnd(rows, d), rnd(d, 2 * rd)
+    up = timed(X, Wuv, reps)
+    del X, Wuv
+    H, Wo = rnd(rows, rd), rnd(rd, d)
+    down = timed(H, Wo, reps)
+    del H, Wo
+    S1, S2 = rnd(16384, 16384), rnd(16384, 16384)
+    square = timed(S1, S2, reps)
+    del S1, S2
+    enc_ms = up["avg_ms"] + down["avg_ms"]
+    enc_flops = 6.0 * cfg.r * d * d * rows
+    print(json.dumps({
+        "metric": "vendor bf16 GEMM throughput at the encode's shapes (ceiling reference)",
+        "library": "torch.matmul (hipBLASLt), torch " + torch.__version__, "workload": cfg.key,
+        "up_gate": up, "down": down, "square_16384": square,
+        "encode_gemms_only": {"rows": rows, "ms": enc_ms, "tflops": enc_flops / enc_ms / 1e9,
+                              "frac": enc_flops / enc_ms / 1e9 / PEAK_BF16_TFLOPS},
+        "peak_tflops": PEAK_BF16_TFLOPS, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,9 +508,20 @@ def main():
                     help="time stca_backward instead (default workload: the training-shaped ragged batch)")
     ap.add_argument("--no-keep", action="store_true",
                     help="with --backward: the minimum workspace (recompute the encode's intermediates)")
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="write a 512 MiB buffer before every timed forward (evicts the Infinity Cache) and time "
+                         "each forward on its own with HIP events")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time torch.matmul (hipBLASLt) bf16 GEMMs at the encode's shapes instead")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of STCA, run K device copies of 2 GiB (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_FETCH_DIR",
+                                                           "CALIB_WRITE_DIR"),
+                    help="summarise four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of this workload's "
+                         "bench, then of --calib-copy) and record the traffic per launch; no GPU needed")
     a = ap.parse_args()
+    if a.traffic_summary:
+        return traffic_summary(a.workload, *a.traffic_summary)
 
     if a.gpus != 1:
         print(json.dumps({"error": "the STCA path here runs on one GPU; --gpus must be 1 "
@@ -396,6 +546,8 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "copies": a.calib_copy}))
         return
 
+    if a.vendor_gemm:
+        return bench_vendor_gemm(a, dev)
     if a.backward and a.workload == "dense10k":
         a.workload = "ragged"
     cfg = SI.get_config(a.workload)
@@ -425,17 +577,33 @@ def main():
     torch.cuda.synchronize()
 
     prof = B.Profiler()
-    log(f"timing {a.steps} steps")
+    log(f"timing {a.steps} steps" + (" (Infinity Cache flushed before each)" if a.flush_cache else ""))
+    flush = torch.empty(2 * INFINITY_CACHE_BYTES, dtype=torch.uint8, device=dev) if a.flush_cache else None
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(a.steps):
-        B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=stream, profiler=prof)
-        ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    step_ms = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(a.steps))
+    if a.flush_cache:
+        # each forward timed on its own, after a write of twice the cache's size; the flush is
+        # outside the events
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+        t0 = time.perf_counter()
+        for k in range(a.steps):
+            flush.fill_(k & 0xFF)
+            ev[k][0].record(stream)
+            B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=stream, profiler=prof)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        dt = sum(step_ms) / 1e3
+        del flush
+    else:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for k in range(a.steps):
+            B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=stream, profiler=prof)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        step_ms = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(a.steps))
     phases = prof.read()
     prof.close()
     assert np.isfinite(Z.sum().item()), "non-finite output"
@@ -492,8 +660,15 @@ def main():
     att_flops = 4.0 * cfg.h * cfg.d * float((db.inp.L * db.inp.m).sum())
     att_traffic = measured_traffic(cfg.key, "attend", ["attend.hip", "device_common.hpp"])
 
+    # The attention reads the X~ that the encode wrote just before it; when one layer's X~ fits the
+    # Infinity Cache it is read from there, not from HBM, and the GB/s figure is not an HBM fraction.
+    att_cache_resident = att_bytes <= INFINITY_CACHE_BYTES
+    enc_label = ("encode (fused SwiGLU FFN + LayerNorm, bf16 MFMA)" if bf16 else
+                 "encode (SwiGLU FFN + LayerNorm, fp32 GEMMs: matrix cores for large products, vector ALU "
+                 "otherwise)")
+
     out = {
-        "metric": "STCA fwd history-tokens/s at L=10k (dense-inference workload)",
+        "metric": metric_for(cfg),
         "value": tokens_per_s,
         "unit": "history-tokens/s",
         "n_gpus": 1,
@@ -506,11 +681,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
-        "data": "synthetic (seeded; shapes of the pages' dense-inference serving workload)",
+        "data": f"synthetic (seeded; shapes of the pages' {cfg.key} workload)",
         "config": {"workload": cfg.description, "key": cfg.key, "users": db.inp.n_users,
                    "history_tokens": db.total_L, "targets": db.total_T, "d": cfg.d, "h": cfg.h, "M": cfg.M,
-                   "r": cfg.r, "attn_chunk": a.attn_chunk or "auto"},
-        "roofline": {"kernel": "encode (fused SwiGLU FFN + LayerNorm, bf16 MFMA)",
+                   "r": cfg.r, "attn_chunk": a.attn_chunk or "auto",
+                   "infinity_cache": "flushed before each timed forward" if a.flush_cache else "not flushed"},
+        "roofline": {"kernel": enc_label,
                      "bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
                      "frac": achieved / peak_mm, "traffic": traffic,
                      "algorithmic_flops_per_launch": enc_flops, "algorithmic_bytes_per_launch": enc_bytes,
@@ -519,7 +695,12 @@ def main():
                                "achieved": att_bytes / att_avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": att_bytes / att_avg_s / 1e9 / PEAK_HBM_GBS, "traffic": att_traffic,
                                "mfma_tflops": att_flops / att_avg_s / 1e12,
-                               "avg_launch_ms": att_avg_s * 1e3, "launches": att_n},
+                               "avg_launch_ms": att_avg_s * 1e3, "launches": att_n,
+                               "cache_resident": att_cache_resident,
+                               "note": ("one layer's X~ fits the 256 MB Infinity Cache and is read from there "
+                                        "right after the encode writes it: the GB/s figure is not an HBM "
+                                        "fraction" if att_cache_resident else
+                                        "one layer's X~ exceeds the Infinity Cache: read from HBM")},
         "targets_per_s": targets_per_s,
         "graph_replay": {"ms_per_step": graph_ms, "history_tokens_per_s": db.total_L / graph_ms * 1e3,
                          "replays": a.steps},

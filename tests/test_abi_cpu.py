@@ -4,6 +4,7 @@ placeholder device addresses are never dereferenced)."""
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -278,3 +279,51 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_bench_traffic_summary(tmp_path, monkeypatch):
+    """bench.py --traffic-summary scales the counters by the copy calibration and records the
+    encode's and the attention's bytes per launch with their source hashes."""
+    import csv
+    import json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+    def write(d, counter, rows):
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(cols)
+            for i, (k, v) in enumerate(rows):
+                w.writerow([i, k, counter, v])
+
+    enc, att = "encode_pair_kernel<256>", "void stca::attend_mfma_kernel<256>(...)"
+    write(tmp_path / "f", "FETCH_SIZE", [(enc, 1000.0), (enc, 3000.0), (att, 500.0), ("other", 7.0)])
+    write(tmp_path / "w", "WRITE_SIZE", [(enc, 2000.0), (enc, 2000.0), (att, 100.0), ("other", 1.0)])
+    # a 2 GiB copy that reads back half its bytes (factor 2) and writes all of them (factor 1)
+    write(tmp_path / "cf", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 4.0), ("__amd_rocclr_copyBuffer", 1 << 20)])
+    write(tmp_path / "cw", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1 << 21)])
+    rec_file = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(rec_file))
+    bench.traffic_summary("ragged", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
+                          str(tmp_path / "cw"))
+    rec = json.loads(rec_file.read_text())["ragged"]
+    assert rec["encode"]["bytes_per_launch"] == int(2000 * 1024 * 2 + 2000 * 1024)
+    assert rec["attend"]["bytes_per_launch"] == int(500 * 1024 * 2 + 100 * 1024)
+    assert rec["encode"]["source_hash"] == bench.kernel_source_hash(["encode_mfma.hip", "device_common.hpp"])
+    assert bench.measured_traffic("ragged", "attend", ["attend.hip", "device_common.hpp"]) == \
+        rec["attend"]["bytes_per_launch"]
+
+
+def test_bench_metric_names_the_workload():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    import stca_inputs as SI
+    assert bench.metric_for(SI.get_config("dense10k")) == \
+        "STCA fwd history-tokens/s at L=10k; achieved HBM GB/s & MFMA % of peak"
+    for key in ("tiny", "uniform", "ragged", "stress20k"):
+        m = bench.metric_for(SI.get_config(key))
+        assert key in m and "L=10k" not in m
