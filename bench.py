@@ -643,13 +643,17 @@ def main():
     tokens_per_s = db.total_L * a.steps / dt
     targets_per_s = db.total_T * a.steps / dt
 
-    # Dominant kernel: the fused encode (M launches per step).  Algorithmic work per launch:
-    # 6 r d^2 FLOP per history token (up + gate d x rd, down rd x d, 2 FLOP per multiply-add).
+    # Dominant kernel: the fused encode.  bf16: one launch per step encodes all M layers; fp32: one
+    # launch sequence per layer.  Algorithmic work: 6 r d^2 FLOP per history token and layer (up +
+    # gate d x rd, down rd x d, 2 FLOP per multiply-add); bytes: X read once per launch (2d per
+    # token in bf16), X~ written once per layer (2d).
+    bf16 = cfg.dtype == "bf16"
     enc_ms, enc_n = phases["encode"]
     enc_avg_s = enc_ms / max(enc_n, 1) / 1e3
-    enc_flops = 6.0 * cfg.r * cfg.d * cfg.d * db.total_L
-    enc_bytes = 4.0 * cfg.d * db.total_L  # read X (bf16) + write X~ (bf16)
-    bf16 = cfg.dtype == "bf16"
+    layers_per_launch = cfg.M * a.steps / max(enc_n, 1)
+    esz = 2.0 if bf16 else 4.0
+    enc_flops = 6.0 * cfg.r * cfg.d * cfg.d * db.total_L * layers_per_launch
+    enc_bytes = esz * cfg.d * db.total_L * (1.0 + layers_per_launch)
     peak_mm = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     achieved = enc_flops / enc_avg_s / 1e12
     traffic = measured_traffic(cfg.key, "encode", ["encode_mfma.hip", "device_common.hpp"])
@@ -690,7 +694,8 @@ def main():
                      "bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
                      "frac": achieved / peak_mm, "traffic": traffic,
                      "algorithmic_flops_per_launch": enc_flops, "algorithmic_bytes_per_launch": enc_bytes,
-                     "avg_launch_ms": enc_avg_s * 1e3, "launches": enc_n},
+                     "avg_launch_ms": enc_avg_s * 1e3, "launches": enc_n,
+                     "layers_per_launch": layers_per_launch},
         "attention_roofline": {"kernel": "split-L attention", "bound": "hbm",
                                "achieved": att_bytes / att_avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": att_bytes / att_avg_s / 1e9 / PEAK_HBM_GBS, "traffic": att_traffic,

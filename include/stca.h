@@ -76,6 +76,11 @@ typedef struct {
   float ln_eps;       /* LayerNorm epsilon (biased variance); must be > 0 */
   int32_t query_ln;   /* 1: apply the layer's LayerNorm after the FFN of eq. (7); 0: as printed */
   int32_t attn_chunk; /* history tokens per attention work item, multiple of 32; 0 = automatic */
+  int32_t encode_layers; /* bf16 history encodes of stca_forward (eq. (2)): 1 = one launch per layer,
+                          * each followed by that layer's attention; 2 = every layer in one launch
+                          * that reads each tile of X once (M encoded buffers in the workspace);
+                          * 0 = automatic (2 where one layer's X~ exceeds 1 GiB at d <= 256).
+                          * Results are identical either way. */
 } stca_dims;
 
 /* One SwiGLU FFN + LayerNorm block (eqs. (1)-(3), (7)).  Wu, Wv: d x rd; Wo: rd x d (dtype);

@@ -35,7 +35,7 @@ EXPORTS = [
 
 class Dims(ctypes.Structure):
     _fields_ = [("d", c_int32), ("h", c_int32), ("M", c_int32), ("r", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float), ("query_ln", c_int32), ("attn_chunk", c_int32)]
+                ("ln_eps", c_float), ("query_ln", c_int32), ("attn_chunk", c_int32), ("encode_layers", c_int32)]
 
 
 class Ffn(ctypes.Structure):
@@ -153,8 +153,9 @@ def _ref(s):
 # plain structs
 # ----------------------------------------------------------------------------------------------
 def make_dims(d: int, h: int, M: int, r: int, dtype: str = "bf16", ln_eps: float = 1e-5,
-              query_ln: bool = False, attn_chunk: int = 0) -> Dims:
-    return Dims(d, h, M, r, BF16 if dtype == "bf16" else F32, ln_eps, int(bool(query_ln)), attn_chunk)
+              query_ln: bool = False, attn_chunk: int = 0, encode_layers: int = 0) -> Dims:
+    return Dims(d, h, M, r, BF16 if dtype == "bf16" else F32, ln_eps, int(bool(query_ln)), attn_chunk,
+                encode_layers)
 
 
 def dims_for(cfg, **kw) -> Dims:

@@ -40,6 +40,8 @@ int check_dims(const stca_dims *dm) {
   if (!(dm->ln_eps > 0.f)) return fail(STCA_E_DIMS, "ln_eps must be > 0");
   if (dm->attn_chunk < 0 || dm->attn_chunk % 32 != 0)
     return fail(STCA_E_DIMS, "attn_chunk=%d must be 0 or a positive multiple of 32", dm->attn_chunk);
+  if (dm->encode_layers < 0 || dm->encode_layers > 2)
+    return fail(STCA_E_DIMS, "encode_layers=%d must be 0, 1 or 2", dm->encode_layers);
   return STCA_OK;
 }
 
@@ -358,16 +360,33 @@ struct ForwardWs {
 
 bool same_ffn(const stca_ffn &a, const stca_ffn &b) { return a.Wu == b.Wu && a.Wv == b.Wv && a.Wo == b.Wo; }
 
+// All M history encodes in one launch (X read once, M encoded buffers) or one launch per layer,
+// each followed by that layer's attention (one buffer).  Per layer, the attention then reads an X~
+// the encode has just written, which a batch of moderate size finds in the 256 MB last-level cache;
+// automatically, the single launch is used where one layer's X~ is far larger than that cache (and
+// at d <= 256, where the kernel keeps a tile's rows on chip between layers); stca_dims can force
+// either way.
+bool fused_encode(const stca_dims *dm, const stca_batch *b) {
+  if (dm->dtype != STCA_BF16 || dm->encode_layers == 1) return false;
+  if (dm->encode_layers == 2) return true;
+  return dm->M > 1 && dm->d <= 256 && b->total_L * dm->d * 2 > ((int64_t)1 << 30);
+}
+
 size_t carve_forward(void *base, const stca_dims *dm, const stca_batch *b, const AttnPlan &p, ForwardWs &w,
                      const stca_weights *wt) {
   Carver c(base);
   if (dm->dtype == STCA_BF16) {
+    // History FFNs: every layer's fragments and LayerNorm parameters at one stride, for the
+    // single multi-layer encode launch.
+    const size_t ls = encode_layer_stride(dm->d, dm->r);
+    char *hist = c.take<char>(ls * dm->M);
+    for (int i = 0; i < dm->M; ++i) w.packed_hist[i] = hist ? hist + ls * i : nullptr;
     const size_t pb = encode_packed_bytes(dm->d, dm->r);
-    for (int i = 0; i < dm->M; ++i) w.packed_hist[i] = c.take<char>(pb);
     for (int i = 0; i < dm->M; ++i) w.packed_query[i] = c.take<char>(pb);
     (void)wt;
   }
-  w.Xt = c.take<char>((size_t)(b->total_L * dm->d) * esize(dm));
+  const int n_xt = fused_encode(dm, b) ? dm->M : 1;
+  w.Xt = c.take<char>((size_t)(b->total_L * dm->d) * esize(dm) * n_xt);
   w.q = c.take<float>((size_t)(b->total_T * dm->d));
   w.c = c.take<float>((size_t)(b->total_T * dm->d));
   if (dm->dtype == STCA_BF16) w.cb = c.take<char>((size_t)(b->total_T * dm->d) * 2);
@@ -400,16 +419,9 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
 
   if (bf) {
     Phase ph(prof, s, STCA_PHASE_PACK);
-    for (int i = 0; i < M; ++i) {
-      int j = 0;
-      for (; j < i; ++j)
-        if (same_ffn(w->hist[j], w->hist[i])) break;
-      if (j < i) {
-        fw.packed_hist[i] = fw.packed_hist[j];
-        continue;
-      }
-      HIP_TRY(encode_pack(s, d, dm->r, w->hist[i].Wu, w->hist[i].Wv, w->hist[i].Wo, fw.packed_hist[i]));
-    }
+    for (int i = 0; i < M; ++i)
+      HIP_TRY(encode_pack(s, d, dm->r, w->hist[i].Wu, w->hist[i].Wv, w->hist[i].Wo, fw.packed_hist[i],
+                          w->hist[i].gamma, w->hist[i].beta));
     // Query FFNs (eqs. (3), (7)) run on the same MFMA kernel; they usually share the history
     // FFN's weights (reused), otherwise they are packed here.
     for (int i = 0; i < M; ++i) {
@@ -440,14 +452,27 @@ int forward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *b
     }
     HIP_TRY(ph.end());
   }
+  // eq. (2) for every layer: in one launch before the loop, or layer by layer inside it.
+  const bool fused = fused_encode(dm, b);
+  const size_t xt_layer = (size_t)(b->total_L * d) * esize(dm);
+  if (fused) {
+    Phase ph(prof, s, STCA_PHASE_ENCODE);
+    const size_t ls = encode_layer_stride(d, dm->r), pb = encode_packed_bytes(d, dm->r);
+    const float *ln0 = reinterpret_cast<const float *>((const char *)fw.packed_hist[0] + pb);
+    const EncodeLayers lay{fw.packed_hist[0], (int64_t)ls, fw.Xt, b->total_L * d, ln0, ln0 + d,
+                           (int64_t)(ls / sizeof(float)), M};
+    HIP_TRY(encode_mfma_layers(s, d, dm->r, b->total_L, X, d, lay, d, true, true, dm->ln_eps));
+    HIP_TRY(ph.end());
+  }
   for (int i = 0; i < M; ++i) {
-    {
+    const char *Xt_i = (const char *)fw.Xt + (fused ? xt_layer * i : 0);
+    if (!fused) {
       Phase ph(prof, s, STCA_PHASE_ENCODE);
       if ((st = encode_rows(s, dm, &w->hist[i], b->total_L, X, fw.Xt, fw.packed_hist[i], fw.ffn)) != STCA_OK)
         return st;
       HIP_TRY(ph.end());
     }
-    if ((st = attend_layer(s, dm, w, i, b, p, fw.Xt, fw.q, Z + (size_t)i * d, (int64_t)M * d, fw.aw, prof)) !=
+    if ((st = attend_layer(s, dm, w, i, b, p, Xt_i, fw.q, Z + (size_t)i * d, (int64_t)M * d, fw.aw, prof)) !=
         STCA_OK)
       return st;
     if (i + 1 < M) {  // eq. (7): q(i+1) = SwiGLUFFN([o(1..i) || x_t] W_C) (+LN)

@@ -1,4 +1,5 @@
-// Fused history encode on bf16 MFMA: X~ = LN(((X W_u) * SiLU(X W_v)) W_o), one launch per layer.
+// Fused history encode on bf16 MFMA: X~ = LN(((X W_u) * SiLU(X W_v)) W_o), for one layer or for
+// all layers of the stack in one launch (each tile of X read once).
 //
 // Equations: SwiGLU FFN of eq. (1) with the three-matrix shapes of the STCA review page
 // (section 2.2), followed by the LayerNorm of eq. (2) ("Make It Long, Keep It Fast", section 2.1).
@@ -19,8 +20,10 @@
 //     staged step by step into LDS with direct global->LDS loads and shared by all waves of the
 //     workgroup, or read by each wave from L2 straight into registers (down fragments at d >= 256);
 //   * LayerNorm statistics of a token combine the two waves of its pair through LDS;
-//   * workgroups are persistent and walk 128-token tiles (64 at d = 512); a tile's rows and
-//     first weight steps are loaded while the previous tile finishes.
+//   * workgroups are persistent and walk 128-token tiles (64 at d = 512), every layer of a tile
+//     before the next tile; the next item's rows and first weight steps are loaded while the
+//     current one finishes.  Between the layers of a tile the rows stay on chip (d <= 256: the
+//     pair's B operands are written back to the LDS row buffer; d = 512: re-read, from L2).
 // d <= 256: a workgroup is 8 waves (TB = 1, two per SIMD; d < 256) or 4 (TB = 2, one per SIMD;
 // d = 256) over 128 tokens, whose rows are staged in LDS with coalesced loads and read out in the
 // B-operand layout; the up/gate fragments are staged two steps ahead in a 3-slot ring.  d = 512: a
@@ -36,6 +39,7 @@
 namespace stca {
 
 size_t encode_packed_bytes(int d, int r) { return (size_t)(r * d / 32) * (size_t)(3 * d / 16) * 1024; }
+size_t encode_layer_stride(int d, int r) { return (encode_packed_bytes(d, r) + 8 * (size_t)d + 255) / 256 * 256; }
 
 // ------------------------------------------------------------------------------------------
 // Fragment re-layout.  Step s (hidden features 32s .. 32s+31) holds 3d/16 fragments of 64 lanes x
@@ -51,14 +55,25 @@ size_t encode_packed_bytes(int d, int r) { return (size_t)(r * d / 32) * (size_t
 //     accumulates block ob, so a wave finds its own-feature blocks and its partner-feature blocks
 //     as two runs at power-of-two offsets.
 // ------------------------------------------------------------------------------------------
+// With gamma and beta given, the layer's LayerNorm parameters follow the fragments (gamma, then
+// beta, d floats each), so that a multi-layer encode finds every layer's data at one stride.
 __global__ __launch_bounds__(256) void encode_pack_kernel(int d, int rd, const uint16_t *__restrict__ Wu,
                                                           const uint16_t *__restrict__ Wv,
                                                           const uint16_t *__restrict__ Wo,
-                                                          uint16_t *__restrict__ out) {
+                                                          uint16_t *__restrict__ out,
+                                                          const float *__restrict__ gamma,
+                                                          const float *__restrict__ beta) {
   const int NKS = d / 16, NOB = d / 32, FPS = 2 * NKS + 2 * NOB;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)(rd / 32) * FPS * 64;
-  if (gid >= total) return;
+  if (gid >= total) {
+    const int64_t i = gid - total;
+    if (gamma && i < 2 * d) {
+      float *ln = reinterpret_cast<float *>(out + total * 8);
+      ln[i] = i < d ? gamma[i] : beta[i - d];
+    }
+    return;
+  }
   const int lane = (int)(gid & 63);
   const int64_t fr = gid >> 6;
   const int s = (int)(fr / FPS), f = (int)(fr % FPS);
@@ -91,11 +106,12 @@ __global__ __launch_bounds__(256) void encode_pack_kernel(int d, int rd, const u
 }
 
 hipError_t encode_pack(hipStream_t s, int d, int r, const void *Wu, const void *Wv, const void *Wo,
-                       void *packed) {
+                       void *packed, const float *gamma, const float *beta) {
   const int rd = r * d;
-  const int64_t total = (int64_t)(rd / 32) * (3 * d / 16) * 64;
+  const int64_t total = (int64_t)(rd / 32) * (3 * d / 16) * 64 + (gamma ? 2 * d : 0);
   hipLaunchKernelGGL(encode_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, d, rd,
-                     (const uint16_t *)Wu, (const uint16_t *)Wv, (const uint16_t *)Wo, (uint16_t *)packed);
+                     (const uint16_t *)Wu, (const uint16_t *)Wv, (const uint16_t *)Wo, (uint16_t *)packed,
+                     gamma, beta);
   return hipGetLastError();
 }
 
@@ -154,10 +170,7 @@ template <int D, int TB> struct PairLaunch {
 template <int D, int TB, bool LN, typename TO>
 __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_kernel(int64_t n_rows, int n_steps,
                                                              const bf16 *__restrict__ X, int64_t ldx,
-                                                             const bf16x8 *__restrict__ packed,
-                                                             TO *__restrict__ out, int64_t ldo,
-                                                             const float *__restrict__ gamma,
-                                                             const float *__restrict__ beta, float eps,
+                                                             const EncodeLayers lay, int64_t ldo, float eps,
                                                              int stagger) {
   using S = PairShape<D>;
   constexpr bool kWide = PairLaunch<D, TB>::kWide;
@@ -198,14 +211,23 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
 
   // LayerNorm scale and shift, staged once into LDS (visible after the first barrier) so that the
   // epilogue does not wait on global loads.
-  __shared__ __attribute__((aligned(16))) float gb[LN ? 2 : 1][LN ? D : 4];
+  // With several layers, the next item's parameters are written into the other half of a double
+  // buffer while an item runs: gb[parity][gamma / beta][feature].
+  const int NL = lay.n;
+  __shared__ __attribute__((aligned(16))) float gb[LN ? 2 : 1][2][LN ? D : 4];
   if constexpr (LN) {
     for (int i = threadIdx.x; i < D; i += 64 * NW) {
-      gb[0][i] = gamma[i];
-      gb[1][i] = beta[i];
+      gb[0][0][i] = lay.gamma[i];
+      gb[0][1][i] = lay.beta[i];
     }
   }
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)n_steps * SLOT);
+  // The layer in flight: its packed weights (and a buffer resource over them for the staging loads).
+  const bf16x8 *packed = (const bf16x8 *)lay.packed;
+  __amdgpu_buffer_rsrc_t wrs = make_rsrc(packed, (uint32_t)n_steps * SLOT);
+  auto use_layer = [&](int l) {
+    packed = (const bf16x8 *)((const char *)lay.packed + (int64_t)l * lay.packed_stride);
+    wrs = make_rsrc(packed, (uint32_t)n_steps * SLOT);
+  };
   auto stage_uv = [&](int t, int b) {
 #pragma unroll
     for (int j = 0; j < LUV; ++j) {
@@ -292,6 +314,28 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     }
   };
 
+  // d <= 256, between two layers of a tile: the pair's rows back into the row buffer (the inverse of
+  // read_x; both waves of a pair hold the same rows, the first writes them).  The buffer is free:
+  // the last step's barrier has passed every read of ring slot 2, and nothing is staged into it
+  // before the next layer has read its rows.
+  auto write_x = [&]() {
+    if constexpr (!kWide) {
+      if (role == 0) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const int row = (wave >> 1) * 32 * TB + 32 * tb;
+          const int r = (row & 63) + col;
+          STCA_LDS char *half = row < 64 ? (STCA_LDS char *)&uv2[0][0] : (STCA_LDS char *)&xs[0][0];
+#pragma unroll
+          for (int ks = 0; ks < S::NKS; ++ks) {
+            const int c = 2 * ks + grp;
+            *(STCA_LDS bf16x8 *)(half + (r * CPR + (c ^ (r & 7))) * 16) = xb[tb][ks];
+          }
+        }
+      }
+    }
+  };
+
   // Persistent workgroups walk the token tiles tile = blockIdx.x + k gridDim.x.  A tile's rows and
   // first weight steps are loaded while the previous tile finishes (its last down product,
   // LayerNorm and stores), so only the first tile waits for them.  Every workgroup does the same
@@ -311,17 +355,62 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     stage_first();
     barrier_vm<0>();
   }
+  // Work items are (tile, layer) pairs, a tile's layers one after another.
+  int item = 0;
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  for (int layer = 0; layer < NL; ++layer, ++item) {
   const int64_t tok0 = tile * kTokens + (wave >> 1) * 32 * TB + col;  // block tb: + 32 tb
-  // Issued after the last loads this tile waits for: vector-memory loads complete in order.
+  TO *__restrict__ out = (TO *)lay.out + (int64_t)layer * lay.out_stride;
+  const int par = NL > 1 ? (item & 1) : 0;  // LayerNorm parameter buffer of this item
+  // Issued after the last loads this item waits for: vector-memory loads complete in order.  The
+  // next item is the tile's next layer (its first weight steps; at d = 512 the tile's rows again)
+  // or the next tile's first layer (its rows and first weight steps).
   auto prefetch_next = [&]() {
+    if (layer + 1 < NL) {
+      use_layer(layer + 1);
+      if constexpr (kWide) load_x(tile);
+      stage_first();
+      return;
+    }
     const int64_t nt = tile + gridDim.x;
+    if (NL > 1) use_layer(0);
     if (nt < n_tiles) {
       if constexpr (kWide)
         load_x(nt);
       else
         stage_x(nt);
       stage_first();
+    }
+  };
+  // LayerNorm parameters of the next item, loaded at the start of this one and written to the other
+  // half of gb after the first step's barrier (that half was last read by the previous item).
+  constexpr int kGB = (D + 64 * NW - 1) / (64 * NW);
+  float gnext[kGB], bnext[kGB];
+  auto load_next_gb = [&]() {
+    if constexpr (LN) {
+      if (NL > 1) {
+        const int64_t o = (int64_t)(layer + 1 < NL ? layer + 1 : 0) * lay.ln_stride;
+#pragma unroll
+        for (int j = 0; j < kGB; ++j) {
+          const int i = threadIdx.x + 64 * NW * j;
+          gnext[j] = i < D ? lay.gamma[o + i] : 0.f;
+          bnext[j] = i < D ? lay.beta[o + i] : 0.f;
+        }
+      }
+    }
+  };
+  auto store_next_gb = [&]() {
+    if constexpr (LN) {
+      if (NL > 1) {
+#pragma unroll
+        for (int j = 0; j < kGB; ++j) {
+          const int i = threadIdx.x + 64 * NW * j;
+          if (i < D) {
+            gb[par ^ 1][0][i] = gnext[j];
+            gb[par ^ 1][1][i] = bnext[j];
+          }
+        }
+      }
     }
   };
 
@@ -409,9 +498,11 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         wo[1][ob] = base[(S::NOB + ob) * 64];
       }
     };
-    // The tile's rows and first fragments landed before the barrier that ended the previous tile.
+    // The item's rows and first fragments landed before the barrier that ended the previous item.
+    load_next_gb();
     up_all(0);
     barrier_vm<0>();  // slot 0 is restaged in step 0
+    store_next_gb();
     for (int t = 0; t < S_; ++t) {
       const bool has_up = t + 1 < S_, has_down = t >= 1;
       bf16x8 wo[2][S::NOBW];
@@ -461,8 +552,9 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     };
     bf16x8 wring[WR];
 
-    // The tile's rows and first fragments landed before the barrier that ended the previous tile.
+    // The item's rows and first fragments landed before the barrier that ended the previous item.
     read_x();
+    load_next_gb();
     barrier_lds();  // every wave has read its rows out of slot 2
     if (S_ > 2) stage_uv(2, 2);
     if constexpr (!kGO) stage_o(0, 0);
@@ -573,6 +665,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     general(0);
+    store_next_gb();
     int t = 1;
     for (; t + 3 < S_; t += 3) {
       steady(t, I1{});
@@ -580,6 +673,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       steady(t + 2, I0{});
     }
     for (; t < S_; ++t) general(t);
+    if (layer + 1 < NL) write_x();
     // The down product of the last step remains.
     swap_in(S_ - 1);
     if constexpr (kGO) {
@@ -652,8 +746,8 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   auto normalised = [&](int ob, int tb, int q, float (&v)[4]) {
     const int f0 = 32 * (S::NOBW * role + ob) + 8 * q + 4 * grp;
     if constexpr (LN) {
-      const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gb[0][f0]);
-      const f32x4 bt = *reinterpret_cast<const f32x4 *>(&gb[1][f0]);
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gb[par][0][f0]);
+      const f32x4 bt = *reinterpret_cast<const f32x4 *>(&gb[par][1][f0]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = (yacc[ob][tb][4 * q + j] - mean[tb]) * inv[tb] * gm[j] + bt[j];
     } else {
@@ -702,14 +796,14 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       }
     }
   }
-  barrier_vm<0>();  // the next tile restages the ring and reuses the swap and statistics buffers
+  barrier_vm<0>();  // the next item restages the ring and reuses the swap and statistics buffers
+  }
   }
 }
 
 template <int D, bool LN, typename TO>
 static hipError_t launch_encode(hipStream_t s, int r, int64_t n_rows, const void *X, int64_t ldx,
-                                const void *packed, void *out, int64_t ldo, const float *gamma,
-                                const float *beta, float eps) {
+                                const EncodeLayers &lay, int64_t ldo, float eps) {
   constexpr int TB = D > 256 ? 1 : D == 256 ? STCA_ENC_TB : STCA_ENC_TB_SMALL;
   using PL = PairLaunch<D, TB>;
   auto kern = encode_pair_kernel<D, TB, LN, TO>;
@@ -726,36 +820,41 @@ static hipError_t launch_encode(hipStream_t s, int r, int64_t n_rows, const void
   const int64_t tiles = (n_rows + PL::kTokens - 1) / PL::kTokens;
   const int64_t blocks = std::min<int64_t>(tiles, resident);
   // Stagger the first tiles over about half a tile's time only when every workgroup has many
-  // tiles to do, so that the start-up delay is amortised.
-  const int stagger = tiles >= 8 * blocks ? STCA_ENC_STAGGER * (r * D / 32) : 0;
+  // items to do, so that the start-up delay is amortised.
+  const int stagger = tiles * lay.n >= 8 * blocks ? STCA_ENC_STAGGER * (r * D / 32) : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PL::NW), 0, s, n_rows, r * D / 32, (const bf16 *)X, ldx,
-                     (const bf16x8 *)packed, (TO *)out, ldo, gamma, beta, eps, stagger);
+                     lay, ldo, eps, stagger);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t encode_d(hipStream_t s, int r, int64_t n_rows, const void *X, int64_t ldx,
-                           const void *packed, void *out, int64_t ldo, bool out_bf16, bool apply_ln,
-                           const float *gamma, const float *beta, float eps) {
-  if (apply_ln) {
-    return out_bf16 ? launch_encode<D, true, bf16>(s, r, n_rows, X, ldx, packed, out, ldo, gamma, beta, eps)
-                    : launch_encode<D, true, float>(s, r, n_rows, X, ldx, packed, out, ldo, gamma, beta, eps);
+                           const EncodeLayers &lay, int64_t ldo, bool out_bf16, bool apply_ln, float eps) {
+  if (apply_ln)
+    return out_bf16 ? launch_encode<D, true, bf16>(s, r, n_rows, X, ldx, lay, ldo, eps)
+                    : launch_encode<D, true, float>(s, r, n_rows, X, ldx, lay, ldo, eps);
+  return out_bf16 ? launch_encode<D, false, bf16>(s, r, n_rows, X, ldx, lay, ldo, eps)
+                  : launch_encode<D, false, float>(s, r, n_rows, X, ldx, lay, ldo, eps);
+}
+
+hipError_t encode_mfma_layers(hipStream_t s, int d, int r, int64_t n_rows, const void *X, int64_t ldx,
+                              const EncodeLayers &lay, int64_t ldo, bool out_bf16, bool apply_ln, float eps) {
+  if (n_rows <= 0) return hipSuccess;
+  if (lay.n < 1 || lay.n > STCA_MAX_M) return hipErrorInvalidValue;
+  switch (d) {
+    case 64: return encode_d<64>(s, r, n_rows, X, ldx, lay, ldo, out_bf16, apply_ln, eps);
+    case 128: return encode_d<128>(s, r, n_rows, X, ldx, lay, ldo, out_bf16, apply_ln, eps);
+    case 256: return encode_d<256>(s, r, n_rows, X, ldx, lay, ldo, out_bf16, apply_ln, eps);
+    case 512: return encode_d<512>(s, r, n_rows, X, ldx, lay, ldo, out_bf16, apply_ln, eps);
+    default: return hipErrorInvalidValue;
   }
-  return out_bf16 ? launch_encode<D, false, bf16>(s, r, n_rows, X, ldx, packed, out, ldo, gamma, beta, eps)
-                  : launch_encode<D, false, float>(s, r, n_rows, X, ldx, packed, out, ldo, gamma, beta, eps);
 }
 
 hipError_t encode_mfma(hipStream_t s, int d, int r, int64_t n_rows, const void *X, int64_t ldx,
                        const void *packed, void *out, int64_t ldo, bool out_bf16, bool apply_ln,
                        const float *gamma, const float *beta, float eps) {
-  if (n_rows <= 0) return hipSuccess;
-  switch (d) {
-    case 64: return encode_d<64>(s, r, n_rows, X, ldx, packed, out, ldo, out_bf16, apply_ln, gamma, beta, eps);
-    case 128: return encode_d<128>(s, r, n_rows, X, ldx, packed, out, ldo, out_bf16, apply_ln, gamma, beta, eps);
-    case 256: return encode_d<256>(s, r, n_rows, X, ldx, packed, out, ldo, out_bf16, apply_ln, gamma, beta, eps);
-    case 512: return encode_d<512>(s, r, n_rows, X, ldx, packed, out, ldo, out_bf16, apply_ln, gamma, beta, eps);
-    default: return hipErrorInvalidValue;
-  }
+  const EncodeLayers lay{packed, 0, out, 0, gamma, beta, 0, 1};
+  return encode_mfma_layers(s, d, r, n_rows, X, ldx, lay, ldo, out_bf16, apply_ln, eps);
 }
 
 }  // namespace stca

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "stca.h"
 
 namespace stca {
 
@@ -44,12 +45,29 @@ hipError_t to_bf16(hipStream_t s, int64_t n, const float *src, void *dst);
 // Re-layout of one FFN's W_u, W_v (d x rd) and W_o (rd x d) into MFMA fragment order.
 size_t encode_packed_bytes(int d, int r);
 hipError_t encode_pack(hipStream_t s, int d, int r, const void *Wu, const void *Wv, const void *Wo,
-                       void *packed);
+                       void *packed, const float *gamma = nullptr, const float *beta = nullptr);
 // out[n x d] = LN(SwiGLUFFN(X)) (apply_ln) or SwiGLUFFN(X); X bf16 (row stride ldx);
 // out bf16 or fp32 (row stride ldo).
 hipError_t encode_mfma(hipStream_t s, int d, int r, int64_t n_rows, const void *X, int64_t ldx,
                        const void *packed, void *out, int64_t ldo, bool out_bf16, bool apply_ln,
                        const float *gamma, const float *beta, float eps);
+// Several FFNs of the same shape over the same rows in one launch (the history encodes of all
+// layers, eq. (2)): out_l = LN_l(SwiGLUFFN_l(X)) for l < n, each tile of X read from memory once.
+// Layer l's packed weights, output and LayerNorm parameters sit at fixed strides from layer 0's.
+struct EncodeLayers {
+  const void *packed;
+  int64_t packed_stride;  // bytes
+  void *out;
+  int64_t out_stride;     // elements
+  const float *gamma, *beta;
+  int64_t ln_stride;      // floats
+  int n;
+};
+hipError_t encode_mfma_layers(hipStream_t s, int d, int r, int64_t n_rows, const void *X, int64_t ldx,
+                              const EncodeLayers &layers, int64_t ldo, bool out_bf16, bool apply_ln, float eps);
+// Bytes between consecutive layers' packed weights when each is followed by its LayerNorm
+// parameters (gamma then beta, d floats each), as encode_pack writes them when given.
+size_t encode_layer_stride(int d, int r);
 
 // ---- ragged split-L attention (attend.hip) --------------------------------------------------
 // Query rows one attention work item covers: 4 waves x 32 rows, or at d = 512 (where two waves

@@ -78,6 +78,9 @@ static void argument_errors() {
   stca_dims chunk = good;
   chunk.attn_chunk = 33;
   EXPECT(stca_encode_workspace_size(&chunk, 10, &n) == STCA_E_DIMS);
+  stca_dims layers = good;
+  layers.encode_layers = 3;
+  EXPECT(stca_encode_workspace_size(&layers, 10, &n) == STCA_E_DIMS);
   EXPECT(stca_encode_workspace_size(nullptr, 10, &n) == STCA_E_ARG);
   EXPECT(stca_encode_workspace_size(&good, -1, &n) == STCA_E_ARG);
   EXPECT(stca_encode_workspace_size(&good, 10, nullptr) == STCA_E_ARG);

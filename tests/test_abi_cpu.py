@@ -79,7 +79,7 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("change,code", [
     (dict(d=96), -2), (dict(d=0), -2), (dict(h=3), -2), (dict(h=0), -2), (dict(r=0), -2), (dict(r=9), -2),
     (dict(M=0), -2), (dict(M=9), -2), (dict(dtype=7), -2), (dict(ln_eps=0.0), -2), (dict(attn_chunk=33), -2),
-    (dict(attn_chunk=-32), -2),
+    (dict(attn_chunk=-32), -2), (dict(encode_layers=3), -2), (dict(encode_layers=-1), -2),
 ])
 def test_forward_rejects_bad_dims(change, code):
     kw = dict(d=256, h=8, M=3, r=4, dtype="bf16", ln_eps=1e-5, attn_chunk=0)
@@ -327,3 +327,19 @@ def test_bench_metric_names_the_workload():
     for key in ("tiny", "uniform", "ragged", "stress20k"):
         m = bench.metric_for(SI.get_config(key))
         assert key in m and "L=10k" not in m
+
+
+def test_forward_workspace_holds_every_layer_when_encodes_share_a_launch():
+    """encode_layers = 2 (all history encodes in one launch) keeps M encoded buffers, 1 keeps one;
+    automatic picks the single launch only where one layer's X~ exceeds 1 GiB at d <= 256."""
+    import numpy as np
+    for key, auto_fused in [("dense10k", True), ("ragged", False), ("uniform", False), ("stress20k", False)]:
+        cfg = SI.get_config(key)
+        L, m = SI.batch_layout(cfg)
+        hist = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
+        tgt = np.concatenate([[0], np.cumsum(m)]).astype(np.int64)
+        c = B.BatchC(cfg.n_users, FAKE, FAKE + 4096, int(hist[-1]), int(tgt[-1]), int(L.max()), int(m.max()))
+        sizes = {k: B.forward_workspace_size(B.dims_for(cfg, encode_layers=k), c) for k in (0, 1, 2)}
+        xt = int(hist[-1]) * cfg.d * 2
+        assert sizes[2] - sizes[1] == (cfg.M - 1) * xt
+        assert sizes[0] == (sizes[2] if auto_fused else sizes[1])

@@ -55,6 +55,24 @@ def test_forward_reduced(B, key, change):
     assert err <= tol_for(cfg)
 
 
+@pytest.mark.parametrize("key,change", REDUCED[1:] + [("ragged", dict(n_users=7, M=1)),
+                                                    ("uniform", dict(n_users=5, d=64, h=4, M=4))],
+                         ids=[k for k, _ in REDUCED[1:]] + ["ragged-M1", "d64-M4"])
+def test_forward_one_encode_launch_for_all_layers(B, key, change):
+    """encode_layers = 2 (every history encode in one launch, X read once per tile) gives exactly the
+    results of one launch per layer, and the oracle's within the bar."""
+    cfg = SI.scaled(SI.get_config(key), **change)
+    announce("forward-encode-layers", cfg.key, change)
+    W = SI.make_weights(cfg, random_ln=True)
+    inp = SI.make_inputs(cfg)
+    Z1 = run_forward(B, cfg, inp, W, encode_layers=1)
+    Z2 = run_forward(B, cfg, inp, W, encode_layers=2)
+    assert np.array_equal(Z1, Z2)
+    err = row_rel(Z2, O.forward_batch(inp, W))
+    print(f"  {key}: users={inp.n_users} L={inp.total_L} M={cfg.M} err={err:.3e}", flush=True)
+    assert err <= tol_for(cfg)
+
+
 FP32_SHAPES = [
     ("uniform", dict(n_users=3, dtype="f32")),
     ("ragged", dict(n_users=10, dtype="f32", length=("lognormal", 300.0, 400.0, 1, 2000))),
