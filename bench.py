@@ -132,7 +132,7 @@ def bench_sl(a, cfg, dev):
     L, off = B.sl_plan(prm, inp.L, s, order)
     plan_ms = (time.perf_counter() - t) * 1e3
     total = int(off[-1])
-    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk)
+    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk, encode_layers=a.encode_layers)
     Xf = B.to_device(inp.X, cfg.dtype, dev)
     del inp.X
     full_off = torch.from_numpy(inp.hist_off.astype(np.int64)).to(dev)
@@ -202,7 +202,7 @@ def bench_litm(a, cfg, dev):
     mo, go, mem = B.litm_plan(inp.hist_off, inp.item_id, T_gap)
     plan_ms = (time.perf_counter() - t) * 1e3
     n_groups = len(go) - 1
-    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk)
+    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk, encode_layers=a.encode_layers)
     Xf = B.to_device(inp.X, cfg.dtype, dev)
     del inp.X
     god, memd = torch.from_numpy(go).to(dev), torch.from_numpy(mem).to(dev)
@@ -497,6 +497,8 @@ def main():
     ap.add_argument("--workload", default="dense10k")
     ap.add_argument("--users", type=int, default=0, help="override the number of users (0 = workload's)")
     ap.add_argument("--attn-chunk", type=int, default=0)
+    ap.add_argument("--encode-layers", type=int, default=0, choices=(0, 1, 2),
+                    help="history encodes: 0 automatic, 1 one launch per layer, 2 every layer in one launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sl", action="store_true",
                     help="time a stochastic-length batch built from the workload's histories instead "
@@ -564,7 +566,7 @@ def main():
     inp = SI.make_inputs(cfg)
     log(f"inputs {cfg.key}: {inp.n_users} users, {inp.total_L} history tokens, {inp.total_T} targets "
         f"({time.perf_counter() - t:.1f} s)")
-    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk)
+    dims = B.dims_for(cfg, attn_chunk=a.attn_chunk, encode_layers=a.encode_layers)
     dw = B.DeviceWeights(W, cfg.dtype, dev)
     db = B.DeviceBatch(inp, dev)
     del inp.X
@@ -689,6 +691,7 @@ def main():
         "config": {"workload": cfg.description, "key": cfg.key, "users": db.inp.n_users,
                    "history_tokens": db.total_L, "targets": db.total_T, "d": cfg.d, "h": cfg.h, "M": cfg.M,
                    "r": cfg.r, "attn_chunk": a.attn_chunk or "auto",
+                   "encode_layers": {0: "auto", 1: "one launch per layer", 2: "one launch"}[a.encode_layers],
                    "infinity_cache": "flushed before each timed forward" if a.flush_cache else "not flushed"},
         "roofline": {"kernel": enc_label,
                      "bound": "mfma", "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s",
