@@ -55,10 +55,6 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float swiglu_gate(float a, float g) {
   return a * g * fast_rcp(1.0f + fast_exp2(-g * kLog2e));
 }
-// The same gate on pre-scaled inputs a' = -ln2 a, g' = -log2(e) g: a' g' = a g and 2^g' = e^-g.
-__device__ __forceinline__ float swiglu_gate_scaled(float a, float g) {
-  return a * g * fast_rcp(1.0f + fast_exp2(g));
-}
 
 // ---- wave (64-lane) reductions -------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

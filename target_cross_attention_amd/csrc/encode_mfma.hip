@@ -15,8 +15,8 @@
 //   * the gated values of a lane form exactly one B operand (16 hidden features x 32 tokens) of
 //     the down product; the pair swaps these through LDS (1 KiB per wave, block and step), and
 //     each wave accumulates half of the d outputs, Y^T[d/2 x tokens] += W_o^T[d/2 x 32] H^T;
-//   * weights are pre-packed in fragment order (1 KiB = one wave operand); the up/gate columns are
-//     pre-scaled (by -ln 2 and -log2 e) so that the gate needs no scaling multiply; fragments are
+//   * weights are pre-packed in fragment order (1 KiB = one wave operand), bit for bit as given
+//     (the gate applies its exp2 scaling in fp32, so no weight is rounded twice); fragments are
 //     staged step by step into LDS with direct global->LDS loads and shared by all waves of the
 //     workgroup, or read by each wave from L2 straight into registers (down fragments at d >= 256);
 //   * LayerNorm statistics of a token combine the two waves of its pair through LDS;
@@ -35,6 +35,7 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+
 
 namespace stca {
 
@@ -82,15 +83,9 @@ __global__ __launch_bounds__(256) void encode_pack_kernel(int d, int rd, const u
   if (f < 2 * NKS) {
     const int role = f / NKS, ks = f % NKS;
     const uint16_t *W = col < 16 ? Wu : Wv;
-    // Pre-scaled so that the kernel's accumulators hold u' = -ln2 u and v' = -log2(e) v: then
-    // u v SiLU(v) = u' v' / (1 + 2^v'), with no scaling multiply in the gate.
-    const float scale = col < 16 ? -0.69314718055994531f : -1.4426950408889634f;
     const int fc = 32 * s + 16 * role + (col & 15);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float w = __uint_as_float((uint32_t)W[(int64_t)(16 * ks + 8 * g + e) * rd + fc] << 16);
-      v[e] = f32_to_bf16_bits(w * scale);
-    }
+    for (int e = 0; e < 8; ++e) v[e] = W[(int64_t)(16 * ks + 8 * g + e) * rd + fc];
   } else {
     const int idx = f - 2 * NKS;
     const int ob = idx % NOB, kk = (idx / NOB) ^ (ob / (NOB / 2));
@@ -445,7 +440,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[tb][j] = f32_to_bf16(swiglu_gate_scaled(ga[tb][j], ga[tb][j + 8]));
+      for (int j = 0; j < 8; ++j) h[tb][j] = f32_to_bf16(swiglu_gate(ga[tb][j], ga[tb][j + 8]));
   };
   auto copy_acc = [&](float (&ga)[TB][16]) {
 #pragma unroll
@@ -638,13 +633,13 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         }
         if (k % 3 == 0 && k / 3 < 8 * TB) {
           const int e = k / 3;
-          hv[e] = swiglu_gate_scaled(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+          hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
           asm volatile("" : "+v"(hv[e]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
   #pragma unroll
-      for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate_scaled(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+      for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
       bf16x8 h[TB];
   #pragma unroll
       for (int e = 0; e < 8 * TB; ++e) h[e >> 3][e & 7] = f32_to_bf16(hv[e]);
