@@ -276,7 +276,8 @@ def bench_backward(a, cfg, dev):
     del inp.X
     dZ = torch.from_numpy(np.random.default_rng(11).standard_normal((db.total_T, cfg.M, cfg.d), np.float32)).to(dev)
     grads = B.DeviceGrads(dims, db.total_L, db.total_T, dev)
-    keep = not a.no_keep
+    mixed = cfg.dtype == "bf16"   # bf16 storage: the mixed-precision path
+    keep = not a.no_keep and not mixed
     ws = B.workspace(B.backward_workspace_size(dims, db.c, keep), dev)
     stream = torch.cuda.current_stream()
     log(f"backward workspace {ws.numel() / 2**30:.2f} GiB; warmup {a.warmup}")
@@ -298,12 +299,13 @@ def bench_backward(a, cfg, dev):
     pairs = float((db.inp.L * db.inp.m).sum()) * h
     # Dominant phase: the derivative of eq. (2) over the history rows, one per layer.  Algorithmic
     # FLOP per history token: the products dW_o, dH, dW_u, dW_v, dx (12 r d^2, 2 FLOP per
-    # multiply-add), plus with the minimum workspace the recomputed A = x W_u, G = x W_v and
-    # Y = H W_o (6 r d^2).
+    # multiply-add), plus, unless the fp32 path's keep workspace holds them, the recomputed
+    # A = x W_u, G = x W_v and Y = H W_o (6 r d^2).
     enc_ms, enc_n = phases["bwd_encode"]
     enc_avg_s = enc_ms / max(enc_n, 1) / 1e3
     enc_flops = (12.0 if keep else 18.0) * r * d * d * L
     achieved = enc_flops / enc_avg_s / 1e12
+    peak = PEAK_BF16_TFLOPS if mixed else PEAK_FP32_TFLOPS
     # Per (target, head, history token) pair: the scores twice (statistics, then again for alpha), abar,
     # dA, du and the two products of dX~, each 2d FLOP.
     att_layer_ms = phases["bwd_attend"][0] / a.steps / M
@@ -311,14 +313,20 @@ def bench_backward(a, cfg, dev):
         "metric": "STCA backward history-tokens/s (gradients of every weight, X and x_t)",
         "value": L * a.steps / dt, "unit": "history-tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": dt * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded; training-shaped ragged batch)",
+        "vs_baseline": None, "dtype": "bf16" if mixed else "f32",
+        "precision": ("mixed: bf16 operands, fp32 accumulation, LayerNorm and softmax statistics in fp32 "
+                      "(encode derivative); fp32 attention derivative" if mixed else "fp32 throughout"),
+        "data": "synthetic (seeded; training-shaped ragged batch)",
         "config": {"workload": cfg.description, "key": cfg.key, "users": db.inp.n_users, "history_tokens": L,
                    "targets": T, "storage": cfg.dtype,
-                   "workspace": ("keep (encode intermediates kept from the recompute)" if keep else "minimum"),
+                   "workspace": ("keep (encode intermediates kept from the recompute)" if keep else
+                                 "mixed path (encode recomputed per row chunk)" if mixed else "minimum"),
                    "workspace_gib": ws.numel() / 2**30},
-        "roofline": {"kernel": "encode backward (fp32 matrix-core GEMMs + SwiGLU/LayerNorm derivatives)",
-                     "bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+        "roofline": {"kernel": ("encode backward (bf16 matrix-core GEMMs with fused SwiGLU epilogues, fp32 "
+                                "LayerNorm derivative)" if mixed else
+                                "encode backward (fp32 matrix-core GEMMs + SwiGLU/LayerNorm derivatives)"),
+                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
                      "algorithmic_flops_per_launch": enc_flops, "avg_launch_ms": enc_avg_s * 1e3,
                      "launches": enc_n},
         "attention_backward": {"kernels": "ragged per-user fp32 matrix-core products + softmax/dS row passes",

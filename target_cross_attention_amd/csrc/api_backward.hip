@@ -14,6 +14,7 @@ namespace {
 // ---- backward (gradients of eqs. (2)-(8)) ------------------------------------------------------
 constexpr int kWgradParts = 32;    // split-K blocks of one weight gradient
 constexpr int kLnBlocks = 256;     // row blocks of the LayerNorm derivative (partial column sums)
+constexpr int64_t kMixedRows = 65536;  // row chunk of the mixed-precision encode backward
 
 struct BackwardWs {
   float *Xt = nullptr;      // M x total_L x d: encoded history of every layer (fp32)
@@ -30,12 +31,17 @@ struct BackwardWs {
   float *S = nullptr, *S2 = nullptr;  // every user's score matrix (R_u x Lp_u), twice
   RaggedDesc *desc = nullptr;         // 3 n_users product descriptors
   int64_t rows = 0;         // history rows per encode-backward chunk
-  // With a workspace of the "keep" size: A = X W_u, G = X W_v (M x total_L x rd) and the pre-LN rows
-  // Y (M x total_L x d) of every layer, kept from the forward recompute for the encode backward.
+  // fp32 path, with a workspace of the "keep" size: A = X W_u, G = X W_v (M x total_L x rd) and the
+  // pre-LN rows Y (M x total_L x d) of every layer, kept from the forward recompute.
   float *kA = nullptr, *kG = nullptr, *kY = nullptr;
-  // bf16 storage: W_u^T and W_v^T (rd x d each) of every layer's history FFN, the k-contiguous B operands
-  // of the bf16 matrix-core products A = X W_u, G = X W_v.
-  void *WuT[STCA_MAX_M] = {}, *WvT[STCA_MAX_M] = {};
+  // Mixed-precision path (bf16 storage): bf16 operands for the matrix cores, per row chunk: H (rows x
+  // rd), H^T, u^T, g^T (rd x ldt), dY (rows x d) and dY^T (d x ldt), [dU | dG] (rows x 2rd) and its
+  // transpose (2rd x ldt); X^T (d x ldx) for all rows; per layer the re-laid-out weights (see
+  // bwd_weights) and the forward encode's packed weights.
+  int64_t ldt = 0, ldx = 0;
+  void *mH = nullptr, *mHt = nullptr, *mUt = nullptr, *mGt = nullptr, *mdY = nullptr, *mdYt = nullptr;
+  void *mdUG = nullptr, *mdUGt = nullptr, *XT = nullptr;
+  void *uvt[STCA_MAX_M] = {}, *uvc[STCA_MAX_M] = {}, *ot[STCA_MAX_M] = {}, *packed[STCA_MAX_M] = {};
 };
 
 // Upper bound on sum_u R_u Lp_u (R_u = m_u h query rows, Lp_u = L_u rounded up to 4):
@@ -47,6 +53,8 @@ int64_t score_elems(const stca_dims *dm, const stca_batch *b) {
 
 size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, BackwardWs &w, bool keep) {
   Carver c(base);
+  const bool mixed = dm->dtype == STCA_BF16;
+  if (mixed) keep = false;  // the mixed path recomputes the encode per chunk on the bf16 matrix cores
   const int64_t L = b->total_L, T = b->total_T, d = dm->d, h = dm->h, rd = (int64_t)dm->r * dm->d, M = dm->M;
   w.Xt = c.take<float>((size_t)(M * L * d));
   w.dXt = c.take<float>((size_t)(L * d));
@@ -75,21 +83,37 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   w.Dv = c.take<float>((size_t)(T * h));
   w.du = c.take<float>((size_t)(T * h * d));
   w.dP = c.take<float>((size_t)(T * d));
-  w.rows = std::min<int64_t>(std::max<int64_t>(L, 1), kFfnRows);
-  w.eA = c.take<float>((size_t)(w.rows * rd));
-  w.eG = c.take<float>((size_t)(w.rows * rd));
-  w.eH = c.take<float>((size_t)(w.rows * rd));
+  w.rows = std::min<int64_t>(std::max<int64_t>(L, 1), mixed ? kMixedRows : kFfnRows);
+  if (!mixed) {
+    w.eA = c.take<float>((size_t)(w.rows * rd));
+    w.eG = c.take<float>((size_t)(w.rows * rd));
+    w.eH = c.take<float>((size_t)(w.rows * rd));
+  }
   w.eY = c.take<float>((size_t)(w.rows * d));
   w.edY = c.take<float>((size_t)(w.rows * d));
   w.parts = c.take<float>((size_t)kWgradParts * std::max<int64_t>(d * rd, M * d * d));
   w.S = c.take<float>((size_t)score_elems(dm, b));
   w.S2 = c.take<float>((size_t)score_elems(dm, b));
   w.desc = c.take<RaggedDesc>((size_t)std::max(3 * b->n_users, 1));
-  if (dm->dtype == STCA_BF16)
+  if (mixed) {
+    w.ldt = round_up(w.rows, 8);
+    w.ldx = round_up(std::max<int64_t>(L, 1), 8);
+    w.mH = c.take<char>((size_t)(w.rows * rd) * 2);
+    w.mHt = c.take<char>((size_t)(rd * w.ldt) * 2);
+    w.mUt = c.take<char>((size_t)(rd * w.ldt) * 2);
+    w.mGt = c.take<char>((size_t)(rd * w.ldt) * 2);
+    w.mdY = c.take<char>((size_t)(w.rows * d) * 2);
+    w.mdYt = c.take<char>((size_t)(d * w.ldt) * 2);
+    w.mdUG = c.take<char>((size_t)(w.rows * 2 * rd) * 2);
+    w.mdUGt = c.take<char>((size_t)(2 * rd * w.ldt) * 2);
+    w.XT = c.take<char>((size_t)(d * w.ldx) * 2);
     for (int i = 0; i < M; ++i) {
-      w.WuT[i] = c.take<char>((size_t)(d * rd) * 2);
-      w.WvT[i] = c.take<char>((size_t)(d * rd) * 2);
+      w.uvt[i] = c.take<char>((size_t)(2 * rd * d) * 2);
+      w.uvc[i] = c.take<char>((size_t)(2 * rd * d) * 2);
+      w.ot[i] = c.take<char>((size_t)(rd * d) * 2);
+      w.packed[i] = c.take<char>(encode_packed_bytes(dm->d, dm->r));
     }
+  }
   if (keep) {
     w.kA = c.take<float>((size_t)(M * L * rd));
     w.kG = c.take<float>((size_t)(M * L * rd));
@@ -159,18 +183,12 @@ hipError_t mm(hipStream_t s, int m, int n, int k, const void *A, int64_t lda, bo
 }
 
 // eq. (1) on n rows with its intermediates kept: A = x W_u, G = x W_v, H = A * SiLU(G), Y = H W_o.
-// With bf16 x and the transposed weights WuT/WvT (rd x d, bf16) A and G run on the bf16 matrix cores.
 int ffn_saved(hipStream_t s, const stca_dims *dm, const stca_ffn *f, int64_t n, const void *x, bool x_bf16,
-              float *A, float *G, float *H, float *Y, const void *WuT = nullptr, const void *WvT = nullptr) {
+              float *A, float *G, float *H, float *Y) {
   const int d = dm->d, rd = dm->r * dm->d;
   const bool wb = dm->dtype == STCA_BF16;
-  if (x_bf16 && wb && WuT && WvT) {
-    HIP_TRY(gemm_bf16_nt(s, (int)n, rd, d, x, d, WuT, d, A, rd));
-    HIP_TRY(gemm_bf16_nt(s, (int)n, rd, d, x, d, WvT, d, G, rd));
-  } else {
-    HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wu, rd, wb, false, A, rd, 0.f));
-    HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wv, rd, wb, false, G, rd, 0.f));
-  }
+  HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wu, rd, wb, false, A, rd, 0.f));
+  HIP_TRY(mm(s, (int)n, rd, d, x, d, x_bf16, f->Wv, rd, wb, false, G, rd, 0.f));
   HIP_TRY(swiglu_fwd(s, n * rd, A, G, H));
   HIP_TRY(mm(s, (int)n, d, rd, H, rd, false, f->Wo, d, wb, false, Y, d, 0.f));
   return STCA_OK;
@@ -199,6 +217,79 @@ int ffn_backward(hipStream_t s, const stca_dims *dm, const stca_ffn *f, const st
   if (dx) {
     HIP_TRY(mm(s, (int)n, d, rd, dA, rd, false, f->Wu, rd, wb, true, dx, d, accumulate ? 1.f : 0.f));
     HIP_TRY(mm(s, (int)n, d, rd, dG, rd, false, f->Wv, rd, wb, true, dx, d, 1.f));
+  }
+  return STCA_OK;
+}
+
+// Mixed-precision backward of eq. (2) for layer i over all history rows, in row chunks: every product
+// on the bf16 matrix cores with fp32 accumulation (gemm_nt), the SwiGLU and its derivative fused into
+// the products that produce their inputs, the LayerNorm derivative and the weight-gradient sums in
+// fp32.  Per chunk of n rows (x = X rows, dXt = dL/dX~ rows):
+//   [u | g] = x [W_u | W_v]   -> H = u SiLU(g) (bf16, row-major and transposed), u^T, g^T   (kEpiSwigluFwd)
+//   Y = H W_o                 -> fp32, then the LayerNorm derivative: dY (bf16, both layouts), dgamma, dbeta
+//   dW_o += H^T dY            (split over rows, partial sums added in order)
+//   dH = dY W_o^T             -> dU = dH SiLU(g), dG = dH u SiLU'(g) (bf16, both layouts)  (kEpiSwigluBwd)
+//   [dW_u | dW_v] += x^T [dU | dG]
+//   dX += [dU | dG] [W_u | W_v]^T
+int encode_backward_mixed(hipStream_t s, const stca_dims *dm, const stca_ffn &f, const stca_ffn_grad &g, int i,
+                          const BackwardWs &bw, int64_t L, const void *X, const float *dXt, float *dX) {
+  const int d = dm->d, rd = dm->r * dm->d;
+  for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
+    const int n = (int)std::min<int64_t>(bw.rows, L - r0);
+    const void *x = (const char *)X + (size_t)r0 * d * 2;
+    NtEpilogue e1;
+    e1.H = bw.mH;
+    e1.ldh = rd;
+    e1.Ht = bw.mHt;
+    e1.Ut = bw.mUt;
+    e1.Gt = bw.mGt;
+    e1.ldt = bw.ldt;
+    HIP_TRY(gemm_nt(s, kEpiSwigluFwd, n, 2 * rd, d, 0, 1, x, d, 0, bw.uvt[i], d, 0, e1));
+    NtEpilogue e2;
+    e2.C = bw.eY;
+    e2.ldc = d;
+    HIP_TRY(gemm_nt(s, kEpiStore, n, d, rd, 0, 1, bw.mH, rd, 0, bw.ot[i], rd, 0, e2));
+    HIP_TRY(ln_bwd(s, n, d, dXt + (size_t)r0 * d, d, bw.eY, d, f.gamma, dm->ln_eps, bw.edY, g.dgamma, g.dbeta,
+                   bw.parts, kLnBlocks));
+    HIP_TRY(to_bf16_rt(s, n, d, bw.edY, d, bw.mdY, d, bw.mdYt, bw.ldt));
+    // dW_o (rd x d) over the chunk's rows, split into blocks of ks rows
+    {
+      const int64_t ks = round_up((n + kWgradParts - 1) / kWgradParts, 64), parts = (n + ks - 1) / ks;
+      NtEpilogue e3;
+      e3.C = bw.parts;
+      e3.ldc = d;
+      e3.sC = (int64_t)rd * d;
+      HIP_TRY(gemm_nt(s, kEpiStore, rd, d, n, (int)ks, (int)parts, bw.mHt, bw.ldt, 0, bw.mdYt, bw.ldt, 0, e3));
+      HIP_TRY(sum_parts_strided(s, rd, d, (int)parts, bw.parts, d, (int64_t)rd * d, g.dWo, d, true));
+    }
+    NtEpilogue e4;
+    e4.Ut = bw.mUt;
+    e4.Gt = bw.mGt;
+    e4.ldt = bw.ldt;
+    e4.dUG = bw.mdUG;
+    e4.lddug = 2 * rd;
+    e4.dUGt = bw.mdUGt;
+    e4.rd = rd;
+    HIP_TRY(gemm_nt(s, kEpiSwigluBwd, n, rd, d, 0, 1, bw.mdY, d, 0, f.Wo, d, 0, e4));
+    // [dW_u | dW_v] (d x 2rd) over the chunk's rows
+    {
+      const int max_parts = kWgradParts / 2;  // the parts buffer holds 16 blocks of d x 2rd
+      const int64_t ks = round_up((n + max_parts - 1) / max_parts, 64), parts = (n + ks - 1) / ks;
+      NtEpilogue e5;
+      e5.C = bw.parts;
+      e5.ldc = 2 * rd;
+      e5.sC = (int64_t)d * 2 * rd;
+      HIP_TRY(gemm_nt(s, kEpiStore, d, 2 * rd, n, (int)ks, (int)parts, (const char *)bw.XT + (size_t)r0 * 2, bw.ldx,
+                      0, bw.mdUGt, bw.ldt, 0, e5));
+      HIP_TRY(sum_parts_strided(s, d, rd, (int)parts, bw.parts, 2 * rd, (int64_t)d * 2 * rd, g.dWu, rd, true));
+      HIP_TRY(sum_parts_strided(s, d, rd, (int)parts, bw.parts + rd, 2 * rd, (int64_t)d * 2 * rd, g.dWv, rd, true));
+    }
+    if (dX) {
+      NtEpilogue e6;
+      e6.C = dX + (size_t)r0 * d;
+      e6.ldc = d;
+      HIP_TRY(gemm_nt(s, kEpiAcc, n, d, 2 * rd, 0, 1, bw.mdUG, 2 * rd, 0, bw.uvc[i], 2 * rd, 0, e6));
+    }
   }
   return STCA_OK;
 }
@@ -268,11 +359,14 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
   if (T == 0) return STCA_OK;  // no target, no gradient
   HIP_TRY(ragged_plan(s, b->n_users, b->hist_off, b->tgt_off, h, d, b->total_L, b->total_T, b->max_L, b->max_T,
                       score_elems(dm, b), bw.desc));
-  if (bf)
+  if (bf) {  // mixed path: weight layouts of every history FFN, X^T, the forward encode's packed weights
     for (int i = 0; i < M; ++i) {
-      HIP_TRY(transpose_bf16(s, d, rd, w->hist[i].Wu, bw.WuT[i]));
-      HIP_TRY(transpose_bf16(s, d, rd, w->hist[i].Wv, bw.WvT[i]));
+      const stca_ffn &f = w->hist[i];
+      HIP_TRY(bwd_weights(s, d, dm->r, f.Wu, f.Wv, f.Wo, bw.uvt[i], bw.uvc[i], bw.ot[i]));
+      HIP_TRY(encode_pack(s, d, dm->r, f.Wu, f.Wv, f.Wo, bw.packed[i]));
     }
+    HIP_TRY(transpose_tiled_bf16(s, L, d, X, d, bw.XT, bw.ldx));
+  }
   const int64_t T_rows = b->max_T * h, max_L = b->max_L;  // bounds of the ragged products' sizes
   auto rg = [](const float *A, const float *B, float *C, float alpha, float beta, bool ta, bool tb) {
     GemmArgs g;
@@ -309,8 +403,12 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     float *Xt = bw.Xt + (size_t)i * L * d;
     {
       Phase ph(prof, s, STCA_PHASE_BWD_RECOMPUTE);
-      // eq. (2) in row chunks; with the keep workspace A, G and the pre-LN rows stay for the backward
-      for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
+      // eq. (2): the mixed path runs the forward's fused encode with an fp32 output; the fp32 path in row
+      // chunks, keeping A, G and the pre-LN rows with the keep workspace
+      if (bf)
+        HIP_TRY(encode_mfma(s, d, dm->r, L, X, d, bw.packed[i], Xt, d, false, true, w->hist[i].gamma,
+                            w->hist[i].beta, dm->ln_eps));
+      for (int64_t r0 = 0; r0 < (bf ? 0 : L); r0 += bw.rows) {
         const int64_t n = std::min<int64_t>(bw.rows, L - r0);
         float *A = bw.eA, *G = bw.eG, *Y = bw.eY;
         if (keep) {
@@ -318,8 +416,8 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
           G = bw.kG + ((size_t)i * L + r0) * rd;
           Y = bw.kY + ((size_t)i * L + r0) * d;
         }
-        if ((st = ffn_saved(s, dm, &w->hist[i], n, (const char *)X + (size_t)r0 * d * esize(dm), bf, A, G, bw.eH, Y,
-                            bw.WuT[i], bw.WvT[i])) != STCA_OK)
+        if ((st = ffn_saved(s, dm, &w->hist[i], n, (const char *)X + (size_t)r0 * d * esize(dm), bf, A, G, bw.eH,
+                            Y)) != STCA_OK)
           return st;
         HIP_TRY(layernorm_rows(s, n, d, Y, d, Xt + (size_t)r0 * d, d, false, w->hist[i].gamma, w->hist[i].beta,
                                dm->ln_eps));
@@ -474,8 +572,10 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     HIP_TRY(pt2.end());
     // eq. (2): LayerNorm and SwiGLU FFN of every history row, in row chunks
     Phase pe(prof, s, STCA_PHASE_BWD_ENCODE);
+    if (bf && (st = encode_backward_mixed(s, dm, w->hist[i], g->hist[i], i, bw, L, X, bw.dXt, g->dX)) != STCA_OK)
+      return st;
     const size_t xes = esize(dm);
-    for (int64_t r0 = 0; r0 < L; r0 += bw.rows) {
+    for (int64_t r0 = 0; r0 < (bf ? 0 : L); r0 += bw.rows) {
       const int64_t n = std::min<int64_t>(bw.rows, L - r0);
       const void *Xc = (const char *)X + (size_t)r0 * d * xes;
       float *A = bw.eA, *G = bw.eG, *Y = bw.eY;
@@ -484,7 +584,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
         G = bw.kG + ((size_t)i * L + r0) * rd;
         Y = bw.kY + ((size_t)i * L + r0) * d;
         HIP_TRY(swiglu_fwd(s, n * rd, A, G, bw.eH));
-      } else if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, A, G, bw.eH, Y, bw.WuT[i], bw.WvT[i])) != STCA_OK) {
+      } else if ((st = ffn_saved(s, dm, &w->hist[i], n, Xc, bf, A, G, bw.eH, Y)) != STCA_OK) {
         return st;
       }
       if ((st = ffn_backward(s, dm, &w->hist[i], g->hist[i], true, n, Xc, bf, A, G, bw.eH, Y,

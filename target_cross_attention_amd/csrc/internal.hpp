@@ -30,12 +30,6 @@ struct RaggedDesc {
 hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs, int n, int64_t max_m,
                        int64_t max_n);
 hipError_t swiglu_gate_inplace(hipStream_t s, int64_t n, float *A, const float *G);
-// C[M x N] (fp32) = A[M x K] Bt[N x K]^T, A and Bt bf16 (exact products, fp32 accumulation) on bf16
-// matrix cores; K, lda, ldb multiples of 8, bases 16-byte aligned.
-hipError_t gemm_bf16_nt(hipStream_t s, int M, int N, int K, const void *A, int64_t lda, const void *Bt, int64_t ldb,
-                        float *C, int64_t ldc);
-// out (cols x rows) = in (rows x cols)^T, bf16.
-hipError_t transpose_bf16(hipStream_t s, int rows, int cols, const void *in, void *out);
 hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, int64_t ldy, void *out,
                           int64_t ldo, bool out_bf16, const float *gamma, const float *beta, float eps);
 // dst[n] (bf16) = src[n] (fp32) rounded to nearest even; n a multiple of 4.
@@ -141,6 +135,35 @@ hipError_t litm_merge(hipStream_t s, bool bf16_rows, int d, int64_t n_rows, int6
                       const int64_t *group_off, const int64_t *members, const void *X, void *out);
 hipError_t sl_pack(hipStream_t s, int n_users, const int64_t *full_off, const int64_t *hist_off, int64_t total,
                    int64_t max_len, int row16, const void *X_full, void *X_packed);
+
+// ---- bf16 matrix-core GEMM with fused epilogues (gemm_bf16.hip), mixed-precision backward ------
+enum { kEpiStore = 0, kEpiAcc = 1, kEpiSwigluFwd = 2, kEpiSwigluBwd = 3 };
+struct NtEpilogue {
+  float *C = nullptr;            // kEpiStore / kEpiAcc: fp32 output (row stride ldc, batch stride sC)
+  int64_t ldc = 0, sC = 0;
+  void *H = nullptr;             // kEpiSwigluFwd: H (bf16, rows x rd, row stride ldh)
+  int64_t ldh = 0;
+  void *Ht = nullptr;            // kEpiSwigluFwd: H^T; both: u^T, g^T (bf16, rd x rows, row stride ldt)
+  void *Ut = nullptr, *Gt = nullptr;
+  int64_t ldt = 0;
+  void *dUG = nullptr;           // kEpiSwigluBwd: [dU | dG] (bf16, rows x 2rd, row stride lddug)
+  int64_t lddug = 0;
+  void *dUGt = nullptr;          // kEpiSwigluBwd: [dU | dG]^T (bf16, 2rd x rows, row stride ldt)
+  int rd = 0;
+};
+// C = A[M x K] Bt[N x K]^T (bf16 operands, k-contiguous rows, lda/ldb multiples of 8, bases 16-byte
+// aligned) through epilogue `epi`.  ksplit > 0: blockIdx.z = z takes k in [z ksplit, (z+1) ksplit)
+// and writes C + z sC; otherwise batch z reads A + z sA, Bt + z sB and writes C + z sC.
+hipError_t gemm_nt(hipStream_t s, int epi, int M, int N, int K, int ksplit, int batch, const void *A, int64_t lda,
+                   int64_t sA, const void *Bt, int64_t ldb, int64_t sB, const NtEpilogue &ep);
+hipError_t transpose_tiled_bf16(hipStream_t s, int64_t rows, int cols, const void *in, int64_t ldi, void *out,
+                                int64_t ldo);
+hipError_t to_bf16_rt(hipStream_t s, int64_t rows, int cols, const float *in, int64_t ldi, void *out_r, int64_t ldr,
+                      void *out_t, int64_t ldt);
+hipError_t bwd_weights(hipStream_t s, int d, int r, const void *Wu, const void *Wv, const void *Wo, void *uvt,
+                       void *uvc, void *ot);
+hipError_t sum_parts_strided(hipStream_t s, int rows, int cols, int nparts, const float *parts, int64_t ldp,
+                             int64_t pstride, float *out, int64_t ldo, bool accumulate);
 
 // ---- backward pieces (backward.hip); all fp32 ------------------------------------------------
 hipError_t fill_f32(hipStream_t s, int64_t n, float *y, float v);

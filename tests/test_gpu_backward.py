@@ -2,13 +2,26 @@
 differences of the forward oracle in test_oracle_grad.py) on identical seeded inputs.
 
 Both sides differentiate the same function of the same stored values (bf16 workloads: the
-bf16-rounded X, x_t and weights); the library computes in fp32 throughout, the oracle in
-float64.  Bar: for every gradient tensor, max |gpu - oracle| / max |oracle| <= 1e-4.  Where it
-comes from: each gradient is a short chain (<= 4 layers x ~10 products) of fp32 sums; at these
-sizes a sum runs over at most ~1500 terms, whose relative error is of order sqrt(K) u in the mean
-and K u at worst (u = 2^-24: 2e-6 .. 9e-5), and no step divides by a small quantity (LayerNorm
-rows have unit scale, far from rstd = 1/sqrt(eps)).  A wrong term (a dropped softmax centring,
-a transposed operand, a missing LayerNorm mean) gives errors of order 1e-2 .. 1.
+bf16-rounded X, x_t and weights); the oracle computes in float64.  Bar: for every gradient tensor,
+max |gpu - oracle| / max |oracle| <= tol, per tensor rather than per row (weight gradients are sums
+over all rows and have no natural row scale).
+
+* fp32 path (dtype f32): fp32 arithmetic throughout, tol 1e-4.  Each gradient is a short chain
+  (<= 4 layers x ~10 products) of fp32 sums; at these sizes a sum runs over at most ~1500 terms,
+  whose relative error is of order sqrt(K) u in the mean and K u at worst (u = 2^-24: 2e-6 ..
+  9e-5), and no step divides by a small quantity (LayerNorm rows have unit scale, far from
+  rstd = 1/sqrt(eps)).
+* mixed-precision path (dtype bf16): the history encode's derivative runs its products on bf16
+  operands with fp32 accumulation, and the recomputed X~ comes from the forward's bf16 encode.
+  Every operand rounding is a relative error of at most u = 2^-8 (8 significant bits); an element
+  of a gradient passes through at most four such roundings (dY, then dU or dG, plus the bf16 H
+  and the recomputed pre-activations), whose independent errors largely cancel in the fp32 sums:
+  a sum of K terms with independent relative errors of at most u has a relative error of about
+  u / sqrt(3) per rounding stage, so four stages give about 2u / sqrt(3) = 4.5e-3 in the mean.
+  tol 2e-2 (about 5 u), the forward's bf16 bar.
+A wrong term (a dropped softmax centring, a transposed operand, a missing LayerNorm mean) gives
+errors of order 1e-2 .. 1 in the fp32 path, where the bar is tight; the mixed path's cases also run
+through the fp32 path (dtype f32) at 1e-4.
 """
 import dataclasses
 
@@ -23,7 +36,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-GRAD_TOL = 1e-4
+GRAD_TOL = 1e-4    # fp32 path
+MIXED_TOL = 2e-2   # mixed-precision path (bf16 storage)
 SLOTS = ["Wu", "Wv", "Wo", "gamma", "beta", "qWu", "qWv", "qWo", "qgamma", "qbeta", "WQ", "WK", "WV", "WO", "WC"]
 
 
@@ -76,8 +90,10 @@ def run_case(B, cfg, inp, W, query_ln=False, seed=5, keep=False):
                 continue
             errs[f"{name}[{i}]"] = tensor_rel(t.cpu().numpy(), want)
     worst = max(errs, key=errs.get)
-    print(f"  users={inp.n_users} L={inp.total_L} T={inp.total_T} worst {worst}={errs[worst]:.3e}", flush=True)
-    bad = {k: v for k, v in errs.items() if not v <= GRAD_TOL}
+    tol = GRAD_TOL if cfg.dtype == "f32" else MIXED_TOL
+    print(f"  {cfg.dtype} users={inp.n_users} L={inp.total_L} T={inp.total_T} worst {worst}={errs[worst]:.3e} "
+          f"(tol {tol})", flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
     return errs
 
@@ -105,12 +121,23 @@ def test_backward_matches_oracle(B, key, change, query_ln, separate):
     run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln)
 
 
+@pytest.mark.parametrize("key,change,query_ln,separate", [c for c in CASES if SI.scaled(SI.get_config(c[0]), **c[1]).dtype == "bf16"],
+                         ids=[f"{k}-{i}-f32" for i, (k, ch, *_) in enumerate(CASES)
+                              if SI.scaled(SI.get_config(k), **ch).dtype == "bf16"])
+def test_backward_fp32_path_on_mixed_cases(B, key, change, query_ln, separate):
+    """The cases the mixed-precision path runs, through the fp32 debug path (fp32 storage) at 1e-4."""
+    cfg = SI.scaled(SI.get_config(key), **dict(change, dtype="f32"))
+    announce("backward-f32", cfg.key, change, "query_ln" if query_ln else "", "separate" if separate else "")
+    W = SI.make_weights(cfg, random_ln=True, separate_query_ffn=separate)
+    run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln)
+
+
 @pytest.mark.parametrize("key,change,query_ln,separate", [CASES[1], CASES[4], CASES[7]],
                          ids=["tiny-M3", "ragged-small", "ragged-40"])
 def test_backward_keep_workspace(B, key, change, query_ln, separate):
-    """The larger workspace that keeps the encode's intermediates from the forward recompute gives
-    the same gradients (the same bar against the oracle)."""
-    cfg = SI.scaled(SI.get_config(key), **change)
+    """The fp32 path's larger workspace, which keeps the encode's intermediates from the forward
+    recompute, gives the same gradients (the same bar against the oracle)."""
+    cfg = SI.scaled(SI.get_config(key), **dict(change, dtype="f32"))
     announce("backward-keep", cfg.key, cfg.dtype, change)
     W = SI.make_weights(cfg, random_ln=True, separate_query_ffn=separate)
     run_case(B, cfg, SI.make_inputs(cfg), W, query_ln=query_ln, keep=True)
@@ -147,11 +174,11 @@ def test_backward_no_targets_gives_zero(B):
 
 def test_backward_full_size_ragged_sampled(B):
     """The whole training-shaped batch (512 users, ~1M history tokens, the size the backward bench
-    times) in one call.  Every gradient is linear in dZ and a user's dX and dx_t depend only on its
-    own dZ, so: (a) with dZ random everywhere, the dX / dx_t rows of sampled users equal the oracle
-    run on those users alone; (b) with dZ zero outside the sampled users, every weight gradient
-    equals the oracle's over those users and every other dX / dx_t row is exactly zero.  Bar 1e-3:
-    the weight-gradient sums here run over up to ~2e4 nonzero rows (sqrt(K) u ~ 1e-5 in the mean)."""
+    times) in one call, on the mixed-precision path.  Every gradient is linear in dZ and a user's dX and
+    dx_t depend only on its own dZ, so: (a) with dZ random everywhere, the dX / dx_t rows of sampled
+    users equal the oracle run on those users alone; (b) with dZ zero outside the sampled users, every
+    weight gradient equals the oracle's over those users and every other dX / dx_t row is exactly
+    zero.  Bar: the mixed path's 2e-2."""
     cfg = SI.get_config("ragged")
     announce("backward-fullsize", cfg.key)
     W = SI.make_weights(cfg)
@@ -190,5 +217,5 @@ def test_backward_full_size_ragged_sampled(B):
     worst = max(errs, key=errs.get)
     print(f"  users={inp.n_users} L={inp.total_L} T={inp.total_T} sampled={sample} (L={L[sample].tolist()}) "
           f"worst {worst}={errs[worst]:.3e}", flush=True)
-    bad = {k: v for k, v in errs.items() if not v <= 1e-3}
+    bad = {k: v for k, v in errs.items() if not v <= MIXED_TOL}
     assert not bad, bad
