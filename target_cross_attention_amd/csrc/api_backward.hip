@@ -249,9 +249,8 @@ int encode_backward_mixed(hipStream_t s, const stca_dims *dm, const stca_ffn &f,
     e2.C = bw.eY;
     e2.ldc = d;
     HIP_TRY(gemm_nt(s, kEpiStore, n, d, rd, 0, 1, bw.mH, rd, 0, bw.ot[i], rd, 0, e2));
-    HIP_TRY(ln_bwd(s, n, d, dXt + (size_t)r0 * d, d, bw.eY, d, f.gamma, dm->ln_eps, bw.edY, g.dgamma, g.dbeta,
-                   bw.parts, kLnBlocks));
-    HIP_TRY(to_bf16_rt(s, n, d, bw.edY, d, bw.mdY, d, bw.mdYt, bw.ldt));
+    HIP_TRY(ln_bwd_bf16(s, n, d, dXt + (size_t)r0 * d, bw.eY, f.gamma, dm->ln_eps, bw.mdY, bw.mdYt, bw.ldt, g.dgamma,
+                        g.dbeta, bw.parts));
     // dW_o (rd x d) over the chunk's rows, split into blocks of ks rows
     {
       const int64_t ks = round_up((n + kWgradParts - 1) / kWgradParts, 64), parts = (n + ks - 1) / ks;

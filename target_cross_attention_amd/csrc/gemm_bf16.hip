@@ -92,8 +92,10 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
     Bt += z * sB;
   }
 
-  bf16x8 ra[LA], rb[LB];
-  auto load = [&](int k0) {
+  // Two register sets: the slab of step s + 2 is loaded during step s and written to LDS at the end of
+  // step s + 1, so every load has two steps of MFMA work to land.
+  bf16x8 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
+  auto load = [&](int k0, bf16x8(&ra)[LA], bf16x8(&rb)[LB]) {
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
       const int q = tid + 256 * j, r = q >> 3, k = k0 + 8 * (q & 7);
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
       rb[j] = v;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const bf16x8(&ra)[LA], const bf16x8(&rb)[LB]) {
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
       const int q = tid + 256 * j, r = q >> 3;
@@ -141,15 +143,7 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   const int steps = ke > kb ? (ke - kb + kBK - 1) / kBK : 0;
-  if (steps > 0) {
-    load(kb);
-    store(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < steps; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < steps;
-    if (more) load(kb + (st + 1) * kBK);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = 2 * kk + g;
@@ -169,7 +163,25 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
     }
-    if (more) store(cur ^ 1);
+  };
+  // Step s computes from LDS half s & 1, loads the slab of s + 2 into one register set and writes the
+  // other (the slab of s + 1, loaded during step s - 1) into LDS half (s + 1) & 1, which step s - 1
+  // finished reading before the barrier that ended it.
+  if (steps > 0) {
+    load(kb, ra0, rb0);
+    store(0, ra0, rb0);
+  }
+  if (steps > 1) load(kb + kBK, ra1, rb1);
+  __syncthreads();
+  for (int st = 0; st < steps; st += 2) {
+    if (st + 2 < steps) load(kb + (st + 2) * kBK, ra0, rb0);
+    compute(0);
+    if (st + 1 < steps) store(1, ra1, rb1);
+    __syncthreads();
+    if (st + 1 >= steps) break;
+    if (st + 3 < steps) load(kb + (st + 3) * kBK, ra1, rb1);
+    compute(1);
+    if (st + 2 < steps) store(0, ra0, rb0);
     __syncthreads();
   }
 
@@ -439,6 +451,116 @@ hipError_t bwd_weights(hipStream_t s, int d, int r, const void *Wu, const void *
   return hipGetLastError();
 }
 
+// LayerNorm derivative of the mixed path (the same arithmetic as ln_bwd, fp32): workgroups walk
+// 64-row tiles (tile = blockIdx.x + k gridDim.x), each wave 16 rows of a tile one at a time; dY goes
+// out as bf16, row-major (rows x D) and transposed (D x ldt), both staged in LDS so that every global
+// store is a whole row chunk.  A workgroup's column sums of dgamma and dbeta over its tiles go to
+// parts[blk][c] and parts[gridDim.x + blk][c].
+template <int D>
+__global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const float *__restrict__ dout,
+                                                          const float *__restrict__ Y,
+                                                          const float *__restrict__ gamma, float eps,
+                                                          uint16_t *__restrict__ dY, uint16_t *__restrict__ dYt,
+                                                          int64_t ldt, float *__restrict__ parts) {
+  constexpr int E = D / 64, TS = 68;  // transposed rows of 64 tokens + 4 (8-byte aligned, 2-way banks)
+  __shared__ __attribute__((aligned(16))) uint16_t sR[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sT[D * TS];
+  __shared__ float red[4][2][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float pg[E], pb[E], gm[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    pg[e] = pb[e] = 0.f;
+    gm[e] = gamma[lane + 64 * e];
+  }
+  const int64_t ntiles = (rows + 63) / 64;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int64_t r0 = tile * 64;
+  __syncthreads();  // the previous tile's stores have read the staging area
+  for (int k = 0; k < 16; ++k) {
+    const int t = wave * 16 + k;
+    const int64_t row = r0 + t;
+    float y[E], go[E], dy[E];
+    const bool ok = row < rows;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      y[e] = ok ? Y[row * D + lane + 64 * e] : 0.f;
+      go[e] = ok ? dout[row * D + lane + 64 * e] : 0.f;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) sum += y[e];
+    const float mean = wave_sum(sum) / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) q += (y[e] - mean) * (y[e] - mean);
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + eps);
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float xh = (y[e] - mean) * rstd, g = go[e] * gm[e];
+      s1 += g;
+      s2 += g * xh;
+      pg[e] = fmaf(go[e], xh, pg[e]);
+      pb[e] += go[e];
+      y[e] = xh;
+      dy[e] = g;
+    }
+    const float m1 = wave_sum(s1) / (float)D, m2 = wave_sum(s2) / (float)D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint16_t b = ok ? bf16_bits(rstd * (dy[e] - m1 - y[e] * m2)) : 0;
+      sR[t * D + lane + 64 * e] = b;
+      sT[(lane + 64 * e) * TS + t] = b;
+    }
+  }
+  __syncthreads();
+  // row-major: 64 rows x D/8 chunks of 16 bytes
+  for (int qd = threadIdx.x; qd < 64 * (D / 8); qd += 256) {
+    const int t = qd / (D / 8), c = qd % (D / 8);
+    if (r0 + t < rows)
+      *reinterpret_cast<u32x4 *>(dY + (r0 + t) * D + 8 * c) = *reinterpret_cast<const u32x4 *>(sR + t * D + 8 * c);
+  }
+  // transposed: D rows x 16 chunks of 4 tokens (8 bytes); rows past the end carry zeros
+  for (int qd = threadIdx.x; qd < D * 16; qd += 256) {
+    const int f = qd >> 4, c = qd & 15;
+    if (r0 + 4 * c < rows)
+      *reinterpret_cast<uint2 *>(dYt + (int64_t)f * ldt + r0 + 4 * c) = *reinterpret_cast<const uint2 *>(sT + f * TS + 4 * c);
+  }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    red[wave][0][lane + 64 * e] = pg[e];
+    red[wave][1][lane + 64 * e] = pb[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += 256) {
+    parts[(int64_t)blockIdx.x * D + c] = red[0][0][c] + red[1][0][c] + red[2][0][c] + red[3][0][c];
+    parts[(int64_t)(gridDim.x + blockIdx.x) * D + c] = red[0][1][c] + red[1][1][c] + red[2][1][c] + red[3][1][c];
+  }
+}
+
+hipError_t ln_bwd_bf16(hipStream_t s, int64_t rows, int d, const float *dout, const float *Y, const float *gamma,
+                       float eps, void *dY, void *dYt, int64_t ldt, float *dgamma, float *dbeta, float *parts) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t nblk = std::min<int64_t>((rows + 63) / 64, 256);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), 0, s, rows, dout, Y, gamma, eps, (uint16_t *)dY,
+                       (uint16_t *)dYt, ldt, parts);
+  };
+  switch (d) {
+    case 64: go(ln_bwd_bf16_kernel<64>); break;
+    case 128: go(ln_bwd_bf16_kernel<128>); break;
+    case 256: go(ln_bwd_bf16_kernel<256>); break;
+    case 512: go(ln_bwd_bf16_kernel<512>); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = sum_parts_strided(s, 1, d, (int)nblk, parts, d, d, dgamma, d, true)) != hipSuccess) return e;
+  return sum_parts_strided(s, 1, d, (int)nblk, parts + nblk * d, d, d, dbeta, d, true);
+}
+
 // out (+)= sum over k of the parts' [rows x cols] blocks (part k at parts + k pstride, row stride ldp),
 // in k order.
 __global__ __launch_bounds__(256) void sum_parts_strided_kernel(int rows, int cols, int nparts,
@@ -450,6 +572,7 @@ __global__ __launch_bounds__(256) void sum_parts_strided_kernel(int rows, int co
     const int64_t r = i / cols, c = i % cols;
     float *o = out + r * ldo + c;
     float a = accumulate ? *o : 0.f;
+#pragma unroll 8
     for (int k = 0; k < nparts; ++k) a += parts[k * pstride + r * ldp + c];
     *o = a;
   }

@@ -164,6 +164,11 @@ hipError_t bwd_weights(hipStream_t s, int d, int r, const void *Wu, const void *
                        void *uvc, void *ot);
 hipError_t sum_parts_strided(hipStream_t s, int rows, int cols, int nparts, const float *parts, int64_t ldp,
                              int64_t pstride, float *out, int64_t ldo, bool accumulate);
+// LayerNorm derivative (mixed path) from the pre-LN rows Y (rows x d, fp32) and dout (rows x d): dY
+// as bf16 row-major (rows x d) and transposed (d x ldt), dgamma and dbeta accumulated through
+// per-block partial sums (2 ceil(rows / 64) d floats of parts).
+hipError_t ln_bwd_bf16(hipStream_t s, int64_t rows, int d, const float *dout, const float *Y, const float *gamma,
+                       float eps, void *dY, void *dYt, int64_t ldt, float *dgamma, float *dbeta, float *parts);
 
 // ---- backward pieces (backward.hip); all fp32 ------------------------------------------------
 hipError_t fill_f32(hipStream_t s, int64_t n, float *y, float v);
