@@ -351,6 +351,30 @@ enum {
 };
 STCA_API int stca_validate_batch(const stca_batch *batch, int32_t *result, void *stream);
 
+/* ---- index checks of the debug build --------------------------------------------------------
+ * A library built with STCA_DEBUG_BOUNDS defined (libstca_debug.so next to libstca.so) checks, in
+ * its kernels, the indices that ragged offsets and workspace plans drive (history tile rows
+ * against the work item's chunk, output and partial-state rows against their buffers, work items
+ * against the list's capacity, padded operand rows against their strides).  A failed check never
+ * faults: it sets a bit in a device word and the kernel runs on.  stca_debug_flags synchronises the
+ * device, writes the OR of the bits recorded since the last clear to *flags (STCA_DBG_* below) and
+ * clears them if `clear` is nonzero; *checks_enabled (may be NULL) is 1 in the debug build and 0 in
+ * the ordinary one, where *flags is always 0 and no device work is done.  stca_debug_selftest
+ * records STCA_DBG_SELFTEST from a kernel on `stream` (debug build; a no-op otherwise), to show the
+ * mechanism reports what it records. */
+enum {
+  STCA_DBG_ATTEND_RANGE = 1,     /* a work item's history range outside [0, total_L] */
+  STCA_DBG_ATTEND_FETCH = 2,     /* a history tile row outside the item's chunk */
+  STCA_DBG_ATTEND_OUT = 4,       /* an attention output row past total_T * h */
+  STCA_DBG_ATTEND_PART = 8,      /* a partial-state row past the workspace's partial rows */
+  STCA_DBG_COMBINE_PART = 16,    /* the combine reading partial rows past the workspace's */
+  STCA_DBG_WORKLIST = 32,        /* a work item written past the list's capacity */
+  STCA_DBG_GEMM_PAD = 64,        /* a transposed backward operand's row chunk past its row stride */
+  STCA_DBG_SELFTEST = (int)0x80000000u
+};
+STCA_API int stca_debug_flags(uint32_t *flags, int32_t *checks_enabled, int32_t clear);
+STCA_API int stca_debug_selftest(void *stream);
+
 /* ---- diagnostics ---------------------------------------------------------------------------- */
 STCA_API const char *stca_status_string(int status);
 STCA_API const char *stca_last_error(void); /* thread-local detail of the last failure in this thread */

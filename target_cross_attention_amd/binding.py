@@ -12,7 +12,10 @@ from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstca.so")
+# STCA_LIB may name another build of the same library (for instance libstca_debug.so, whose kernels
+# check their ragged indices); the default is the ordinary build next to this file.
+LIB_PATH = os.environ.get("STCA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstca.so")
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstca_debug.so")
 MAX_M = 8
 
 F32, BF16 = 0, 1
@@ -29,7 +32,8 @@ EXPORTS = [
     "stca_backward_workspace_size", "stca_backward_workspace_size_keep", "stca_backward", "stca_backward_profiled",
     "stca_forward_graph_create", "stca_graph_launch", "stca_graph_destroy", "stca_profiler_create", "stca_profiler_destroy",
     "stca_profiler_reset", "stca_profiler_read", "stca_forward_profiled", "stca_status_string",
-    "stca_last_error", "stca_version", "stca_validate_batch", "stca_attend_noalloc",
+    "stca_last_error", "stca_version", "stca_validate_batch", "stca_attend_noalloc", "stca_debug_flags",
+    "stca_debug_selftest",
 ]
 
 
@@ -114,6 +118,8 @@ def _load() -> ctypes.CDLL:
         "stca_profiler_read": [P, P],
         "stca_validate_batch": [P, P, P],
         "stca_attend_noalloc": [P, P, c_int32, P, P, P, P, P],
+        "stca_debug_flags": [POINTER(ctypes.c_uint32), POINTER(c_int32), c_int32],
+        "stca_debug_selftest": [P],
         "stca_status_string": [c_int],
         "stca_last_error": [],
         "stca_version": [],
@@ -379,6 +385,19 @@ def validate_batch(batch: DeviceBatch, stream=None) -> int:
     _check(LIB.stca_validate_batch(_ref(batch.c), _ptr(res), _stream(stream)), "stca_validate_batch")
     (stream or torch.cuda.current_stream()).synchronize()
     return int(res[0].item())
+
+
+def debug_flags(clear: bool = True) -> tuple[int, bool]:
+    """(bits recorded by the kernels' index checks since the last clear, whether this build checks);
+    see stca_debug_flags."""
+    f = ctypes.c_uint32(0)
+    en = c_int32(0)
+    _check(LIB.stca_debug_flags(ctypes.byref(f), ctypes.byref(en), int(clear)), "stca_debug_flags")
+    return int(f.value), bool(en.value)
+
+
+def debug_selftest(stream=None):
+    _check(LIB.stca_debug_selftest(_stream(stream)), "stca_debug_selftest")
 
 
 def sl_beta(params: SlParams, alpha: float) -> float:

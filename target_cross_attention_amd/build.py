@@ -2,6 +2,8 @@
 
     python -m target_cross_attention_amd.build          # compile every source, link
     python -m target_cross_attention_amd.build --asm    # also write gfx950 assembly next to the objects
+    python -m target_cross_attention_amd.build --debug-bounds   # libstca_debug.so: kernels check their
+                                                                # ragged indices (STCA_DEBUG_BOUNDS)
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstca.so")
+BUILD_DEBUG = os.path.join(PKG, "_build_debug")
+LIB_DEBUG = os.path.join(PKG, "libstca_debug.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 add/mul/fma instructions.
@@ -35,9 +39,10 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, asm: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, asm: bool, debug_bounds: bool = False) -> str:
+    bdir = BUILD_DEBUG if debug_bounds else BUILD
+    obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
+    cmd = [hipcc(), *FLAGS, *(["-DSTCA_DEBUG_BOUNDS"] if debug_bounds else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -48,24 +53,26 @@ def _compile(src: str, asm: bool) -> str:
     return obj
 
 
-def build(asm: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(asm: bool = False, jobs: int | None = None, debug_bounds: bool = False) -> str:
+    out = LIB_DEBUG if debug_bounds else LIB
+    os.makedirs(BUILD_DEBUG if debug_bounds else BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, asm and not debug_bounds, debug_bounds), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", action="store_true")
+    ap.add_argument("--debug-bounds", action="store_true")
     a = ap.parse_args()
-    print(build(asm=a.asm))
+    print(build(asm=a.asm, debug_bounds=a.debug_bounds))
     sys.exit(0)

@@ -930,6 +930,34 @@ int stca_validate_batch(const stca_batch *batch, int32_t *result, void *stream) 
   return STCA_OK;
 }
 
+static_assert(kDbgAttendRange == STCA_DBG_ATTEND_RANGE && kDbgAttendFetch == STCA_DBG_ATTEND_FETCH &&
+                  kDbgAttendOut == STCA_DBG_ATTEND_OUT && kDbgAttendPart == STCA_DBG_ATTEND_PART &&
+                  kDbgCombinePart == STCA_DBG_COMBINE_PART && kDbgWorklist == STCA_DBG_WORKLIST &&
+                  kDbgGemmPad == STCA_DBG_GEMM_PAD && kDbgSelfTest == (uint32_t)STCA_DBG_SELFTEST,
+              "debug check bits match the header");
+
+int stca_debug_flags(uint32_t *flags, int32_t *checks_enabled, int32_t clear) {
+  if (!flags) return fail(STCA_E_ARG, "flags is NULL");
+#ifdef STCA_DEBUG_BOUNDS
+  if (checks_enabled) *checks_enabled = 1;
+  HIP_TRY(hipDeviceSynchronize());
+  uint32_t a = 0, g = 0;
+  HIP_TRY(debug_flags_attend(&a, clear != 0));
+  HIP_TRY(debug_flags_gemm(&g, clear != 0));
+  *flags = a | g;
+#else
+  (void)clear;
+  if (checks_enabled) *checks_enabled = 0;
+  *flags = 0;
+#endif
+  return STCA_OK;
+}
+
+int stca_debug_selftest(void *stream) {
+  HIP_TRY(debug_selftest((hipStream_t)stream));
+  return STCA_OK;
+}
+
 const char *stca_status_string(int status) {
   switch (status) {
     case STCA_OK: return "ok";

@@ -21,6 +21,8 @@
 
 namespace stca {
 
+STCA_DEBUG_WORD
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // One workgroup: the OR of every user's violations into *result.
@@ -144,7 +146,10 @@ __global__ __launch_bounds__(1024) void worklist_kernel(int n_users, const int64
       int64_t k = carry_i + sc_i[tid] - ni;
       if (ni > 0)
         for (int c = 0; c < nc; ++c)
-          for (int g = 0; g < ng; ++g, ++k) items[k] = WorkItem{u, c, g, nc};
+          for (int g = 0; g < ng; ++g, ++k) {
+            STCA_CHECK(k < max_items, kDbgWorklist);
+            items[k] = WorkItem{u, c, g, nc};
+          }
     }
     carry_i += sc_i[1023];
     carry_p += sc_p[1023];
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
     const int64_t *__restrict__ toff, int h, int chunk, const bf16 *__restrict__ Xt,
     const bf16 *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
-    float *__restrict__ part_ms, const int64_t *__restrict__ part_base) {
+    float *__restrict__ part_ms, const int64_t *__restrict__ part_base, const AttnBounds bnd) {
   constexpr int CPR = D / 8;                      // 16-byte chunks per history row
   constexpr int SWZ = (CPR < 32 ? CPR : 32) - 1;  // swizzle mask
   constexpr int NKS = D / 16, NOB = D / 32;
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   const int myrow = r0 + col;
   const bool row_ok = myrow < R;
   const int ntiles = (int)((t1 - t0 + 31) / 32);
+  STCA_CHECK(L0 >= 0 && L0 <= L1 && L1 <= bnd.total_L && t0 < t1, kDbgAttendRange);
 
   // U rows as B operands (loaded first so that the tile loads below are the youngest in flight):
   // this wave's k-steps fh NKW .. fh NKW + NKW - 1 of the score reduction.
@@ -292,12 +298,16 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
     const bf16 *tile = Xt + (t0 + 32 * (int64_t)k) * D;
     if (32 * (int64_t)(k + 1) <= len) {
 #pragma unroll
-      for (int jj = 0; jj < LPW; ++jj) rg[jj] = *reinterpret_cast<const u32x4 *>(tile + foff[jj]);
+      for (int jj = 0; jj < LPW; ++jj) {
+        STCA_CHECK(32 * (int64_t)k + frow[jj] < len, kDbgAttendFetch);
+        rg[jj] = *reinterpret_cast<const u32x4 *>(tile + foff[jj]);
+      }
     } else {  // partial last tile: rows past the end repeat the last row
       const int rem = (int)(len - 32 * (int64_t)k);
 #pragma unroll
       for (int jj = 0; jj < LPW; ++jj) {
         const int back = frow[jj] < rem ? 0 : (frow[jj] - rem + 1) * D;
+        STCA_CHECK(rem > 0 && 32 * (int64_t)k + frow[jj] - back / D < len, kDbgAttendFetch);
         rg[jj] = *reinterpret_cast<const u32x4 *>(tile + (foff[jj] - back));
       }
     }
@@ -709,6 +719,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
   if (!row_ok) return;
   if (it.n_chunks == 1) {
     const float inv = 1.0f / s_tot;
+    STCA_CHECK(rowbase + myrow < bnd.rows, kDbgAttendOut);
     float *dst = abar + (rowbase + myrow) * D + fh * (D / FH);
 #pragma unroll
     for (int ob = 0; ob < NOBW; ++ob)
@@ -720,6 +731,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
       }
   } else {
     const int64_t p = part_base[it.user] + (int64_t)it.chunk * R + myrow;
+    STCA_CHECK(p >= 0 && p < bnd.part_rows, kDbgAttendPart);
     float *dst = part_A + p * D + fh * (D / FH);
 #pragma unroll
     for (int ob = 0; ob < NOBW; ++ob)
@@ -744,7 +756,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
     const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
     const int64_t *__restrict__ toff, int h, int chunk, const float *__restrict__ Xt,
     const float *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
-    float *__restrict__ part_ms, const int64_t *__restrict__ part_base) {
+    float *__restrict__ part_ms, const int64_t *__restrict__ part_base, const AttnBounds bnd) {
   constexpr int E = D / 64;
   WorkItem it;
   if (!my_item(items, n_items, it)) return;
@@ -757,6 +769,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
   const int64_t rowbase = T0 * h;
   const int RG = attn_rows_per_group(D);
   const int rend = (it.group + 1) * RG < R ? (it.group + 1) * RG : R;
+  STCA_CHECK(L0 >= 0 && L0 <= L1 && L1 <= bnd.total_L && t0 < t1, kDbgAttendRange);
 
   for (int r = it.group * RG + wave; r < rend; r += 4) {
     float u[E], a[E];
@@ -798,10 +811,12 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
     }
     if (it.n_chunks == 1) {
       const float inv = 1.0f / s;
+      STCA_CHECK(rowbase + r < bnd.rows, kDbgAttendOut);
 #pragma unroll
       for (int e = 0; e < E; ++e) abar[(rowbase + r) * D + lane + 64 * e] = a[e] * inv;
     } else {
       const int64_t pidx = part_base[it.user] + (int64_t)it.chunk * R + r;
+      STCA_CHECK(pidx >= 0 && pidx < bnd.part_rows, kDbgAttendPart);
 #pragma unroll
       for (int e = 0; e < E; ++e) part_A[pidx * D + lane + 64 * e] = a[e];
       if (lane == 0) {
@@ -817,12 +832,13 @@ static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_pat
                                  const int64_t *toff, const void *Xt, const void *U, float *abar,
                                  const AttnBuffers &b) {
   const dim3 grid((unsigned)p.max_items), block(256);
+  const AttnBounds bnd{p.total_L, p.total_T * p.h, p.max_part_rows};
   if (bf16_path)
     hipLaunchKernelGGL((attend_mfma_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
-                       (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base);
+                       (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
   else
     hipLaunchKernelGGL((attend_f32_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
-                       (const float *)Xt, (const float *)U, abar, b.part_A, b.part_ms, b.part_base);
+                       (const float *)Xt, (const float *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
   return hipGetLastError();
 }
 
@@ -851,7 +867,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t n_rows, int h, int
                                                       const int64_t *__restrict__ toff,
                                                       const int64_t *__restrict__ part_base,
                                                       const float *__restrict__ part_A,
-                                                      const float *__restrict__ part_ms, float *__restrict__ abar) {
+                                                      const float *__restrict__ part_ms, float *__restrict__ abar,
+                                                      int64_t part_rows) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;
@@ -870,6 +887,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t n_rows, int h, int
   const int64_t R = (toff[u + 1] - toff[u]) * h;
   const int64_t r = row - toff[u] * h;
   const int64_t p0 = part_base[u] + r;
+  STCA_CHECK(p0 >= 0 && p0 + (int64_t)(nc - 1) * R < part_rows, kDbgCombinePart);
+  (void)part_rows;
   float mstar = -INFINITY;
   for (int c = 0; c < nc; ++c) mstar = fmaxf(mstar, part_ms[2 * (p0 + c * R)]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -897,8 +916,37 @@ hipError_t attend_combine(hipStream_t s, const AttnPlan &p, const int64_t *tgt_o
   const int64_t rows = p.total_T * p.h;
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, p.h, p.d,
-                     b.n_items, b.tgt_user, b.user_nchunks, tgt_off, b.part_base, b.part_A, b.part_ms, abar);
+                     b.n_items, b.tgt_user, b.user_nchunks, tgt_off, b.part_base, b.part_A, b.part_ms, abar,
+                     p.max_part_rows);
   return hipGetLastError();
+}
+
+// Debug build: the file's check word, read (and cleared) through its symbol.
+#ifdef STCA_DEBUG_BOUNDS
+__global__ void debug_selftest_kernel() { STCA_CHECK(threadIdx.x != 0, kDbgSelfTest); }
+#endif
+
+hipError_t debug_flags_attend(uint32_t *flags, bool clear) {
+  *flags = 0;
+#ifdef STCA_DEBUG_BOUNDS
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(stca_dbg_word), sizeof(uint32_t));
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(stca_dbg_word), &zero, sizeof(uint32_t));
+#else
+  (void)clear;
+  return hipSuccess;
+#endif
+}
+
+hipError_t debug_selftest(hipStream_t s) {
+#ifdef STCA_DEBUG_BOUNDS
+  hipLaunchKernelGGL(debug_selftest_kernel, dim3(1), dim3(64), 0, s);
+  return hipGetLastError();
+#else
+  (void)s;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace stca

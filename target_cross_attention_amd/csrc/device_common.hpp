@@ -56,6 +56,23 @@ __device__ __forceinline__ float swiglu_gate(float a, float g) {
   return a * g * fast_rcp(1.0f + fast_exp2(-g * kLog2e));
 }
 
+// ---- index checks of the debug build (-DSTCA_DEBUG_BOUNDS) -------------------------------------
+// A failed check sets bit `code` of a per-file device word with a vector atomic instead of faulting,
+// so a kernel always runs to its normal end; the library's stca_debug_flags reads and clears the
+// words.  In the ordinary build the checks compile to nothing.
+#ifdef STCA_DEBUG_BOUNDS
+#define STCA_DEBUG_WORD static __device__ unsigned int stca_dbg_word;
+#define STCA_CHECK(cond, code)                                           \
+  do {                                                                   \
+    if (!(cond)) atomicOr(&stca_dbg_word, (unsigned int)(code));         \
+  } while (0)
+#else
+#define STCA_DEBUG_WORD
+#define STCA_CHECK(cond, code) \
+  do {                         \
+  } while (0)
+#endif
+
 // ---- wave (64-lane) reductions -------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

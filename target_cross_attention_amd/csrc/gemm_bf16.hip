@@ -27,6 +27,9 @@
 #include "internal.hpp"
 
 namespace stca {
+
+STCA_DEBUG_WORD
+
 namespace {
 
 constexpr int kTN = 128, kBK = 64;
@@ -247,9 +250,11 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // 64 feature rows x 16 chunks of 8 rows
         const int qd = tid + 256 * j, f = qd >> 4, c = qd & 15;
-        if (m0 + 8 * c < M)  // a partial chunk fills padding columns (< ldt) that no reader uses
+        if (m0 + 8 * c < M) {  // a partial chunk fills padding columns (< ldt) that no reader uses
+          STCA_CHECK(m0 + 8 * c + 8 <= ep.ldt, kDbgGemmPad);
           *reinterpret_cast<u32x4 *>(dst[a] + (int64_t)(f0 + f) * ep.ldt + m0 + 8 * c) =
               *reinterpret_cast<const u32x4 *>(src[a] + f * kTP + 8 * c);
+        }
       }
   } else if constexpr (EPI == kEpiSwigluBwd) {
     static_assert(TM == 128, "staging layout");
@@ -274,6 +279,7 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
             const int t0 = wm + 32 * i + 8 * q + 4 * g;
             float u[4] = {0.f, 0.f, 0.f, 0.f}, gg[4] = {0.f, 0.f, 0.f, 0.f}, v[4];
             if (f < N && m0 + t0 < M) {  // rows up to round_up(M, 4) - 1 < ldt
+              STCA_CHECK(m0 + t0 + 4 <= ep.ldt, kDbgGemmPad);
               load4(Ut + f * ep.ldt + m0 + t0, u);
               load4(Gt + f * ep.ldt + m0 + t0, gg);
             }
@@ -298,9 +304,11 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {  // [feature][row]: 128 feature rows x 16 chunks
         const int qd = tid + 256 * j, fr = qd >> 4, c = qd & 15;
-        if (n0 + fr < N && m0 + 8 * c < M)
+        if (n0 + fr < N && m0 + 8 * c < M) {
+          STCA_CHECK(m0 + 8 * c + 8 <= ep.ldt, kDbgGemmPad);
           *reinterpret_cast<u32x4 *>(dUGt + (col0 + fr) * ep.ldt + m0 + 8 * c) =
               *reinterpret_cast<const u32x4 *>(sT + fr * kTP + 8 * c);
+        }
       }
     }
   }
@@ -524,8 +532,10 @@ __global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const fl
   // transposed: D rows x 16 chunks of 4 tokens (8 bytes); rows past the end carry zeros
   for (int qd = threadIdx.x; qd < D * 16; qd += 256) {
     const int f = qd >> 4, c = qd & 15;
-    if (r0 + 4 * c < rows)
+    if (r0 + 4 * c < rows) {
+      STCA_CHECK(r0 + 4 * c + 4 <= ldt, kDbgGemmPad);
       *reinterpret_cast<uint2 *>(dYt + (int64_t)f * ldt + r0 + 4 * c) = *reinterpret_cast<const uint2 *>(sT + f * TS + 4 * c);
+    }
   }
   }
 #pragma unroll
@@ -584,6 +594,19 @@ hipError_t sum_parts_strided(hipStream_t s, int rows, int cols, int nparts, cons
   hipLaunchKernelGGL(sum_parts_strided_kernel, dim3(grid_for((int64_t)rows * cols)), dim3(256), 0, s, rows, cols,
                      nparts, parts, ldp, pstride, out, ldo, accumulate);
   return hipGetLastError();
+}
+
+hipError_t debug_flags_gemm(uint32_t *flags, bool clear) {
+  *flags = 0;
+#ifdef STCA_DEBUG_BOUNDS
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(stca_dbg_word), sizeof(uint32_t));
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(stca_dbg_word), &zero, sizeof(uint32_t));
+#else
+  (void)clear;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace stca

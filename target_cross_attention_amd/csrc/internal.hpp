@@ -35,6 +35,24 @@ hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, in
 // dst[n] (bf16) = src[n] (fp32) rounded to nearest even; n a multiple of 4.
 hipError_t to_bf16(hipStream_t s, int64_t n, const float *src, void *dst);
 
+// ---- debug build (-DSTCA_DEBUG_BOUNDS): index-check words of the kernel files ------------------
+enum : uint32_t {
+  kDbgAttendRange = 1u << 0,     // a work item's history range outside [0, total_L]
+  kDbgAttendFetch = 1u << 1,     // a history tile row outside the item's chunk
+  kDbgAttendOut = 1u << 2,       // an output row past total_T h
+  kDbgAttendPart = 1u << 3,      // a partial-state row past the workspace's partial rows
+  kDbgCombinePart = 1u << 4,     // the combine reading partial rows past the workspace's
+  kDbgWorklist = 1u << 5,        // a work item written past the list's capacity
+  kDbgGemmPad = 1u << 6,         // a transposed operand's row chunk past its row stride
+  kDbgSelfTest = 1u << 31,       // set on purpose by stca_debug_selftest
+};
+// Bits recorded by the kernels of one file since the last clear (0 in the ordinary build, where
+// no device memory is touched).
+hipError_t debug_flags_attend(uint32_t *flags, bool clear);
+hipError_t debug_flags_gemm(uint32_t *flags, bool clear);
+// Debug build: one kernel records kDbgSelfTest, to show the mechanism reports what it records.
+hipError_t debug_selftest(hipStream_t s);
+
 // ---- fused bf16 MFMA encode (encode_mfma.hip) -----------------------------------------------
 // Re-layout of one FFN's W_u, W_v (d x rd) and W_o (rd x d) into MFMA fragment order.
 size_t encode_packed_bytes(int d, int r);
@@ -68,6 +86,11 @@ size_t encode_layer_stride(int d, int r);
 // split the output features of a 32-row block) 2 x 32 rows.
 constexpr int attn_feature_halves(int d) { return d > 256 ? 2 : 1; }
 constexpr int attn_rows_per_group(int d) { return 4 * 32 / attn_feature_halves(d); }
+
+// Sizes the attention kernels check their indices against in the debug build.
+struct AttnBounds {
+  int64_t total_L, rows, part_rows;
+};
 
 struct WorkItem {
   int32_t user, chunk, group, n_chunks;

@@ -142,6 +142,12 @@ static void argument_errors() {
   EXPECT(stca_backward(&good, &w, &b, fake(4096), fake(4096), (const float *)fake(4096), &g, fake(4096), 1 << 30,
                        nullptr) == STCA_E_ARG);
 
+  // debug-build flags: the ordinary build checks nothing and touches no device
+  uint32_t dflags = 123;
+  int32_t denabled = 7;
+  EXPECT(stca_debug_flags(&dflags, &denabled, 1) == STCA_OK && dflags == 0 && denabled == 0);
+  EXPECT(stca_debug_flags(nullptr, &denabled, 0) == STCA_E_ARG);
+
   // diagnostics
   for (int s = -6; s <= 1; ++s) EXPECT(stca_status_string(s) != nullptr);
   EXPECT(strlen(stca_version()) > 0);

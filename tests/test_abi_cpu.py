@@ -29,6 +29,20 @@ def test_every_declared_function_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_debug_build_exports_the_same_calls():
+    """libstca_debug.so (kernels with index checks) exports every declared call too; the ordinary
+    build reports that it does not check, with no device work (callable without a GPU)."""
+    assert os.path.exists(B.DEBUG_LIB_PATH), "build() also builds the debug library"
+    dbg = ctypes.CDLL(B.DEBUG_LIB_PATH)
+    for n in header_functions():
+        assert hasattr(dbg, n), n
+    if os.path.realpath(B.LIB_PATH) != os.path.realpath(B.DEBUG_LIB_PATH):
+        assert B.debug_flags() == (0, False)
+    f = ctypes.c_uint32(0)
+    assert B.LIB.stca_debug_flags(None, None, 0) == -1
+    assert B.LIB.stca_debug_flags(ctypes.byref(f), None, 1) == 0
+
+
 def test_status_strings_and_version():
     assert B.status_string(0) == "ok"
     for code in (-1, -2, -3, -4, -5):
