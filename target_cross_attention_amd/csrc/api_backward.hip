@@ -90,7 +90,7 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
     w.eH = c.take<float>((size_t)(w.rows * rd));
   }
   w.eY = c.take<float>((size_t)(w.rows * d));
-  w.edY = c.take<float>((size_t)(w.rows * d));
+  if (!mixed) w.edY = c.take<float>((size_t)(w.rows * d));
   w.parts = c.take<float>((size_t)kWgradParts * std::max<int64_t>(d * rd, M * d * d));
   w.S = c.take<float>((size_t)score_elems(dm, b));
   w.S2 = c.take<float>((size_t)score_elems(dm, b));

@@ -391,41 +391,6 @@ hipError_t transpose_tiled_bf16(hipStream_t s, int64_t rows, int cols, const voi
   return hipGetLastError();
 }
 
-// fp32 rows (rows x cols, stride ldi) to bf16, row-major (stride ldr, if out_r) and transposed
-// (cols x rows, stride ldt, if out_t).
-__global__ __launch_bounds__(256) void to_bf16_rt_kernel(int64_t rows, int cols, const float *__restrict__ in,
-                                                         int64_t ldi, uint16_t *__restrict__ out_r, int64_t ldr,
-                                                         uint16_t *__restrict__ out_t, int64_t ldt) {
-  __shared__ uint16_t t[64][66];
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k;
-    const int c = c0 + tx;
-    const uint16_t v = (r < rows && c < cols) ? f32_to_bf16_bits(in[r * ldi + c]) : 0;
-    t[k][tx] = v;
-    if (out_r && r < rows && c < cols) out_r[r * ldr + c] = v;
-  }
-  __syncthreads();
-  if (!out_t) return;
-  for (int k = ty; k < 64; k += 4) {
-    const int c = c0 + k;
-    const int64_t r = r0 + tx;
-    if (c < cols && r < rows) out_t[(int64_t)c * ldt + r] = t[tx][k];
-  }
-}
-
-hipError_t to_bf16_rt(hipStream_t s, int64_t rows, int cols, const float *in, int64_t ldi, void *out_r, int64_t ldr,
-                      void *out_t, int64_t ldt) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  const int64_t gy = (rows + 63) / 64;
-  if (gy > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(to_bf16_rt_kernel, dim3((unsigned)((cols + 63) / 64), (unsigned)gy), dim3(256), 0, s, rows, cols,
-                     in, ldi, (uint16_t *)out_r, ldr, (uint16_t *)out_t, ldt);
-  return hipGetLastError();
-}
-
 // Weight layouts for the mixed backward of one history FFN (Wu, Wv: d x rd; Wo: rd x d; bf16):
 //   uvt [2rd x d]: row 64 q + t = column 32 q + t of Wu, row 64 q + 32 + t = the same column of Wv
 //                  (the up/gate pairs of the kSwigluFwd epilogue), t < 32;

@@ -181,8 +181,6 @@ hipError_t gemm_nt(hipStream_t s, int epi, int M, int N, int K, int ksplit, int 
                    int64_t sA, const void *Bt, int64_t ldb, int64_t sB, const NtEpilogue &ep);
 hipError_t transpose_tiled_bf16(hipStream_t s, int64_t rows, int cols, const void *in, int64_t ldi, void *out,
                                 int64_t ldo);
-hipError_t to_bf16_rt(hipStream_t s, int64_t rows, int cols, const float *in, int64_t ldi, void *out_r, int64_t ldr,
-                      void *out_t, int64_t ldt);
 hipError_t bwd_weights(hipStream_t s, int d, int r, const void *Wu, const void *Wv, const void *Wo, void *uvt,
                        void *uvc, void *ot);
 hipError_t sum_parts_strided(hipStream_t s, int rows, int cols, int nparts, const float *parts, int64_t ldp,
