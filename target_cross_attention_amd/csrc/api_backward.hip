@@ -445,10 +445,10 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     HIP_TRY(pt.end());
     {
       Phase ph(prof, s, STCA_PHASE_BWD_ATTEND);
-      HIP_TRY(gemm_ragged(s, rg(bw.U[i], Xt, bw.S, 1.f, 0.f, false, true), bw.desc, b->n_users, T_rows, max_L));
+      HIP_TRY(gemm_ragged(s, rg(bw.U[i], Xt, bw.S, 1.f, 0.f, false, true), bw.desc, b->n_users, T_rows, max_L, bf));
       HIP_TRY(ragged_rows(s, 0, T * h, h, b->n_users, b->tgt_off, bw.desc, bw.S, nullptr, sc, bw.lse[i], nullptr));
       HIP_TRY(gemm_ragged(s, rg(bw.S, Xt, bw.abar[i], 1.f, 0.f, false, false), bw.desc + b->n_users, b->n_users,
-                          T_rows, d));
+                          T_rows, d, bf));
       HIP_TRY(ph.end());
     }
     Phase pt2(prof, s, STCA_PHASE_BWD_TARGET);
@@ -536,13 +536,13 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     {  // alpha again (saved lse), dA = dabar X~^T, dS, then du and dX~ (eq. (13))
       Phase ph(prof, s, STCA_PHASE_BWD_ATTEND);
       const RaggedDesc *d_s = bw.desc, *d_row = bw.desc + b->n_users, *d_key = bw.desc + 2 * b->n_users;
-      HIP_TRY(gemm_ragged(s, rg(bw.U[i], Xt, bw.S, 1.f, 0.f, false, true), d_s, b->n_users, T_rows, max_L));
+      HIP_TRY(gemm_ragged(s, rg(bw.U[i], Xt, bw.S, 1.f, 0.f, false, true), d_s, b->n_users, T_rows, max_L, bf));
       HIP_TRY(ragged_rows(s, 1, T * h, h, b->n_users, b->tgt_off, d_s, bw.S, nullptr, sc, bw.lse[i], nullptr));
-      HIP_TRY(gemm_ragged(s, rg(bw.dabar, Xt, bw.S2, 1.f, 0.f, false, true), d_s, b->n_users, T_rows, max_L));
+      HIP_TRY(gemm_ragged(s, rg(bw.dabar, Xt, bw.S2, 1.f, 0.f, false, true), d_s, b->n_users, T_rows, max_L, bf));
       HIP_TRY(ragged_rows(s, 2, T * h, h, b->n_users, b->tgt_off, d_s, bw.S, bw.S2, sc, nullptr, bw.Dv));
-      HIP_TRY(gemm_ragged(s, rg(bw.S2, Xt, bw.du, sc, 0.f, false, false), d_row, b->n_users, T_rows, d));
-      HIP_TRY(gemm_ragged(s, rg(bw.S, bw.dabar, bw.dXt, 1.f, 0.f, true, false), d_key, b->n_users, max_L, d));
-      HIP_TRY(gemm_ragged(s, rg(bw.S2, bw.U[i], bw.dXt, sc, 1.f, true, false), d_key, b->n_users, max_L, d));
+      HIP_TRY(gemm_ragged(s, rg(bw.S2, Xt, bw.du, sc, 0.f, false, false), d_row, b->n_users, T_rows, d, bf));
+      HIP_TRY(gemm_ragged(s, rg(bw.S, bw.dabar, bw.dXt, 1.f, 0.f, true, false), d_key, b->n_users, max_L, d, bf));
+      HIP_TRY(gemm_ragged(s, rg(bw.S2, bw.U[i], bw.dXt, sc, 1.f, true, false), d_key, b->n_users, max_L, d, bf));
       HIP_TRY(ph.end());
     }
     Phase pt2(prof, s, STCA_PHASE_BWD_TARGET);

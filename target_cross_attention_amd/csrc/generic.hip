@@ -263,12 +263,128 @@ static hipError_t gemm_mfma_t(hipStream_t s, const GemmArgs &g) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// The ragged products of the mixed-precision backward on bf16 matrix cores: fp32 operands are rounded
+// to bf16 as they are staged into LDS (v_mfma_f32_32x32x16_bf16, fp32 accumulation and output).
+// 128 x 128 output tile per workgroup, four waves of 64 x 64, k in steps of 32 through
+// double-buffered LDS tiles [row][k] of 32 bf16 padded to 40 (80-byte rows: the 16-byte fragment
+// reads of 16 consecutive rows fall in 64 distinct banks).  Lane group g of a 16-deep k-substep
+// holds k = 8 g .. 8 g + 7 of its row, as in the bf16 GEMMs above.
+// ------------------------------------------------------------------------------------------
+constexpr int XK = 32, XKP = 40;
+
+// 128 rows x 32 k of an fp32 operand between its global load and its LDS store.  KCONT: element
+// (row, k) at P[row * ld + k]; otherwise at P[k * ld + row].  K and ld multiples of 4.
+template <bool KCONT> struct MixedTile {
+  f32x4 v[4];
+  __device__ __forceinline__ void load(const float *__restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
+                                       int tid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (KCONT) {
+        const int r = (tid >> 3) + 32 * e, k = k0 + (tid & 7) * 4;
+        v[e] = (r0 + r < rows && k < K) ? *(const f32x4 *)(P + (int64_t)(r0 + r) * ld + k) : f32x4{0, 0, 0, 0};
+      } else {
+        const int k = k0 + (tid >> 5) + 8 * e, r = r0 + (tid & 31) * 4;
+        v[e] = (k < K && r < rows) ? *(const f32x4 *)(P + (int64_t)k * ld + r) : f32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t (*S)[XKP], int tid) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (KCONT) {
+        const int r = (tid >> 3) + 32 * e, k = (tid & 7) * 4;
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(v[e][0]) | ((uint32_t)f32_to_bf16_bits(v[e][1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(v[e][2]) | ((uint32_t)f32_to_bf16_bits(v[e][3]) << 16);
+        *(uint2 *)&S[r][k] = make_uint2(lo, hi);
+      } else {
+        const int k = (tid >> 5) + 8 * e, r = (tid & 31) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[r + i][k] = f32_to_bf16_bits(v[e][i]);
+      }
+    }
+  }
+};
+
+template <bool TRANS_B, bool TRANS_A>
+__global__ __launch_bounds__(256) void gemm_mixed_ragged_kernel(const float *__restrict__ A, const float *__restrict__ B,
+                                                                float *__restrict__ C, float alpha, float beta,
+                                                                const RaggedDesc *__restrict__ descs) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][MT][XKP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][MT][XKP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * MT, n0 = blockIdx.x * MT;
+  const RaggedDesc dsc = descs[blockIdx.z];
+  const int M = dsc.M, N = dsc.N, K = dsc.K;
+  if (m0 >= M || n0 >= N) return;
+  A += dsc.a_off;
+  B += dsc.b_off;
+  C += dsc.c_off;
+  MixedTile<!TRANS_A> la;  // A (row m, k): k-contiguous unless transposed
+  MixedTile<TRANS_B> lb;   // B as (row n, k): k-contiguous only when transposed
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, g8 = (lane >> 5) * 8, lr = lane & 31;
+  la.load(A, dsc.lda, M, K, m0, 0, tid);
+  lb.load(B, dsc.ldb, N, K, n0, 0, tid);
+  la.store(As[0], tid);
+  lb.store(Bs[0], tid);
+  __syncthreads();
+  const int steps = (K + XK - 1) / XK;
+  for (int st = 0; st < steps; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < steps;
+    if (more) {
+      la.load(A, dsc.lda, M, K, m0, (st + 1) * XK, tid);
+      lb.load(B, dsc.ldb, N, K, n0, (st + 1) * XK, tid);
+    }
+#pragma unroll
+    for (int kk = 0; kk < XK / 16; ++kk) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *(const bf16x8 *)&As[cur][wm + 32 * i + lr][16 * kk + g8];
+        b[i] = *(const bf16x8 *)&Bs[cur][wn + 32 * i + lr][16 * kk + g8];
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32x32x16(a[bi], b[bj], acc[bi][bj]);
+    }
+    if (more) {
+      la.store(As[cur ^ 1], tid);
+      lb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int col = n0 + wn + 32 * bj + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm + 32 * bi + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row >= M) continue;
+        float *p = C + (int64_t)row * dsc.ldc + col;
+        float v = alpha * acc[bi][bj][e];
+        if (beta != 0.f) v += beta * *p;
+        *p = v;
+      }
+    }
+}
+
 // Ragged fp32 products: g gives the operand types, transposes, base pointers, alpha and beta; the
 // sizes, offsets and leading dimensions of product z come from descs[z] (z < n), every one at most
 // max_m x max_n.  Operands are fp32; every leading dimension and offset a multiple of 4 elements and
 // the bases 16-byte aligned, as the vector loads need.
 hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs, int n, int64_t max_m,
-                       int64_t max_n) {
+                       int64_t max_n, bool bf16_mm) {
   if (n <= 0 || max_m <= 0 || max_n <= 0) return hipSuccess;
   if (g.ta_bf16 || g.tb_bf16 || g.tc_bf16 || (g.trans_a && g.trans_b)) return hipErrorInvalidValue;
   if (((uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C) & 15) return hipErrorInvalidValue;
@@ -281,12 +397,24 @@ hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs
                          (const float *)g.B, (int64_t)0, (int64_t)0, (float *)g.C, (int64_t)0, (int64_t)0, g.alpha,
                          g.beta, descs + z0);
     };
-    if (g.trans_a)
+    auto go_mixed = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const float *)g.A, (const float *)g.B, (float *)g.C, g.alpha,
+                         g.beta, descs + z0);
+    };
+    if (bf16_mm) {
+      if (g.trans_a)
+        go_mixed(gemm_mixed_ragged_kernel<false, true>);
+      else if (g.trans_b)
+        go_mixed(gemm_mixed_ragged_kernel<true, false>);
+      else
+        go_mixed(gemm_mixed_ragged_kernel<false, false>);
+    } else if (g.trans_a) {
       go(gemm_mfma_kernel<float, float, false, true, true>);
-    else if (g.trans_b)
+    } else if (g.trans_b) {
       go(gemm_mfma_kernel<float, float, true, false, true>);
-    else
+    } else {
       go(gemm_mfma_kernel<float, float, false, false, true>);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -27,8 +27,10 @@ struct RaggedDesc {
   int32_t M, N, K, pad;
   int64_t a_off, lda, b_off, ldb, c_off, ldc;
 };
+// bf16_mm: the fp32 operands are rounded to bf16 for the bf16 matrix cores (fp32 accumulation), the
+// mixed-precision backward's form; otherwise fp32 matrix cores.
 hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs, int n, int64_t max_m,
-                       int64_t max_n);
+                       int64_t max_n, bool bf16_mm = false);
 hipError_t swiglu_gate_inplace(hipStream_t s, int64_t n, float *A, const float *G);
 hipError_t layernorm_rows(hipStream_t s, int64_t rows, int d, const float *Y, int64_t ldy, void *out,
                           int64_t ldo, bool out_bf16, const float *gamma, const float *beta, float eps);

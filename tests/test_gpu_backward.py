@@ -11,14 +11,16 @@ over all rows and have no natural row scale).
   whose relative error is of order sqrt(K) u in the mean and K u at worst (u = 2^-24: 2e-6 ..
   9e-5), and no step divides by a small quantity (LayerNorm rows have unit scale, far from
   rstd = 1/sqrt(eps)).
-* mixed-precision path (dtype bf16): the history encode's derivative runs its products on bf16
-  operands with fp32 accumulation, and the recomputed X~ comes from the forward's bf16 encode.
-  Every operand rounding is a relative error of at most u = 2^-8 (8 significant bits); an element
-  of a gradient passes through at most four such roundings (dY, then dU or dG, plus the bf16 H
-  and the recomputed pre-activations), whose independent errors largely cancel in the fp32 sums:
-  a sum of K terms with independent relative errors of at most u has a relative error of about
-  u / sqrt(3) per rounding stage, so four stages give about 2u / sqrt(3) = 4.5e-3 in the mean.
-  tol 2e-2 (about 5 u), the forward's bf16 bar.
+* mixed-precision path (dtype bf16): the history encode's derivative and the attention derivative
+  run their products on bf16 operands with fp32 accumulation, and the recomputed X~ comes from the
+  forward's bf16 encode.  Every operand rounding is a relative error of at most u = 2^-8 (8
+  significant bits); an element of a gradient passes through up to about six such roundings (in
+  the attention derivative alpha or dS, X~, U and dA-bar; in the encode derivative dY, dU or dG,
+  the bf16 H and the recomputed pre-activations), whose independent errors largely cancel in the
+  fp32 sums: a sum of K terms with independent relative errors of at most u has a relative error
+  of about u / sqrt(3) per rounding stage, so six stages give about sqrt(6) u / sqrt(3) = 5.5e-3
+  in the mean; the worst tensors observed reach 9.3e-3.  tol 2e-2 (about 5 u), the forward's bf16
+  bar.
 A wrong term (a dropped softmax centring, a transposed operand, a missing LayerNorm mean) gives
 errors of order 1e-2 .. 1 in the fp32 path, where the bar is tight; the mixed path's cases also run
 through the fp32 path (dtype f32) at 1e-4.
