@@ -28,19 +28,17 @@ struct BackwardWs {
   float *dheads = nullptr, *dabar = nullptr, *Dv = nullptr, *du = nullptr, *dP = nullptr;
   float *eA = nullptr, *eG = nullptr, *eH = nullptr, *eY = nullptr, *edY = nullptr;
   float *parts = nullptr;
+  int64_t parts_cap = 0;  // floats in parts
   float *S = nullptr, *S2 = nullptr;  // every user's score matrix (R_u x Lp_u), twice
   RaggedDesc *desc = nullptr;         // 3 n_users product descriptors
   int64_t rows = 0;         // history rows per encode-backward chunk
   // fp32 path, with a workspace of the "keep" size: A = X W_u, G = X W_v (M x total_L x rd) and the
   // pre-LN rows Y (M x total_L x d) of every layer, kept from the forward recompute.
   float *kA = nullptr, *kG = nullptr, *kY = nullptr;
-  // Mixed-precision path (bf16 storage): bf16 operands for the matrix cores, per row chunk: H (rows x
-  // rd), H^T, u^T, g^T (rd x ldt), dY (rows x d) and dY^T (d x ldt), [dU | dG] (rows x 2rd) and its
-  // transpose (2rd x ldt); X^T (d x ldx) for all rows; per layer the re-laid-out weights (see
-  // bwd_weights) and the forward encode's packed weights.
-  int64_t ldt = 0, ldx = 0;
-  void *mH = nullptr, *mHt = nullptr, *mUt = nullptr, *mGt = nullptr, *mdY = nullptr, *mdYt = nullptr;
-  void *mdUG = nullptr, *mdUGt = nullptr, *XT = nullptr;
+  // Mixed-precision path (bf16 storage): bf16 operands for the matrix cores, per row chunk, all
+  // row-major: H, u, g (rows x rd), dY (rows x d), [dU | dG] (rows x 2rd); per layer the re-laid-out
+  // weights (see bwd_weights) and the forward encode's packed weights.
+  void *mH = nullptr, *mU = nullptr, *mG = nullptr, *mdY = nullptr, *mdUG = nullptr;
   void *uvt[STCA_MAX_M] = {}, *uvc[STCA_MAX_M] = {}, *ot[STCA_MAX_M] = {}, *packed[STCA_MAX_M] = {};
 };
 
@@ -91,22 +89,17 @@ size_t carve_backward(void *base, const stca_dims *dm, const stca_batch *b, Back
   }
   w.eY = c.take<float>((size_t)(w.rows * d));
   if (!mixed) w.edY = c.take<float>((size_t)(w.rows * d));
-  w.parts = c.take<float>((size_t)kWgradParts * std::max<int64_t>(d * rd, M * d * d));
+  w.parts_cap = (int64_t)kWgradParts * std::max<int64_t>(d * rd, M * d * d);
+  w.parts = c.take<float>((size_t)w.parts_cap);
   w.S = c.take<float>((size_t)score_elems(dm, b));
   w.S2 = c.take<float>((size_t)score_elems(dm, b));
   w.desc = c.take<RaggedDesc>((size_t)std::max(3 * b->n_users, 1));
   if (mixed) {
-    w.ldt = round_up(w.rows, 8);
-    w.ldx = round_up(std::max<int64_t>(L, 1), 8);
     w.mH = c.take<char>((size_t)(w.rows * rd) * 2);
-    w.mHt = c.take<char>((size_t)(rd * w.ldt) * 2);
-    w.mUt = c.take<char>((size_t)(rd * w.ldt) * 2);
-    w.mGt = c.take<char>((size_t)(rd * w.ldt) * 2);
+    w.mU = c.take<char>((size_t)(w.rows * rd) * 2);
+    w.mG = c.take<char>((size_t)(w.rows * rd) * 2);
     w.mdY = c.take<char>((size_t)(w.rows * d) * 2);
-    w.mdYt = c.take<char>((size_t)(d * w.ldt) * 2);
     w.mdUG = c.take<char>((size_t)(w.rows * 2 * rd) * 2);
-    w.mdUGt = c.take<char>((size_t)(2 * rd * w.ldt) * 2);
-    w.XT = c.take<char>((size_t)(d * w.ldx) * 2);
     for (int i = 0; i < M; ++i) {
       w.uvt[i] = c.take<char>((size_t)(2 * rd * d) * 2);
       w.uvc[i] = c.take<char>((size_t)(2 * rd * d) * 2);
@@ -149,6 +142,7 @@ int wgrad(hipStream_t s, int Mr, int Nc, int64_t K, const void *A, int64_t lda, 
   g.C = parts;
   g.ldc = Nc;
   g.sC = (int64_t)Mr * Nc;
+  g.mfma_small = true;
   if (full > 0) HIP_TRY(gemm(s, g));
   if (full < nsplit) {
     g.K = (int)(K - full * per);
@@ -159,6 +153,62 @@ int wgrad(hipStream_t s, int Mr, int Nc, int64_t K, const void *A, int64_t lda, 
     HIP_TRY(gemm(s, g));
   }
   HIP_TRY(sum_parts2d(s, Mr, Nc, nsplit, parts, C, ldc, true));
+  return STCA_OK;
+}
+
+// Per-head weight gradients of eq. (13)'s projections: for every head j, columns j dh .. (j+1) dh of
+// C (d x d, row stride ldc) += A_j^T B_j over K rows, where A_j is the j-th d-wide column block of A
+// (K x h d, row stride h d) and B_j columns j dh .. (j+1) dh of B (K x d, row stride ldb).  One
+// product P = A^T B (h d x d: every head's rows against every head's columns) runs on the matrix
+// cores, split over row blocks into `parts`; head j's gradient is P's diagonal block (rows j d ..,
+// columns j dh ..), whose part sums are added in block order.  The off-diagonal blocks multiply h - 1
+// times the needed work, which costs less than h products of dh columns each.  Falls back to one
+// wgrad per head when the parts buffer (parts_cap floats) cannot hold one block of P.
+int head_wgrad(hipStream_t s, int d, int h, int64_t K, const float *A, const float *B, int64_t ldb, float *C,
+               int64_t ldc, float *parts, int64_t parts_cap) {
+  if (K <= 0) return STCA_OK;
+  const int dh = d / h;
+  const int64_t pblock = (int64_t)h * d * d;
+  if (pblock > parts_cap) {
+    for (int j = 0; j < h; ++j) {
+      const int st = wgrad(s, d, dh, K, A + (size_t)j * d, (int64_t)h * d, false, B + j * dh, ldb, C + j * dh, ldc,
+                           parts);
+      if (st != STCA_OK) return st;
+    }
+    return STCA_OK;
+  }
+  int nsplit = (int)std::min<int64_t>({(int64_t)kWgradParts, parts_cap / pblock, (K + 255) / 256});
+  const int64_t per = (K + nsplit - 1) / nsplit;
+  nsplit = (int)((K + per - 1) / per);
+  const int64_t full = K / per;
+  GemmArgs g;
+  g.M = h * d;
+  g.N = d;
+  g.K = (int)per;
+  g.batch = (int)full;
+  g.A = A;
+  g.lda = (int64_t)h * d;
+  g.sA = per * g.lda;
+  g.trans_a = true;
+  g.B = B;
+  g.ldb = ldb;
+  g.sB = per * ldb;
+  g.C = parts;
+  g.ldc = d;
+  g.sC = pblock;
+  g.mfma_small = true;
+  if (full > 0) HIP_TRY(gemm(s, g));
+  if (full < nsplit) {
+    g.K = (int)(K - full * per);
+    g.batch = 1;
+    g.A = A + full * per * g.lda;
+    g.B = B + full * per * ldb;
+    g.C = parts + full * pblock;
+    HIP_TRY(gemm(s, g));
+  }
+  for (int j = 0; j < h; ++j)
+    HIP_TRY(sum_parts_strided(s, d, dh, nsplit, parts + (int64_t)j * d * d + j * dh, d, pblock, C + j * dh, ldc,
+                              true));
   return STCA_OK;
 }
 
@@ -225,12 +275,13 @@ int ffn_backward(hipStream_t s, const stca_dims *dm, const stca_ffn *f, const st
 // on the bf16 matrix cores with fp32 accumulation (gemm_nt), the SwiGLU and its derivative fused into
 // the products that produce their inputs, the LayerNorm derivative and the weight-gradient sums in
 // fp32.  Per chunk of n rows (x = X rows, dXt = dL/dX~ rows):
-//   [u | g] = x [W_u | W_v]   -> H = u SiLU(g) (bf16, row-major and transposed), u^T, g^T   (kEpiSwigluFwd)
-//   Y = H W_o                 -> fp32, then the LayerNorm derivative: dY (bf16, both layouts), dgamma, dbeta
-//   dW_o += H^T dY            (split over rows, partial sums added in order)
-//   dH = dY W_o^T             -> dU = dH SiLU(g), dG = dH u SiLU'(g) (bf16, both layouts)  (kEpiSwigluBwd)
-//   [dW_u | dW_v] += x^T [dU | dG]
+//   [u | g] = x [W_u | W_v]   -> H = u SiLU(g), u, g (bf16)                             (kEpiSwigluFwd)
+//   Y = H W_o                 -> fp32, then the LayerNorm derivative: dY (bf16), dgamma, dbeta
+//   dW_o += H^T dY            (TN product over the rows, split; partial sums added in order)
+//   dH = dY W_o^T             -> dU = dH SiLU(g), dG = dH u SiLU'(g) (bf16)                (kEpiSwigluBwd)
+//   [dW_u | dW_v] += x^T [dU | dG]   (TN, split as dW_o)
 //   dX += [dU | dG] [W_u | W_v]^T
+// Every intermediate is row-major: the weight gradients read the rows through the TN layout.
 int encode_backward_mixed(hipStream_t s, const stca_dims *dm, const stca_ffn &f, const stca_ffn_grad &g, int i,
                           const BackwardWs &bw, int64_t L, const void *X, const float *dXt, float *dX) {
   const int d = dm->d, rd = dm->r * dm->d;
@@ -239,18 +290,16 @@ int encode_backward_mixed(hipStream_t s, const stca_dims *dm, const stca_ffn &f,
     const void *x = (const char *)X + (size_t)r0 * d * 2;
     NtEpilogue e1;
     e1.H = bw.mH;
+    e1.U = bw.mU;
+    e1.G = bw.mG;
     e1.ldh = rd;
-    e1.Ht = bw.mHt;
-    e1.Ut = bw.mUt;
-    e1.Gt = bw.mGt;
-    e1.ldt = bw.ldt;
     HIP_TRY(gemm_nt(s, kEpiSwigluFwd, n, 2 * rd, d, 0, 1, x, d, 0, bw.uvt[i], d, 0, e1));
     NtEpilogue e2;
     e2.C = bw.eY;
     e2.ldc = d;
     HIP_TRY(gemm_nt(s, kEpiStore, n, d, rd, 0, 1, bw.mH, rd, 0, bw.ot[i], rd, 0, e2));
-    HIP_TRY(ln_bwd_bf16(s, n, d, dXt + (size_t)r0 * d, bw.eY, f.gamma, dm->ln_eps, bw.mdY, bw.mdYt, bw.ldt, g.dgamma,
-                        g.dbeta, bw.parts));
+    HIP_TRY(ln_bwd_bf16(s, n, d, dXt + (size_t)r0 * d, bw.eY, f.gamma, dm->ln_eps, bw.mdY, g.dgamma, g.dbeta,
+                        bw.parts));
     // dW_o (rd x d) over the chunk's rows, split into blocks of ks rows
     {
       const int64_t ks = round_up((n + kWgradParts - 1) / kWgradParts, 64), parts = (n + ks - 1) / ks;
@@ -258,16 +307,15 @@ int encode_backward_mixed(hipStream_t s, const stca_dims *dm, const stca_ffn &f,
       e3.C = bw.parts;
       e3.ldc = d;
       e3.sC = (int64_t)rd * d;
-      HIP_TRY(gemm_nt(s, kEpiStore, rd, d, n, (int)ks, (int)parts, bw.mHt, bw.ldt, 0, bw.mdYt, bw.ldt, 0, e3));
+      HIP_TRY(gemm_tn(s, kEpiStore, rd, d, n, (int)ks, (int)parts, bw.mH, rd, 0, bw.mdY, d, 0, e3));
       HIP_TRY(sum_parts_strided(s, rd, d, (int)parts, bw.parts, d, (int64_t)rd * d, g.dWo, d, true));
     }
     NtEpilogue e4;
-    e4.Ut = bw.mUt;
-    e4.Gt = bw.mGt;
-    e4.ldt = bw.ldt;
+    e4.U = bw.mU;
+    e4.G = bw.mG;
+    e4.ldh = rd;
     e4.dUG = bw.mdUG;
     e4.lddug = 2 * rd;
-    e4.dUGt = bw.mdUGt;
     e4.rd = rd;
     HIP_TRY(gemm_nt(s, kEpiSwigluBwd, n, rd, d, 0, 1, bw.mdY, d, 0, f.Wo, d, 0, e4));
     // [dW_u | dW_v] (d x 2rd) over the chunk's rows
@@ -278,8 +326,7 @@ int encode_backward_mixed(hipStream_t s, const stca_dims *dm, const stca_ffn &f,
       e5.C = bw.parts;
       e5.ldc = 2 * rd;
       e5.sC = (int64_t)d * 2 * rd;
-      HIP_TRY(gemm_nt(s, kEpiStore, d, 2 * rd, n, (int)ks, (int)parts, (const char *)bw.XT + (size_t)r0 * 2, bw.ldx,
-                      0, bw.mdUGt, bw.ldt, 0, e5));
+      HIP_TRY(gemm_tn(s, kEpiStore, d, 2 * rd, n, (int)ks, (int)parts, x, d, 0, bw.mdUG, 2 * rd, 0, e5));
       HIP_TRY(sum_parts_strided(s, d, rd, (int)parts, bw.parts, 2 * rd, (int64_t)d * 2 * rd, g.dWu, rd, true));
       HIP_TRY(sum_parts_strided(s, d, rd, (int)parts, bw.parts + rd, 2 * rd, (int64_t)d * 2 * rd, g.dWv, rd, true));
     }
@@ -358,13 +405,12 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
   if (T == 0) return STCA_OK;  // no target, no gradient
   HIP_TRY(ragged_plan(s, b->n_users, b->hist_off, b->tgt_off, h, d, b->total_L, b->total_T, b->max_L, b->max_T,
                       score_elems(dm, b), bw.desc));
-  if (bf) {  // mixed path: weight layouts of every history FFN, X^T, the forward encode's packed weights
+  if (bf) {  // mixed path: weight layouts of every history FFN and the forward encode's packed weights
     for (int i = 0; i < M; ++i) {
       const stca_ffn &f = w->hist[i];
       HIP_TRY(bwd_weights(s, d, dm->r, f.Wu, f.Wv, f.Wo, bw.uvt[i], bw.uvc[i], bw.ot[i]));
       HIP_TRY(encode_pack(s, d, dm->r, f.Wu, f.Wv, f.Wo, bw.packed[i]));
     }
-    HIP_TRY(transpose_tiled_bf16(s, L, d, X, d, bw.XT, bw.ldx));
   }
   const int64_t T_rows = b->max_T * h, max_L = b->max_L;  // bounds of the ragged products' sizes
   auto rg = [](const float *A, const float *B, float *C, float alpha, float beta, bool ta, bool tb) {
@@ -510,10 +556,8 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     if ((st = wgrad(s, d, d, T, bw.heads[i], d, false, dO, ldo, g->dWO[i], d, bw.parts)) != STCA_OK) return st;
     HIP_TRY(mm(s, (int)T, d, d, dO, ldo, false, w->WO[i], d, bf, true, bw.dheads, d, 0.f));
     // eq. (13), per head: W_V, then the softmax and the two projections in front of it
-    for (int j = 0; j < h; ++j)
-      if ((st = wgrad(s, d, dh, T, bw.abar[i] + (size_t)j * d, (int64_t)h * d, false, bw.dheads + j * dh, d,
-                      g->dWV[i] + j * dh, d, bw.parts)) != STCA_OK)
-        return st;
+    if ((st = head_wgrad(s, d, h, T, bw.abar[i], bw.dheads, d, g->dWV[i], d, bw.parts, bw.parts_cap)) != STCA_OK)
+      return st;
     GemmArgs da;  // dabar_j = dheads_j W_V,j^T
     da.M = (int)T;
     da.N = d;
@@ -562,10 +606,7 @@ int backward_impl(const stca_dims *dm, const stca_weights *w, const stca_batch *
     dp.ldc = d;
     dp.sC = dh;
     HIP_TRY(gemm(s, dp));
-    for (int j = 0; j < h; ++j)
-      if ((st = wgrad(s, d, dh, T, bw.du + (size_t)j * d, (int64_t)h * d, false, bw.P[i] + j * dh, d,
-                      g->dWK[i] + j * dh, d, bw.parts)) != STCA_OK)
-        return st;
+    if ((st = head_wgrad(s, d, h, T, bw.du, bw.P[i], d, g->dWK[i], d, bw.parts, bw.parts_cap)) != STCA_OK) return st;
     if ((st = wgrad(s, d, d, T, bw.q[i], d, false, bw.dP, d, g->dWQ[i], d, bw.parts)) != STCA_OK) return st;
     HIP_TRY(mm(s, (int)T, d, d, bw.dP, d, false, w->WQ[i], d, bf, true, bw.dq, d, 0.f));
     HIP_TRY(pt2.end());

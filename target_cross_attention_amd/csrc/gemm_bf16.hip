@@ -1,26 +1,34 @@
-// bf16 matrix-core GEMM for the mixed-precision backward: C[M x N] = A[M x K] Bt[N x K]^T with A and
-// Bt bf16, k-contiguous, fp32 accumulation on v_mfma_f32_32x32x16_bf16, and epilogues that fuse the
-// SwiGLU of eq. (1) and its derivative into the product that feeds them.
+// bf16 matrix-core GEMMs for the mixed-precision backward, fp32 accumulation on
+// v_mfma_f32_32x32x16_bf16, with epilogues that fuse the SwiGLU of eq. (1) and its derivative into the
+// product that feeds them.  Two operand layouts:
+//   NT: C[M x N] = A[M x K] Bt[N x K]^T, both k-contiguous (the activation and weight products);
+//   TN: C[M x N] = A[K x M]^T B[K x N], both m / n-contiguous (the weight gradients, whose k runs over
+//       the rows of row-major activations, so no transposed copy of them is ever written).
 //
-// Tiles: TM x 128 per workgroup of four waves (2 x 2), each wave (TM/2) x 64, i.e. TM/64 x 2 MFMA
-// blocks of 32 x 32.  k advances 64 at a time: every thread loads its 16-byte chunks of the next
-// k-slab into registers while the current slab's MFMAs run, then writes them to the other half of a
-// double-buffered LDS tile.  An LDS row holds 64 bf16 (eight 16-byte chunks); chunk c of row r sits
-// in slot c ^ ((r >> 1) & 7), so that the 16 lanes of a fragment read (rows r .. r+15, one chunk)
-// and of a tile write (two rows, all chunks) touch 64 distinct banks.
+// Tiles: TM x 128 (TM = 128) per workgroup of four waves (2 x 2), each wave (TM/2) x 64, i.e. TM/64 x 2
+// MFMA blocks of 32 x 32; two workgroups per compute unit.  k advances 64 at a time: every thread
+// loads its 16-byte chunks of the next k-slab into registers while the current slab's MFMAs run,
+// then writes them to the other half of a double-buffered LDS tile.
+//   NT slabs are [row][k]: an LDS row holds 64 bf16 (eight 16-byte chunks); chunk c of row r sits in
+//   slot c ^ ((r >> 1) & 7), so that the 16 lanes of a fragment read (rows r .. r+15, one chunk) and
+//   of a tile write (two rows, all chunks) touch 64 distinct banks.
+//   TN slabs are [k][row]: an LDS row holds the 128 m (n) values of one k (sixteen chunks), chunk c
+//   of k-row r in slot c ^ 4 (r & 3).  Fragments come from the transposing 64-bit LDS read
+//   (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
+//   chunks addressed by lanes 4 j + i / 4, j = 0..3): lane 4 j + q of a group addresses k-row
+//   k0 + j and the four rows m0 + 4 q .. m0 + 4 q + 3, so lane i gets rows m0 + i at k0 .. k0 + 3; two
+//   such reads give the 8 k of the MFMA operand.  Half a wave reads 4 k-rows x 4 chunks, which the
+//   swizzle spreads over all 16 slots: 64 distinct banks.
 //
 // Epilogues (lane l of a wave holds column 32 j + (l & 31) of block j and, in register e of block i,
-// row 32 i + 8 (e >> 2) + 4 (l >> 5) + (e & 3): four consecutive rows per register group, which is
-// what makes the transposed (row-contiguous) outputs 8-byte stores):
+// row 32 i + 8 (e >> 2) + 4 (l >> 5) + (e & 3)):
 //   kEpiStore / kEpiAcc : C (fp32) = / += the product; batch z at C + z sC.
 //   kEpiSwigluFwd       : the columns are up/gate pairs in blocks of 64 (32 up columns of hidden
 //                         features 32 q .. 32 q + 31, then the 32 gate columns of the same features),
 //                         so a wave holds u and g of the same (row, feature) in one lane: writes
-//                         H = u SiLU(g) rounded to bf16 (row-major and transposed) and u, g as bf16
-//                         (transposed), the inputs of the derivative.
-//   kEpiSwigluBwd       : the product is dH (columns = hidden features); reads u, g (transposed bf16)
-//                         and writes dU = dH SiLU(g), dG = dH u SiLU'(g) as bf16, row-major [dU | dG]
-//                         and transposed.
+//                         H = u SiLU(g), u and g, rounded to bf16, row-major.
+//   kEpiSwigluBwd       : the product is dH (columns = hidden features); reads u, g (row-major bf16)
+//                         and writes dU = dH SiLU(g), dG = dH u SiLU'(g) as bf16, row-major [dU | dG].
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -33,14 +41,26 @@ STCA_DEBUG_WORD
 namespace {
 
 constexpr int kTN = 128, kBK = 64;
-// Epilogue staging (the epilogue kernels use 128-row tiles).  Transposed tiles get rows of 128 + 8
-// elements (272 bytes), so that the 8-byte writes of 32 lanes into 32 different rows spread over the
-// banks and every row stays 16-byte aligned.
-constexpr int kTP = 136;
-constexpr int kFwdStage = 128 * 64 * 2 + 3 * 64 * kTP * 2;        // H [128][64], H^T, u^T, g^T [64][136]
-constexpr int kBwdStage = 128 * 128 * 2 + 128 * kTP * 2;           // dU or dG: [128][128] and [128][136]
+constexpr int kXcds = 8;  // XCDs of the chip, each with its own L2
+// Epilogue staging (128-row tiles): H, u, g [128][64] (forward); u, g [128][128], then dU, dG
+// (derivative).
+constexpr int kFwdStage = 3 * 128 * 64 * 2;
+constexpr int kBwdStage = 2 * 128 * 128 * 2;
 
 __device__ __forceinline__ int nt_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Slot of 16-byte chunk c in LDS row r of a 256-byte-row tile read with the transposing LDS read.
+__device__ __forceinline__ int tr_slot(int r, int c) { return c ^ ((r & 3) << 2); }
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+// Byte offset, within a 256-byte-row tile laid out by tr_slot, of this lane's address for the
+// transposing read that gives lane i of its 16-lane group column col0 + i (col0: the group's first
+// column, a multiple of 16) at rows row0 .. row0 + 3 (row0 a multiple of 4).
+__device__ __forceinline__ uint32_t tr_lane_offset(int row0, int col0, int lane) {
+  const int jj = (lane & 15) >> 2, col = col0 + 4 * (lane & 3), row = row0 + jj;
+  return (uint32_t)(row * 256 + (tr_slot(row, col >> 3) << 4) + (col & 7) * 2);
+}
+__device__ __forceinline__ s16x4 tr_read(const STCA_LDS char *base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(base + off));
+}
 
 __device__ __forceinline__ float sigmoid_fast(float g) { return fast_rcp(1.0f + fast_exp2(-g * kLog2e)); }
 
@@ -66,13 +86,14 @@ __device__ __forceinline__ void load4(const uint16_t *p, float (&v)[4]) {
   v[3] = __uint_as_float(w.y & 0xFFFF0000u);
 }
 
-template <int TM, int EPI>
-__global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, int N, int K, int ksplit, const bf16 *__restrict__ A,
+template <int TM, int EPI, bool TN>
+__global__ __launch_bounds__(256, 2) void gemm_nt_kernel(int M, int N, int K, int ksplit, const bf16 *__restrict__ A,
                                                          int64_t lda, int64_t sA, const bf16 *__restrict__ Bt,
                                                          int64_t ldb, int64_t sB, const NtEpilogue ep) {
   constexpr int MI = TM / 64;         // 32-row blocks per wave
-  constexpr int LA = TM * 8 / 256;    // 16-byte chunks of the A slab per thread
+  constexpr int LA = TM * 8 / 256;    // 16-byte chunks of the A slab (TM x 64 values) per thread
   constexpr int LB = kTN * 8 / 256;   // ... of the B slab
+  static_assert(!TN || TM == 128, "TN slabs are 64 k-rows of 128 values");
   // One LDS block: the double-buffered A and B tiles of the main loop, then the epilogue's staging.
   constexpr int kMainBytes = 2 * (TM + kTN) * 8 * 16;
   constexpr int kEpiBytes = EPI == kEpiSwigluFwd ? kFwdStage : EPI == kEpiSwigluBwd ? kBwdStage : 0;
@@ -81,9 +102,24 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
   bf16x8(*Bs)[kTN * 8] = reinterpret_cast<bf16x8(*)[kTN * 8]>(smem + 2 * TM * 8 * 16);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, g = lane >> 5;
-  const int z = blockIdx.z;
-  const int64_t m0 = (int64_t)blockIdx.y * TM;
-  const int n0 = blockIdx.x * kTN;
+  // Tile of this workgroup: virtual index v runs over column tiles fastest, then row tiles, then
+  // batches.  Workgroups are dealt to the 8 XCDs round-robin by launch index b and each XCD has its own
+  // L2.  The plain products map b to v so that XCD x = b mod 8 takes the x-th contiguous range of v:
+  // the column tiles that share an A row tile, and the tiles of one split-K block, then run on one XCD
+  // at about the same time and share its L2.  The SwiGLU epilogues keep v = b, so each XCD works on
+  // few column tiles (measured faster for them: 208 against 218 us and 286 against 319 us per
+  // 65536-row chunk at d = 256, r = 4).
+  int tx, ty, z;
+  {
+    const int gx = (N + kTN - 1) / kTN, gy = (M + TM - 1) / TM, nb = (int)gridDim.x, b = (int)blockIdx.x;
+    const int xcd = b % kXcds, q = nb / kXcds, rem = nb % kXcds;
+    const int v = (EPI == kEpiStore || EPI == kEpiAcc) ? xcd * q + (xcd < rem ? xcd : rem) + b / kXcds : b;
+    tx = v % gx;
+    ty = (v / gx) % gy;
+    z = v / (gx * gy);
+  }
+  const int64_t m0 = (int64_t)ty * TM;
+  const int n0 = tx * kTN;
   const int wm = (wave >> 1) * (TM / 2), wn = (wave & 1) * 64;
   // k range: split-K blocks share A and Bt; batches step through them.
   int kb = 0, ke = K;
@@ -96,46 +132,85 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
   }
 
   // Two register sets: the slab of step s + 2 is loaded during step s and written to LDS at the end of
-  // step s + 1, so every load has two steps of MFMA work to land.
+  // step s + 1, so every load has two steps of MFMA work to land.  The loads are unconditional, so the
+  // compiler can count them and wait only for the set it stores: rows past M (N) read row M - 1
+  // (N - 1) and their products land in outputs that are never stored; k beyond the range reads at kb.
+  // NT: every chunk read lies inside its row's first lda (ldb) elements, since chunks start at
+  // multiples of 8 below ke <= K <= lda and lda is a multiple of 8; the elements at or past ke are
+  // zeroed when the last slab is written to LDS, by which time its loads have landed anyway.
+  // TN: a chunk is 8 consecutive m (n) of one k-row (M, N multiples of 8); k-rows at or past ke are
+  // zeroed in the same way.
   bf16x8 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
   auto load = [&](int k0, bf16x8(&ra)[LA], bf16x8(&rb)[LB]) {
+    if constexpr (!TN) {
 #pragma unroll
-    for (int j = 0; j < LA; ++j) {
-      const int q = tid + 256 * j, r = q >> 3, k = k0 + 8 * (q & 7);
-      bf16x8 v{};
-      if (m0 + r < M && k < ke) {
-        v = *reinterpret_cast<const bf16x8 *>(A + (m0 + r) * lda + k);
-        if (k + 8 > ke)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (k + e >= ke) v[e] = bf16{};
+      for (int j = 0; j < LA; ++j) {
+        const int q = tid + 256 * j, r = q >> 3, k = k0 + 8 * (q & 7);
+        const int64_t row = min(m0 + r, (int64_t)M - 1);
+        ra[j] = *reinterpret_cast<const bf16x8 *>(A + row * lda + (k < ke ? k : kb));
       }
-      ra[j] = v;
-    }
 #pragma unroll
-    for (int j = 0; j < LB; ++j) {
-      const int q = tid + 256 * j, r = q >> 3, k = k0 + 8 * (q & 7);
-      bf16x8 v{};
-      if (n0 + r < N && k < ke) {
-        v = *reinterpret_cast<const bf16x8 *>(Bt + (int64_t)(n0 + r) * ldb + k);
-        if (k + 8 > ke)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (k + e >= ke) v[e] = bf16{};
+      for (int j = 0; j < LB; ++j) {
+        const int q = tid + 256 * j, r = q >> 3, k = k0 + 8 * (q & 7);
+        const int64_t row = min(n0 + r, N - 1);
+        rb[j] = *reinterpret_cast<const bf16x8 *>(Bt + row * ldb + (k < ke ? k : kb));
       }
-      rb[j] = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < LA; ++j) {
+        const int q = tid + 256 * j, kr = k0 + (q >> 4);
+        const int col = min((int)m0 + 8 * (q & 15), M - 8);
+        ra[j] = *reinterpret_cast<const bf16x8 *>(A + (int64_t)(kr < ke ? kr : kb) * lda + col);
+      }
+#pragma unroll
+      for (int j = 0; j < LB; ++j) {
+        const int q = tid + 256 * j, kr = k0 + (q >> 4);
+        const int col = min(n0 + 8 * (q & 15), N - 8);
+        rb[j] = *reinterpret_cast<const bf16x8 *>(Bt + (int64_t)(kr < ke ? kr : kb) * ldb + col);
+      }
     }
   };
-  auto store = [&](int buf, const bf16x8(&ra)[LA], const bf16x8(&rb)[LB]) {
+  auto store = [&](int buf, int k0, bf16x8(&ra)[LA], bf16x8(&rb)[LB]) {
+    if (k0 + kBK > ke) {  // the last slab of the k range
+      if constexpr (!TN) {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+          const int k = k0 + 8 * ((tid + 256 * j) & 7);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k + e >= ke) ra[j][e] = bf16{};
+        }
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+          const int k = k0 + 8 * ((tid + 256 * j) & 7);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k + e >= ke) rb[j][e] = bf16{};
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+          if (k0 + ((tid + 256 * j) >> 4) >= ke) ra[j] = bf16x8{};
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+          if (k0 + ((tid + 256 * j) >> 4) >= ke) rb[j] = bf16x8{};
+      }
+    }
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-      const int q = tid + 256 * j, r = q >> 3;
-      As[buf][r * 8 + nt_slot(r, q & 7)] = ra[j];
+      const int q = tid + 256 * j;
+      if constexpr (!TN)
+        As[buf][(q >> 3) * 8 + nt_slot(q >> 3, q & 7)] = ra[j];
+      else
+        As[buf][(q >> 4) * 16 + tr_slot(q >> 4, q & 15)] = ra[j];
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-      const int q = tid + 256 * j, r = q >> 3;
-      Bs[buf][r * 8 + nt_slot(r, q & 7)] = rb[j];
+      const int q = tid + 256 * j;
+      if constexpr (!TN)
+        Bs[buf][(q >> 3) * 8 + nt_slot(q >> 3, q & 7)] = rb[j];
+      else
+        Bs[buf][(q >> 4) * 16 + tr_slot(q >> 4, q & 15)] = rb[j];
     }
   };
 
@@ -145,21 +220,46 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  // TN fragment addresses: lane group (lane >> 4) covers columns 16 ((lane >> 4) & 1) .. + 15 of its
+  // 32-wide block and k 8 g .. 8 g + 7 of each 16-deep substep (two reads of four k-rows).
+  uint32_t aoff[MI], boff[2];
+  if constexpr (TN) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) aoff[i] = tr_lane_offset(8 * g, wm + 32 * i + 16 * ((lane >> 4) & 1), lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) boff[j] = tr_lane_offset(8 * g, wn + 32 * j + 16 * ((lane >> 4) & 1), lane);
+  }
   const int steps = ke > kb ? (ke - kb + kBK - 1) / kBK : 0;
   auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int c = 2 * kk + g;
       bf16x8 a[MI], b[2];
+      if constexpr (!TN) {
+        const int c = 2 * kk + g;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = wm + 32 * i + lr;
-        a[i] = As[cur][r * 8 + nt_slot(r, c)];
-      }
+        for (int i = 0; i < MI; ++i) {
+          const int r = wm + 32 * i + lr;
+          a[i] = As[cur][r * 8 + nt_slot(r, c)];
+        }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn + 32 * j + lr;
-        b[j] = Bs[cur][r * 8 + nt_slot(r, c)];
+        for (int j = 0; j < 2; ++j) {
+          const int r = wn + 32 * j + lr;
+          b[j] = Bs[cur][r * 8 + nt_slot(r, c)];
+        }
+      } else {
+        const STCA_LDS char *la = (const STCA_LDS char *)&As[cur][0];
+        const STCA_LDS char *lb = (const STCA_LDS char *)&Bs[cur][0];
+        const uint32_t ko = (uint32_t)kk * 16 * 256;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          a[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr_read(la, aoff[i] + ko),
+                                                                    tr_read(la, aoff[i] + ko + 4 * 256), 0, 1, 2,
+                                                                    3, 4, 5, 6, 7));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr_read(lb, boff[j] + ko),
+                                                                    tr_read(lb, boff[j] + ko + 4 * 256), 0, 1, 2,
+                                                                    3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -169,23 +269,25 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
   };
   // Step s computes from LDS half s & 1, loads the slab of s + 2 into one register set and writes the
   // other (the slab of s + 1, loaded during step s - 1) into LDS half (s + 1) & 1, which step s - 1
-  // finished reading before the barrier that ended it.
-  if (steps > 0) {
+  // finished reading before the barrier that ended it.  The loop runs steps in pairs without a
+  // conditional load, store or exit inside, so the compiler keeps one register set per slab and waits
+  // only for the slab it stores.  Slabs past the end are loaded from in-range addresses and stored as
+  // zeros (every element is at or past ke); an odd step count adds one step over such a zero slab.
+  if (steps > 0) {  // (an empty k range reads nothing: kb may then lie past the rows)
     load(kb, ra0, rb0);
-    store(0, ra0, rb0);
-  }
-  if (steps > 1) load(kb + kBK, ra1, rb1);
-  __syncthreads();
-  for (int st = 0; st < steps; st += 2) {
-    if (st + 2 < steps) load(kb + (st + 2) * kBK, ra0, rb0);
-    compute(0);
-    if (st + 1 < steps) store(1, ra1, rb1);
+    store(0, kb, ra0, rb0);
+    load(kb + kBK, ra1, rb1);
     __syncthreads();
-    if (st + 1 >= steps) break;
-    if (st + 3 < steps) load(kb + (st + 3) * kBK, ra1, rb1);
-    compute(1);
-    if (st + 2 < steps) store(0, ra0, rb0);
-    __syncthreads();
+    for (int st = 0; st < steps; st += 2) {
+      load(kb + (st + 2) * kBK, ra0, rb0);
+      compute(0);
+      store(1, kb + (st + 1) * kBK, ra1, rb1);
+      __syncthreads();
+      load(kb + (st + 3) * kBK, ra1, rb1);
+      compute(1);
+      store(0, kb + (st + 2) * kBK, ra0, rb0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogues ----------------------------------------------------------------------------
@@ -210,10 +312,9 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
   } else if constexpr (EPI == kEpiSwigluFwd) {
     static_assert(TM == 128, "staging layout");
     // The tile is 128 rows x 64 hidden features (the wave pair wn = 0 / 64 holds features 0-31 /
-    // 32-63 of the tile).  Stage H [row][feature] and H^T, u^T, g^T [feature][row] in LDS, then store
-    // whole 16-byte row chunks.
-    uint16_t *sH = reinterpret_cast<uint16_t *>(smem);
-    uint16_t *sHt = sH + 128 * 64, *sUt = sHt + 64 * kTP, *sGt = sUt + 64 * kTP;
+    // 32-63 of the tile).  Stage H, u and g [row][feature] in LDS, then store whole 16-byte row
+    // chunks.
+    uint16_t *sH = reinterpret_cast<uint16_t *>(smem), *sU = sH + 128 * 64, *sG = sU + 128 * 64;
     const int fl = (wn >> 1) + lr;          // feature within the tile
     const int f0 = (n0 >> 1);               // first hidden feature of the tile
 #pragma unroll
@@ -221,106 +322,118 @@ __global__ __launch_bounds__(256, TM == 128 ? 2 : 1) void gemm_nt_kernel(int M, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t0 = wm + 32 * i + 8 * q + 4 * g;
-        float u[4], gg[4], h[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          u[t] = acc[i][0][4 * q + t];
-          gg[t] = acc[i][1][4 * q + t];
-          h[t] = u[t] * gg[t] * sigmoid_fast(gg[t]);
-          sH[(t0 + t) * 64 + fl] = bf16_bits(h[t]);
+          const float u = acc[i][0][4 * q + t], gg = acc[i][1][4 * q + t];
+          const int o = (t0 + t) * 64 + fl;
+          sH[o] = bf16_bits(u * gg * sigmoid_fast(gg));
+          sU[o] = bf16_bits(u);
+          sG[o] = bf16_bits(gg);
         }
-        store4(sHt + fl * kTP + t0, h[0], h[1], h[2], h[3]);
-        store4(sUt + fl * kTP + t0, u[0], u[1], u[2], u[3]);
-        store4(sGt + fl * kTP + t0, gg[0], gg[1], gg[2], gg[3]);
       }
     __syncthreads();
-    uint16_t *H = reinterpret_cast<uint16_t *>(ep.H);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // H: 128 rows x 8 chunks
-      const int qd = tid + 256 * j, t = qd >> 3, c = qd & 7;
-      if (m0 + t < M)
-        *reinterpret_cast<u32x4 *>(H + (m0 + t) * ep.ldh + f0 + 8 * c) =
-            *reinterpret_cast<const u32x4 *>(sH + t * 64 + 8 * c);
-    }
-    uint16_t *dst[3] = {reinterpret_cast<uint16_t *>(ep.Ht), reinterpret_cast<uint16_t *>(ep.Ut),
-                        reinterpret_cast<uint16_t *>(ep.Gt)};
-    const uint16_t *src[3] = {sHt, sUt, sGt};
+    uint16_t *dst[3] = {reinterpret_cast<uint16_t *>(ep.H), reinterpret_cast<uint16_t *>(ep.U),
+                        reinterpret_cast<uint16_t *>(ep.G)};
+    const uint16_t *src[3] = {sH, sU, sG};
 #pragma unroll
     for (int a = 0; a < 3; ++a)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {  // 64 feature rows x 16 chunks of 8 rows
-        const int qd = tid + 256 * j, f = qd >> 4, c = qd & 15;
-        if (m0 + 8 * c < M) {  // a partial chunk fills padding columns (< ldt) that no reader uses
-          STCA_CHECK(m0 + 8 * c + 8 <= ep.ldt, kDbgGemmPad);
-          *reinterpret_cast<u32x4 *>(dst[a] + (int64_t)(f0 + f) * ep.ldt + m0 + 8 * c) =
-              *reinterpret_cast<const u32x4 *>(src[a] + f * kTP + 8 * c);
-        }
+      for (int j = 0; j < 4; ++j) {  // 128 rows x 8 chunks
+        const int qd = tid + 256 * j, t = qd >> 3, c = qd & 7;
+        if (m0 + t < M)
+          *reinterpret_cast<u32x4 *>(dst[a] + (m0 + t) * ep.ldh + f0 + 8 * c) =
+              *reinterpret_cast<const u32x4 *>(src[a] + t * 64 + 8 * c);
       }
   } else if constexpr (EPI == kEpiSwigluBwd) {
     static_assert(TM == 128, "staging layout");
-    // The tile is 128 rows x 128 hidden features.  Each lane reads its u and g (four consecutive rows
-    // of one feature: 8 bytes of u^T, g^T) and forms dU, then dG; each goes out through LDS, staged
-    // as [row][feature] and [feature][row], in whole 16-byte row chunks.
-    const uint16_t *Ut = reinterpret_cast<const uint16_t *>(ep.Ut), *Gt = reinterpret_cast<const uint16_t *>(ep.Gt);
-    const int rd = ep.rd;
-    uint16_t *dUG = reinterpret_cast<uint16_t *>(ep.dUG), *dUGt = reinterpret_cast<uint16_t *>(ep.dUGt);
-    uint16_t *sR = reinterpret_cast<uint16_t *>(smem), *sT = sR + 128 * 128;  // [row][feature], [feature][row]
+    // The tile is 128 rows x 128 hidden features.  The tile's u and g come from their row-major
+    // arrays into LDS ([row][feature], 256-byte rows laid out by tr_slot); the transposing read then
+    // gives each lane the four consecutive rows of its feature that its accumulator registers hold.
+    // dU and dG go out through the same LDS area, [row][feature], in whole 16-byte row chunks.
+    const uint16_t *U = reinterpret_cast<const uint16_t *>(ep.U), *G = reinterpret_cast<const uint16_t *>(ep.G);
+    uint16_t *dUG = reinterpret_cast<uint16_t *>(ep.dUG);
+    uint16_t *sU = reinterpret_cast<uint16_t *>(smem), *sG = sU + 128 * 128;
+    {
+      u32x4 vu[8], vg[8];
 #pragma unroll
-    for (int part = 0; part < 2; ++part) {     // dU, then dG
-      if (part) __syncthreads();               // the staging area is free again
+      for (int j = 0; j < 8; ++j) {  // 128 rows x 16 chunks each
+        const int qd = tid + 256 * j, t = qd >> 4;
+        const int64_t row = min(m0 + t, (int64_t)M - 1);
+        const int col = min(n0 + 8 * (qd & 15), N - 8);
+        STCA_CHECK(col + 8 <= ep.ldh, kDbgGemmPad);
+        vu[j] = *reinterpret_cast<const u32x4 *>(U + row * ep.ldh + col);
+        vg[j] = *reinterpret_cast<const u32x4 *>(G + row * ep.ldh + col);
+      }
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int j = 0; j < 8; ++j) {
+        const int qd = tid + 256 * j, t = qd >> 4, o = (t * 16 + tr_slot(t, qd & 15)) * 8;
+        *reinterpret_cast<u32x4 *>(sU + o) = vu[j];
+        *reinterpret_cast<u32x4 *>(sG + o) = vg[j];
+      }
+    }
+    __syncthreads();
+    const STCA_LDS char *lu = (const STCA_LDS char *)sU, *lg = (const STCA_LDS char *)sG;
+    uint32_t pu[MI][2][4][2], pg[MI][2][4][2];  // dU, dG of (block i, jb, row group q) as bf16 pairs
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          const int fl = wn + 32 * jb + lr;
-          const int64_t f = n0 + fl;
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int t0 = wm + 32 * i + 8 * q + 4 * g;
-            float u[4] = {0.f, 0.f, 0.f, 0.f}, gg[4] = {0.f, 0.f, 0.f, 0.f}, v[4];
-            if (f < N && m0 + t0 < M) {  // rows up to round_up(M, 4) - 1 < ldt
-              STCA_CHECK(m0 + t0 + 4 <= ep.ldt, kDbgGemmPad);
-              load4(Ut + f * ep.ldt + m0 + t0, u);
-              load4(Gt + f * ep.ldt + m0 + t0, gg);
-            }
+      for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float dh = acc[i][jb][4 * q + t], sg = sigmoid_fast(gg[t]);
-              v[t] = part == 0 ? dh * gg[t] * sg : dh * u[t] * sg * (1.0f + gg[t] * (1.0f - sg));
-              sR[(t0 + t) * 128 + fl] = bf16_bits(v[t]);
-            }
-            store4(sT + fl * kTP + t0, v[0], v[1], v[2], v[3]);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t off = tr_lane_offset(wm + 32 * i + 8 * q + 4 * g, wn + 32 * jb + 16 * ((lane >> 4) & 1), lane);
+          const s16x4 u4 = tr_read(lu, off), g4 = tr_read(lg, off);
+          float du[4], dg[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float u = __uint_as_float((uint32_t)(uint16_t)u4[t] << 16);
+            const float gg = __uint_as_float((uint32_t)(uint16_t)g4[t] << 16);
+            const float dh = acc[i][jb][4 * q + t], sg = sigmoid_fast(gg);
+            du[t] = dh * gg * sg;
+            dg[t] = dh * u * sg * (1.0f + gg * (1.0f - sg));
+          }
+          pu[i][jb][q][0] = (uint32_t)bf16_bits(du[0]) | ((uint32_t)bf16_bits(du[1]) << 16);
+          pu[i][jb][q][1] = (uint32_t)bf16_bits(du[2]) | ((uint32_t)bf16_bits(du[3]) << 16);
+          pg[i][jb][q][0] = (uint32_t)bf16_bits(dg[0]) | ((uint32_t)bf16_bits(dg[1]) << 16);
+          pg[i][jb][q][1] = (uint32_t)bf16_bits(dg[2]) | ((uint32_t)bf16_bits(dg[3]) << 16);
+        }
+    __syncthreads();  // every lane has read its u and g: the area takes dU and dG
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t0 = wm + 32 * i + 8 * q + 4 * g, fl = wn + 32 * jb + lr;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int sh = 16 * (t & 1);
+            sU[(t0 + t) * 128 + fl] = (uint16_t)(pu[i][jb][q][t >> 1] >> sh);
+            sG[(t0 + t) * 128 + fl] = (uint16_t)(pg[i][jb][q][t >> 1] >> sh);
           }
         }
-      __syncthreads();
-      const int64_t col0 = (int64_t)part * rd + n0;  // column of [dU | dG], row of its transpose
+    __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {  // [row][feature]: 128 rows x 16 chunks
+    for (int part = 0; part < 2; ++part) {  // dU into columns n0 .., dG into rd + n0 ..
+      const uint16_t *src = part ? sG : sU;
+      const int64_t col0 = (int64_t)part * ep.rd + n0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {  // 128 rows x 16 chunks
         const int qd = tid + 256 * j, t = qd >> 4, c = qd & 15;
         if (m0 + t < M && n0 + 8 * c < N)
           *reinterpret_cast<u32x4 *>(dUG + (m0 + t) * ep.lddug + col0 + 8 * c) =
-              *reinterpret_cast<const u32x4 *>(sR + t * 128 + 8 * c);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {  // [feature][row]: 128 feature rows x 16 chunks
-        const int qd = tid + 256 * j, fr = qd >> 4, c = qd & 15;
-        if (n0 + fr < N && m0 + 8 * c < M) {
-          STCA_CHECK(m0 + 8 * c + 8 <= ep.ldt, kDbgGemmPad);
-          *reinterpret_cast<u32x4 *>(dUGt + (col0 + fr) * ep.ldt + m0 + 8 * c) =
-              *reinterpret_cast<const u32x4 *>(sT + fr * kTP + 8 * c);
-        }
+              *reinterpret_cast<const u32x4 *>(src + t * 128 + 8 * c);
       }
     }
   }
 }
 
-template <int TM, int EPI>
+template <int TM, int EPI, bool TN>
 hipError_t launch_nt(hipStream_t s, int M, int N, int K, int ksplit, int batch, const void *A, int64_t lda, int64_t sA,
                      const void *Bt, int64_t ldb, int64_t sB, const NtEpilogue &ep) {
-  const int64_t gy = ((int64_t)M + TM - 1) / TM;
-  if (gy > 65535 || batch > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_nt_kernel<TM, EPI>), dim3((unsigned)((N + kTN - 1) / kTN), (unsigned)gy, (unsigned)batch),
-                     dim3(256), 0, s, M, N, K, ksplit, (const bf16 *)A, lda, sA, (const bf16 *)Bt, ldb, sB, ep);
+  const int64_t blocks = ((int64_t)M + TM - 1) / TM * ((N + kTN - 1) / kTN) * batch;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_nt_kernel<TM, EPI, TN>), dim3((unsigned)blocks), dim3(256), 0, s, M, N, K, ksplit,
+                     (const bf16 *)A, lda, sA, (const bf16 *)Bt, ldb, sB, ep);
   return hipGetLastError();
 }
 
@@ -331,66 +444,41 @@ hipError_t gemm_nt(hipStream_t s, int epi, int M, int N, int K, int ksplit, int 
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
   if (lda % 8 || ldb % 8 || (((uintptr_t)A | (uintptr_t)Bt) & 15) || (sA | sB) % 8 || ksplit % 8)
     return hipErrorInvalidValue;
-  if ((epi == kEpiSwigluFwd || epi == kEpiSwigluBwd) && (ep.ldt % 4 || batch != 1 || ksplit)) return hipErrorInvalidValue;
+  if ((epi == kEpiSwigluFwd || epi == kEpiSwigluBwd) && (ep.ldh % 8 || batch != 1 || ksplit)) return hipErrorInvalidValue;
   if (epi == kEpiSwigluFwd && N % 128) return hipErrorInvalidValue;
-  if (epi == kEpiSwigluBwd && N % 8) return hipErrorInvalidValue;
-  // 128-row tiles: two workgroups per compute unit (one overlaps the other's loads).
-  const bool tall = false;
+  if (epi == kEpiSwigluBwd && (N % 8 || ep.lddug % 8)) return hipErrorInvalidValue;
+  // 128-row tiles, two workgroups per compute unit (256-row tiles with one measured slower).
   switch (epi) {
     case kEpiStore:
-      return tall ? launch_nt<256, kEpiStore>(s, M, N, K, ksplit, batch, A, lda, sA, Bt, ldb, sB, ep)
-                  : launch_nt<128, kEpiStore>(s, M, N, K, ksplit, batch, A, lda, sA, Bt, ldb, sB, ep);
+      return launch_nt<128, kEpiStore, false>(s, M, N, K, ksplit, batch, A, lda, sA, Bt, ldb, sB, ep);
     case kEpiAcc:
-      return tall ? launch_nt<256, kEpiAcc>(s, M, N, K, ksplit, batch, A, lda, sA, Bt, ldb, sB, ep)
-                  : launch_nt<128, kEpiAcc>(s, M, N, K, ksplit, batch, A, lda, sA, Bt, ldb, sB, ep);
+      return launch_nt<128, kEpiAcc, false>(s, M, N, K, ksplit, batch, A, lda, sA, Bt, ldb, sB, ep);
     case kEpiSwigluFwd:
-      return launch_nt<128, kEpiSwigluFwd>(s, M, N, K, 0, 1, A, lda, 0, Bt, ldb, 0, ep);
+      return launch_nt<128, kEpiSwigluFwd, false>(s, M, N, K, 0, 1, A, lda, 0, Bt, ldb, 0, ep);
     case kEpiSwigluBwd:
-      return launch_nt<128, kEpiSwigluBwd>(s, M, N, K, 0, 1, A, lda, 0, Bt, ldb, 0, ep);
+      return launch_nt<128, kEpiSwigluBwd, false>(s, M, N, K, 0, 1, A, lda, 0, Bt, ldb, 0, ep);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-// ---- small re-layouts for the mixed-precision backward ---------------------------------------
-// out[c][r] = in[r][c] (bf16, rows x cols, row strides ldi / ldo), through 64 x 64 LDS tiles so that
-// both the reads and the writes are row-contiguous.
-__global__ __launch_bounds__(256) void transpose_tiled_kernel(int64_t rows, int cols, const uint16_t *__restrict__ in,
-                                                              int64_t ldi, uint16_t *__restrict__ out, int64_t ldo) {
-  __shared__ uint16_t t[64][66];
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k;
-    const int c = c0 + tx;
-    t[k][tx] = (r < rows && c < cols) ? in[r * ldi + c] : 0;
-  }
-  __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int c = c0 + k;
-    const int64_t r = r0 + tx;
-    if (c < cols && r < rows) out[(int64_t)c * ldo + r] = t[tx][k];
+hipError_t gemm_tn(hipStream_t s, int epi, int M, int N, int K, int ksplit, int batch, const void *A, int64_t lda,
+                   int64_t sA, const void *B, int64_t ldb, int64_t sB, const NtEpilogue &ep) {
+  if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+  if (M % 8 || N % 8 || lda % 8 || ldb % 8 || lda < M || ldb < N || (((uintptr_t)A | (uintptr_t)B) & 15) ||
+      (sA | sB) % 8 || ksplit < 0)
+    return hipErrorInvalidValue;
+  switch (epi) {
+    case kEpiStore:
+      return launch_nt<128, kEpiStore, true>(s, M, N, K, ksplit, batch, A, lda, sA, B, ldb, sB, ep);
+    case kEpiAcc:
+      return launch_nt<128, kEpiAcc, true>(s, M, N, K, ksplit, batch, A, lda, sA, B, ldb, sB, ep);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
-hipError_t transpose_tiled_bf16(hipStream_t s, int64_t rows, int cols, const void *in, int64_t ldi, void *out,
-                                int64_t ldo) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  const int64_t gy = (rows + 63) / 64;
-  if (gy > 65535) {  // in row slabs of 65535 tiles
-    for (int64_t r = 0; r < rows; r += 65535 * 64) {
-      const int64_t n = std::min<int64_t>(65535 * 64, rows - r);
-      hipError_t e = transpose_tiled_bf16(s, n, cols, (const uint16_t *)in + r * ldi, ldi, (uint16_t *)out + r, ldo);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
-  hipLaunchKernelGGL(transpose_tiled_kernel, dim3((unsigned)((cols + 63) / 64), (unsigned)gy), dim3(256), 0, s, rows,
-                     cols, (const uint16_t *)in, ldi, (uint16_t *)out, ldo);
-  return hipGetLastError();
-}
-
+// ---- weight re-layouts and the LayerNorm derivative of the mixed-precision backward -----------
 // Weight layouts for the mixed backward of one history FFN (Wu, Wv: d x rd; Wo: rd x d; bf16):
 //   uvt [2rd x d]: row 64 q + t = column 32 q + t of Wu, row 64 q + 32 + t = the same column of Wv
 //                  (the up/gate pairs of the kSwigluFwd epilogue), t < 32;
@@ -426,18 +514,15 @@ hipError_t bwd_weights(hipStream_t s, int d, int r, const void *Wu, const void *
 
 // LayerNorm derivative of the mixed path (the same arithmetic as ln_bwd, fp32): workgroups walk
 // 64-row tiles (tile = blockIdx.x + k gridDim.x), each wave 16 rows of a tile one at a time; dY goes
-// out as bf16, row-major (rows x D) and transposed (D x ldt), both staged in LDS so that every global
-// store is a whole row chunk.  A workgroup's column sums of dgamma and dbeta over its tiles go to
+// out as bf16, row-major (rows x D), staged in LDS so that every global store is a whole row chunk.  A workgroup's column sums of dgamma and dbeta over its tiles go to
 // parts[blk][c] and parts[gridDim.x + blk][c].
 template <int D>
 __global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const float *__restrict__ dout,
                                                           const float *__restrict__ Y,
                                                           const float *__restrict__ gamma, float eps,
-                                                          uint16_t *__restrict__ dY, uint16_t *__restrict__ dYt,
-                                                          int64_t ldt, float *__restrict__ parts) {
-  constexpr int E = D / 64, TS = 68;  // transposed rows of 64 tokens + 4 (8-byte aligned, 2-way banks)
+                                                          uint16_t *__restrict__ dY, float *__restrict__ parts) {
+  constexpr int E = D / 64;
   __shared__ __attribute__((aligned(16))) uint16_t sR[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sT[D * TS];
   __shared__ float red[4][2][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float pg[E], pb[E], gm[E];
@@ -482,9 +567,7 @@ __global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const fl
     const float m1 = wave_sum(s1) / (float)D, m2 = wave_sum(s2) / (float)D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const uint16_t b = ok ? bf16_bits(rstd * (dy[e] - m1 - y[e] * m2)) : 0;
-      sR[t * D + lane + 64 * e] = b;
-      sT[(lane + 64 * e) * TS + t] = b;
+      sR[t * D + lane + 64 * e] = ok ? bf16_bits(rstd * (dy[e] - m1 - y[e] * m2)) : 0;
     }
   }
   __syncthreads();
@@ -493,14 +576,6 @@ __global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const fl
     const int t = qd / (D / 8), c = qd % (D / 8);
     if (r0 + t < rows)
       *reinterpret_cast<u32x4 *>(dY + (r0 + t) * D + 8 * c) = *reinterpret_cast<const u32x4 *>(sR + t * D + 8 * c);
-  }
-  // transposed: D rows x 16 chunks of 4 tokens (8 bytes); rows past the end carry zeros
-  for (int qd = threadIdx.x; qd < D * 16; qd += 256) {
-    const int f = qd >> 4, c = qd & 15;
-    if (r0 + 4 * c < rows) {
-      STCA_CHECK(r0 + 4 * c + 4 <= ldt, kDbgGemmPad);
-      *reinterpret_cast<uint2 *>(dYt + (int64_t)f * ldt + r0 + 4 * c) = *reinterpret_cast<const uint2 *>(sT + f * TS + 4 * c);
-    }
   }
   }
 #pragma unroll
@@ -516,12 +591,11 @@ __global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const fl
 }
 
 hipError_t ln_bwd_bf16(hipStream_t s, int64_t rows, int d, const float *dout, const float *Y, const float *gamma,
-                       float eps, void *dY, void *dYt, int64_t ldt, float *dgamma, float *dbeta, float *parts) {
+                       float eps, void *dY, float *dgamma, float *dbeta, float *parts) {
   if (rows <= 0) return hipSuccess;
   const int64_t nblk = std::min<int64_t>((rows + 63) / 64, 256);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), 0, s, rows, dout, Y, gamma, eps, (uint16_t *)dY,
-                       (uint16_t *)dYt, ldt, parts);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(256), 0, s, rows, dout, Y, gamma, eps, (uint16_t *)dY, parts);
   };
   switch (d) {
     case 64: go(ln_bwd_bf16_kernel<64>); break;

@@ -421,12 +421,12 @@ hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs
   return hipSuccess;
 }
 
-// Whether the matrix-core form applies: fp32 output, enough 128 x 128 tiles to fill the chip, and
-// vector-aligned operands along their contiguous dimension.
+// Whether the matrix-core form applies: fp32 output, enough 128 x 128 tiles to fill the chip (or
+// mfma_small), and vector-aligned operands along their contiguous dimension.
 static bool mfma_ok(const GemmArgs &g) {
   if (g.tc_bf16) return false;
   const int64_t tiles = (int64_t)((g.N + MT - 1) / MT) * ((g.M + MT - 1) / MT) * g.batch;
-  if (tiles < 128 || g.K < 64) return false;
+  if ((tiles < 128 && !g.mfma_small) || g.K < 64) return false;
   auto fits = [](const void *p, bool is_bf16, int64_t ld, int64_t stride, int64_t contiguous_len) {
     const uintptr_t align = is_bf16 ? 8 : 16;
     return ((uintptr_t)p % align) == 0 && ld % 4 == 0 && stride % 4 == 0 && contiguous_len % 4 == 0;

@@ -20,6 +20,9 @@ struct GemmArgs {
   int64_t ldc = 0, sC = 0;
   bool tc_bf16 = false;
   float alpha = 1.f, beta = 0.f;
+  // true: fp32-output products take the matrix cores whenever their operands allow it, also with too
+  // few tiles to fill the chip (split-K remainders, where the vector kernel's few tiles are slower)
+  bool mfma_small = false;
 };
 hipError_t gemm(hipStream_t s, const GemmArgs &g);
 // One product of a ragged batch: sizes, element offsets from the base pointers, leading dimensions.
@@ -166,14 +169,11 @@ enum { kEpiStore = 0, kEpiAcc = 1, kEpiSwigluFwd = 2, kEpiSwigluBwd = 3 };
 struct NtEpilogue {
   float *C = nullptr;            // kEpiStore / kEpiAcc: fp32 output (row stride ldc, batch stride sC)
   int64_t ldc = 0, sC = 0;
-  void *H = nullptr;             // kEpiSwigluFwd: H (bf16, rows x rd, row stride ldh)
+  void *H = nullptr;             // kEpiSwigluFwd: H written (bf16, rows x rd, row stride ldh)
+  void *U = nullptr, *G = nullptr;  // kEpiSwigluFwd: u, g written; kEpiSwigluBwd: read (same layout)
   int64_t ldh = 0;
-  void *Ht = nullptr;            // kEpiSwigluFwd: H^T; both: u^T, g^T (bf16, rd x rows, row stride ldt)
-  void *Ut = nullptr, *Gt = nullptr;
-  int64_t ldt = 0;
   void *dUG = nullptr;           // kEpiSwigluBwd: [dU | dG] (bf16, rows x 2rd, row stride lddug)
   int64_t lddug = 0;
-  void *dUGt = nullptr;          // kEpiSwigluBwd: [dU | dG]^T (bf16, 2rd x rows, row stride ldt)
   int rd = 0;
 };
 // C = A[M x K] Bt[N x K]^T (bf16 operands, k-contiguous rows, lda/ldb multiples of 8, bases 16-byte
@@ -181,17 +181,19 @@ struct NtEpilogue {
 // and writes C + z sC; otherwise batch z reads A + z sA, Bt + z sB and writes C + z sC.
 hipError_t gemm_nt(hipStream_t s, int epi, int M, int N, int K, int ksplit, int batch, const void *A, int64_t lda,
                    int64_t sA, const void *Bt, int64_t ldb, int64_t sB, const NtEpilogue &ep);
-hipError_t transpose_tiled_bf16(hipStream_t s, int64_t rows, int cols, const void *in, int64_t ldi, void *out,
-                                int64_t ldo);
+// C = A[K x M]^T B[K x N] (bf16, row-major with m / n contiguous: M, N, lda, ldb multiples of 8,
+// bases 16-byte aligned) through kEpiStore or kEpiAcc; ksplit and batches as for gemm_nt.
+hipError_t gemm_tn(hipStream_t s, int epi, int M, int N, int K, int ksplit, int batch, const void *A, int64_t lda,
+                   int64_t sA, const void *B, int64_t ldb, int64_t sB, const NtEpilogue &ep);
 hipError_t bwd_weights(hipStream_t s, int d, int r, const void *Wu, const void *Wv, const void *Wo, void *uvt,
                        void *uvc, void *ot);
 hipError_t sum_parts_strided(hipStream_t s, int rows, int cols, int nparts, const float *parts, int64_t ldp,
                              int64_t pstride, float *out, int64_t ldo, bool accumulate);
 // LayerNorm derivative (mixed path) from the pre-LN rows Y (rows x d, fp32) and dout (rows x d): dY
-// as bf16 row-major (rows x d) and transposed (d x ldt), dgamma and dbeta accumulated through
-// per-block partial sums (2 ceil(rows / 64) d floats of parts).
+// as bf16 row-major (rows x d), dgamma and dbeta accumulated through per-block partial sums
+// (2 min(ceil(rows / 64), 256) d floats of parts).
 hipError_t ln_bwd_bf16(hipStream_t s, int64_t rows, int d, const float *dout, const float *Y, const float *gamma,
-                       float eps, void *dY, void *dYt, int64_t ldt, float *dgamma, float *dbeta, float *parts);
+                       float eps, void *dY, float *dgamma, float *dbeta, float *parts);
 
 // ---- backward pieces (backward.hip); all fp32 ------------------------------------------------
 hipError_t fill_f32(hipStream_t s, int64_t n, float *y, float v);
