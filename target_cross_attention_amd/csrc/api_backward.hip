@@ -229,6 +229,7 @@ hipError_t mm(hipStream_t s, int m, int n, int k, const void *A, int64_t lda, bo
   g.C = C;
   g.ldc = ldc;
   g.beta = beta;
+  g.mfma_small = true;  // the per-target products have few tiles; the matrix cores still win
   return gemm(s, g);
 }
 

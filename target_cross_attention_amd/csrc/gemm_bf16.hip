@@ -269,16 +269,17 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(int M, int N, int K, in
   };
   // Step s computes from LDS half s & 1, loads the slab of s + 2 into one register set and writes the
   // other (the slab of s + 1, loaded during step s - 1) into LDS half (s + 1) & 1, which step s - 1
-  // finished reading before the barrier that ended it.  The loop runs steps in pairs without a
-  // conditional load, store or exit inside, so the compiler keeps one register set per slab and waits
-  // only for the slab it stores.  Slabs past the end are loaded from in-range addresses and stored as
-  // zeros (every element is at or past ke); an odd step count adds one step over such a zero slab.
+  // finished reading before the barrier that ended it.  The main loop runs steps in pairs while both
+  // of its loads are in range, with no conditional load, store or exit inside, so the compiler keeps
+  // one register set per slab and waits only for the slab it stores; the last one to three steps
+  // follow with plain conditions.
   if (steps > 0) {  // (an empty k range reads nothing: kb may then lie past the rows)
     load(kb, ra0, rb0);
     store(0, kb, ra0, rb0);
-    load(kb + kBK, ra1, rb1);
+    if (steps > 1) load(kb + kBK, ra1, rb1);
     __syncthreads();
-    for (int st = 0; st < steps; st += 2) {
+    int st = 0;
+    for (; st + 3 < steps; st += 2) {
       load(kb + (st + 2) * kBK, ra0, rb0);
       compute(0);
       store(1, kb + (st + 1) * kBK, ra1, rb1);
@@ -288,6 +289,21 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(int M, int N, int K, in
       store(0, kb + (st + 2) * kBK, ra0, rb0);
       __syncthreads();
     }
+    // slab st in LDS half 0, slab st + 1 (if any) in register set 1
+    const int left = steps - st;
+    if (left > 2) load(kb + (st + 2) * kBK, ra0, rb0);
+    compute(0);
+    if (left > 1) {
+      store(1, kb + (st + 1) * kBK, ra1, rb1);
+      __syncthreads();
+      compute(1);
+      if (left > 2) {
+        store(0, kb + (st + 2) * kBK, ra0, rb0);
+        __syncthreads();
+        compute(0);
+      }
+    }
+    __syncthreads();  // the epilogues reuse the LDS block
   }
 
   // ---- epilogues ----------------------------------------------------------------------------
@@ -535,39 +551,66 @@ __global__ __launch_bounds__(256) void ln_bwd_bf16_kernel(int64_t rows, const fl
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
   const int64_t r0 = tile * 64;
   __syncthreads();  // the previous tile's stores have read the staging area
-  for (int k = 0; k < 16; ++k) {
-    const int t = wave * 16 + k;
-    const int64_t row = r0 + t;
-    float y[E], go[E], dy[E];
-    const bool ok = row < rows;
+  // Four rows at a time, so that their loads are in flight together and their reductions interleave.
+  for (int k = 0; k < 16; k += 4) {
+    float y[4][E], go[4][E], dy[4][E];
+    bool ok[4];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      y[e] = ok ? Y[row * D + lane + 64 * e] : 0.f;
-      go[e] = ok ? dout[row * D + lane + 64 * e] : 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const int64_t row = r0 + wave * 16 + k + w;
+      ok[w] = row < rows;
+      const int64_t rr = ok[w] ? row : rows - 1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        y[w][e] = Y[rr * D + lane + 64 * e];
+        go[w][e] = dout[rr * D + lane + 64 * e];
+      }
     }
-    float sum = 0.f;
+    float sum[4], q[4], s1[4], s2[4], mean[4], rstd[4];
 #pragma unroll
-    for (int e = 0; e < E; ++e) sum += y[e];
-    const float mean = wave_sum(sum) / (float)D;
-    float q = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      sum[w] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) q += (y[e] - mean) * (y[e] - mean);
-    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + eps);
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float xh = (y[e] - mean) * rstd, g = go[e] * gm[e];
-      s1 += g;
-      s2 += g * xh;
-      pg[e] = fmaf(go[e], xh, pg[e]);
-      pb[e] += go[e];
-      y[e] = xh;
-      dy[e] = g;
+      for (int e = 0; e < E; ++e) sum[w] += y[w][e];
     }
-    const float m1 = wave_sum(s1) / (float)D, m2 = wave_sum(s2) / (float)D;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      sR[t * D + lane + 64 * e] = ok ? bf16_bits(rstd * (dy[e] - m1 - y[e] * m2)) : 0;
+    for (int w = 0; w < 4; ++w) mean[w] = wave_sum(sum[w]) / (float)D;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      q[w] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) q[w] += (y[w][e] - mean[w]) * (y[w][e] - mean[w]);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) rstd[w] = 1.0f / sqrtf(wave_sum(q[w]) / (float)D + eps);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s1[w] = s2[w] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xh = (y[w][e] - mean[w]) * rstd[w], gg = go[w][e] * gm[e];
+        s1[w] += gg;
+        s2[w] += gg * xh;
+        if (ok[w]) {
+          pg[e] = fmaf(go[w][e], xh, pg[e]);
+          pb[e] += go[w][e];
+        }
+        y[w][e] = xh;
+        dy[w][e] = gg;
+      }
+    }
+    float m1[4], m2[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      m1[w] = wave_sum(s1[w]) / (float)D;
+      m2[w] = wave_sum(s2[w]) / (float)D;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t = wave * 16 + k + w;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        sR[t * D + lane + 64 * e] = ok[w] ? bf16_bits(rstd[w] * (dy[w][e] - m1[w] - y[w][e] * m2[w])) : 0;
     }
   }
   __syncthreads();

@@ -277,8 +277,25 @@ constexpr int XK = 32, XKP = 40;
 // (row, k) at P[row * ld + k]; otherwise at P[k * ld + row].  K and ld multiples of 4.
 template <bool KCONT> struct MixedTile {
   f32x4 v[4];
+  // Unconditional loads, so that the compiler can count them: a row chunk past `rows` or a k past K
+  // reads the last chunk that the bounds allow (the same addresses the bounded form reads), and the
+  // values at k >= K are zeroed in store().  Rows past `rows` feed outputs that are never written.
   __device__ __forceinline__ void load(const float *__restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
                                        int tid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (KCONT) {
+        const int r = min(r0 + (tid >> 3) + 32 * e, rows - 1), k = min(k0 + (tid & 7) * 4, (K - 1) & ~3);
+        v[e] = *(const f32x4 *)(P + (int64_t)r * ld + k);
+      } else {
+        const int k = min(k0 + (tid >> 5) + 8 * e, K - 1), r = min(r0 + (tid & 31) * 4, (rows - 1) & ~3);
+        v[e] = *(const f32x4 *)(P + (int64_t)k * ld + r);
+      }
+    }
+  }
+  // The bounded form: lanes whose chunk lies past `rows` or K skip the load and hold zeros.
+  __device__ __forceinline__ void load_bounded(const float *__restrict__ P, int64_t ld, int rows, int K, int r0,
+                                               int k0, int tid) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (KCONT) {
@@ -290,7 +307,20 @@ template <bool KCONT> struct MixedTile {
       }
     }
   }
-  __device__ __forceinline__ void store(uint16_t (*S)[XKP], int tid) const {
+  __device__ __forceinline__ void store(uint16_t (*S)[XKP], int tid, int K, int k0) {
+    if (k0 + XK > K) {  // the last slab: zero every value at k >= K
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (KCONT) {
+          const int k = k0 + (tid & 7) * 4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k + i >= K) v[e][i] = 0.f;
+        } else if (k0 + (tid >> 5) + 8 * e >= K) {
+          v[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (KCONT) {
@@ -307,7 +337,13 @@ template <bool KCONT> struct MixedTile {
   }
 };
 
-template <bool TRANS_B, bool TRANS_A>
+// PIPE: two register sets per operand: the slab of step s + 2 is loaded during step s and stored at
+// the end of step s + 1.  The main loop runs steps in pairs while both of its loads are in range, with
+// no conditional load, store or exit inside, so the compiler waits only for the set it stores; the
+// last one to three steps follow with plain conditions.  Otherwise one set, loaded one step ahead with
+// bounded loads: fewer registers and more workgroups per compute unit, which serves products whose k
+// range is a few steps (the history-side products, k = a user's query rows).
+template <bool TRANS_B, bool TRANS_A, bool PIPE>
 __global__ __launch_bounds__(256) void gemm_mixed_ragged_kernel(const float *__restrict__ A, const float *__restrict__ B,
                                                                 float *__restrict__ C, float alpha, float beta,
                                                                 const RaggedDesc *__restrict__ descs) {
@@ -321,27 +357,15 @@ __global__ __launch_bounds__(256) void gemm_mixed_ragged_kernel(const float *__r
   A += dsc.a_off;
   B += dsc.b_off;
   C += dsc.c_off;
-  MixedTile<!TRANS_A> la;  // A (row m, k): k-contiguous unless transposed
-  MixedTile<TRANS_B> lb;   // B as (row n, k): k-contiguous only when transposed
+  MixedTile<!TRANS_A> la0, la1;  // A (row m, k): k-contiguous unless transposed
+  MixedTile<TRANS_B> lb0, lb1;   // B as (row n, k): k-contiguous only when transposed
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, g8 = (lane >> 5) * 8, lr = lane & 31;
-  la.load(A, dsc.lda, M, K, m0, 0, tid);
-  lb.load(B, dsc.ldb, N, K, n0, 0, tid);
-  la.store(As[0], tid);
-  lb.store(Bs[0], tid);
-  __syncthreads();
-  const int steps = (K + XK - 1) / XK;
-  for (int st = 0; st < steps; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < steps;
-    if (more) {
-      la.load(A, dsc.lda, M, K, m0, (st + 1) * XK, tid);
-      lb.load(B, dsc.ldb, N, K, n0, (st + 1) * XK, tid);
-    }
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < XK / 16; ++kk) {
       bf16x8 a[2], b[2];
@@ -355,11 +379,72 @@ __global__ __launch_bounds__(256) void gemm_mixed_ragged_kernel(const float *__r
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32x32x16(a[bi], b[bj], acc[bi][bj]);
     }
-    if (more) {
-      la.store(As[cur ^ 1], tid);
-      lb.store(Bs[cur ^ 1], tid);
+  };
+  const int steps = (K + XK - 1) / XK;
+  if (!PIPE) {
+    la0.load_bounded(A, dsc.lda, M, K, m0, 0, tid);
+    lb0.load_bounded(B, dsc.ldb, N, K, n0, 0, tid);
+    la0.store(As[0], tid, K, 0);
+    lb0.store(Bs[0], tid, K, 0);
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+      const int cur = st & 1;
+      const bool more = st + 1 < steps;
+      if (more) {
+        la0.load_bounded(A, dsc.lda, M, K, m0, (st + 1) * XK, tid);
+        lb0.load_bounded(B, dsc.ldb, N, K, n0, (st + 1) * XK, tid);
+      }
+      compute(cur);
+      if (more) {
+        la0.store(As[cur ^ 1], tid, K, (st + 1) * XK);
+        lb0.store(Bs[cur ^ 1], tid, K, (st + 1) * XK);
+      }
+      __syncthreads();
+    }
+  } else if (steps > 0) {
+    la0.load(A, dsc.lda, M, K, m0, 0, tid);
+    lb0.load(B, dsc.ldb, N, K, n0, 0, tid);
+    la0.store(As[0], tid, K, 0);
+    lb0.store(Bs[0], tid, K, 0);
+    if (steps > 1) {
+      la1.load(A, dsc.lda, M, K, m0, XK, tid);
+      lb1.load(B, dsc.ldb, N, K, n0, XK, tid);
     }
     __syncthreads();
+    int st = 0;
+    for (; st + 3 < steps; st += 2) {
+      la0.load(A, dsc.lda, M, K, m0, (st + 2) * XK, tid);
+      lb0.load(B, dsc.ldb, N, K, n0, (st + 2) * XK, tid);
+      compute(0);
+      la1.store(As[1], tid, K, (st + 1) * XK);
+      lb1.store(Bs[1], tid, K, (st + 1) * XK);
+      __syncthreads();
+      la1.load(A, dsc.lda, M, K, m0, (st + 3) * XK, tid);
+      lb1.load(B, dsc.ldb, N, K, n0, (st + 3) * XK, tid);
+      compute(1);
+      la0.store(As[0], tid, K, (st + 2) * XK);
+      lb0.store(Bs[0], tid, K, (st + 2) * XK);
+      __syncthreads();
+    }
+    // slab st in LDS half 0, slab st + 1 (if any) in register set 1
+    const int left = steps - st;
+    if (left > 2) {
+      la0.load(A, dsc.lda, M, K, m0, (st + 2) * XK, tid);
+      lb0.load(B, dsc.ldb, N, K, n0, (st + 2) * XK, tid);
+    }
+    compute(0);
+    if (left > 1) {
+      la1.store(As[1], tid, K, (st + 1) * XK);
+      lb1.store(Bs[1], tid, K, (st + 1) * XK);
+      __syncthreads();
+      compute(1);
+      if (left > 2) {
+        la0.store(As[0], tid, K, (st + 2) * XK);
+        lb0.store(Bs[0], tid, K, (st + 2) * XK);
+        __syncthreads();
+        compute(0);
+      }
+    }
   }
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
@@ -403,11 +488,11 @@ hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs
     };
     if (bf16_mm) {
       if (g.trans_a)
-        go_mixed(gemm_mixed_ragged_kernel<false, true>);
+        go_mixed(gemm_mixed_ragged_kernel<false, true, false>);
       else if (g.trans_b)
-        go_mixed(gemm_mixed_ragged_kernel<true, false>);
+        go_mixed(gemm_mixed_ragged_kernel<true, false, true>);
       else
-        go_mixed(gemm_mixed_ragged_kernel<false, false>);
+        go_mixed(gemm_mixed_ragged_kernel<false, false, true>);
     } else if (g.trans_a) {
       go(gemm_mfma_kernel<float, float, false, true, true>);
     } else if (g.trans_b) {
