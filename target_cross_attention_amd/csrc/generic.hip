@@ -125,53 +125,64 @@ template <> struct vec4_of<bf16> {
   }
 };
 
-// One operand tile (128 rows x 16 k) of a K-step, in registers between its global load and its
-// LDS store.  KCONT: the operand's k index is contiguous in memory (element (row, k) at
+// One operand tile (TT rows x 16 k, TT = 128 or 64) of a K-step, in registers between its global
+// load and its LDS store.  KCONT: the operand's k index is contiguous in memory (element (row, k) at
 // P[row * ld + k]); otherwise rows are (element (row, k) at P[k * ld + row]).
-template <typename T, bool KCONT> struct TileLoader {
+template <typename T, bool KCONT, int TT = MT> struct TileLoader {
   f32x4 v[2];
   __device__ __forceinline__ void load(const T *__restrict__ P, int64_t ld, int rows, int K, int r0, int k0,
                                        int tid) {
+    if constexpr (KCONT) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      if (KCONT) {
+      for (int e = 0; e < TT / 64; ++e) {
         const int r = (tid >> 2) + 64 * e, k = k0 + (tid & 3) * 4;
         v[e] = (r0 + r < rows && k < K) ? vec4_of<T>::load(P + (int64_t)(r0 + r) * ld + k) : f32x4{0, 0, 0, 0};
-      } else {  // a 2 (k) x 4 (rows) block per thread: k = 2 (tid >> 5) + e, rows 4 (tid & 31) ..
+      }
+    } else if constexpr (TT == 128) {  // a 2 (k) x 4 (rows) block per thread: k = 2 (tid >> 5) + e, rows 4 (tid & 31) ..
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
         const int k = k0 + 2 * (tid >> 5) + e, r = r0 + (tid & 31) * 4;
         v[e] = (k < K && r < rows) ? vec4_of<T>::load(P + (int64_t)k * ld + r) : f32x4{0, 0, 0, 0};
       }
+    } else {  // 64 rows: one k, rows 4 (tid & 15) .. per thread
+      const int k = k0 + (tid >> 4), r = r0 + (tid & 15) * 4;
+      v[0] = (k < K && r < rows) ? vec4_of<T>::load(P + (int64_t)k * ld + r) : f32x4{0, 0, 0, 0};
     }
   }
   __device__ __forceinline__ void store(float (*S)[MKP], int tid) const {
+    if constexpr (KCONT) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      if (KCONT) {
-        *(f32x4 *)&S[(tid >> 2) + 64 * e][(tid & 3) * 4] = v[e];
-      } else if (e == 0) {  // transposed in registers: row r + i gets (k, k + 1) as one 8-byte store
-        const int k = 2 * (tid >> 5), r = (tid & 31) * 4;
+      for (int e = 0; e < TT / 64; ++e) *(f32x4 *)&S[(tid >> 2) + 64 * e][(tid & 3) * 4] = v[e];
+    } else if constexpr (TT == 128) {  // transposed in registers: row r + i gets (k, k + 1) as one 8-byte store
+      const int k = 2 * (tid >> 5), r = (tid & 31) * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
-          *(f32x2 *)&S[r + i][k] = f32x2{v[0][i], v[1][i]};
-        }
+      for (int i = 0; i < 4; ++i) {
+        typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+        *(f32x2 *)&S[r + i][k] = f32x2{v[0][i], v[1][i]};
       }
+    } else {
+      const int k = tid >> 4, r = (tid & 15) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[r + i][k] = v[0][i];
     }
   }
 };
 
 // RAGGED: blockIdx.z picks a descriptor (one per user of a ragged batch) that gives the product's
 // sizes, element offsets and leading dimensions; blocks outside that user's tiles return at once.
-template <typename TA, typename TB, bool TRANS_B, bool TRANS_A, bool RAGGED>
+// TT: output tile TT x TT (128, or 64 for products with too few 128 x 128 tiles to fill the chip);
+// each of the four waves holds (TT/2) x (TT/2), TT/64 x TT/64 MFMA blocks.
+template <typename TA, typename TB, bool TRANS_B, bool TRANS_A, bool RAGGED, int TT = MT>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, const TA *__restrict__ A, int64_t lda,
                                                         int64_t sA, const TB *__restrict__ B, int64_t ldb,
                                                         int64_t sB, float *__restrict__ C, int64_t ldc, int64_t sC,
                                                         float alpha, float beta,
                                                         const RaggedDesc *__restrict__ descs) {
-  __shared__ __attribute__((aligned(16))) float As[2][MT][MKP];
-  __shared__ __attribute__((aligned(16))) float Bs[2][MT][MKP];
+  constexpr int BW = TT / 64;  // MFMA blocks per wave along each dimension
+  __shared__ __attribute__((aligned(16))) float As[2][TT][MKP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][TT][MKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * MT, n0 = blockIdx.x * MT;
+  const int m0 = blockIdx.y * TT, n0 = blockIdx.x * TT;
   if constexpr (RAGGED) {
     const RaggedDesc dsc = descs[blockIdx.z];
     M = dsc.M;
@@ -189,17 +200,17 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, con
     B += (int64_t)blockIdx.z * sB;
     C += (int64_t)blockIdx.z * sC;
   }
-  TileLoader<TA, !TRANS_A> la;  // A (row m, k): k-contiguous unless transposed
-  TileLoader<TB, TRANS_B> lb;   // B as (row n, k): k-contiguous only when transposed
-  f32x16 acc[2][2];
+  TileLoader<TA, !TRANS_A, TT> la;  // A (row m, k): k-contiguous unless transposed
+  TileLoader<TB, TRANS_B, TT> lb;   // B as (row n, k): k-contiguous only when transposed
+  f32x16 acc[BW][BW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < BW; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, g8 = (lane >> 5) * 8, lr = lane & 31;
+  const int wm = (wave >> 1) * (TT / 2), wn = (wave & 1) * (TT / 2), g8 = (lane >> 5) * 8, lr = lane & 31;
   la.load(A, lda, M, K, m0, 0, tid);
   lb.load(B, ldb, N, K, n0, 0, tid);
   la.store(As[0], tid);
@@ -213,9 +224,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, con
       la.load(A, lda, M, K, m0, (st + 1) * MK, tid);
       lb.load(B, ldb, N, K, n0, (st + 1) * MK, tid);
     }
-    f32x4 a[2][2], b[2][2];
+    f32x4 a[BW][2], b[BW][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < BW; ++i) {
       a[i][0] = *(const f32x4 *)&As[cur][wm + 32 * i + lr][g8];
       a[i][1] = *(const f32x4 *)&As[cur][wm + 32 * i + lr][g8 + 4];
       b[i][0] = *(const f32x4 *)&Bs[cur][wn + 32 * i + lr][g8];
@@ -224,9 +235,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, con
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
+      for (int bi = 0; bi < BW; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < BW; ++bj)
           acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[bi][j >> 2][j & 3], b[bj][j >> 2][j & 3],
                                                              acc[bi][bj], 0, 0, 0);
     if (more) {
@@ -237,9 +248,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, con
   }
   // D layout: lane holds column lr; register e holds row 8 (e >> 2) + 4 (lane >> 5) + (e & 3).
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < BW; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
+    for (int bj = 0; bj < BW; ++bj) {
       const int col = n0 + wn + 32 * bj + lr;
       if (col >= N) continue;
 #pragma unroll
@@ -254,12 +265,22 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K, con
     }
 }
 
+// 128 x 128 tiles, or 64 x 64 where 128 x 128 tiles would give the chip's 256 compute units fewer
+// than four workgroups each.
 template <typename TA, typename TB, bool TB_T, bool TA_T>
 static hipError_t gemm_mfma_t(hipStream_t s, const GemmArgs &g) {
-  dim3 grid((g.N + MT - 1) / MT, (g.M + MT - 1) / MT, g.batch);
-  hipLaunchKernelGGL((gemm_mfma_kernel<TA, TB, TB_T, TA_T, false>), grid, dim3(256), 0, s, g.M, g.N, g.K,
-                     (const TA *)g.A, g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (float *)g.C, g.ldc, g.sC, g.alpha,
-                     g.beta, nullptr);
+  const int64_t tiles = (int64_t)((g.N + MT - 1) / MT) * ((g.M + MT - 1) / MT) * g.batch;
+  if (tiles < 1024) {
+    dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.batch);
+    hipLaunchKernelGGL((gemm_mfma_kernel<TA, TB, TB_T, TA_T, false, 64>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                       (const TA *)g.A, g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (float *)g.C, g.ldc, g.sC, g.alpha,
+                       g.beta, nullptr);
+  } else {
+    dim3 grid((g.N + MT - 1) / MT, (g.M + MT - 1) / MT, g.batch);
+    hipLaunchKernelGGL((gemm_mfma_kernel<TA, TB, TB_T, TA_T, false>), grid, dim3(256), 0, s, g.M, g.N, g.K,
+                       (const TA *)g.A, g.lda, g.sA, (const TB *)g.B, g.ldb, g.sB, (float *)g.C, g.ldc, g.sC, g.alpha,
+                       g.beta, nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -506,12 +527,12 @@ hipError_t gemm_ragged(hipStream_t s, const GemmArgs &g, const RaggedDesc *descs
   return hipSuccess;
 }
 
-// Whether the matrix-core form applies: fp32 output, enough 128 x 128 tiles to fill the chip (or
+// Whether the matrix-core form applies: fp32 output, enough 64 x 64 tiles to fill the chip (or
 // mfma_small), and vector-aligned operands along their contiguous dimension.
 static bool mfma_ok(const GemmArgs &g) {
   if (g.tc_bf16) return false;
-  const int64_t tiles = (int64_t)((g.N + MT - 1) / MT) * ((g.M + MT - 1) / MT) * g.batch;
-  if ((tiles < 128 && !g.mfma_small) || g.K < 64) return false;
+  const int64_t tiles64 = (int64_t)((g.N + 63) / 64) * ((g.M + 63) / 64) * g.batch;
+  if ((tiles64 < 128 && !g.mfma_small) || g.K < 64) return false;
   auto fits = [](const void *p, bool is_bf16, int64_t ld, int64_t stride, int64_t contiguous_len) {
     const uintptr_t align = is_bf16 ? 8 : 16;
     return ((uintptr_t)p % align) == 0 && ld % 4 == 0 && stride % 4 == 0 && contiguous_len % 4 == 0;
