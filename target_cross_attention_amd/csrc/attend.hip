@@ -749,6 +749,308 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// bf16 MFMA kernel with 16 query rows per wave (v_mfma_f32_16x16x32_bf16) and eight waves per
+// workgroup, two per SIMD, so that one wave's score -> softmax -> PV chain runs while the other's
+// waits (d = 256: a wave then needs ~190 registers instead of ~470).
+//   scores  S^T[16 tok x 16 row] = X~[16 tok x 32 k] U^T[32 k x 16 row], two token blocks per tile
+//   update  O^T[16 f x 16 row]  += X~^T[16 f x 32 tok] P^T[32 tok x 16 row], d/16 feature blocks
+// Lane l holds query row l & 15; its score registers hold tokens 4 g + i (block 0) and 16 + 4 g + i
+// (block 1), g = l >> 4.  Those eight probabilities are directly its PV B operand if k-slot
+// (g, j) stands for token 4 g + j (j < 4) or 16 + 4 g + j - 4 (j >= 4); the A operand then takes,
+// per lane group g, rows 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 of the tile at 16 consecutive
+// features, two transposing LDS reads.  The row maximum and sum run over the four lanes of a row.
+// LDS tile layout: chunk c of token row t at position c ^ sigma16(t), the linear map of t's low four
+// bits that sends bits 0, 1, 2, 3 to 2, 4, 8, 9.  Rows are 512 bytes, so a chunk's banks are set by
+// its position mod 16.  The bank-conflict counters of layout variants on gfx950 fit a 16-byte read
+// served in four passes of 16 lanes, lanes l and l' sharing a pass when they share bit 5 and the
+// parity of bits 2..4, and an 8-byte transposing read in two passes of 32 lanes (the two halves of
+// the wave); this map gives every pass of both reads 64 distinct banks (a map that only keeps the
+// 16 rows of a row-wise read apart conflicts 2-way).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int tile_sigma16(int t) { return ((t & 7) << 1) ^ (((t >> 3) & 1) * 9); }
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of a query row) with the lane-swap
+// instructions, which stay on the vector ALU.
+__device__ __forceinline__ float quad_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void attend16_kernel(
+    const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
+    const int64_t *__restrict__ toff, int h, int chunk, const bf16 *__restrict__ Xt,
+    const bf16 *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
+    float *__restrict__ part_ms, const int64_t *__restrict__ part_base, const AttnBounds bnd) {
+  static_assert(D == 256, "16-row variant laid out for d = 256");
+  constexpr int CPR = D / 8;                      // 16-byte chunks per history row
+  constexpr int NKS = D / 32, NFB = D / 16;
+  constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
+  constexpr int LPW = INSTR / 8;                  // per wave
+  constexpr int NSL = 3, NB = 2;
+  constexpr uint32_t kRowBytes = CPR * 16, kTileBytes = 32 * kRowBytes;
+  static_assert(INSTR % 8 == 0, "tile loads split evenly over 8 waves");
+  __shared__ bf16x8 tiles[NSL][32 * CPR];
+
+  WorkItem it;
+  if (!my_item(items, n_items, it)) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lc = lane & 15, g = lane >> 4;
+  const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
+  const int64_t t0 = L0 + (int64_t)it.chunk * chunk;
+  const int64_t t1 = (t0 + chunk < L1) ? t0 + chunk : L1;
+  const int64_t T0 = toff[it.user];
+  const int R = (int)((toff[it.user + 1] - T0) * h);
+  const int64_t rowbase = T0 * h;
+  const int r0 = it.group * attn_rows_per_group(D) + wave * 16;
+  const bool wave_active = r0 < R;
+  const int myrow = r0 + lc;
+  const bool row_ok = myrow < R;
+  const int ntiles = (int)((t1 - t0 + 31) / 32);
+  STCA_CHECK(L0 >= 0 && L0 <= L1 && L1 <= bnd.total_L && t0 < t1, kDbgAttendRange);
+
+  // U row of this lane as B operands: k = 32 ks + 8 g .. + 7.
+  bf16x8 ub[NKS];
+  {
+    const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) ub[ks] = row_ok ? *reinterpret_cast<const bf16x8 *>(urow + 32 * ks) : bf16x8{};
+  }
+
+  // Tile staging: wave piece j = wave + 8 jj (1 KiB) holds, at byte 16 i, chunk (i mod CPR) ^
+  // sigma16(row) of history row 32 k + row, row = (64 j + i) / CPR (rows past the chunk's end repeat
+  // its last row; their scores are masked).
+  int frow[LPW];
+  uint32_t foff[LPW];
+#pragma unroll
+  for (int jj = 0; jj < LPW; ++jj) {
+    const int slot = (wave + 8 * jj) * 64 + lane;
+    const int row = slot / CPR, cs = slot % CPR;
+    frow[jj] = row;
+    foff[jj] = (uint32_t)(row * D + (cs ^ tile_sigma16(row)) * 8);
+  }
+  const int64_t len = t1 - t0;
+  auto fetch = [&](int k, u32x4 (&rg)[LPW]) {
+    const bf16 *tile = Xt + (t0 + 32 * (int64_t)k) * D;
+    if (32 * (int64_t)(k + 1) <= len) {
+#pragma unroll
+      for (int jj = 0; jj < LPW; ++jj) {
+        STCA_CHECK(32 * (int64_t)k + frow[jj] < len, kDbgAttendFetch);
+        rg[jj] = *reinterpret_cast<const u32x4 *>(tile + foff[jj]);
+      }
+    } else {  // partial last tile: rows past the end repeat the last row
+      const int rem = (int)(len - 32 * (int64_t)k);
+#pragma unroll
+      for (int jj = 0; jj < LPW; ++jj) {
+        const int back = frow[jj] < rem ? 0 : (frow[jj] - rem + 1) * D;
+        STCA_CHECK(rem > 0 && 32 * (int64_t)k + frow[jj] - back / D < len, kDbgAttendFetch);
+        rg[jj] = *reinterpret_cast<const u32x4 *>(tile + (foff[jj] - back));
+      }
+    }
+  };
+  auto put = [&](int b, const u32x4 (&rg)[LPW]) {
+#pragma unroll
+    for (int jj = 0; jj < LPW; ++jj) tiles[b][(wave + 8 * jj) * 64 + lane] = __builtin_bit_cast(bf16x8, rg[jj]);
+  };
+  auto sync = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Register set b holds tile j >= 2 with (j - 2) mod NB = b between its fetch and its put.  Every
+  // step fetches (past the last tile it re-reads the last one, which is never consumed), so the
+  // compiler sees the same loads in flight on every path and each put waits for the older set only.
+  u32x4 rgb[NB][LPW];
+  fetch(0, rgb[0]);
+  put(0, rgb[0]);
+  if (1 < ntiles) {
+    fetch(1, rgb[0]);
+    put(1, rgb[0]);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) fetch(min(2 + b, ntiles - 1), rgb[b]);
+
+  // LDS byte offsets.  Scores: token row 16 tb + lc, chunk 4 ks + g at position
+  // (4 ks + g) ^ sigma = 4 ks ^ (g ^ sigma): offset row + ((64 ks) ^ (16 x)).  PV: lane 4 j + q of
+  // group g reads token 16 h + 4 g + j (sigma = 2 (4 (g & 1) + j) + (g >> 1), the same for both h),
+  // features 16 fb + 4 q .. + 3: chunk 2 fb + (q >> 1) at position 2 fb ^ y, y = (q >> 1) ^ sigma,
+  // i.e. 2 ((fb & 8) | ((fb & 7) ^ (y >> 1))) + (y & 1); one base per fb & 7.
+  const STCA_LDS char *lds = (const STCA_LDS char *)&tiles[0][0];
+  uint32_t srow[2], sx[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int t = 16 * tb + lc;
+    srow[tb] = (uint32_t)t * kRowBytes;
+    sx[tb] = (uint32_t)(16 * (g ^ tile_sigma16(t)));
+  }
+  uint32_t pvb[8];
+  {
+    const int j = lc >> 2, q = lc & 3;
+    const int sig = tile_sigma16(4 * g + j);
+    const int y = (q >> 1) ^ sig;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      pvb[m] = (uint32_t)((4 * g + j) * kRowBytes + 32 * (m ^ (y >> 1)) + 16 * (y & 1) + 8 * (q & 1));
+  }
+
+  f32x4 oacc[NFB];
+#pragma unroll
+  for (int fb = 0; fb < NFB; ++fb) oacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, s_run = 0.f;
+
+  // Rescale (a row maximum outgrew the slack; the first tile always does), then the probabilities of
+  // tile k against the new maximum.
+  auto rescale_probs = [&](const f32x4 (&sc)[2], float mx, bf16x8 &pb, float &psum) {
+    const float m_new = fmaxf(m_run, mx);
+    const float sf = fast_exp2(m_run - m_new);
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) oacc[fb] *= sf;
+    s_run *= sf;
+    m_run = m_new;
+    psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(sc[e >> 2][e & 3] - m_run);
+      pb[e] = f32_to_bf16(p);
+      psum += p;
+    }
+  };
+  auto mask = [&](int k, f32x4 (&sc)[2]) {
+    const int64_t remk = len - 32 * (int64_t)k;
+    if (remk < 32) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * tb + 4 * g + i >= remk) sc[tb][i] = -INFINITY;
+    }
+  };
+  // Scores of tile k (16 MFMAs) into sc, with no other work (the first tile).
+  constexpr int SA = 3;
+  auto frag_at = [&](int k, int i) {  // i = 2 ks + tb
+    const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
+    const int ks = i >> 1, tb = i & 1;
+    return *(const STCA_LDS bf16x8 *)(lds + toff + srow[tb] + (((uint32_t)(64 * ks)) ^ sx[tb]));
+  };
+  // PV product of tile k: the transposed operands of feature block fb + PA are read while block fb
+  // multiplies.
+  constexpr int PA = 3;
+  auto pv = [&](int k, const bf16x8 &pb) {
+    const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
+    auto xfrag = [&](int fb) {
+      const uint32_t o = toff + pvb[fb & 7] + 256 * (fb >> 3);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + o));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + o + 16 * kRowBytes));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 xr[PA + 1];
+#pragma unroll
+    for (int fb = 0; fb < PA; ++fb) xr[fb] = xfrag(fb);
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) {
+      if (fb + PA < NFB) xr[(fb + PA) % (PA + 1)] = xfrag(fb + PA);
+      oacc[fb] = mfma16x16x32(xr[fb % (PA + 1)], pb, oacc[fb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Step k: the scores of tile k + 1 on the matrix cores while the vector ALU turns tile k's scores
+  // (from step k - 1) into probabilities, one MFMA and one probability per group in an order pinned
+  // with sched_barrier; then the PV product of tile k.  The probabilities are taken against the
+  // running maximum before the tile's own maximum is known; if that maximum outgrew the slack they
+  // are recomputed after the rescale (exact either way).  Score operand reads run SA fragments
+  // ahead.  Register set BI holds the staged tile and names the score buffers (tile k's in
+  // sc2[BI], tile k + 1's into sc2[BI ^ 1]).
+  f32x4 sc2[2][2];
+  auto step = [&](int k, auto BI) {
+    constexpr int b = decltype(BI)::value;
+    sync();  // tile k+1 is in LDS; tile k-1's slot is free
+    // Unconditional, like the fetch: past the last tile this writes a tile no step reads into the
+    // free slot, and the compiler's count of loads in flight stays the same on every path.
+    put((k + 2) % NSL, rgb[b]);
+    fetch(min(k + 2 + NB, ntiles - 1), rgb[b]);
+    if (!wave_active) return;
+    f32x4(&cur)[2] = sc2[b];
+    f32x4(&nxt)[2] = sc2[b ^ 1];
+    mask(k, cur);
+    bf16x8 pb;
+    float psum = 0.f, mx = -INFINITY;
+    auto element = [&](int e) {
+      const float v = cur[e >> 2][e & 3];
+      const float p = fast_exp2(v - m_run);
+      pb[e] = f32_to_bf16(p);
+      psum += p;
+      mx = fmaxf(mx, v);
+    };
+    if (k + 1 < ntiles) {
+      bf16x8 fr[SA + 1];
+#pragma unroll
+      for (int i = 0; i < SA; ++i) fr[i] = frag_at(k + 1, i);
+      nxt[0] = nxt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2 * NKS; ++i) {
+        if (i + SA < 2 * NKS) fr[(i + SA) % (SA + 1)] = frag_at(k + 1, i + SA);
+        nxt[i & 1] = mfma16x16x32(fr[i % (SA + 1)], ub[i >> 1], nxt[i & 1]);
+        if (i < 8) element(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) element(e);
+    }
+    mx = quad_max(mx);
+    if (wave_any(mx > m_run + kLazy)) rescale_probs(cur, mx, pb, psum);
+    s_run += psum;
+    pv(k, pb);
+  };
+  sync();
+  if (wave_active) {  // scores of the first tile
+    sc2[0][0] = sc2[0][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2 * NKS; ++i) sc2[0][i & 1] = mfma16x16x32(frag_at(0, i), ub[i >> 1], sc2[0][i & 1]);
+  }
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  int k = 0;
+  for (; k + 1 < ntiles; k += 2) {  // the back edge follows a step on register set 1 only
+    step(k, B0{});
+    step(k + 1, B1{});
+  }
+  if (k < ntiles) step(k, B0{});
+
+  if (!wave_active) return;
+  const float s_tot = quad_sum(s_run);
+  if (!row_ok) return;
+  if (it.n_chunks == 1) {
+    const float inv = 1.0f / s_tot;
+    STCA_CHECK(rowbase + myrow < bnd.rows, kDbgAttendOut);
+    float *dst = abar + (rowbase + myrow) * D + 4 * g;
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) *reinterpret_cast<f32x4 *>(dst + 16 * fb) = oacc[fb] * inv;
+  } else {
+    const int64_t p = part_base[it.user] + (int64_t)it.chunk * R + myrow;
+    STCA_CHECK(p >= 0 && p < bnd.part_rows, kDbgAttendPart);
+    float *dst = part_A + p * D + 4 * g;
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) *reinterpret_cast<f32x4 *>(dst + 16 * fb) = oacc[fb];
+    if (g == 0) {
+      part_ms[2 * p] = m_run;
+      part_ms[2 * p + 1] = s_tot;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // fp32 debug kernel (vector ALU): one wave per query row, tokens streamed four at a time.
 // ------------------------------------------------------------------------------------------
 template <int D>
@@ -827,13 +1129,22 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
   }
 }
 
+// The 16-row kernel at d = 256 where users hold fewer than 96 query rows on average: a 128-row work
+// item then leaves fewer rows of a 32-row wave block idle, and it measured faster there (ragged
+// batch, ~49 rows per user: 0.172 against 0.200 ms per launch); at 128 rows per user (dense10k) the
+// two measured within noise of each other, and the 32-row kernel is kept.
+static bool use_rows16(const AttnPlan &p) { return p.n_users > 0 && p.total_T * p.h < 96 * (int64_t)p.n_users; }
+
 template <int D>
 static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_path, const int64_t *hoff,
                                  const int64_t *toff, const void *Xt, const void *U, float *abar,
                                  const AttnBuffers &b) {
   const dim3 grid((unsigned)p.max_items), block(256);
   const AttnBounds bnd{p.total_L, p.total_T * p.h, p.max_part_rows};
-  if (bf16_path)
+  if (bf16_path && D == 256 && use_rows16(p))
+    hipLaunchKernelGGL((attend16_kernel<256>), grid, dim3(512), 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
+                       (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
+  else if (bf16_path)
     hipLaunchKernelGGL((attend_mfma_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
                        (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
   else
