@@ -373,8 +373,8 @@ def cpu_baseline_backward(cfg, W, target_s: float = 12.0, max_users: int = 64):
 
 
 # Kernels whose HBM traffic the bench line reports: role -> (name fragment, source files).
-TRAFFIC_KERNELS = {"encode": ("encode_", ["encode_mfma.hip", "device_common.hpp"]),
-                   "attend": ("attend_mfma_kernel", ["attend.hip", "device_common.hpp"])}
+TRAFFIC_KERNELS = {"encode": (("encode_",), ["encode_mfma.hip", "device_common.hpp"]),
+                   "attend": (("attend_mfma_kernel", "attend16_kernel"), ["attend.hip", "device_common.hpp"])}
 
 
 def _counter_rows(d: str, counter: str):
@@ -431,8 +431,8 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, cfetch_dir: s
     rec["_note"] = ("HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE passes scaled by a device copy of "
                     "known size (bench.py --traffic-summary); valid only while the kernel source hash matches")
     entry = rec.setdefault(workload, {})
-    for role, (frag, files) in TRAFFIC_KERNELS.items():
-        cands = [k for k in fetch if frag in k]
+    for role, (frags, files) in TRAFFIC_KERNELS.items():
+        cands = [k for k in fetch if any(f in k for f in frags)]
         if not cands:
             continue
         k = max(cands, key=lambda k: fetch[k][1])
