@@ -314,8 +314,9 @@ def bench_backward(a, cfg, dev):
         "value": L * a.steps / dt, "unit": "history-tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": dt * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if mixed else "f32",
-        "precision": ("mixed: bf16 operands, fp32 accumulation, LayerNorm and softmax statistics in fp32 "
-                      "(encode derivative); fp32 attention derivative" if mixed else "fp32 throughout"),
+        "precision": ("mixed: bf16 operands, fp32 accumulation (encode and attention derivatives); LayerNorm "
+                      "and softmax statistics, weight-gradient sums and per-target steps in fp32" if mixed
+                      else "fp32 throughout"),
         "data": "synthetic (seeded; training-shaped ragged batch)",
         "config": {"workload": cfg.description, "key": cfg.key, "users": db.inp.n_users, "history_tokens": L,
                    "targets": T, "storage": cfg.dtype,
@@ -329,10 +330,12 @@ def bench_backward(a, cfg, dev):
                      "frac": achieved / peak, "traffic": None,
                      "algorithmic_flops_per_launch": enc_flops, "avg_launch_ms": enc_avg_s * 1e3,
                      "launches": enc_n},
-        "attention_backward": {"kernels": "ragged per-user fp32 matrix-core products + softmax/dS row passes",
+        "attention_backward": {"kernels": ("ragged per-user bf16 matrix-core products (fp32 operands rounded as "
+                                           "they are staged) + softmax/dS row passes" if mixed else
+                                           "ragged per-user fp32 matrix-core products + softmax/dS row passes"),
                                "ms_per_layer": att_layer_ms, "pairs_per_layer": pairs, "bound": "mfma",
                                "achieved": 14.0 * d * pairs / (att_layer_ms / 1e3) / 1e12,
-                               "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"},
+                               "peak": PEAK_BF16_TFLOPS if mixed else PEAK_FP32_TFLOPS, "unit": "TFLOP/s"},
         "phase_ms_per_step": {k: v[0] / a.steps for k, v in phases.items() if k.startswith("bwd")},
     }
     if not a.no_cpu_baseline:
