@@ -751,7 +751,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attend_mfma_kernel(
 // ------------------------------------------------------------------------------------------
 // bf16 MFMA kernel with 16 query rows per wave (v_mfma_f32_16x16x32_bf16) and eight waves per
 // workgroup, two per SIMD, so that one wave's score -> softmax -> PV chain runs while the other's
-// waits (d = 256: a wave then needs ~190 registers instead of ~470).
+// waits (a wave then needs ~220 registers at d = 256 instead of ~470; at d = 512 two waves share 16
+// rows, each with half of d, as in the 32-row kernel's pairs).
 //   scores  S^T[16 tok x 16 row] = X~[16 tok x 32 k] U^T[32 k x 16 row], two token blocks per tile
 //   update  O^T[16 f x 16 row]  += X~^T[16 f x 32 tok] P^T[32 tok x 16 row], d/16 feature blocks
 // Lane l holds query row l & 15; its score registers hold tokens 4 g + i (block 0) and 16 + 4 g + i
@@ -792,15 +793,20 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     const int64_t *__restrict__ toff, int h, int chunk, const bf16 *__restrict__ Xt,
     const bf16 *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
     float *__restrict__ part_ms, const int64_t *__restrict__ part_base, const AttnBounds bnd) {
-  static_assert(D == 256, "16-row variant laid out for d = 256");
+  static_assert(D == 256 || D == 512, "16-row variant laid out for d = 256 and 512");
   constexpr int CPR = D / 8;                      // 16-byte chunks per history row
-  constexpr int NKS = D / 32, NFB = D / 16;
+  // At d = 512 the two waves w, w ^ 1 share 16 rows: each scores over its half of d and keeps half
+  // of the output features, and the pair adds the partial score tiles through LDS.
+  constexpr int FH = attn_feature_halves(D);
+  constexpr int NKW = D / 32 / FH, NFBW = D / 16 / FH;  // score k-steps, output blocks per wave
   constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
   constexpr int LPW = INSTR / 8;                  // per wave
   constexpr int NSL = 3, NB = 2;
   constexpr uint32_t kRowBytes = CPR * 16, kTileBytes = 32 * kRowBytes;
   static_assert(INSTR % 8 == 0, "tile loads split evenly over 8 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
+  // Partial score tiles of the pairs (FH = 2): [tile parity][wave][token block][lane].
+  __shared__ f32x4 exch[FH > 1 ? 2 : 1][FH > 1 ? 8 : 1][2][64];
 
   WorkItem it;
   if (!my_item(items, n_items, it)) return;
@@ -812,19 +818,20 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   const int64_t T0 = toff[it.user];
   const int R = (int)((toff[it.user + 1] - T0) * h);
   const int64_t rowbase = T0 * h;
-  const int r0 = it.group * attn_rows_per_group(D) + wave * 16;
+  const int fh = wave % FH;
+  const int r0 = it.group * attn_rows_per_group(D) + (wave / FH) * 16;
   const bool wave_active = r0 < R;
   const int myrow = r0 + lc;
   const bool row_ok = myrow < R;
   const int ntiles = (int)((t1 - t0 + 31) / 32);
   STCA_CHECK(L0 >= 0 && L0 <= L1 && L1 <= bnd.total_L && t0 < t1, kDbgAttendRange);
 
-  // U row of this lane as B operands: k = 32 ks + 8 g .. + 7.
-  bf16x8 ub[NKS];
+  // U row of this lane as B operands: k = (D / FH) fh + 32 ks + 8 g .. + 7.
+  bf16x8 ub[NKW];
   {
-    const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + 8 * g;
+    const bf16 *urow = U + (rowbase + (row_ok ? myrow : 0)) * D + (D / FH) * fh + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) ub[ks] = row_ok ? *reinterpret_cast<const bf16x8 *>(urow + 32 * ks) : bf16x8{};
+    for (int ks = 0; ks < NKW; ++ks) ub[ks] = row_ok ? *reinterpret_cast<const bf16x8 *>(urow + 32 * ks) : bf16x8{};
   }
 
   // Tile staging: wave piece j = wave + 8 jj (1 KiB) holds, at byte 16 i, chunk (i mod CPR) ^
@@ -903,9 +910,9 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
       pvb[m] = (uint32_t)((4 * g + j) * kRowBytes + 32 * (m ^ (y >> 1)) + 16 * (y & 1) + 8 * (q & 1));
   }
 
-  f32x4 oacc[NFB];
+  f32x4 oacc[NFBW];
 #pragma unroll
-  for (int fb = 0; fb < NFB; ++fb) oacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int fb = 0; fb < NFBW; ++fb) oacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, s_run = 0.f;
 
   // Rescale (a row maximum outgrew the slack; the first tile always does), then the probabilities of
@@ -914,7 +921,7 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     const float m_new = fmaxf(m_run, mx);
     const float sf = fast_exp2(m_run - m_new);
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) oacc[fb] *= sf;
+    for (int fb = 0; fb < NFBW; ++fb) oacc[fb] *= sf;
     s_run *= sf;
     m_run = m_new;
     psum = 0.f;
@@ -935,20 +942,36 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
           if (16 * tb + 4 * g + i >= remk) sc[tb][i] = -INFINITY;
     }
   };
-  // Scores of tile k (16 MFMAs) into sc, with no other work (the first tile).
+  // Score operand i = 2 ks + tb of tile k: this wave's half of d starts (D / FH) fh features into a
+  // row, a multiple of 16 chunks, which the swizzle (low four bits of the chunk index) leaves alone.
   constexpr int SA = 3;
-  auto frag_at = [&](int k, int i) {  // i = 2 ks + tb
+  const uint32_t hofs = (uint32_t)(fh * (D / FH) * 2);
+  auto frag_at = [&](int k, int i) {
     const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
     const int ks = i >> 1, tb = i & 1;
-    return *(const STCA_LDS bf16x8 *)(lds + toff + srow[tb] + (((uint32_t)(64 * ks)) ^ sx[tb]));
+    return *(const STCA_LDS bf16x8 *)(lds + toff + srow[tb] + hofs + (((uint32_t)(64 * ks)) ^ sx[tb]));
+  };
+  // Pairs: publish this wave's partial score tile of tile k; after the next workgroup barrier the
+  // partner adds it (both then hold bit-identical scores, a + b = b + a, and take the same decisions).
+  auto publish = [&](int k, const f32x4 (&part)[2]) {
+    if constexpr (FH > 1) {
+      exch[k & 1][wave][0][lane] = part[0];
+      exch[k & 1][wave][1][lane] = part[1];
+    }
+  };
+  auto add_partner = [&](int k, f32x4 (&sc)[2]) {
+    if constexpr (FH > 1) {
+      sc[0] += exch[k & 1][wave ^ 1][0][lane];
+      sc[1] += exch[k & 1][wave ^ 1][1][lane];
+    }
   };
   // PV product of tile k: the transposed operands of feature block fb + PA are read while block fb
   // multiplies.
   constexpr int PA = 3;
   auto pv = [&](int k, const bf16x8 &pb) {
     const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
-    auto xfrag = [&](int fb) {
-      const uint32_t o = toff + pvb[fb & 7] + 256 * (fb >> 3);
+    auto xfrag = [&](int fb) {  // this wave's feature block fb: global block (NFBW fh + fb)
+      const uint32_t o = toff + pvb[fb & 7] + 256 * (fb >> 3) + hofs;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + o));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + o + 16 * kRowBytes));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -957,8 +980,8 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
 #pragma unroll
     for (int fb = 0; fb < PA; ++fb) xr[fb] = xfrag(fb);
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) {
-      if (fb + PA < NFB) xr[(fb + PA) % (PA + 1)] = xfrag(fb + PA);
+    for (int fb = 0; fb < NFBW; ++fb) {
+      if (fb + PA < NFBW) xr[(fb + PA) % (PA + 1)] = xfrag(fb + PA);
       oacc[fb] = mfma16x16x32(xr[fb % (PA + 1)], pb, oacc[fb]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -981,6 +1004,7 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     if (!wave_active) return;
     f32x4(&cur)[2] = sc2[b];
     f32x4(&nxt)[2] = sc2[b ^ 1];
+    add_partner(k, cur);
     mask(k, cur);
     bf16x8 pb;
     float psum = 0.f, mx = -INFINITY;
@@ -998,12 +1022,13 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
       nxt[0] = nxt[1] = f32x4{0.f, 0.f, 0.f, 0.f};
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2 * NKS; ++i) {
-        if (i + SA < 2 * NKS) fr[(i + SA) % (SA + 1)] = frag_at(k + 1, i + SA);
+      for (int i = 0; i < 2 * NKW; ++i) {
+        if (i + SA < 2 * NKW) fr[(i + SA) % (SA + 1)] = frag_at(k + 1, i + SA);
         nxt[i & 1] = mfma16x16x32(fr[i % (SA + 1)], ub[i >> 1], nxt[i & 1]);
         if (i < 8) element(i);
         __builtin_amdgcn_sched_barrier(0);
       }
+      publish(k + 1, nxt);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) element(e);
@@ -1014,10 +1039,11 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     pv(k, pb);
   };
   sync();
-  if (wave_active) {  // scores of the first tile
+  if (wave_active) {  // scores of the first tile (step 0 adds the partner's half after its barrier)
     sc2[0][0] = sc2[0][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 2 * NKS; ++i) sc2[0][i & 1] = mfma16x16x32(frag_at(0, i), ub[i >> 1], sc2[0][i & 1]);
+    for (int i = 0; i < 2 * NKW; ++i) sc2[0][i & 1] = mfma16x16x32(frag_at(0, i), ub[i >> 1], sc2[0][i & 1]);
+    publish(0, sc2[0]);
   }
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -1034,16 +1060,16 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   if (it.n_chunks == 1) {
     const float inv = 1.0f / s_tot;
     STCA_CHECK(rowbase + myrow < bnd.rows, kDbgAttendOut);
-    float *dst = abar + (rowbase + myrow) * D + 4 * g;
+    float *dst = abar + (rowbase + myrow) * D + (D / FH) * fh + 4 * g;
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) *reinterpret_cast<f32x4 *>(dst + 16 * fb) = oacc[fb] * inv;
+    for (int fb = 0; fb < NFBW; ++fb) *reinterpret_cast<f32x4 *>(dst + 16 * fb) = oacc[fb] * inv;
   } else {
     const int64_t p = part_base[it.user] + (int64_t)it.chunk * R + myrow;
     STCA_CHECK(p >= 0 && p < bnd.part_rows, kDbgAttendPart);
-    float *dst = part_A + p * D + 4 * g;
+    float *dst = part_A + p * D + (D / FH) * fh + 4 * g;
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) *reinterpret_cast<f32x4 *>(dst + 16 * fb) = oacc[fb];
-    if (g == 0) {
+    for (int fb = 0; fb < NFBW; ++fb) *reinterpret_cast<f32x4 *>(dst + 16 * fb) = oacc[fb];
+    if (g == 0 && fh == 0) {
       part_ms[2 * p] = m_run;
       part_ms[2 * p + 1] = s_tot;
     }
@@ -1129,10 +1155,11 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
   }
 }
 
-// The 16-row kernel at d = 256 where users hold fewer than 96 query rows on average: a 128-row work
-// item then leaves fewer rows of a 32-row wave block idle, and it measured faster there (ragged
-// batch, ~49 rows per user: 0.172 against 0.200 ms per launch); at 128 rows per user (dense10k) the
-// two measured within noise of each other, and the 32-row kernel is kept.
+// The 16-row kernel at d = 512 always (stress20k: 209.8 against 214.5 ms per forward), and at d = 256
+// where users hold fewer than 96 query rows on average: a 128-row work item then leaves fewer rows of
+// a 32-row wave block idle, and it measured faster there (ragged batch, ~49 rows per user: 0.172
+// against 0.200 ms per launch); at 128 rows per user (dense10k) the two measured within noise of
+// each other, and the 32-row kernel is kept.
 static bool use_rows16(const AttnPlan &p) { return p.n_users > 0 && p.total_T * p.h < 96 * (int64_t)p.n_users; }
 
 template <int D>
@@ -1141,9 +1168,10 @@ static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_pat
                                  const AttnBuffers &b) {
   const dim3 grid((unsigned)p.max_items), block(256);
   const AttnBounds bnd{p.total_L, p.total_T * p.h, p.max_part_rows};
-  if (bf16_path && D == 256 && use_rows16(p))
-    hipLaunchKernelGGL((attend16_kernel<256>), grid, dim3(512), 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
-                       (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
+  if (bf16_path && ((D == 256 && use_rows16(p)) || D == 512))
+    hipLaunchKernelGGL((attend16_kernel<D == 512 ? 512 : 256>), grid, dim3(512), 0, s, b.items, b.n_items, hoff,
+                       toff, p.h, p.chunk, (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms,
+                       b.part_base, bnd);
   else if (bf16_path)
     hipLaunchKernelGGL((attend_mfma_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
                        (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
