@@ -185,7 +185,10 @@ __device__ __forceinline__ bool my_item(const WorkItem *__restrict__ items, cons
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 MFMA kernel (v_mfma_f32_32x32x16_bf16 for both contractions).
+// bf16 MFMA kernel with 32 query rows per wave (v_mfma_f32_32x32x16_bf16 for both contractions).
+// attend_split runs it at d = 64 and 128; d = 256 and 512 run attend16_kernel below, which measured
+// faster there.  The kernel stays written for every width (at d = 512 with its two-wave score split),
+// which is where the 16-row kernel's pairs come from.
 //   scores  S^T[tok x row] = X~_tile[tok x d] U^T[d x row]      (A from LDS, B = U in registers)
 //   update  O^T[d x row]  += X~_tile^T[d x tok] P^T[tok x row]  (A from LDS, B = P in registers)
 // The accumulator layout of S^T is, per lane, one query row and 16 tokens; taking the
@@ -801,7 +804,11 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   constexpr int NKW = D / 32 / FH, NFBW = D / 16 / FH;  // score k-steps, output blocks per wave
   constexpr int INSTR = 32 * D * 2 / 1024;        // 1 KiB wave loads per 32-token tile
   constexpr int LPW = INSTR / 8;                  // per wave
-  constexpr int NSL = 3, NB = 2;
+  // Register sets of staged tiles: NB tiles in flight from HBM per wave (four at d = 256, where the
+  // staging takes 8 registers a set; two at d = 512, where the kernel is at 256 registers).  Even, so
+  // that step k's score buffers sc2[k & 1] follow from its set index.
+  constexpr int NSL = 3, NB = D > 256 ? 2 : 4;
+  static_assert(NB % 2 == 0, "score buffers alternate with the register sets");
   constexpr uint32_t kRowBytes = CPR * 16, kTileBytes = 32 * kRowBytes;
   static_assert(INSTR % 8 == 0, "tile loads split evenly over 8 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
@@ -1002,8 +1009,8 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     put((k + 2) % NSL, rgb[b]);
     fetch(min(k + 2 + NB, ntiles - 1), rgb[b]);
     if (!wave_active) return;
-    f32x4(&cur)[2] = sc2[b];
-    f32x4(&nxt)[2] = sc2[b ^ 1];
+    f32x4(&cur)[2] = sc2[b & 1];
+    f32x4(&nxt)[2] = sc2[(b & 1) ^ 1];
     add_partner(k, cur);
     mask(k, cur);
     bf16x8 pb;
@@ -1047,12 +1054,19 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   }
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, (NB > 2 ? 2 : 0)>;
+  using B3 = std::integral_constant<int, (NB > 3 ? 3 : 0)>;
   int k = 0;
-  for (; k + 1 < ntiles; k += 2) {  // the back edge follows a step on register set 1 only
+  for (; k + NB - 1 < ntiles; k += NB) {  // the back edge follows a step on the last register set only
     step(k, B0{});
     step(k + 1, B1{});
+    if constexpr (NB > 2) step(k + 2, B2{});
+    if constexpr (NB > 3) step(k + 3, B3{});
   }
   if (k < ntiles) step(k, B0{});
+  if (k + 1 < ntiles) step(k + 1, B1{});
+  if constexpr (NB > 2)
+    if (k + 2 < ntiles) step(k + 2, B2{});
 
   if (!wave_active) return;
   const float s_tot = quad_sum(s_run);
@@ -1155,12 +1169,9 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
   }
 }
 
-// The 16-row kernel at d = 512 always (stress20k: 209.8 against 214.5 ms per forward), and at d = 256
-// where users hold fewer than 96 query rows on average: a 128-row work item then leaves fewer rows of
-// a 32-row wave block idle, and it measured faster there (ragged batch, ~49 rows per user: 0.172
-// against 0.200 ms per launch); at 128 rows per user (dense10k) the two measured within noise of
-// each other, and the 32-row kernel is kept.
-static bool use_rows16(const AttnPlan &p) { return p.n_users > 0 && p.total_T * p.h < 96 * (int64_t)p.n_users; }
+// The 16-row kernel serves d = 256 and 512 (measured against the 32-row kernel in same-process A/Bs of
+// whole forwards: stress20k 209.8 against 214.5 ms, dense10k 51.14 against 51.33 ms, ragged attention
+// 0.172 against 0.200 ms per launch); d = 64 and 128 keep the 32-row kernel.
 
 template <int D>
 static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_path, const int64_t *hoff,
@@ -1168,13 +1179,14 @@ static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_pat
                                  const AttnBuffers &b) {
   const dim3 grid((unsigned)p.max_items), block(256);
   const AttnBounds bnd{p.total_L, p.total_T * p.h, p.max_part_rows};
-  if (bf16_path && ((D == 256 && use_rows16(p)) || D == 512))
-    hipLaunchKernelGGL((attend16_kernel<D == 512 ? 512 : 256>), grid, dim3(512), 0, s, b.items, b.n_items, hoff,
-                       toff, p.h, p.chunk, (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms,
-                       b.part_base, bnd);
-  else if (bf16_path)
-    hipLaunchKernelGGL((attend_mfma_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
-                       (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
+  if (bf16_path) {
+    if constexpr (D >= 256)
+      hipLaunchKernelGGL((attend16_kernel<D>), grid, dim3(512), 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
+                         (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
+    else
+      hipLaunchKernelGGL((attend_mfma_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
+                         (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
+  }
   else
     hipLaunchKernelGGL((attend_f32_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
                        (const float *)Xt, (const float *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);

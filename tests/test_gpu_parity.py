@@ -150,8 +150,8 @@ def test_attend_ragged_split(B, dtype, chunk, d, h):
     """Ragged lengths (1 .. ~1500, not multiples of 32), 1..several targets, several chunk sizes
     so users span one or many split-L chunks and the combine step runs.  Chunks of 64 and 96
     tokens give work items of 1, 2 and 3 tiles: an odd or even count, shorter than the kernel's
-    tile prefetch distance.  At d = 256 these batches (about 19 query rows per user) run the
-    16-row kernel; test_attend_many_rows (296 rows per user) runs the 32-row one."""
+    tile prefetch distance.  At d = 256 and 512 these batches run the 16-row kernel
+    (attend16_kernel), at d = 64 and 128 the 32-row one."""
     cfg = SI.scaled(SI.get_config("ragged"), d=d, h=h, M=2, r=2, dtype=dtype)
     announce("attend", d, dtype, "chunk", chunk)
     W = SI.make_weights(cfg)
