@@ -1091,18 +1091,28 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// fp32 debug kernel (vector ALU): one wave per query row, tokens streamed four at a time.
+// fp32 kernel (vector ALU): 16 waves per work item, one wave per query row, the history taken 64 tokens
+// at a time.
+//   * scores: one token per lane, the lane's dot product of its token row with u (u staged in LDS and
+//     read as a broadcast), so a block's maximum costs one wave reduction instead of one per token;
+//   * weighted sum: one output feature per lane (E = D / 64 of them), each token's probability read
+//     from the lane that scored it; token rows past the chunk are clamped to its last row and carry
+//     probability 0.
 // ------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attend_f32_kernel(
+__global__ __launch_bounds__(1024) void attend_f32_kernel(
     const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
     const int64_t *__restrict__ toff, int h, int chunk, const float *__restrict__ Xt,
     const float *__restrict__ U, float *__restrict__ abar, float *__restrict__ part_A,
     float *__restrict__ part_ms, const int64_t *__restrict__ part_base, const AttnBounds bnd) {
   constexpr int E = D / 64;
+  constexpr int UJ = E >= 4 ? 8 : 16;  // tokens whose rows are in flight at once in the weighted sum
+  constexpr int W = 16;
+  __shared__ f32x4 us[W][D / 4];
   WorkItem it;
   if (!my_item(items, n_items, it)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t L0 = hoff[it.user], L1 = hoff[it.user + 1];
   const int64_t t0 = L0 + (int64_t)it.chunk * chunk;
   const int64_t t1 = (t0 + chunk < L1) ? t0 + chunk : L1;
@@ -1112,45 +1122,55 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(
   const int RG = attn_rows_per_group(D);
   const int rend = (it.group + 1) * RG < R ? (it.group + 1) * RG : R;
   STCA_CHECK(L0 >= 0 && L0 <= L1 && L1 <= bnd.total_L && t0 < t1, kDbgAttendRange);
+  float *ul = reinterpret_cast<float *>(us[wave]);
 
-  for (int r = it.group * RG + wave; r < rend; r += 4) {
-    float u[E], a[E];
+  for (int r = it.group * RG + wave; r < rend; r += W) {
+    // The wave's LDS accesses complete in issue order, so the staged row is seen by every lane's reads,
+    // and the previous row's reads are done before it is overwritten.
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      u[e] = U[(rowbase + r) * D + lane + 64 * e];
-      a[e] = 0.f;
-    }
-    float m = -INFINITY, s = 0.f;
-    for (int64_t p = t0; p < t1; p += 4) {
-      float x[4][E], dot[4];
+    for (int e = 0; e < E; ++e) ul[lane + 64 * e] = U[(rowbase + r) * D + lane + 64 * e];
+    float a[E];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t pj = (p + j < t1) ? p + j : t1 - 1;
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          x[j][e] = Xt[pj * D + lane + 64 * e];
-          acc = fmaf(u[e], x[j][e], acc);
-        }
-        dot[j] = acc;
+    for (int e = 0; e < E; ++e) a[e] = 0.f;
+    float m = -INFINITY, sl = 0.f;
+    for (int64_t p = t0; p < t1; p += 64) {
+      const int64_t key = p + lane;
+      const int64_t kr = key < t1 ? key : t1 - 1;
+      const f32x4 *xr = reinterpret_cast<const f32x4 *>(Xt + kr * D);
+      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll 16
+      for (int f = 0; f < D / 4; ++f) {
+        const f32x4 x = xr[f], u = us[wave][f];
+        d0 = fmaf(x[0], u[0], d0);
+        d1 = fmaf(x[1], u[1], d1);
+        d2 = fmaf(x[2], u[2], d2);
+        d3 = fmaf(x[3], u[3], d3);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dot[j] = (p + j < t1) ? wave_sum(dot[j]) : -INFINITY;
-      const float mx = fmaxf(fmaxf(dot[0], dot[1]), fmaxf(dot[2], dot[3]));
-      const float m_new = fmaxf(m, mx);
+      const float sc = key < t1 ? (d0 + d1) + (d2 + d3) : -INFINITY;
+      const float m_new = fmaxf(m, wave_max(sc));
       const float sf = exp2f(m - m_new);
-      s *= sf;
+      const float pj = exp2f(sc - m_new);
+      sl = fmaf(sl, sf, pj);
 #pragma unroll
       for (int e = 0; e < E; ++e) a[e] *= sf;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float w = exp2f(dot[j] - m_new);
-        s += w;
-#pragma unroll
-        for (int e = 0; e < E; ++e) a[e] = fmaf(w, x[j][e], a[e]);
-      }
       m = m_new;
+      const int nk = (int)(t1 - p < 64 ? t1 - p : 64);
+      for (int jb = 0; jb < nk; jb += UJ) {
+        float x[UJ][E], w[UJ];
+#pragma unroll
+        for (int jj = 0; jj < UJ; ++jj) {
+          const int64_t row = (p + jb + jj < t1) ? p + jb + jj : t1 - 1;
+          w[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jb + jj));
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[jj][e] = Xt[row * D + lane + 64 * e];
+        }
+#pragma unroll
+        for (int jj = 0; jj < UJ; ++jj)
+#pragma unroll
+          for (int e = 0; e < E; ++e) a[e] = fmaf(w[jj], x[jj][e], a[e]);
+      }
     }
+    const float s = wave_sum(sl);
     if (it.n_chunks == 1) {
       const float inv = 1.0f / s;
       STCA_CHECK(rowbase + r < bnd.rows, kDbgAttendOut);
@@ -1188,7 +1208,7 @@ static hipError_t attend_split_d(hipStream_t s, const AttnPlan &p, bool bf16_pat
                          (const bf16 *)Xt, (const bf16 *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
   }
   else
-    hipLaunchKernelGGL((attend_f32_kernel<D>), grid, block, 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
+    hipLaunchKernelGGL((attend_f32_kernel<D>), grid, dim3(1024), 0, s, b.items, b.n_items, hoff, toff, p.h, p.chunk,
                        (const float *)Xt, (const float *)U, abar, b.part_A, b.part_ms, b.part_base, bnd);
   return hipGetLastError();
 }
