@@ -853,21 +853,23 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     frow[jj] = row;
     foff[jj] = (uint32_t)(row * D + (cs ^ tile_sigma16(row)) * 8);
   }
-  const int64_t len = t1 - t0;
+  // The chunk length (at most the chunk size, an int) is uniform; read it into a scalar register so
+  // that the tile tests below are scalar branches on 32-bit values.
+  const int len = __builtin_amdgcn_readfirstlane((int)(t1 - t0));
   auto fetch = [&](int k, u32x4 (&rg)[LPW]) {
     const bf16 *tile = Xt + (t0 + 32 * (int64_t)k) * D;
-    if (32 * (int64_t)(k + 1) <= len) {
+    if (32 * (k + 1) <= len) {
 #pragma unroll
       for (int jj = 0; jj < LPW; ++jj) {
-        STCA_CHECK(32 * (int64_t)k + frow[jj] < len, kDbgAttendFetch);
+        STCA_CHECK(32 * k + frow[jj] < len, kDbgAttendFetch);
         rg[jj] = *reinterpret_cast<const u32x4 *>(tile + foff[jj]);
       }
     } else {  // partial last tile: rows past the end repeat the last row
-      const int rem = (int)(len - 32 * (int64_t)k);
+      const int rem = len - 32 * k;
 #pragma unroll
       for (int jj = 0; jj < LPW; ++jj) {
         const int back = frow[jj] < rem ? 0 : (frow[jj] - rem + 1) * D;
-        STCA_CHECK(rem > 0 && 32 * (int64_t)k + frow[jj] - back / D < len, kDbgAttendFetch);
+        STCA_CHECK(rem > 0 && 32 * k + frow[jj] - back / D < len, kDbgAttendFetch);
         rg[jj] = *reinterpret_cast<const u32x4 *>(tile + (foff[jj] - back));
       }
     }
@@ -940,7 +942,7 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
     }
   };
   auto mask = [&](int k, f32x4 (&sc)[2]) {
-    const int64_t remk = len - 32 * (int64_t)k;
+    const int remk = len - 32 * k;
     if (remk < 32) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -953,6 +955,10 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   // row, a multiple of 16 chunks, which the swizzle (low four bits of the chunk index) leaves alone.
   constexpr int SA = 3;
   const uint32_t hofs = (uint32_t)(fh * (D / FH) * 2);
+  // The feature half enters the PV bases once here: added per read, next to the slot offset, the
+  // compiler recomputed every transposed read's address (three vector instructions each).
+#pragma unroll
+  for (int m = 0; m < 8; ++m) pvb[m] += hofs;
   auto frag_at = [&](int k, int i) {
     const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
     const int ks = i >> 1, tb = i & 1;
@@ -977,8 +983,17 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   constexpr int PA = 3;
   auto pv = [&](int k, const bf16x8 &pb) {
     const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
+    // The eight lane bases of this tile's slot.  At d = 512 they are formed once per step (left to
+    // itself the compiler re-derived an address per read there); the feature-block offsets then fit
+    // the reads' immediates.  At d = 256 the compiler's own choice is as good and needs fewer registers.
+    uint32_t bs[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      bs[m] = pvb[m] + toff;
+      if constexpr (FH > 1) asm volatile("" : "+v"(bs[m]));
+    }
     auto xfrag = [&](int fb) {  // this wave's feature block fb: global block (NFBW fh + fb)
-      const uint32_t o = toff + pvb[fb & 7] + 256 * (fb >> 3) + hofs;
+      const uint32_t o = bs[fb & 7] + 256 * (fb >> 3);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + o));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((STCA_LDS s16x4 *)(lds + o + 16 * kRowBytes));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
