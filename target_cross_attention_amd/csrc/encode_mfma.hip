@@ -448,12 +448,23 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
 #pragma unroll
       for (int e = 0; e < 16; ++e) ga[tb][e] = acc[tb][e];
   };
+  // Up/gate products of one step outside the steady loop (every step at d = 512).  The fragment
+  // reads run UA ahead of their MFMAs in a pinned order, so LDS latency hides behind the MFMAs:
+  // left to itself the compiler reused one register for every fragment and waited for each read
+  // before its MFMA.
   auto up_all = [&](int b) {
+    constexpr int UA = kWide ? 6 : 3;  // at d = 512 a fragment feeds one MFMA, at d = 256 two
+    bf16x8 fr[UA + 1];
+#pragma unroll
+    for (int p = 0; p < UA && p < S::NKS; ++p) fr[p] = frag_at(uv_slot(b), uv_off + p * 1024u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < S::NKS; ++ks) {
-      const bf16x8 a = frag_at(uv_slot(b), uv_off + ks * 1024u);
+      if (ks + UA < S::NKS) fr[(ks + UA) % (UA + 1)] = frag_at(uv_slot(b), uv_off + (ks + UA) * 1024u);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) acc[tb] = mfma32x32x16(a, xb[tb][ks], ks == 0 ? f32x16{} : acc[tb]);
+      for (int tb = 0; tb < TB; ++tb)
+        acc[tb] = mfma32x32x16(fr[ks % (UA + 1)], xb[tb][ks], ks == 0 ? f32x16{} : acc[tb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto down_all = [&](int b) {
