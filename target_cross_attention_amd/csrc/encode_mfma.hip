@@ -504,31 +504,87 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         wo[1][ob] = base[(S::NOB + ob) * 64];
       }
     };
-    // The item's rows and first fragments landed before the barrier that ended the previous item.
-    load_next_gb();
-    up_all(0);
-    barrier_vm<0>();  // slot 0 is restaged in step 0
-    store_next_gb();
-    for (int t = 0; t < S_; ++t) {
-      const bool has_up = t + 1 < S_, has_down = t >= 1;
-      bf16x8 wo[2][S::NOBW];
-      if (has_down) load_wo(t - 1, wo);
-      if (t + 2 < S_) stage_uv(t + 2, t % 2);
-      if (has_down) swap_in(t - 1);
+    // Step t's W_o fragments (for the down product of its gated block, run in step t + 1) are
+    // loaded right after step t's own down product and stay in flight across the step's barrier,
+    // so they have the next step's up/gate product to land: issued at the start of the step that
+    // uses them, their L2 latency (about 1900 cycles, half of a step, in timestamp probes) was
+    // exposed every step.  The first and the last two steps are peeled off the loop, so that the
+    // loop body has no conditional loads: with them the compiler's count of loads in flight
+    // differed between paths and it waited for the W_o loads at the swap-buffer read.
+    // (S_ = r d / 32 >= 16 at d = 512.)
+    // The loads are spread over the MFMAs: one wave's 16 staging loads and 16 W_o loads of a step
+    // move 32 KiB through the CU's vector-memory path, and issued in bursts they stalled the wave
+    // (one per SIMD) with the matrix cores idle.  The staging loads of step t + 2 go out one after
+    // every second up/gate MFMA, each W_o pair right after the two down MFMAs that last read it.
+    constexpr int kWoLoads = 2 * S::NOBW;  // W_o loads per wave and step
+    static_assert(S::FUP % NW == 0 && 2 * LUV <= S::NKS, "one staging load per two up/gate MFMAs");
+    bf16x8 wo[2][S::NOBW];
+    auto up_stage = [&](int b, int t2, int sb) {
+      constexpr int UA = 6;
+      bf16x8 fr[UA + 1];
+#pragma unroll
+      for (int p = 0; p < UA; ++p) fr[p] = frag_at(uv_slot(b), uv_off + p * 1024u);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < S::NKS; ++ks) {
+        if (ks + UA < S::NKS) fr[(ks + UA) % (UA + 1)] = frag_at(uv_slot(b), uv_off + (ks + UA) * 1024u);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+          acc[tb] = mfma32x32x16(fr[ks % (UA + 1)], xb[tb][ks], ks == 0 ? f32x16{} : acc[tb]);
+        if (ks % 2 == 1 && ks / 2 < LUV) {
+          const int f = wave + NW * (ks / 2);
+          load_lds16(wrs, (STCA_LDS void *)(uv_slot(sb) + f * 1024), (uint32_t)(f * 64 + lane) * 16u,
+                     (uint32_t)t2 * SLOT);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto down_load = [&](int tn) {  // the down product, each fragment pair then reloaded for step tn
+      const bf16x8 *base = packed + ((int64_t)tn * S::FPS + S::FUP + S::NOBW * role) * 64 + lane;
+#pragma unroll
+      for (int ob = 0; ob < S::NOBW; ++ob) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) yacc[ob][tb] = mfma32x32x16(wo[0][ob], hb_prev[tb], yacc[ob][tb]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) yacc[ob][tb] = mfma32x32x16(wo[1][ob], hp[tb], yacc[ob][tb]);
+        wo[0][ob] = base[ob * 64];
+        wo[1][ob] = base[(S::NOB + ob) * 64];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto wide_step = [&](int t, auto DOWN, auto UP, auto STAGE) {
+      if constexpr (decltype(DOWN)::value) swap_in(t - 1);
       float ga[TB][16];
       copy_acc(ga);
-      if (has_up) up_all((t + 1) % 2);
-      if (has_down) down_regs(wo);
+      if constexpr (decltype(UP)::value) {
+        if constexpr (decltype(STAGE)::value)
+          up_stage((t + 1) % 2, t + 2, t % 2);
+        else
+          up_all((t + 1) % 2);
+      }
+      if constexpr (decltype(DOWN)::value)
+        down_load(t);
+      else
+        load_wo(t, wo);
       bf16x8 h[TB];
       gate_all(ga, h);
       swap_out(t, h);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
-      barrier_vm<0>();
-    }
+      barrier_vm<kWoLoads>();  // the W_o loads just issued may stay in flight
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+    // The item's rows and first fragments landed before the barrier that ended the previous item.
+    load_next_gb();
+    up_all(0);
+    barrier_vm<0>();  // slot 0 is restaged in step 0
+    store_next_gb();
+    wide_step(0, No{}, Yes{}, Yes{});
+    for (int t = 1; t + 2 < S_; ++t) wide_step(t, Yes{}, Yes{}, Yes{});
+    wide_step(S_ - 2, Yes{}, Yes{}, No{});
+    wide_step(S_ - 1, Yes{}, No{}, No{});
     swap_in(S_ - 1);
-    bf16x8 wo[2][S::NOBW];
-    load_wo(S_ - 1, wo);
     prefetch_next();
     down_regs(wo);
   } else {
