@@ -659,7 +659,15 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       constexpr int T3 = decltype(T3c)::value;
       constexpr int BU = (T3 + 1) % 3, BD = (T3 + 2) % 3;
       const bool stage = t + 3 < S_;  // the last steps have nothing left to stage
-      if (stage) stage_uv(t + 3, T3);
+      // With kGO the up/gate staging loads are spread over the step's MFMAs (one per kSp MFMAs)
+      // rather than issued in a burst at its start; they only have to land before step t + 2.
+      // They are issued in every steady step: a step with nothing left to stage (t + 3 >= S_)
+      // copies the last step's fragments into its free slot (t % 3, not read again in this item;
+      // the next item's staging comes after the final step's full drain), so the compiler sees
+      // the same loads on every path and its waits for the W_o ring do not cover them.
+      constexpr int kMM = TB * S::NG, kSp = kMM / LUV;
+      if constexpr (!kGO)
+        if (stage) stage_uv(t + 3, T3);
       if constexpr (!kGO) stage_o(t + 1, BU);
       swap_in(t - 1);
       auto frag = [&](int g) -> bf16x8 {
@@ -678,9 +686,15 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         if (!(kGO && pair_is_down(p, S::FD))) ring[p] = frag(p);
       float hv[8 * TB];
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int kMM = TB * S::NG;
   #pragma unroll
       for (int k = 0; k < kMM; ++k) {
+        if constexpr (kGO)
+          if (k % kSp == kSp / 2 && k / kSp < LUV) {
+            const int f = wave + NW * (k / kSp);
+            if (S::FUP % NW == 0 || f < S::FUP)
+              load_lds16(wrs, (STCA_LDS void *)(uv_slot(T3) + f * 1024), (uint32_t)(f * 64 + lane) * 16u,
+                         (uint32_t)(stage ? t + 3 : S_ - 1) * SLOT);
+          }
         const int g = k / TB, tb = k % TB;
         if (tb == 0 && g + kAhead < S::NG && !(kGO && pair_is_down(g + kAhead, S::FD)))
           ring[(g + kAhead) % kRing] = frag(g + kAhead);
