@@ -602,17 +602,21 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)lo, (int)((uint32_t)(t * S::FPS + f) * 1024u), 0);
       return __builtin_bit_cast(bf16x8, v);
     };
-    auto down_go = [&](int t) {
-      bf16x8 wo[S::FD];
-#pragma unroll
-      for (int di = 0; di < S::FD; ++di) wo[di] = wo_frag(t, di);
+    bf16x8 wring[WR];
+    // Outside the steady steps the ring holds the first WR down fragments of the previous step (the
+    // step before refilled it); the other FD - WR are loaded at the start of the step, ahead of its
+    // up/gate product, and the last step loads all fragments of the final down product (ring and
+    // wfin) before its barrier.  Loaded right before their MFMAs, as before, their L2 latency was
+    // exposed twice per item (some 2k cycles of an 89k-cycle item in timestamp probes).
+    bf16x8 wfin[S::FD - WR];
+    auto down_ring = [&](const bf16x8 (&rest)[S::FD - WR]) {
 #pragma unroll
       for (int di = 0; di < S::FD; ++di)
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
-          yacc[di % S::NOBW][tb] = mfma32x32x16(wo[di], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[di % S::NOBW][tb]);
+          yacc[di % S::NOBW][tb] = mfma32x32x16(di < WR ? wring[di] : rest[di - WR],
+                                                di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[di % S::NOBW][tb]);
     };
-    bf16x8 wring[WR];
 
     // The item's rows and first fragments landed before the barrier that ended the previous item.
     read_x();
@@ -625,26 +629,41 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
 
     // Any step, plain order (first and last steps).
     auto general = [&](int t) {
-      const bool has_up = t + 1 < S_, has_down = t >= 1;
+      const bool has_up = t + 1 < S_, has_down = t >= 1, last = t + 1 == S_;
       if (t + 3 < S_) stage_uv(t + 3, t % 3);
       if constexpr (!kGO)
         if (t + 1 < S_) stage_o(t + 1, (t + 1) % 3);
+      bf16x8 rest[S::FD - WR];
+      if constexpr (kGO)
+        if (has_down)
+  #pragma unroll
+          for (int j = 0; j < S::FD - WR; ++j) rest[j] = wo_frag(t - 1, WR + j);
       if (has_down) swap_in(t - 1);
       float ga[TB][16];
       copy_acc(ga);
       if (has_up) up_all((t + 1) % 3);
       if (has_down) {
         if constexpr (kGO)
-          down_go(t - 1);
+          down_ring(rest);
         else
           down_all((t + 2) % 3);
       }
+      if constexpr (kGO)
+        if (last) {
+  #pragma unroll
+          for (int j = 0; j < WR; ++j) wring[j] = wo_frag(t, j);
+  #pragma unroll
+          for (int j = 0; j < S::FD - WR; ++j) wfin[j] = wo_frag(t, WR + j);
+        }
       bf16x8 h[TB];
       gate_all(ga, h);
       swap_out(t, h);
   #pragma unroll
       for (int tb = 0; tb < TB; ++tb) hb_prev[tb] = h[tb];
-      barrier_vm<0>();
+      if (kGO && last)
+        barrier_vm<S::FD>();  // the final down product's fragments may stay in flight
+      else
+        barrier_vm<0>();
       // The next step, if steady, finds its first WR down fragments in the ring.
       if constexpr (kGO)
         if (t + 1 < S_)
@@ -753,15 +772,8 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     // The down product of the last step remains.
     swap_in(S_ - 1);
     if constexpr (kGO) {
-      bf16x8 wo[S::FD];
-#pragma unroll
-      for (int di = 0; di < S::FD; ++di) wo[di] = wo_frag(S_ - 1, di);
       prefetch_next();
-#pragma unroll
-      for (int di = 0; di < S::FD; ++di)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-          yacc[di % S::NOBW][tb] = mfma32x32x16(wo[di], di < S::NOBW ? hb_prev[tb] : hp[tb], yacc[di % S::NOBW][tb]);
+      down_ring(wfin);
     } else {
       prefetch_next();
       down_all((S_ - 1) % 3);
