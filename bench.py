@@ -676,6 +676,18 @@ def main():
     att_bytes = (2.0 if bf16 else 4.0) * cfg.d * db.total_L
     att_flops = 4.0 * cfg.h * cfg.d * float((db.inp.L * db.inp.m).sum())
     att_traffic = measured_traffic(cfg.key, "attend", ["attend.hip", "device_common.hpp"])
+    # Which roof binds follows from the intensity, 2 m h FLOP per byte of X~ (m targets of h heads
+    # per user, averaged over the batch): below the ridge (peak FLOP/s over peak HBM bytes/s) the
+    # attention is HBM-bound and reported as a share of the HBM peak, above it as a share of the
+    # MFMA peak of its dtype (stress20k: 2 x 32 x 16 = 1024 FLOP/B against a 312 FLOP/B ridge).
+    att_mfma_peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    att_ridge = att_mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if att_flops / att_bytes > att_ridge:
+        att_bound, att_unit, att_peak = "mfma", "TFLOP/s", att_mfma_peak
+        att_achieved = att_flops / att_avg_s / 1e12
+    else:
+        att_bound, att_unit, att_peak = "hbm", "GB/s", PEAK_HBM_GBS
+        att_achieved = att_bytes / att_avg_s / 1e9
 
     # The attention reads the X~ that the encode wrote just before it; when one layer's X~ fits the
     # Infinity Cache it is read from there, not from HBM, and the GB/s figure is not an HBM fraction.
@@ -710,10 +722,15 @@ def main():
                      "algorithmic_flops_per_launch": enc_flops, "algorithmic_bytes_per_launch": enc_bytes,
                      "avg_launch_ms": enc_avg_s * 1e3, "launches": enc_n,
                      "layers_per_launch": layers_per_launch},
-        "attention_roofline": {"kernel": "split-L attention", "bound": "hbm",
-                               "achieved": att_bytes / att_avg_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": att_bytes / att_avg_s / 1e9 / PEAK_HBM_GBS, "traffic": att_traffic,
+        "attention_roofline": {"kernel": "split-L attention", "bound": att_bound,
+                               "achieved": att_achieved, "peak": att_peak, "unit": att_unit,
+                               "frac": att_achieved / att_peak, "traffic": att_traffic,
+                               "intensity_flop_per_byte": att_flops / att_bytes,
+                               "ridge_flop_per_byte": att_ridge,
+                               "hbm_gbs": att_bytes / att_avg_s / 1e9,
+                               "hbm_frac": att_bytes / att_avg_s / 1e9 / PEAK_HBM_GBS,
                                "mfma_tflops": att_flops / att_avg_s / 1e12,
+                               "mfma_frac": att_flops / att_avg_s / 1e12 / att_mfma_peak,
                                "avg_launch_ms": att_avg_s * 1e3, "launches": att_n,
                                "cache_resident": att_cache_resident,
                                "note": ("one layer's X~ fits the 256 MB Infinity Cache and is read from there "
