@@ -448,6 +448,68 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, cfetch_dir: s
     print("\n".join(lines))
 
 
+def bench_compare(a, cfg, dev):
+    """Whole forwards of the same inputs through several builds of the library in one process, the
+    builds taken in turn for `reps` rounds of `steps` forwards each (after `warmup` forwards), so that
+    clock and power drift fall on every build alike.  Reports per build the median and minimum ms per
+    forward, the median per-phase times and whether its Z equals the first build's bit for bit."""
+    import numpy as np
+    import torch
+
+    import stca_inputs as SI
+    from target_cross_attention_amd import binding as B
+
+    W = SI.make_weights(cfg)
+    inp = SI.make_inputs(cfg)
+    dw = B.DeviceWeights(W, cfg.dtype, dev)
+    db = B.DeviceBatch(inp, dev)
+    del inp.X
+    runs = []
+    for spec in a.compare:
+        label, _, path = spec.partition("=")
+        lib = B.load_library(path or label)
+        for el in (a.compare_encode_layers or [a.encode_layers]):
+            runs.append({"label": label, "lib": path or label, "encode_layers": el, "handle": lib,
+                         "ms": [], "phases": {}, "Z": None})
+    stream = torch.cuda.current_stream()
+    default_lib = B.LIB
+    try:
+        for rep in range(a.reps):
+            for r in runs:
+                B.LIB = r["handle"]
+                dims = B.dims_for(cfg, attn_chunk=a.attn_chunk, encode_layers=r["encode_layers"])
+                ws = B.workspace(B.forward_workspace_size(dims, db.c), dev)
+                Z = torch.empty((db.total_T, cfg.M, cfg.d), dtype=torch.float32, device=dev)
+                for _ in range(max(a.warmup, 1)):
+                    B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=stream)
+                prof = B.Profiler()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(a.steps):
+                    B.stca_forward(dims, dw, db, Z=Z, ws=ws, stream=stream, profiler=prof)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                r["ms"].append(e0.elapsed_time(e1) / a.steps)
+                for k, (ms, _) in prof.read().items():
+                    r["phases"].setdefault(k, []).append(ms / a.steps)
+                prof.close()
+                if r["Z"] is None:
+                    r["Z"] = Z.clone()
+                del ws, Z
+                log(f"round {rep} {r['label']} encode_layers={r['encode_layers']}: {r['ms'][-1]:.3f} ms per forward")
+    finally:
+        B.LIB = default_lib
+    ref = runs[0]["Z"]
+    out = {"compare": cfg.key, "workload": cfg.description, "rounds": a.reps, "forwards_per_round": a.steps,
+           "results": [{"label": r["label"], "lib": r["lib"], "encode_layers": r["encode_layers"],
+                        "ms_per_forward_median": float(np.median(r["ms"])), "ms_per_forward_min": float(min(r["ms"])),
+                        "ms_per_forward": [round(x, 3) for x in r["ms"]],
+                        "phase_ms_median": {k: round(float(np.median(v)), 4) for k, v in r["phases"].items()
+                                            if np.median(v) > 0},
+                        "bitwise_equal_to_first": bool(torch.equal(r["Z"], ref))} for r in runs]}
+    print(json.dumps(out))
+
+
 def bench_vendor_gemm(a, dev):
     """torch.matmul (hipBLASLt) bf16 GEMMs at the encode's shapes for the workload (1 Mi history
     rows: up and gate as one [rows x d] x [d x 2rd] product, the down product [rows x rd] x [rd x d])
@@ -532,6 +594,12 @@ def main():
                                                            "CALIB_WRITE_DIR"),
                     help="summarise four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of this workload's "
                          "bench, then of --calib-copy) and record the traffic per launch; no GPU needed")
+    ap.add_argument("--compare", nargs="+", metavar="LABEL=LIB",
+                    help="same-process comparison of whole forwards across builds of the library (variants from "
+                         "build.py --define ... --out LIB), alternating between them; prints one JSON line")
+    ap.add_argument("--compare-encode-layers", nargs="+", type=int, choices=(0, 1, 2), default=None,
+                    help="with --compare: run every build at each of these encode_layers settings")
+    ap.add_argument("--reps", type=int, default=4, help="with --compare: rounds over the builds")
     a = ap.parse_args()
     if a.traffic_summary:
         return traffic_summary(a.workload, *a.traffic_summary)
@@ -572,6 +640,8 @@ def main():
         return bench_litm(a, cfg, dev)
     if a.backward:
         return bench_backward(a, cfg, dev)
+    if a.compare:
+        return bench_compare(a, cfg, dev)
     t = time.perf_counter()
     W = SI.make_weights(cfg)
     inp = SI.make_inputs(cfg)

@@ -81,14 +81,15 @@ class StcaError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)} ({status}): {last_error()}")
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libstca.so not built at {LIB_PATH}; run `python -m target_cross_attention_amd.build`")
+def _load(path: str | None = None) -> ctypes.CDLL:
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"libstca.so not built at {path}; run `python -m target_cross_attention_amd.build`")
     # PyTorch ships its own HIP runtime (same soname, libamdhip64.so.7).  Loading it first makes
     # the dynamic loader bind libstca to that one copy, so device memory and streams created by
     # torch are valid in libstca's calls; loading libstca first would bring in a second runtime.
     import torch  # noqa: F401
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = c_void_p
     sig = {
         "stca_encode_workspace_size": [P, c_int64, POINTER(c_size_t)],
@@ -132,6 +133,13 @@ def _load() -> ctypes.CDLL:
 
 
 LIB = _load()
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Another build of the same library (a variant built with `build.py --define ... --out path`),
+    with the same signatures.  The module's calls go to `LIB`; a caller that compares builds in one
+    process assigns the handle to `LIB` around its calls."""
+    return _load(path)
 
 
 def status_string(status: int) -> str:

@@ -4,6 +4,9 @@
     python -m target_cross_attention_amd.build --asm    # also write gfx950 assembly next to the objects
     python -m target_cross_attention_amd.build --debug-bounds   # libstca_debug.so: kernels check their
                                                                 # ragged indices (STCA_DEBUG_BOUNDS)
+    python -m target_cross_attention_amd.build --define STCA_ENC_STAGGER=0 --out /tmp/libstca_st0.so
+        # a variant build with compile-time tuning macros set, for same-process comparisons
+        # (bench.py --compare)
 """
 from __future__ import annotations
 
@@ -39,10 +42,12 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, asm: bool, debug_bounds: bool = False) -> str:
-    bdir = BUILD_DEBUG if debug_bounds else BUILD
+def _compile(src: str, asm: bool, debug_bounds: bool = False, bdir: str | None = None,
+             defines: tuple[str, ...] = ()) -> str:
+    bdir = bdir or (BUILD_DEBUG if debug_bounds else BUILD)
     obj = os.path.join(bdir, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *FLAGS, *(["-DSTCA_DEBUG_BOUNDS"] if debug_bounds else []), "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *(["-DSTCA_DEBUG_BOUNDS"] if debug_bounds else []), *[f"-D{d}" for d in defines],
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -53,13 +58,23 @@ def _compile(src: str, asm: bool, debug_bounds: bool = False) -> str:
     return obj
 
 
-def build(asm: bool = False, jobs: int | None = None, debug_bounds: bool = False) -> str:
-    out = LIB_DEBUG if debug_bounds else LIB
-    os.makedirs(BUILD_DEBUG if debug_bounds else BUILD, exist_ok=True)
+def build(asm: bool = False, jobs: int | None = None, debug_bounds: bool = False,
+          defines: tuple[str, ...] = (), out: str | None = None) -> str:
+    """Compile every source and link.  With `defines` (NAME=VALUE macros, e.g. the encode's
+    STCA_ENC_* tuning constants) the objects go to a build folder of their own and the library to
+    `out`, so that a variant never replaces libstca.so."""
+    if defines and not out:
+        raise ValueError("a build with --define needs --out")
+    bdir = BUILD_DEBUG if debug_bounds else BUILD
+    if defines:
+        bdir = os.path.join(PKG, "_build_variant", os.path.splitext(os.path.basename(out))[0])
+    out = out or (LIB_DEBUG if debug_bounds else LIB)
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm and not debug_bounds, debug_bounds), srcs))
+        objs = list(ex.map(lambda s: _compile(s, asm and not debug_bounds and not defines, debug_bounds, bdir,
+                                              tuple(defines)), srcs))
     tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,6 +88,9 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", action="store_true")
     ap.add_argument("--debug-bounds", action="store_true")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="compile-time macro for a variant build (repeatable; needs --out)")
+    ap.add_argument("--out", default=None, help="library path of a variant build")
     a = ap.parse_args()
-    print(build(asm=a.asm, debug_bounds=a.debug_bounds))
+    print(build(asm=a.asm, debug_bounds=a.debug_bounds, defines=tuple(a.define), out=a.out))
     sys.exit(0)

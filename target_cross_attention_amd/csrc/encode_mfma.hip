@@ -129,8 +129,13 @@ template <int D> struct PairShape {
 __host__ __device__ constexpr bool pair_is_down(int g, int fd) { return (g % 3) == 2 && (g / 3) < fd; }
 __host__ __device__ constexpr int pair_up_idx(int g, int fd) { return g - (g / 3 < fd ? (g + 1) / 3 : fd); }
 
+// LDS fragment ring of the steady steps (reads run STCA_ENC_RING - 1 groups ahead of their MFMAs):
+// at TB = 2 a fragment feeds two MFMAs and one group ahead covers the LDS latency; TB = 1 keeps four.
 #ifndef STCA_ENC_RING
-#define STCA_ENC_RING 4
+#define STCA_ENC_RING 2
+#endif
+#ifndef STCA_ENC_RING_SMALL
+#define STCA_ENC_RING_SMALL 4
 #endif
 // 32-token blocks per wave at d = 256 and at smaller d.
 #ifndef STCA_ENC_TB
@@ -149,10 +154,11 @@ __host__ __device__ constexpr int pair_up_idx(int g, int fd) { return g - (g / 3
 // TB = 32-token blocks per wave: TB = 2 gives 4 waves of up to 512 registers (one per SIMD), TB = 1
 // gives 8 waves of up to 256 registers (two per SIMD); either way a workgroup covers 128 tokens.
 // At d = 256 TB = 2 reads half as many fragment bytes per MFMA, which saves power: the kernel runs
-// at the chip's power limit, and TB = 2 measured ~1.5% faster than TB = 1 there, slower at d = 128.
+// at the chip's power limit, and with the step schedule below TB = 2 measures 8-9% faster than
+// TB = 1 there (whole forwards); at d = 128 TB = 1 was the faster one when last compared.
 // At d = 512 (wide) a step of weights is 96 KiB: only the up/gate part goes through LDS (two
-// slots), each wave reads its W_o fragments from L2 into registers at the start of the step, and
-// the workgroup is 4 waves of one 32-token block (64 tokens), one wave per SIMD.
+// slots), each wave reads its W_o fragments from L2 into registers one step ahead of their use,
+// and the workgroup is 4 waves of one 32-token block (64 tokens), one wave per SIMD.
 template <int D, int TB> struct PairLaunch {
   static constexpr bool kWide = D > 256;
   static constexpr int NW = kWide ? 4 : 8 / TB;            // waves per workgroup
@@ -177,7 +183,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   // wait uses the smallest per-wave count, which waits for at least all loads of older steps.
   constexpr int LUV = (S::FUP + NW - 1) / NW, LO = (S::FDN + NW - 1) / NW;
   constexpr int kStepLoads = kGO ? S::FD / 2 : S::FUP / NW + S::FDN / NW;
-  constexpr int kRing = STCA_ENC_RING, kAhead = STCA_ENC_RING - 1;  // fragment groups in flight
+  constexpr int kRing = TB == 2 ? STCA_ENC_RING : STCA_ENC_RING_SMALL, kAhead = kRing - 1;  // groups in flight
   constexpr uint32_t SLOT = S::FPS * 1024u;                          // bytes of one ring slot
   // Weight ring: slot b holds the up/gate fragments of one step (uvN) and the down fragments of
   // another (oN), see the step schedule below.  Every part is an array of its own so that the
