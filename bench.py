@@ -380,6 +380,20 @@ TRAFFIC_KERNELS = {"encode": (("encode_",), ["encode_mfma.hip", "device_common.h
                    "attend": (("attend_mfma_kernel", "attend16_kernel"), ["attend.hip", "device_common.hpp"])}
 
 
+def attention_roof(flops: float, nbytes: float, seconds: float, bf16: bool):
+    """The roof that binds one attention launch: (bound, unit, peak, achieved, ridge, mfma peak).
+
+    The intensity is 2 m h FLOP per byte of X~ (m targets of h heads per user, averaged over the
+    batch).  Below the ridge, peak FLOP/s over peak HBM bytes/s, the launch is HBM-bound and priced
+    against the HBM peak; above it against the MFMA peak of its dtype (stress20k: 2 x 32 x 16 =
+    1024 FLOP/B against a 312.5 FLOP/B bf16 ridge)."""
+    mfma_peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / nbytes > ridge:
+        return "mfma", "TFLOP/s", mfma_peak, flops / seconds / 1e12, ridge, mfma_peak
+    return "hbm", "GB/s", PEAK_HBM_GBS, nbytes / seconds / 1e9, ridge, mfma_peak
+
+
 def _counter_rows(d: str, counter: str):
     """(kernel name, value) per dispatch from a rocprofv3 --pmc run's counter_collection.csv under d."""
     import csv
@@ -746,18 +760,8 @@ def main():
     att_bytes = (2.0 if bf16 else 4.0) * cfg.d * db.total_L
     att_flops = 4.0 * cfg.h * cfg.d * float((db.inp.L * db.inp.m).sum())
     att_traffic = measured_traffic(cfg.key, "attend", ["attend.hip", "device_common.hpp"])
-    # Which roof binds follows from the intensity, 2 m h FLOP per byte of X~ (m targets of h heads
-    # per user, averaged over the batch): below the ridge (peak FLOP/s over peak HBM bytes/s) the
-    # attention is HBM-bound and reported as a share of the HBM peak, above it as a share of the
-    # MFMA peak of its dtype (stress20k: 2 x 32 x 16 = 1024 FLOP/B against a 312 FLOP/B ridge).
-    att_mfma_peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    att_ridge = att_mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if att_flops / att_bytes > att_ridge:
-        att_bound, att_unit, att_peak = "mfma", "TFLOP/s", att_mfma_peak
-        att_achieved = att_flops / att_avg_s / 1e12
-    else:
-        att_bound, att_unit, att_peak = "hbm", "GB/s", PEAK_HBM_GBS
-        att_achieved = att_bytes / att_avg_s / 1e9
+    att_bound, att_unit, att_peak, att_achieved, att_ridge, att_mfma_peak = attention_roof(
+        att_flops, att_bytes, att_avg_s, bf16)
 
     # The attention reads the X~ that the encode wrote just before it; when one layer's X~ fits the
     # Infinity Cache it is read from there, not from HBM, and the GB/s figure is not an HBM fraction.

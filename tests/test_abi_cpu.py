@@ -343,6 +343,34 @@ def test_bench_metric_names_the_workload():
         assert key in m and "L=10k" not in m
 
 
+def test_bench_attention_roof_follows_the_intensity():
+    """The attention is priced against HBM below the ridge (2500 TFLOP/s over 8000 GB/s = 312.5 FLOP/B)
+    and against the MFMA peak above it; the intensity of a workload is 2 m h FLOP per byte of X~."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    d, L = 256, 1000
+    for m, h, bound in ((16, 8, "hbm"), (32, 16, "mfma"), (6, 8, "hbm")):
+        flops, nbytes = 4.0 * h * d * L * m, 2.0 * d * L
+        assert flops / nbytes == 2 * m * h
+        b, unit, peak, achieved, ridge, _ = bench.attention_roof(flops, nbytes, 1e-3, bf16=True)
+        assert ridge == 312.5 and b == bound
+        if bound == "hbm":
+            assert (unit, peak) == ("GB/s", bench.PEAK_HBM_GBS) and achieved == nbytes / 1e-3 / 1e9
+        else:
+            assert (unit, peak) == ("TFLOP/s", bench.PEAK_BF16_TFLOPS) and achieved == flops / 1e-3 / 1e12
+    # fp32 (4 bytes per element): the ridge is the fp32 peak over HBM, about 19.7 FLOP/B
+    b, _, peak, _, ridge, _ = bench.attention_roof(4.0 * 4 * 64 * 256 * 4, 4.0 * 64 * 256, 1e-3, bf16=False)
+    assert b == "hbm" and abs(ridge - 157.3 / 8) < 1e-9
+
+
+def test_variant_build_needs_an_output_path():
+    """A build with compile-time macros never replaces libstca.so: it is refused without --out."""
+    from target_cross_attention_amd import build as Bd
+    with pytest.raises(ValueError):
+        Bd.build(defines=("STCA_ENC_RING=3",))
+
+
 def test_forward_workspace_holds_every_layer_when_encodes_share_a_launch():
     """encode_layers = 2 (all history encodes in one launch) keeps M encoded buffers, 1 keeps one;
     automatic picks the single launch only where one layer's X~ exceeds 1 GiB at d <= 256."""
