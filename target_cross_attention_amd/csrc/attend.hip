@@ -790,6 +790,18 @@ __device__ __forceinline__ float quad_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Tuning constants of the 16-row kernel: staged tile sets per wave at d = 256 (even), score and PV
+// operand reads in flight ahead of their MFMAs.
+#ifndef STCA_ATT16_NB256
+#define STCA_ATT16_NB256 4
+#endif
+#ifndef STCA_ATT16_SA
+#define STCA_ATT16_SA 3
+#endif
+#ifndef STCA_ATT16_PA
+#define STCA_ATT16_PA 3
+#endif
+
 template <int D>
 __global__ __launch_bounds__(512, 1) void attend16_kernel(
     const WorkItem *__restrict__ items, const int32_t *__restrict__ n_items, const int64_t *__restrict__ hoff,
@@ -807,8 +819,9 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   // Register sets of staged tiles: NB tiles in flight from HBM per wave (four at d = 256, where the
   // staging takes 8 registers a set; two at d = 512, where the kernel is at 256 registers).  Even, so
   // that step k's score buffers sc2[k & 1] follow from its set index.
-  constexpr int NSL = 3, NB = D > 256 ? 2 : 4;
+  constexpr int NSL = 3, NB = D > 256 ? 2 : STCA_ATT16_NB256;
   static_assert(NB % 2 == 0, "score buffers alternate with the register sets");
+  static_assert(NB == 2 || NB == 4, "the step loop below is unrolled for two or four register sets");
   constexpr uint32_t kRowBytes = CPR * 16, kTileBytes = 32 * kRowBytes;
   static_assert(INSTR % 8 == 0, "tile loads split evenly over 8 waves");
   __shared__ bf16x8 tiles[NSL][32 * CPR];
@@ -953,7 +966,7 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   };
   // Score operand i = 2 ks + tb of tile k: this wave's half of d starts (D / FH) fh features into a
   // row, a multiple of 16 chunks, which the swizzle (low four bits of the chunk index) leaves alone.
-  constexpr int SA = 3;
+  constexpr int SA = STCA_ATT16_SA;
   const uint32_t hofs = (uint32_t)(fh * (D / FH) * 2);
   // The feature half enters the PV bases once here: added per read, next to the slot offset, the
   // compiler recomputed every transposed read's address (three vector instructions each).
@@ -980,7 +993,7 @@ __global__ __launch_bounds__(512, 1) void attend16_kernel(
   };
   // PV product of tile k: the transposed operands of feature block fb + PA are read while block fb
   // multiplies.
-  constexpr int PA = 3;
+  constexpr int PA = STCA_ATT16_PA;
   auto pv = [&](int k, const bf16x8 &pb) {
     const uint32_t toff = (uint32_t)((k % NSL) * kTileBytes);
     // The eight lane bases of this tile's slot.  At d = 512 they are formed once per step (left to

@@ -150,6 +150,14 @@ __host__ __device__ constexpr int pair_up_idx(int g, int fd) { return g - (g / 3
 #ifndef STCA_ENC_STAGGER
 #define STCA_ENC_STAGGER 24
 #endif
+// Up/gate fragment reads in flight ahead of their MFMAs outside the steady loop (every step at
+// d = 512, the first and last steps of an item at d = 256).
+#ifndef STCA_ENC_UA_WIDE
+#define STCA_ENC_UA_WIDE 6
+#endif
+#ifndef STCA_ENC_UA
+#define STCA_ENC_UA 3
+#endif
 
 // TB = 32-token blocks per wave: TB = 2 gives 4 waves of up to 512 registers (one per SIMD), TB = 1
 // gives 8 waves of up to 256 registers (two per SIMD); either way a workgroup covers 128 tokens.
@@ -459,7 +467,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   // left to itself the compiler reused one register for every fragment and waited for each read
   // before its MFMA.
   auto up_all = [&](int b) {
-    constexpr int UA = kWide ? 6 : 3;  // at d = 512 a fragment feeds one MFMA, at d = 256 two
+    constexpr int UA = kWide ? STCA_ENC_UA_WIDE : STCA_ENC_UA;  // d = 512: a fragment feeds one MFMA, d = 256 two
     bf16x8 fr[UA + 1];
 #pragma unroll
     for (int p = 0; p < UA && p < S::NKS; ++p) fr[p] = frag_at(uv_slot(b), uv_off + p * 1024u);
@@ -526,7 +534,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
     static_assert(S::FUP % NW == 0 && 2 * LUV <= S::NKS, "one staging load per two up/gate MFMAs");
     bf16x8 wo[2][S::NOBW];
     auto up_stage = [&](int b, int t2, int sb) {
-      constexpr int UA = 6;
+      constexpr int UA = STCA_ENC_UA_WIDE;
       bf16x8 fr[UA + 1];
 #pragma unroll
       for (int p = 0; p < UA; ++p) fr[p] = frag_at(uv_slot(b), uv_off + p * 1024u);
