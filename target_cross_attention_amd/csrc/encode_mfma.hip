@@ -158,6 +158,14 @@ __host__ __device__ constexpr int pair_up_idx(int g, int fd) { return g - (g / 3
 #ifndef STCA_ENC_UA
 #define STCA_ENC_UA 3
 #endif
+// Steady steps at d = 256: a gate element goes with every MFMA k with k % 3 == STCA_ENC_GATE_PH, a
+// staging load with every k with k % 6 == STCA_ENC_STAGE_PH.
+#ifndef STCA_ENC_GATE_PH
+#define STCA_ENC_GATE_PH 0
+#endif
+#ifndef STCA_ENC_STAGE_PH
+#define STCA_ENC_STAGE_PH 3
+#endif
 
 // TB = 32-token blocks per wave: TB = 2 gives 4 waves of up to 512 registers (one per SIMD), TB = 1
 // gives 8 waves of up to 256 registers (two per SIMD); either way a workgroup covers 128 tokens.
@@ -699,6 +707,9 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
       // the next item's staging comes after the final step's full drain), so the compiler sees
       // the same loads on every path and its waits for the W_o ring do not cover them.
       constexpr int kMM = TB * S::NG, kSp = kMM / LUV;
+      constexpr int kGP = TB == 2 ? STCA_ENC_GATE_PH : 0, kSP = TB == 2 ? STCA_ENC_STAGE_PH : kSp / 2;
+      static_assert(kGP >= 0 && kGP < 3 && kSP >= 0 && kSP < kSp, "gate and staging phases within their periods");
+      constexpr int kGates = (kMM - kGP + 2) / 3 < 8 * TB ? (kMM - kGP + 2) / 3 : 8 * TB;  // in the MFMA loop
       if constexpr (!kGO)
         if (stage) stage_uv(t + 3, T3);
       if constexpr (!kGO) stage_o(t + 1, BU);
@@ -722,7 +733,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
   #pragma unroll
       for (int k = 0; k < kMM; ++k) {
         if constexpr (kGO)
-          if (k % kSp == kSp / 2 && k / kSp < LUV) {
+          if (k % kSp == kSP && k / kSp < LUV) {
             const int f = wave + NW * (k / kSp);
             if (S::FUP % NW == 0 || f < S::FUP)
               load_lds16(wrs, (STCA_LDS void *)(uv_slot(T3) + f * 1024), (uint32_t)(f * 64 + lane) * 16u,
@@ -745,7 +756,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
           const int ui = pair_up_idx(g, S::FD);
           acc[tb] = mfma32x32x16(ring[g % kRing], xb[tb][ui], ui == 0 ? f32x16{} : acc[tb]);
         }
-        if (k % 3 == 0 && k / 3 < 8 * TB) {
+        if (k % 3 == kGP && k / 3 < 8 * TB) {
           const int e = k / 3;
           hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
           asm volatile("" : "+v"(hv[e]));
@@ -753,7 +764,7 @@ __global__ __launch_bounds__((64 * PairLaunch<D, TB>::NW), 1) void encode_pair_k
         __builtin_amdgcn_sched_barrier(0);
       }
   #pragma unroll
-      for (int e = (kMM + 2) / 3; e < 8 * TB; ++e) hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
+      for (int e = kGates; e < 8 * TB; ++e) hv[e] = swiglu_gate(ga[e >> 3][e & 7], ga[e >> 3][(e & 7) + 8]);
       bf16x8 h[TB];
   #pragma unroll
       for (int e = 0; e < 8 * TB; ++e) h[e >> 3][e & 7] = f32_to_bf16(hv[e]);
